@@ -1,0 +1,70 @@
+"""The synthetic workload has the shape the pages describe: a power-law firing
+law at the configured activation fraction, a predictor with recall near 0.95,
+and batch unions that densify as the closed form says."""
+import numpy as np
+import pytest
+
+import workload as wl
+
+
+@pytest.mark.parametrize("name,cap_count", [("tiny_f32", 25), ("opt6.7b_ffn", 264),
+                                            ("llama7b_gated_relu", 271), ("opt13b_batched", 223)])
+def test_firing_law(name, cap_count):
+    idx, sh = wl.CONFIGS[name]
+    rng = np.random.Generator(np.random.PCG64(wl.layer_seed(idx)))
+    p, rank = wl.firing_probabilities(sh.f, sh.rho, rng)
+    assert abs(p.mean() - sh.rho) < 1e-9
+    assert np.all(np.diff(p[np.argsort(rank)]) <= 0)        # decreasing in rank
+    assert int((p >= wl.P_CAP - 1e-12).sum()) == cap_count
+    assert sorted(rank.tolist()) == list(range(1, sh.f + 1))
+
+
+def test_stack_schedule():
+    Hs = [wl.stack_layer_shape(l).H for l in range(wl.STACK_LAYERS)]
+    assert Hs.count(512) == 16 and Hs.count(1024) == 16 and Hs.count(2048) == 16
+    rhos = [wl.stack_layer_shape(l).rho for l in range(wl.STACK_LAYERS)]
+    assert abs(rhos[0] - 0.03) < 1e-12 and abs(rhos[-1] - 0.15) < 1e-12
+
+
+def test_tiny_layer_statistics(orc):
+    """Empirical firing frequencies follow p_i; the predictor sees ~95% of the
+    true activations; the neuron table is the hotness order."""
+    L = wl.config_layer("tiny_f32")
+    x = wl.make_tokens(L.shape.d, 3000, 424242)
+    _, tm = orc.true_mask(L.w_up, x, b1=L.b1)
+    freq = tm.mean(axis=0)
+    assert abs(freq.mean() - L.shape.rho) < 0.01
+    # per-neuron binomial check (6 sigma, plus a small slack for fp rounding of b)
+    sd = np.sqrt(L.p * (1 - L.p) / x.shape[0])
+    assert np.all(np.abs(freq - L.p) < 6 * sd + 0.01)
+    _, _, act = orc.predict(L.p1, L.c1, L.p2, L.c2, x)
+    tp = (act & tm).sum()
+    recall = tp / tm.sum()
+    precision = tp / act.sum()
+    assert 0.93 < recall < 0.97, recall
+    assert precision > 0.9, precision
+    # hot-first table: stored slots in order of decreasing firing probability
+    assert np.all(np.diff(L.p[L.perm]) <= 0)
+
+
+def test_union_closed_form(orc):
+    """E|U|/f = mean_i[1 - (1 - p_i)^B] for independent tokens (checked on a
+    scaled-down layer with the batched workload's firing law)."""
+    _, sh = wl.CONFIGS["opt13b_batched"]
+    L = wl.make_layer(wl.scaled_shape(sh, 128, 2048, 64), 5)
+    B, nb = 16, 40
+    x = wl.make_tokens(128, B * nb, 77)
+    _, tm = orc.true_mask(L.w_up, x, b1=L.b1)
+    fr = np.mean([orc.union(tm[i * B:(i + 1) * B]).mean() for i in range(nb)])
+    expect = np.mean(1 - (1 - L.p) ** B)
+    assert abs(fr - expect) < 0.02, (fr, expect)
+    fr1 = tm.mean()
+    assert abs(fr1 - sh.rho) < 0.01
+
+
+def test_generator_is_deterministic():
+    a = wl.make_layer(wl.LayerShape(64, 256, 32, 0.1, "f16"), 9)
+    b = wl.make_layer(wl.LayerShape(64, 256, 32, 0.1, "f16"), 9)
+    for k in ("w_up", "w_down", "b1", "b2", "p1", "p2", "c2", "perm"):
+        assert np.array_equal(getattr(a, k), getattr(b, k))
+    assert a.w_up.dtype == np.float16 and a.b1.dtype == np.float32
