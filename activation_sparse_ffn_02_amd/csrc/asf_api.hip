@@ -1,0 +1,223 @@
+// asf_api.hip -- host side of the C ABI declared in include/asf.h: argument
+// validation, carving of the caller's storage, the create-time layout pass
+// (hot-first permutation of neuron rows, neuron-major down projection) and
+// launch sequencing.  No device memory is allocated here.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+
+#include "asf_internal.h"
+
+namespace asf {
+
+static inline uintptr_t align_up(uintptr_t v, uintptr_t a) { return (v + a - 1) & ~(a - 1); }
+
+static bool desc_ok(const asf_layer_desc &d) {
+    if (d.d_model <= 0 || d.d_ffn <= 0 || d.pred_hidden <= 0) return false;
+    if (d.max_batch < 1 || d.max_batch > kMaxBatch) return false;
+    if (d.d_ffn > kMaxFfn) return false;
+    if (d.gated != 0 && d.gated != 1) return false;
+    if (d.wtype != ASF_F32 && d.wtype != ASF_F16) return false;
+    const int ws = d.wtype == ASF_F16 ? 2 : 4;
+    if ((d.d_model * ws) % 16 != 0 || (d.pred_hidden * ws) % 16 != 0) return false;
+    // register tiling limits: 16 chunks per lane in pred_l1, 4 in pred_l2,
+    // 2 per thread in the FFN kernel
+    const int cd = d.d_model * ws / 16, ch = d.pred_hidden * ws / 16;
+    if (cd > 1024 || ch > 256) return false;
+    return true;
+}
+
+size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v) {
+    const int ws = desc.wtype == ASF_F16 ? 2 : 4;
+    const size_t d = desc.d_model, f = desc.d_ffn, H = desc.pred_hidden, Bm = desc.max_batch;
+    const int nmat = desc.gated ? 3 : 2;
+    const size_t words = (f + 63) / 64;
+    uintptr_t p = align_up(base, 256);
+    auto take = [&](size_t bytes) {
+        uintptr_t q = p;
+        p = align_up(p + bytes, 256);
+        return q;
+    };
+    LayerView t;
+    t.d = (int)d;
+    t.f = (int)f;
+    t.H = (int)H;
+    t.max_batch = (int)Bm;
+    t.gated = desc.gated;
+    t.wtype = desc.wtype;
+    t.threshold = desc.threshold;
+    t.ws = ws;
+    t.cd = (int)(d * ws / 16);
+    t.ch = (int)(H * ws / 16);
+    t.words = (int)words;
+    t.nmat = nmat;
+    t.p1 = (void *)take(H * d * ws);
+    t.c1 = (float *)take(H * 4);
+    t.p2 = (void *)take(f * H * ws);
+    t.c2 = (float *)take(f * 4);
+    t.bundles = (void *)take(f * nmat * d * ws);
+    t.b1 = (float *)take(f * 4);
+    t.b2 = (float *)take(d * 4);
+    t.perm = (int32_t *)take(f * 4);
+    t.inv = (int32_t *)take(f * 4);
+    t.h = (float *)take(Bm * H * 4);
+    t.masks = (uint64_t *)take(Bm * words * 8);
+    t.umask = (uint64_t *)take(words * 8);
+    t.slots = (int32_t *)take(f * 4);
+    t.count = (int32_t *)take(64);
+    t.partial = (float *)take((size_t)kFfnGroups * Bm * d * 4);
+    if (v) *v = t;
+    return (size_t)(p - align_up(base, 256));
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace asf
+
+using namespace asf;
+
+extern "C" {
+
+const char *asf_version(void) { return "asf 0.1 (gfx950)"; }
+
+const char *asf_status_string(asf_status s) {
+    switch (s) {
+    case ASF_OK: return "ok";
+    case ASF_ERR_ARG: return "invalid argument";
+    case ASF_ERR_SHAPE: return "unsupported shape";
+    case ASF_ERR_ALIGN: return "misaligned pointer or row length";
+    case ASF_ERR_STORAGE: return "storage too small";
+    case ASF_ERR_UNSUPPORTED: return "unsupported combination";
+    case ASF_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t asf_layer_storage_bytes(const asf_layer_desc *desc) {
+    if (!desc || !desc_ok(*desc)) return 0;
+    return carve(*desc, 0, nullptr) + 256;  // slack for aligning an unaligned base
+}
+
+asf_status asf_create_layer(const asf_layer_desc *desc, const asf_layer_weights *w,
+                            const int32_t *neuron_table, void *storage, size_t storage_bytes,
+                            void *stream, asf_layer **out) {
+    if (out) *out = nullptr;
+    if (!desc || !w || !storage || !out) return ASF_ERR_ARG;
+    if (desc->d_model <= 0 || desc->d_ffn <= 0 || desc->pred_hidden <= 0 ||
+        desc->max_batch <= 0 || (desc->gated != 0 && desc->gated != 1) ||
+        (desc->wtype != ASF_F32 && desc->wtype != ASF_F16))
+        return ASF_ERR_ARG;
+    {
+        const int ws = desc->wtype == ASF_F16 ? 2 : 4;
+        if ((desc->d_model * ws) % 16 != 0 || (desc->pred_hidden * ws) % 16 != 0)
+            return ASF_ERR_ALIGN;
+    }
+    if (!desc_ok(*desc)) return ASF_ERR_SHAPE;
+    if (!w->w_up || !w->w_down || !w->p1 || !w->p2) return ASF_ERR_ARG;
+    if (desc->gated ? !w->w_gate : w->w_gate != nullptr) return ASF_ERR_UNSUPPORTED;
+    if (!aligned16(w->w_up) || !aligned16(w->w_down) || !aligned16(w->p1) || !aligned16(w->p2) ||
+        (w->w_gate && !aligned16(w->w_gate)) || !aligned16(storage))
+        return ASF_ERR_ALIGN;
+    if (storage_bytes < asf_layer_storage_bytes(desc)) return ASF_ERR_STORAGE;
+
+    asf_layer *L = new (std::nothrow) asf_layer;
+    if (!L) return ASF_ERR_ARG;
+    carve(*desc, (uintptr_t)storage, &L->v);
+    LayerView &v = L->v;
+    hipStream_t s = (hipStream_t)stream;
+    const int ws = v.ws, d = v.d, f = v.f, H = v.H;
+    hipError_t e = hipSuccess;
+    auto chk = [&](hipError_t r) {
+        if (e == hipSuccess && r != hipSuccess) e = r;
+    };
+    // neuron table and its inverse
+    if (neuron_table)
+        chk(hipMemcpyAsync(v.perm, neuron_table, (size_t)f * 4, hipMemcpyDeviceToDevice, s));
+    else
+        chk(launch_invert(nullptr, f, v.perm, s));  // identity table
+    chk(launch_invert(v.perm, f, v.inv, s));
+    // predictor: layer 1 as given, layer 2 rows and bias in slot order
+    chk(hipMemcpyAsync(v.p1, w->p1, (size_t)H * d * ws, hipMemcpyDeviceToDevice, s));
+    chk(launch_gather_f32(w->c1, nullptr, H, v.c1, s));
+    chk(launch_perm_rows(w->p2, v.ch, v.perm, f, v.p2, v.ch, 0, s));
+    chk(launch_gather_f32(w->c2, v.perm, f, v.c2, s));
+    // neuron bundles: [gate,] up row, down column (W_down transposed), slot order
+    const size_t bstride_chunks = (size_t)v.nmat * v.cd;
+    const int up_idx = v.gated ? 1 : 0, dn_idx = v.nmat - 1;
+    if (v.gated) chk(launch_perm_rows(w->w_gate, v.cd, v.perm, f, v.bundles, bstride_chunks, 0, s));
+    chk(launch_perm_rows(w->w_up, v.cd, v.perm, f, v.bundles, bstride_chunks,
+                         (size_t)up_idx * v.cd, s));
+    chk(launch_transpose_perm(w->w_down, d, f, ws, v.inv, v.bundles, (size_t)v.nmat * d,
+                              (size_t)dn_idx * d, s));
+    chk(launch_gather_f32(w->b1, v.perm, f, v.b1, s));
+    chk(launch_gather_f32(w->b2, nullptr, d, v.b2, s));
+    if (e != hipSuccess) {
+        delete L;
+        return ASF_ERR_HIP;
+    }
+    *out = L;
+    return ASF_OK;
+}
+
+void asf_destroy_layer(asf_layer *layer) { delete layer; }
+
+static asf_status check_call(const asf_layer *layer, const float *x, int32_t B) {
+    if (!layer || !x) return ASF_ERR_ARG;
+    if (B < 1 || B > layer->v.max_batch) return ASF_ERR_SHAPE;
+    if (!aligned16(x)) return ASF_ERR_ALIGN;
+    return ASF_OK;
+}
+
+asf_status asf_predict(const asf_layer *layer, const float *x, int32_t B, int32_t *active,
+                       int32_t *n_active, uint64_t *token_masks, void *stream) {
+    asf_status st = check_call(layer, x, B);
+    if (st != ASF_OK) return st;
+    if (launch_predict(layer->v, x, B, active, n_active, token_masks, (hipStream_t)stream) !=
+        hipSuccess)
+        return ASF_ERR_HIP;
+    return ASF_OK;
+}
+
+asf_status asf_sparse_ffn(const asf_layer *layer, const float *x, int32_t B,
+                          const int32_t *active, const int32_t *n_active, const float *residual,
+                          float *y, void *stream) {
+    asf_status st = check_call(layer, x, B);
+    if (st != ASF_OK) return st;
+    if (!y || (active && !n_active)) return ASF_ERR_ARG;
+    if (!aligned16(y) || (residual && !aligned16(residual))) return ASF_ERR_ALIGN;
+    if (launch_ffn(layer->v, x, B, active ? 1 : 0, active, n_active, residual, y,
+                   (hipStream_t)stream) != hipSuccess)
+        return ASF_ERR_HIP;
+    return ASF_OK;
+}
+
+asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
+                           const float *residual, float *y, int32_t *active, int32_t *n_active,
+                           void *stream) {
+    asf_status st = check_call(layer, x, B);
+    if (st != ASF_OK) return st;
+    if (!y) return ASF_ERR_ARG;
+    if (!aligned16(y) || (residual && !aligned16(residual))) return ASF_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (launch_predict(layer->v, x, B, active, n_active, nullptr, s) != hipSuccess)
+        return ASF_ERR_HIP;
+    if (launch_ffn(layer->v, x, B, 0, nullptr, nullptr, residual, y, s) != hipSuccess)
+        return ASF_ERR_HIP;
+    return ASF_OK;
+}
+
+asf_status asf_dense_ffn_ref(const asf_layer *layer, const float *x, int32_t B,
+                             const float *residual, float *y, void *stream) {
+    asf_status st = check_call(layer, x, B);
+    if (st != ASF_OK) return st;
+    if (!y) return ASF_ERR_ARG;
+    if (!aligned16(y) || (residual && !aligned16(residual))) return ASF_ERR_ALIGN;
+    if (launch_ffn(layer->v, x, B, 2, nullptr, nullptr, residual, y, (hipStream_t)stream) !=
+        hipSuccess)
+        return ASF_ERR_HIP;
+    return ASF_OK;
+}
+
+}  // extern "C"

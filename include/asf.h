@@ -1,0 +1,193 @@
+/*
+ * asf.h -- C ABI of the activation-sparse FFN decode library (libasf.so),
+ * hand-written HIP for gfx950 (MI355X).
+ *
+ * The calls follow the problem statement of the pages:
+ *   1. load a layer's weights and its predictor, arranged through a neuron
+ *      table that maps each stored neuron to its original position
+ *      ("LLM模型之PowerInfer1.0" §4.2; "PowerInfer: Nhanh Large Language Model
+ *      với GPU Tiêu dùng", section "Đặt vị trí và Quản lý Nơ-ron");
+ *   2. predict which neurons the current input activates with a two-layer
+ *      X-H-O MLP ("LLM模型之PowerInfer1.0" §1 and appendix "DejaVu");
+ *   3. compute only those neurons: FC1 as a dot product with each active
+ *      neuron row, FC2 as an AXPY over the matching contiguous columns of the
+ *      down projection ("LLM模型之PowerInfer1.0" §2.1 Fig. 1, §4.4 and "其他"
+ *      question 3);
+ *   4. the dense FFN over all neurons as the comparison ("Técnicas dispersas
+ *      para una aceleración 100X…", section "Viabilidad de la sparsidad de
+ *      activación").
+ *
+ * Memory and ownership
+ *   - Every tensor argument is a DEVICE pointer allocated by the caller; the
+ *     library allocates no device memory.  The only host-side allocation is
+ *     the small opaque asf_layer handle.
+ *   - asf_create_layer copies the weights into caller-provided `storage`
+ *     (size from asf_layer_storage_bytes) in the library's own layout; the
+ *     original weight buffers may be freed once the copy has run on `stream`.
+ *     `storage` must outlive the handle.  Per-call scratch (predictor hidden
+ *     vector, masks, active list, partial sums) also lives in `storage`, so a
+ *     layer serves one call at a time: calls on one layer must be ordered
+ *     (same stream, or synchronised).
+ *   - All calls are asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL means the default stream).  No call synchronises the device, and
+ *     the active count never travels to the host.
+ *
+ * Data types
+ *   Weights (FFN matrices and predictor matrices) are all ASF_F32 or all
+ *   ASF_F16 (IEEE binary16 bits).  Biases, x, h, y are float32.  Products are
+ *   accumulated in float32.
+ *
+ * Errors
+ *   Every call validates its arguments on the host and returns a status
+ *   without touching the device when they are invalid.  Launch failures are
+ *   reported as ASF_ERR_HIP.  Device-side faults surface at the caller's next
+ *   synchronisation.  No C++ exception crosses this ABI.  Neuron ids in a
+ *   caller-supplied active list that are out of range are skipped; duplicate
+ *   ids are the caller's error (they are counted twice).
+ */
+#ifndef ASF_H
+#define ASF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct asf_layer asf_layer; /* opaque host handle */
+
+typedef enum { ASF_F32 = 0, ASF_F16 = 1 } asf_dtype;
+
+typedef enum {
+    ASF_OK = 0,
+    ASF_ERR_ARG = 1,         /* null pointer or invalid scalar argument */
+    ASF_ERR_SHAPE = 2,       /* dimension out of the supported range */
+    ASF_ERR_ALIGN = 3,       /* pointer or row length not 16-byte aligned */
+    ASF_ERR_STORAGE = 4,     /* storage smaller than asf_layer_storage_bytes */
+    ASF_ERR_UNSUPPORTED = 5, /* valid but unsupported combination */
+    ASF_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed */
+} asf_status;
+
+/* Shape and numeric options of one FFN layer.
+ *   d_model      input/output width d (rows of W_down, columns of W_up)
+ *   d_ffn        number of FFN neurons f (1 .. 65536)
+ *   pred_hidden  hidden size H of the X-H-O predictor
+ *   max_batch    largest B any call will use (1 .. 32)
+ *   gated        0: a_i = ReLU(W_up[i].x + b1_i)
+ *                1: a_i = ReLU(W_gate[i].x + b1_i) * (W_up[i].x)
+ *                   (ReLU in place of SiLU on the gate; the gate decides the
+ *                   true active set)
+ *   wtype        asf_dtype of every weight matrix
+ *   threshold    logit threshold theta: neuron i is predicted active when
+ *                its score s_i > theta (strict).  0 is the sigmoid-0.5
+ *                decision of the pages' per-output binary classifier.
+ * Alignment: d_model * sizeof(weight) and pred_hidden * sizeof(weight) must
+ * be multiples of 16 bytes (d_model % 8 == 0 for ASF_F16, % 4 for ASF_F32). */
+typedef struct {
+    int32_t d_model;
+    int32_t d_ffn;
+    int32_t pred_hidden;
+    int32_t max_batch;
+    int32_t gated;
+    int32_t wtype;
+    float threshold;
+} asf_layer_desc;
+
+/* Original weights, DEVICE pointers, row-major in nn.Linear layouts:
+ *   w_up, w_gate [d_ffn][d_model]  (w_gate only when gated, else NULL)
+ *   b1           [d_ffn] float32 or NULL (= 0); the gate bias when gated
+ *   w_down       [d_model][d_ffn]
+ *   b2           [d_model] float32 or NULL (= 0)
+ *   p1           [pred_hidden][d_model]     predictor layer 1
+ *   c1           [pred_hidden] float32 or NULL (= 0)
+ *   p2           [d_ffn][pred_hidden]       predictor layer 2
+ *   c2           [d_ffn] float32 or NULL (= 0)
+ * Matrices must be 16-byte aligned. */
+typedef struct {
+    const void *w_up;
+    const void *w_gate;
+    const float *b1;
+    const void *w_down;
+    const float *b2;
+    const void *p1;
+    const float *c1;
+    const void *p2;
+    const float *c2;
+} asf_layer_weights;
+
+/* Bytes of device storage a layer with this descriptor needs (weights in the
+ * library layout plus per-call scratch).  Returns 0 for an invalid desc. */
+size_t asf_layer_storage_bytes(const asf_layer_desc *desc);
+
+/* Copy a layer into `storage` in hot-first, neuron-major layout and return a
+ * handle.
+ *   neuron_table  DEVICE int32 [d_ffn]: neuron_table[slot] = original id of
+ *                 the neuron stored at `slot` (a permutation of 0..d_ffn-1;
+ *                 hot neurons first).  NULL = identity.  It is not checked
+ *                 on the device: a table that is not a permutation leaves
+ *                 the layer's content undefined (never out-of-bounds).
+ *   storage       DEVICE, 256-byte aligned, >= asf_layer_storage_bytes.
+ * The layout work runs asynchronously on `stream`; the handle is usable by
+ * later work on the same stream at once.  *out receives the handle, or NULL
+ * on error. */
+asf_status asf_create_layer(const asf_layer_desc *desc, const asf_layer_weights *w,
+                            const int32_t *neuron_table, void *storage,
+                            size_t storage_bytes, void *stream, asf_layer **out);
+
+/* Free the host handle (never the caller's storage).  NULL is a no-op. */
+void asf_destroy_layer(asf_layer *layer);
+
+/* Predict the active neurons of B tokens (X-H-O predictor, then threshold,
+ * then compaction of the union of the tokens' sets).
+ *   x            DEVICE float32 [B][d_model]
+ *   B            1 .. max_batch
+ *   active       DEVICE int32 [d_ffn] or NULL: receives the ORIGINAL ids of
+ *                the union of the B tokens' active sets, in ascending stored
+ *                (slot) order; entries past *n_active are left untouched
+ *   n_active     DEVICE int32 [1] or NULL: receives the count
+ *   token_masks  DEVICE uint64 [B][ceil(d_ffn/64)] or NULL: per-token
+ *                bitmasks in STORED (slot) order, bit (slot % 64) of word
+ *                (slot / 64)
+ * The union list is also kept in the layer's scratch, where asf_sparse_ffn
+ * with active == NULL reads it. */
+asf_status asf_predict(const asf_layer *layer, const float *x, int32_t B,
+                       int32_t *active, int32_t *n_active, uint64_t *token_masks,
+                       void *stream);
+
+/* FFN over a neuron set: y[b] = residual[b] + b2 + sum_{i in S} a_{b,i} W_down[:, i]
+ * with a_{b,i} the FC1 (gated) activation of neuron i for token b.
+ *   x         DEVICE float32 [B][d_model]
+ *   active    DEVICE int32 original ids (distinct, any order), or NULL to use
+ *             the set of this layer's last asf_predict call
+ *   n_active  DEVICE int32 [1] count of `active` (ignored when active == NULL;
+ *             required otherwise)
+ *   residual  DEVICE float32 [B][d_model] or NULL (= 0)
+ *   y         DEVICE float32 [B][d_model]; may alias residual
+ * For B > 1 every token computes every neuron of the set (the union of the
+ * batch's sets when the set comes from asf_predict). */
+asf_status asf_sparse_ffn(const asf_layer *layer, const float *x, int32_t B,
+                          const int32_t *active, const int32_t *n_active,
+                          const float *residual, float *y, void *stream);
+
+/* One decode step of one layer: asf_predict followed by asf_sparse_ffn over
+ * the predicted union set, with no host round trip in between.  The optional
+ * outputs are those of asf_predict. */
+asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
+                           const float *residual, float *y, int32_t *active,
+                           int32_t *n_active, void *stream);
+
+/* Dense comparator: the same FFN over all d_ffn neurons. */
+asf_status asf_dense_ffn_ref(const asf_layer *layer, const float *x, int32_t B,
+                             const float *residual, float *y, void *stream);
+
+/* Human-readable name of a status code (static string). */
+const char *asf_status_string(asf_status s);
+
+/* Library version string. */
+const char *asf_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ASF_H */

@@ -1,0 +1,103 @@
+"""The C-ABI library loads, exports every function include/asf.h declares, and
+its host-side validation rejects bad arguments without touching a device.
+No compute call is made here (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "asf.h")
+LIB = os.path.join(ROOT, "activation_sparse_ffn_02_amd", "libasf.so")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(asf_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def asf():
+    if not os.path.exists(LIB):
+        import activation_sparse_ffn_02_amd.build as b
+        b.build()
+    import activation_sparse_ffn_02_amd as m
+    return m
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("asf_layer_storage_bytes", "asf_create_layer", "asf_destroy_layer", "asf_predict",
+              "asf_sparse_ffn", "asf_dense_ffn_ref", "asf_decode_step", "asf_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(asf):
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_storage_bytes_validation(asf):
+    ok = asf.storage_bytes(4096, 16384, 1024, 1, False, asf.F16)
+    assert ok > 2 * 16384 * 4096 * 2 + 16384 * 1024 * 2
+    assert asf.storage_bytes(4096, 16384, 1024, 4, False, asf.F16) > ok       # scratch grows with B
+    assert asf.storage_bytes(4096, 16384, 1024, 1, True, asf.F16) > ok        # gate matrix
+    assert asf.storage_bytes(4096, 16385, 1024, 1, False, asf.F16) > ok       # ragged f
+    assert asf.storage_bytes(4100, 16384, 1024, 1, False, asf.F16) == 0       # d % 8 != 0
+    assert asf.storage_bytes(4096, 16384, 1020, 1, False, asf.F16) == 0       # H % 8 != 0
+    assert asf.storage_bytes(4092, 16384, 1024, 1, False, asf.F32) > 0        # fp32: d % 4
+    assert asf.storage_bytes(4096, 16384, 1024, 0, False, asf.F16) == 0       # B range
+    assert asf.storage_bytes(4096, 16384, 1024, 33, False, asf.F16) == 0
+    assert asf.storage_bytes(4096, 65537, 1024, 1, False, asf.F16) == 0       # f limit
+    assert asf.storage_bytes(16384, 1024, 64, 1, False, asf.F16) == 0         # d tiling limit
+    assert asf.storage_bytes(0, 1024, 64, 1, False, asf.F16) == 0
+
+
+def test_create_layer_host_validation(asf):
+    lib = asf.library()
+    desc = asf.make_desc(256, 1024, 64, 1, False, asf.F32)
+    fake = 1 << 20                         # never dereferenced: validation fails first
+    w = asf.LayerWeights(fake, None, None, fake, None, fake, None, fake, None)
+    out = ctypes.c_void_p(123)
+    need = lib.asf_layer_storage_bytes(ctypes.byref(desc))
+    st = lib.asf_create_layer(None, ctypes.byref(w), None, fake, need, None, ctypes.byref(out))
+    assert st == 1 and out.value is None
+    st = lib.asf_create_layer(ctypes.byref(desc), ctypes.byref(w), None, fake, need - 1, None,
+                              ctypes.byref(out))
+    assert st == 4                                            # ASF_ERR_STORAGE
+    st = lib.asf_create_layer(ctypes.byref(desc), ctypes.byref(w), None, fake + 4, need, None,
+                              ctypes.byref(out))
+    assert st == 3                                            # misaligned storage
+    w2 = asf.LayerWeights(fake + 8, None, None, fake, None, fake, None, fake, None)
+    st = lib.asf_create_layer(ctypes.byref(desc), ctypes.byref(w2), None, fake, need, None,
+                              ctypes.byref(out))
+    assert st == 3                                            # misaligned weight
+    gdesc = asf.make_desc(256, 1024, 64, 1, True, asf.F32)
+    st = lib.asf_create_layer(ctypes.byref(gdesc), ctypes.byref(w), None, fake,
+                              lib.asf_layer_storage_bytes(ctypes.byref(gdesc)), None,
+                              ctypes.byref(out))
+    assert st == 5                                            # gated without w_gate
+    bad = asf.make_desc(260, 1024, 64, 1, False, asf.F16)
+    st = lib.asf_create_layer(ctypes.byref(bad), ctypes.byref(w), None, fake, need, None,
+                              ctypes.byref(out))
+    assert st == 3                                            # d*2 not a multiple of 16
+    w3 = asf.LayerWeights(None, None, None, fake, None, fake, None, fake, None)
+    st = lib.asf_create_layer(ctypes.byref(desc), ctypes.byref(w3), None, fake, need, None,
+                              ctypes.byref(out))
+    assert st == 1
+
+
+def test_calls_reject_null_handle(asf):
+    lib = asf.library()
+    fake = 1 << 20
+    assert lib.asf_predict(None, fake, 1, None, None, None, None) == 1
+    assert lib.asf_sparse_ffn(None, fake, 1, None, None, None, fake, None) == 1
+    assert lib.asf_decode_step(None, fake, 1, None, fake, None, None, None) == 1
+    assert lib.asf_dense_ffn_ref(None, fake, 1, None, fake, None) == 1
+    lib.asf_destroy_layer(None)
+    assert lib.asf_status_string(0) == b"ok"
+    assert lib.asf_status_string(4) == b"storage too small"
+    assert asf.version().startswith("asf")

@@ -1,0 +1,223 @@
+"""GPU parity: the HIP path through the C ABI against the CPU fp64 oracle on
+the same seeded inputs.
+
+* Active sets: bit-exact on every neuron whose predictor margin exceeds 1e-3,
+  listed in ascending stored-slot order.
+* Outputs: per-token relative L2 <= 1e-3 (fp32 weights) / 5e-3 (fp16
+  weights, fp32 accumulate), against the oracle evaluated on the GPU's own
+  set, so set and output parity are checked separately.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workload as wl
+from gpu_util import MARGIN, TOL, asf, check_set, need_gpu, rel_l2, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_tokens(orc, L, x, layer, label, check_dense=True, theta=0.0):
+    """Per token: predict, decode_step, sparse_ffn on the GPU set, dense."""
+    tol = TOL[L.shape.wdtype]
+    f = L.shape.f
+    _, s_orc, _ = orc.predict(L.p1, L.c1, L.p2, L.c2, x, theta=theta)
+    dense_orc = orc.dense_ffn(L.w_up, L.w_down, x, b1=L.b1, b2=L.b2, W_gate=L.w_gate) \
+        if check_dense else None
+    amb = 0
+    worst = 0.0
+    for t in range(x.shape[0]):
+        xt = to_dev(x[t:t + 1])
+        active, n = layer.predict(xt)
+        y1 = layer.sparse_ffn(xt)
+        a2 = torch.empty_like(active)
+        n2 = torch.empty_like(n)
+        y2 = layer.decode_step(xt, active=a2, n_active=n2)
+        torch.cuda.synchronize()
+        k = int(n.item())
+        ids = active[:k].cpu().numpy()
+        assert int(n2.item()) == k and np.array_equal(a2[:k].cpu().numpy(), ids)
+        assert torch.equal(y1, y2), "decode_step differs from predict + sparse_ffn"
+        amb += check_set(ids, s_orc[t], theta, L.perm, "%s token %d" % (label, t))
+        y_orc = orc.ffn(L.w_up, L.w_down, x[t], ids, b1=L.b1, b2=L.b2, W_gate=L.w_gate)
+        e = rel_l2(y1.cpu().numpy()[0], y_orc[0])
+        worst = max(worst, e)
+        assert e <= tol, "%s token %d: rel-L2 %.3g > %.3g" % (label, t, e, tol)
+        if check_dense:
+            yd = layer.dense_ffn_ref(xt)
+            ed = rel_l2(yd.cpu().numpy()[0], dense_orc[t])
+            assert ed <= tol, "%s token %d dense: rel-L2 %.3g" % (label, t, ed)
+    print("%s: %d tokens, worst rel-L2 %.3g, ambiguous flips %d" % (label, x.shape[0], worst, amb))
+    return worst
+
+
+def test_tiny_fp32_full_config(orc):
+    """256x1024 fp32, predictor 256->64->1024, 64 decode tokens (full size)."""
+    need_gpu()
+    L = wl.config_layer("tiny_f32")
+    x = wl.config_tokens("tiny_f32", 64)
+    lay = asf().layer_from_numpy(L)
+    _run_tokens(orc, L, x, lay, "tiny_f32")
+
+
+@pytest.mark.parametrize("d,f,H", [(512, 2000, 128), (1024, 4160, 256), (256, 40, 64)])
+def test_scaled_fp16_ragged(orc, d, f, H):
+    """fp16 layers with the OPT-6.7B firing law at sizes that span several
+    workgroups and end in a ragged mask word."""
+    need_gpu()
+    _, sh = wl.CONFIGS["opt6.7b_ffn"]
+    L = wl.make_layer(wl.scaled_shape(sh, d, f, H), 31 + f)
+    x = wl.make_tokens(d, 6, 41 + f)
+    lay = asf().layer_from_numpy(L)
+    _run_tokens(orc, L, x, lay, "fp16 %dx%d H%d" % (d, f, H))
+
+
+def test_opt67_full_size(orc):
+    """The headline shape: 4096x16384 fp16, predictor 4096->1024->16384."""
+    need_gpu()
+    L = wl.config_layer("opt6.7b_ffn")
+    x = wl.config_tokens("opt6.7b_ffn", 4)
+    lay = asf().layer_from_numpy(L)
+    _run_tokens(orc, L, x, lay, "opt6.7b_ffn")
+
+
+def test_gated_scaled_and_full(orc):
+    need_gpu()
+    _, sh = wl.CONFIGS["llama7b_gated_relu"]
+    Ls = wl.make_layer(wl.scaled_shape(sh, 512, 1376, 128), 77)
+    xs = wl.make_tokens(512, 6, 78)
+    _run_tokens(orc, Ls, xs, asf().layer_from_numpy(Ls), "gated 512x1376")
+    L = wl.config_layer("llama7b_gated_relu")
+    x = wl.config_tokens("llama7b_gated_relu", 3)
+    _run_tokens(orc, L, x, asf().layer_from_numpy(L), "llama7b_gated_relu")
+
+
+def test_user_list_any_order_and_bad_ids(orc):
+    """A caller's id list in any order; out-of-range ids are skipped."""
+    need_gpu()
+    L = wl.random_layer(384, 1000, 64, "f16", False, 5)
+    lay = asf().layer_from_numpy(L)
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((1, 384)).astype(np.float32)
+    ids = rng.choice(1000, 300, replace=False).astype(np.int32)
+    dev = to_dev(np.concatenate([ids, np.array([-5, 1000, 99999], np.int32)]))
+    n = to_dev(np.array([dev.numel()], np.int32))
+    y = lay.sparse_ffn(to_dev(x), active=dev, n_active=n)
+    y_orc = orc.ffn(L.w_up, L.w_down, x, ids, b1=L.b1, b2=L.b2)
+    assert rel_l2(y.cpu().numpy(), y_orc) <= TOL["f16"]
+    # every neuron through the list equals the dense comparator
+    allids = to_dev(rng.permutation(1000).astype(np.int32))
+    yall = lay.sparse_ffn(to_dev(x), active=allids, n_active=to_dev(np.array([1000], np.int32)))
+    yd = lay.dense_ffn_ref(to_dev(x))
+    assert rel_l2(yall.cpu().numpy(), yd.cpu().numpy()) <= 1e-5
+
+
+def test_empty_set_and_residual_alias(orc):
+    need_gpu()
+    L = wl.random_layer(256, 512, 64, "f32", False, 6)
+    lay = asf().layer_from_numpy(L)
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((1, 256)).astype(np.float32)
+    r = rng.standard_normal((1, 256)).astype(np.float32)
+    empty = to_dev(np.zeros(4, np.int32))
+    zero = to_dev(np.array([0], np.int32))
+    y = lay.sparse_ffn(to_dev(x), active=empty, n_active=zero, residual=to_dev(r))
+    expect = (np.float32(0.0) + L.b2) + r
+    assert np.array_equal(y.cpu().numpy(), expect)
+    # y aliasing the residual (in-place residual stream)
+    rd = to_dev(r)
+    ids = to_dev(np.arange(0, 512, 3).astype(np.int32))
+    cnt = to_dev(np.array([ids.numel()], np.int32))
+    lay.sparse_ffn(to_dev(x), active=ids, n_active=cnt, residual=rd, out=rd)
+    y_orc = orc.ffn(L.w_up, L.w_down, x, np.arange(0, 512, 3), b1=L.b1, b2=L.b2, resid=r)
+    assert rel_l2(rd.cpu().numpy(), y_orc) <= TOL["f32"]
+
+
+def test_true_mask_sparse_equals_dense_on_gpu(orc):
+    """With the true mask as the set, the sparse FFN equals the dense one."""
+    need_gpu()
+    L = wl.config_layer("opt6.7b_ffn", shape=wl.scaled_shape(wl.CONFIGS["opt6.7b_ffn"][1],
+                                                             1024, 4096, 256))
+    lay = asf().layer_from_numpy(L)
+    x = wl.make_tokens(1024, 3, 9)
+    _, tm = orc.true_mask(L.w_up, x, b1=L.b1)
+    for t in range(3):
+        ids = np.nonzero(tm[t])[0].astype(np.int32)
+        y = lay.sparse_ffn(to_dev(x[t:t + 1]), active=to_dev(ids),
+                           n_active=to_dev(np.array([ids.size], np.int32)))
+        yd = lay.dense_ffn_ref(to_dev(x[t:t + 1]))
+        assert rel_l2(y.cpu().numpy(), yd.cpu().numpy()) <= 1e-5
+
+
+@pytest.mark.parametrize("B", [2, 4, 7, 32])
+def test_batched_union(orc, B):
+    """B tokens: the union of their predicted sets, every token computing
+    every neuron of the union."""
+    need_gpu()
+    _, sh = wl.CONFIGS["opt13b_batched"]
+    L = wl.make_layer(wl.scaled_shape(sh, 640, 2560, 128), 100 + B)
+    lay = asf().layer_from_numpy(L, max_batch=32)
+    x = wl.make_tokens(640, B, 200 + B)
+    masks = torch.zeros((B, (L.shape.f + 63) // 64), dtype=torch.int64, device="cuda")
+    active, n = lay.predict(to_dev(x), token_masks=masks)
+    y = lay.sparse_ffn(to_dev(x))
+    torch.cuda.synchronize()
+    k = int(n.item())
+    ids = active[:k].cpu().numpy()
+    _, s_orc, act = orc.predict(L.p1, L.c1, L.p2, L.c2, x)
+    # per-token masks (stored order) against the oracle, margin rule
+    mw = masks.cpu().numpy().view(np.uint64)
+    bits = ((mw[:, :, None] >> np.arange(64, dtype=np.uint64)) & np.uint64(1)).reshape(B, -1)
+    bits = bits[:, :L.shape.f].astype(bool)
+    for t in range(B):
+        tok_ids = L.perm[np.nonzero(bits[t])[0]]          # ascending slot order
+        check_set(tok_ids, s_orc[t], 0.0, L.perm, "B%d tok %d" % (B, t))
+    # union list: its members are exactly the OR of the token masks
+    u = bits.any(axis=0)
+    assert np.array_equal(ids, L.perm[np.nonzero(u)[0]])
+    # union margin rule: a neuron surely in / out of every token's set
+    s_max = s_orc.max(axis=0)
+    check_set(ids, s_max, 0.0, L.perm, "B%d union" % B)
+    y_orc = orc.ffn(L.w_up, L.w_down, x, ids, b1=L.b1, b2=L.b2)
+    yg = y.cpu().numpy()
+    for t in range(B):
+        assert rel_l2(yg[t], y_orc[t]) <= TOL["f16"]
+    yd = lay.dense_ffn_ref(to_dev(x)).cpu().numpy()
+    yd_orc = orc.dense_ffn(L.w_up, L.w_down, x, b1=L.b1, b2=L.b2)
+    for t in range(B):
+        assert rel_l2(yd[t], yd_orc[t]) <= TOL["f16"]
+
+
+def test_identity_table_and_threshold(orc):
+    """No neuron table (stored order = original order) and a nonzero logit
+    threshold; all-active and none-active thresholds."""
+    need_gpu()
+    L = wl.random_layer(256, 700, 32, "f32", False, 12)
+    x = np.random.default_rng(3).standard_normal((2, 256)).astype(np.float32)
+    for theta in (0.3, -1e30, 1e30):
+        lay = asf().layer_from_numpy(L, use_table=False, threshold=theta)
+        _, s_orc, _ = orc.predict(L.p1, L.c1, L.p2, L.c2, x, theta=theta)
+        for t in range(2):
+            active, n = lay.predict(to_dev(x[t:t + 1]))
+            y = lay.sparse_ffn(to_dev(x[t:t + 1]))
+            k = int(n.item())
+            if theta == -1e30:
+                assert k == 700
+            if theta == 1e30:
+                assert k == 0
+            ids = active[:k].cpu().numpy()
+            check_set(ids, s_orc[t], theta, np.arange(700), "theta %g" % theta)
+            y_orc = orc.ffn(L.w_up, L.w_down, x[t], ids, b1=L.b1, b2=L.b2)
+            assert rel_l2(y.cpu().numpy()[0], y_orc[0]) <= TOL["f32"]
+
+
+def test_deterministic_repeat():
+    need_gpu()
+    L = wl.random_layer(512, 3000, 64, "f16", True, 13)
+    lay = asf().layer_from_numpy(L)
+    x = to_dev(np.random.default_rng(4).standard_normal((1, 512)).astype(np.float32))
+    y1 = lay.decode_step(x).clone()
+    y2 = lay.decode_step(x).clone()
+    d1 = lay.dense_ffn_ref(x).clone()
+    d2 = lay.dense_ffn_ref(x).clone()
+    assert torch.equal(y1, y2) and torch.equal(d1, d2)
