@@ -68,6 +68,8 @@ size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v) {
     t.slots = (int32_t *)take(f * 4);
     t.count = (int32_t *)take(64);
     t.partial = (float *)take((size_t)kFfnGroups * Bm * d * 4);
+    t.bar = (unsigned *)take(64);
+    t.err = (int *)take(64);
     if (v) *v = t;
     return (size_t)(p - align_up(base, 256));
 }
@@ -124,6 +126,8 @@ asf_status asf_create_layer(const asf_layer_desc *desc, const asf_layer_weights 
 
     asf_layer *L = new (std::nothrow) asf_layer;
     if (!L) return ASF_ERR_ARG;
+    L->tracing = false;
+    memset(&L->trace, 0, sizeof(L->trace));
     carve(*desc, (uintptr_t)storage, &L->v);
     LayerView &v = L->v;
     hipStream_t s = (hipStream_t)stream;
@@ -153,6 +157,9 @@ asf_status asf_create_layer(const asf_layer_desc *desc, const asf_layer_weights 
                               (size_t)dn_idx * d, s));
     chk(launch_gather_f32(w->b1, v.perm, f, v.b1, s));
     chk(launch_gather_f32(w->b2, nullptr, d, v.b2, s));
+    chk(hipMemsetAsync(v.bar, 0, 64, s));
+    chk(hipMemsetAsync(v.err, 0, 64, s));
+    L->fused = fused_supported(v);
     if (e != hipSuccess) {
         delete L;
         return ASF_ERR_HIP;
@@ -174,7 +181,8 @@ asf_status asf_predict(const asf_layer *layer, const float *x, int32_t B, int32_
                        int32_t *n_active, uint64_t *token_masks, void *stream) {
     asf_status st = check_call(layer, x, B);
     if (st != ASF_OK) return st;
-    if (launch_predict(layer->v, x, B, active, n_active, token_masks, (hipStream_t)stream) !=
+    if (launch_predict(layer->v, x, B, active, n_active, token_masks, layer->tr(),
+                       (hipStream_t)stream) !=
         hipSuccess)
         return ASF_ERR_HIP;
     return ASF_OK;
@@ -187,7 +195,7 @@ asf_status asf_sparse_ffn(const asf_layer *layer, const float *x, int32_t B,
     if (st != ASF_OK) return st;
     if (!y || (active && !n_active)) return ASF_ERR_ARG;
     if (!aligned16(y) || (residual && !aligned16(residual))) return ASF_ERR_ALIGN;
-    if (launch_ffn(layer->v, x, B, active ? 1 : 0, active, n_active, residual, y,
+    if (launch_ffn(layer->v, x, B, active ? 1 : 0, active, n_active, residual, y, layer->tr(),
                    (hipStream_t)stream) != hipSuccess)
         return ASF_ERR_HIP;
     return ASF_OK;
@@ -201,9 +209,16 @@ asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
     if (!y) return ASF_ERR_ARG;
     if (!aligned16(y) || (residual && !aligned16(residual))) return ASF_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
-    if (launch_predict(layer->v, x, B, active, n_active, nullptr, s) != hipSuccess)
+    if (layer->fused && B == 1) {
+        if (launch_decode_fused(layer->v, x, residual, y, active, n_active, layer->tr(), s) !=
+            hipSuccess)
+            return ASF_ERR_HIP;
+        return ASF_OK;
+    }
+    if (launch_predict(layer->v, x, B, active, n_active, nullptr, layer->tr(), s) != hipSuccess)
         return ASF_ERR_HIP;
-    if (launch_ffn(layer->v, x, B, 0, nullptr, nullptr, residual, y, s) != hipSuccess)
+    if (launch_ffn(layer->v, x, B, 0, nullptr, nullptr, residual, y, layer->tr(), s) !=
+        hipSuccess)
         return ASF_ERR_HIP;
     return ASF_OK;
 }
@@ -214,9 +229,28 @@ asf_status asf_dense_ffn_ref(const asf_layer *layer, const float *x, int32_t B,
     if (st != ASF_OK) return st;
     if (!y) return ASF_ERR_ARG;
     if (!aligned16(y) || (residual && !aligned16(residual))) return ASF_ERR_ALIGN;
-    if (launch_ffn(layer->v, x, B, 2, nullptr, nullptr, residual, y, (hipStream_t)stream) !=
-        hipSuccess)
+    if (launch_ffn(layer->v, x, B, 2, nullptr, nullptr, residual, y, layer->tr(),
+                   (hipStream_t)stream) != hipSuccess)
         return ASF_ERR_HIP;
+    return ASF_OK;
+}
+
+asf_status asf_layer_read_error(const asf_layer *layer, int32_t *flags, int32_t clear,
+                                void *stream) {
+    if (!layer || !flags) return ASF_ERR_ARG;
+    if (launch_read_error(layer->v, flags, clear ? 1 : 0, (hipStream_t)stream) != hipSuccess)
+        return ASF_ERR_HIP;
+    return ASF_OK;
+}
+
+int32_t asf_layer_is_fused(const asf_layer *layer) { return layer && layer->fused ? 1 : 0; }
+
+asf_status asf_layer_set_trace(asf_layer *layer, void *const *events, int32_t n) {
+    if (!layer || n < 0 || n > ASF_K_COUNT) return ASF_ERR_ARG;
+    memset(&layer->trace, 0, sizeof(layer->trace));
+    layer->tracing = events != nullptr && n > 0;
+    if (layer->tracing)
+        for (int i = 0; i < 2 * n; ++i) layer->trace.ev[i] = (hipEvent_t)events[i];
     return ASF_OK;
 }
 

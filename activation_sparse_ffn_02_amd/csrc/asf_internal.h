@@ -45,6 +45,8 @@ struct LayerView {
     int32_t *slots;    // [f] compacted union list, ascending slot
     int32_t *count;    // [1] its length
     float *partial;    // [kFfnGroups][max_batch][d]
+    unsigned *bar;     // [2] grid barrier: arrivals, generation
+    int *err;          // [1] device error bits (1: a grid barrier wait timed out)
 };
 
 size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v);
@@ -60,17 +62,34 @@ hipError_t launch_invert(const int32_t *perm, int f, int32_t *inv, hipStream_t s
 hipError_t launch_gather_f32(const float *src, const int32_t *perm, int n, float *dst,
                              hipStream_t s);
 
+// Optional HIP events recorded around each kernel (2 per asf_kernel_id).
+struct Trace {
+    hipEvent_t ev[2 * ASF_K_COUNT];
+};
+
 hipError_t launch_predict(const LayerView &L, const float *x, int B, int32_t *active_ids,
-                          int32_t *n_active, uint64_t *token_masks, hipStream_t s);
+                          int32_t *n_active, uint64_t *token_masks, const Trace *tr,
+                          hipStream_t s);
 
 // list_mode: 0 = L.slots/L.count (last prediction), 1 = caller's original ids,
 //            2 = every neuron (dense)
 hipError_t launch_ffn(const LayerView &L, const float *x, int B, int list_mode,
                       const int32_t *ids, const int32_t *n_ids, const float *resid, float *y,
-                      hipStream_t s);
+                      const Trace *tr, hipStream_t s);
+
+// Fused one-launch decode step (B = 1, fp16 weights).
+bool fused_supported(const LayerView &L);
+hipError_t launch_decode_fused(const LayerView &L, const float *x, const float *resid, float *y,
+                               int32_t *active_ids, int32_t *n_active, const Trace *tr,
+                               hipStream_t s);
+hipError_t launch_read_error(const LayerView &L, int32_t *out, int clear, hipStream_t s);
 
 }  // namespace asf
 
 struct asf_layer {
     asf::LayerView v;
+    asf::Trace trace;
+    bool tracing;
+    bool fused;  // the one-launch decode kernel fits this device and shape
+    const asf::Trace *tr() const { return tracing ? &trace : nullptr; }
 };

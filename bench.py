@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Decode benchmark of the activation-sparse FFN on one MI355X.
+
+Workload: one OPT-6.7B-shaped ReLU FFN layer, d_model 4096, d_ffn 16384, fp16
+weights with fp32 accumulate, predictor 4096 -> 1024 -> 16384, power-law
+firing at ~7% active per token, batch 1, seeded N(0,1) hidden states (1000
+decode tokens, cycled).  A step is one decode step of one layer: predictor,
+threshold, compaction, gathered FC1 + ReLU, gathered FC2 AXPY, reduction.
+
+Steps rotate over a ring of identical layer copies at distinct addresses, so
+that the ~61 MB a step reads cannot be served from the 256 MB Infinity Cache
+(a layer ring standing in for the other layers of a model).
+
+Prints ONE JSON line: tokens/s (value), effective HBM GB/s on algorithmic
+bytes, the roofline of the dominant kernel (HIP events around it inside the
+timed region), the dense comparator, and the CPU oracle baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "opt6.7b_ffn"
+KERNELS = ["pred_l1", "pred_l2", "compact", "ffn", "reduce", "decode"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--ring", type=int, default=16, help="distinct layer copies")
+    ap.add_argument("--tokens", type=int, default=1000)
+    ap.add_argument("--dense-steps", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(args, *a):
+    if not args.quiet:
+        print(*a, file=sys.stderr, flush=True)
+
+
+def bytes_model(sh, k_mean):
+    """Algorithmic bytes (each distinct byte the method must read or write,
+    counted once) of one decode step and of each kernel."""
+    d, f, H = sh.d, sh.f, sh.H
+    ws = 2 if sh.wdtype == "f16" else 4
+    nmat = 3 if sh.gated else 2
+    words = (f + 63) // 64
+    per = {
+        "pred_l1": H * d * ws + H * 4 + d * 4 + H * 4,
+        "pred_l2": f * H * ws + f * 4 + H * 4 + words * 8,
+        "compact": words * 8 + k_mean * 4 + 4,
+        "ffn": k_mean * (nmat * d * ws + 4) + d * 4,
+        "reduce": d * 4 + d * 4,
+    }
+    per["decode"] = (H * d * ws + H * 4 + f * H * ws + f * 4 + d * 4
+                     + k_mean * (nmat * d * ws + 4) + d * 4 + d * 4)
+    step = (H * d * ws + H * 4 + f * H * ws + f * 4 + d * 4
+            + k_mean * (nmat * d * ws + 4) + d * 4 + d * 4)
+    dense = f * (nmat * d * ws + 4) + d * 4 * 3
+    return step, per, dense
+
+
+class HipEvents:
+    """A pool of raw hipEvent_t handles (timing enabled), created through the
+    HIP runtime so they exist before the library records them."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(h.value)
+
+    def record(self, i, stream):
+        if self.hip.hipEventRecord(self.ev[i], stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[a], self.ev[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
+
+
+def cpu_baseline(args, L, x):
+    """The oracle as it stands, on the host cores, on a bounded sample of the
+    same workload: predict + FFN over the oracle's own set, token by token."""
+    import oracle
+    n_thr = oracle.num_threads()
+    t0 = time.perf_counter()
+    done = 0
+    while done < x.shape[0]:
+        xt = x[done:done + 1]
+        _, _, act = oracle.predict(L.p1, L.c1, L.p2, L.c2, xt)
+        ids = oracle.active_list(act[0], L.perm)
+        oracle.ffn(L.w_up, L.w_down, xt, ids, b1=L.b1, b2=L.b2, W_gate=L.w_gate)
+        done += 1
+        if time.perf_counter() - t0 > args.cpu_seconds and done >= 3:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "tokens/s", "cores": int(n_thr), "kind": "oracle",
+            "sample": "%d decode tokens of the same layer and token stream (fp64 predictor "
+                      "+ FFN over the predicted set), %.1f s" % (done, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the per-GPU kernel is the neuron-sharded design's shard); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import activation_sparse_ffn_02_amd as asf
+    import workload as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = wl.config_layer(WORKLOAD)
+    sh = L.shape
+    X = wl.config_tokens(WORKLOAD, args.tokens)
+    log(args, "workload generated", sh)
+
+    def up(a):
+        return None if a is None else torch.from_numpy(a).to(dev)
+
+    orig = dict(w_up=up(L.w_up), w_down=up(L.w_down), p1=up(L.p1), p2=up(L.p2),
+                w_gate=up(L.w_gate), b1=up(L.b1), b2=up(L.b2), c1=up(L.c1), c2=up(L.c2),
+                neuron_table=up(L.perm))
+    ring = []
+    for _ in range(args.ring):
+        ring.append(asf.Layer(orig["w_up"], orig["w_down"], orig["p1"], orig["p2"],
+                              w_gate=orig["w_gate"], b1=orig["b1"], b2=orig["b2"],
+                              c1=orig["c1"], c2=orig["c2"], neuron_table=orig["neuron_table"]))
+    torch.cuda.synchronize()
+    del orig
+    torch.cuda.empty_cache()
+    ring_bytes = sum(l.storage.numel() for l in ring)
+    log(args, "ring of %d layers, %.2f GB" % (args.ring, ring_bytes / 1e9))
+
+    Xd = torch.from_numpy(X).to(dev)
+    Y = torch.empty((args.ring, 1, sh.d), dtype=torch.float32, device=dev)
+    K, W = args.steps, args.warmup
+    counts = torch.zeros(K + W, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    lib = asf.library()
+
+    # HIP events around each kernel of every timed step, recorded by the
+    # library on the stream the kernels run on (the fused decode kernel, or
+    # the five separate kernels when the fused one does not apply).
+    fused = ring[0].fused
+    used = [KERNELS.index("decode")] if fused else list(range(5))
+    NE = 2 * len(KERNELS)
+    hev = HipEvents(NE * K + 2)
+    EvArr = ctypes.c_void_p * NE
+
+    def ev_slots(i):
+        slots = [None] * NE
+        for j in used:
+            slots[2 * j] = hev.ev[NE * i + 2 * j]
+            slots[2 * j + 1] = hev.ev[NE * i + 2 * j + 1]
+        return EvArr(*slots)
+
+    arrs = [ev_slots(i) for i in range(K)]
+
+    def step(i, traced):
+        lay = ring[i % args.ring]
+        if traced:
+            lay.set_trace(arrs[i - W], len(KERNELS))
+        lay.decode_step(Xd[i % args.tokens], out=Y[i % args.ring], n_active=counts[i:i + 1])
+        if traced:
+            lay.set_trace(None)
+
+    for i in range(W):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hev.record(NE * K, stream.cuda_stream)
+    for i in range(W, W + K):
+        step(i, True)
+    hev.record(NE * K + 1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gpu_span_ms = hev.ms(NE * K, NE * K + 1)
+    elapsed = t1 - t0
+    ms_per_step = elapsed * 1e3 / K
+    ks = counts[W:].cpu().numpy()
+    k_mean = float(ks.mean())
+
+    # per-kernel durations from the events
+    kt = np.zeros((K, len(KERNELS)))
+    for i in range(K):
+        for j in used:
+            kt[i, j] = hev.ms(NE * i + 2 * j, NE * i + 2 * j + 1)
+    hev.close()
+    kmean = kt.mean(axis=0)             # ms
+    step_bytes, per_bytes, dense_bytes = bytes_model(sh, k_mean)
+    dom = int(np.argmax(kmean))
+    dname = KERNELS[dom]
+    achieved = per_bytes[dname] / (kmean[dom] * 1e-3) / 1e9
+    gpu_kernel_ms = float(kt.sum(axis=1).mean())
+    errs = [l.read_error() for l in ring]
+    if any(errs):
+        raise RuntimeError("device error bits set: %s" % errs)
+
+    # dense comparator on the same ring
+    for i in range(20):
+        ring[i % args.ring].dense_ffn_ref(Xd[i % args.tokens], out=Y[i % args.ring])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.dense_steps):
+        ring[i % args.ring].dense_ffn_ref(Xd[i % args.tokens], out=Y[i % args.ring])
+    e1.record()
+    torch.cuda.synchronize()
+    dense_ms = e0.elapsed_time(e1) / args.dense_steps
+
+    tok_s = K / elapsed
+    eff_gbs = step_bytes * K / elapsed / 1e9
+    out = {
+        "metric": "sparse-FFN decode tokens/s + effective HBM GB/s (% peak), 4096x16384 fp16",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16-weights/f32-accumulate",
+        "data": "synthetic (seeded N(0,1) hidden states; random-init weights with a power-law "
+                "firing law and a training-free predictor)",
+        "config": {"workload": "OPT-6.7B-shaped FFN layer 4096x16384 fp16, predictor "
+                               "4096->1024->16384, ~7% active, batch 1",
+                   "d_model": sh.d, "d_ffn": sh.f, "pred_hidden": sh.H, "batch": 1,
+                   "rho": sh.rho, "ring_layers": args.ring, "tokens": args.tokens},
+        "effective_gbps": eff_gbs,
+        "effective_frac_of_peak": eff_gbs / HBM_PEAK_GBS,
+        "algorithmic_bytes_per_step": step_bytes,
+        "active_mean": k_mean,
+        "active_frac": k_mean / sh.f,
+        "fused_decode_kernel": bool(fused),
+        "kernel_ms_mean": {KERNELS[j]: float(kmean[j]) for j in used},
+        "gpu_kernel_ms_per_step": gpu_kernel_ms,
+        "gpu_span_ms_per_step": gpu_span_ms / K,
+        "dense_ms_per_step": dense_ms,
+        "dense_gbps": dense_bytes / (dense_ms * 1e-3) / 1e9,
+        "sparse_step_speedup_vs_dense": dense_ms / ms_per_step,
+        "roofline": {"bound": "hbm", "kernel": dname, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(args, L, X)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -172,7 +172,13 @@ asf_status asf_sparse_ffn(const asf_layer *layer, const float *x, int32_t B,
 
 /* One decode step of one layer: asf_predict followed by asf_sparse_ffn over
  * the predicted union set, with no host round trip in between.  The optional
- * outputs are those of asf_predict. */
+ * outputs are those of asf_predict.  For B == 1 with fp16 weights this is a
+ * single cooperative kernel (all workgroups co-resident, grid barriers
+ * between the predictor, threshold, compaction/FFN and reduction phases)
+ * whose results are bit-identical to the separate calls; otherwise the
+ * separate kernels run back to back.  A grid-barrier wait that makes no
+ * progress for about a second is abandoned and reported through
+ * asf_layer_read_error instead of hanging the device. */
 asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
                            const float *residual, float *y, int32_t *active,
                            int32_t *n_active, void *stream);
@@ -180,6 +186,35 @@ asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
 /* Dense comparator: the same FFN over all d_ffn neurons. */
 asf_status asf_dense_ffn_ref(const asf_layer *layer, const float *x, int32_t B,
                              const float *residual, float *y, void *stream);
+
+/* Kernels of a decode step, in launch order (ids for asf_layer_set_trace). */
+typedef enum {
+    ASF_K_PRED_L1 = 0, /* predictor layer 1 GEMV */
+    ASF_K_PRED_L2 = 1, /* predictor layer 2 GEMV + threshold -> mask words */
+    ASF_K_COMPACT = 2, /* union + prefix sum -> active list */
+    ASF_K_FFN = 3,     /* gathered FC1 (+ReLU) and FC2 AXPY -> partial sums */
+    ASF_K_REDUCE = 4,  /* partial sums + b2 + residual -> y */
+    ASF_K_DECODE = 5,  /* the one-launch decode step (all of the above fused) */
+    ASF_K_COUNT = 6
+} asf_kernel_id;
+
+/* Kernel tracing, for measuring each kernel with HIP events on the stream it
+ * runs on.  `events` holds 2*n hipEvent_t handles (as void*), n <= ASF_K_COUNT:
+ * events[2k] is recorded on the call's stream right before kernel k is
+ * launched and events[2k+1] right after it, by every later call on this layer
+ * (NULL entries are skipped).  events == NULL or n == 0 turns tracing off.
+ * The handles are borrowed: the caller creates and destroys them. */
+asf_status asf_layer_set_trace(asf_layer *layer, void *const *events, int32_t n);
+
+/* Device-side error bits of a layer (bit 0: a grid-barrier wait of the fused
+ * decode kernel timed out, so that step's outputs are invalid).  Writes the
+ * bits to the DEVICE int32 *flags, stream-ordered after earlier work, and
+ * clears them when `clear` is nonzero. */
+asf_status asf_layer_read_error(const asf_layer *layer, int32_t *flags, int32_t clear,
+                                void *stream);
+
+/* 1 when asf_decode_step runs as the single fused kernel for B == 1. */
+int32_t asf_layer_is_fused(const asf_layer *layer);
 
 /* Human-readable name of a status code (static string). */
 const char *asf_status_string(asf_status s);
