@@ -28,8 +28,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 F32, F16 = 0, 1
 ASF_OK = 0
 # kernels of a decode step in launch order (asf_kernel_id)
-KERNEL_NAMES = ("pred_l1", "pred_l2", "compact", "ffn", "reduce", "decode")
-K_DECODE = 5
+KERNEL_NAMES = ("pred_l1", "score", "score_fc1", "fc1", "fc2", "list")
 STATUS_NAMES = {0: "ASF_OK", 1: "ASF_ERR_ARG", 2: "ASF_ERR_SHAPE", 3: "ASF_ERR_ALIGN",
                 4: "ASF_ERR_STORAGE", 5: "ASF_ERR_UNSUPPORTED", 6: "ASF_ERR_HIP"}
 
@@ -65,10 +64,6 @@ _lib.asf_dense_ffn_ref.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp]
 _lib.asf_dense_ffn_ref.restype = ctypes.c_int
 _lib.asf_layer_set_trace.argtypes = [_vp, ctypes.POINTER(ctypes.c_void_p), _i32]
 _lib.asf_layer_set_trace.restype = ctypes.c_int
-_lib.asf_layer_read_error.argtypes = [_vp, _vp, _i32, _vp]
-_lib.asf_layer_read_error.restype = ctypes.c_int
-_lib.asf_layer_is_fused.argtypes = [_vp]
-_lib.asf_layer_is_fused.restype = _i32
 _lib.asf_status_string.argtypes = [ctypes.c_int]
 _lib.asf_status_string.restype = ctypes.c_char_p
 _lib.asf_version.argtypes = []
@@ -233,6 +228,15 @@ class Layer:
                "asf_decode_step")
         return out
 
+    def decode_step_raw(self, x_ptr: int, B: int, y_ptr: int, stream_handle: int,
+                        residual_ptr: Optional[int] = None) -> None:
+        """decode_step on raw device pointers and a raw stream handle (no
+        tensor checks), for launch-bound loops."""
+        rc = _lib.asf_decode_step(self._h, x_ptr, B, residual_ptr, y_ptr, None, None,
+                                  stream_handle)
+        if rc != ASF_OK:
+            raise AsfError(rc, "asf_decode_step")
+
     def dense_ffn_ref(self, x, residual=None, out=None, stream=None):
         x = self._x(x)
         B = x.shape[0]
@@ -242,19 +246,6 @@ class Layer:
                                       _dev_ptr(out, torch.float32, "out"), _stream(stream)),
                "asf_dense_ffn_ref")
         return out
-
-    @property
-    def fused(self) -> bool:
-        """True when decode_step runs as one fused kernel for B == 1."""
-        return bool(_lib.asf_layer_is_fused(self._h))
-
-    def read_error(self, clear: bool = True, stream=None) -> int:
-        """Device error bits of this layer (bit 0: a grid-barrier wait of the
-        fused kernel timed out).  Synchronises the stream."""
-        out = torch.zeros(1, dtype=torch.int32, device=self.device)
-        _check(_lib.asf_layer_read_error(self._h, out.data_ptr(), int(bool(clear)),
-                                         _stream(stream)), "asf_layer_read_error")
-        return int(out.item())
 
     def set_trace(self, events=None, n: int = 0):
         """Record HIP events (ctypes array of 2*n hipEvent_t) around each of

@@ -21,9 +21,10 @@ static bool desc_ok(const asf_layer_desc &d) {
     if (d.gated != 0 && d.gated != 1) return false;
     if (d.wtype != ASF_F32 && d.wtype != ASF_F16) return false;
     const int ws = d.wtype == ASF_F16 ? 2 : 4;
-    if ((d.d_model * ws) % 16 != 0 || (d.pred_hidden * ws) % 16 != 0) return false;
-    // register tiling limits: 16 chunks per lane in pred_l1, 4 in pred_l2,
-    // 2 per thread in the FFN kernel
+    if ((d.pred_hidden * ws) % 16 != 0) return false;
+    // FC2 splits d into kSlices slices of whole 16-byte chunks
+    if ((d.d_model * ws) % (16 * kSlices) != 0) return false;
+    // register tiling limits: 16 chunks per lane for a d row, 4 for an H row
     const int cd = d.d_model * ws / 16, ch = d.pred_hidden * ws / 16;
     if (cd > 1024 || ch > 256) return false;
     return true;
@@ -33,7 +34,7 @@ size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v) {
     const int ws = desc.wtype == ASF_F16 ? 2 : 4;
     const size_t d = desc.d_model, f = desc.d_ffn, H = desc.pred_hidden, Bm = desc.max_batch;
     const int nmat = desc.gated ? 3 : 2;
-    const size_t words = (f + 63) / 64;
+    const size_t words = (f + 63) / 64, nq = words;
     uintptr_t p = align_up(base, 256);
     auto take = [&](size_t bytes) {
         uintptr_t q = p;
@@ -52,6 +53,7 @@ size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v) {
     t.cd = (int)(d * ws / 16);
     t.ch = (int)(H * ws / 16);
     t.words = (int)words;
+    t.nq = (int)nq;
     t.nmat = nmat;
     t.p1 = (void *)take(H * d * ws);
     t.c1 = (float *)take(H * 4);
@@ -63,13 +65,16 @@ size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v) {
     t.perm = (int32_t *)take(f * 4);
     t.inv = (int32_t *)take(f * 4);
     t.h = (float *)take(Bm * H * 4);
+    t.wbits = (uint64_t *)take(Bm * nq * 8);
+    t.ubits = (uint64_t *)take(nq * 8);
+    t.vbits = (uint64_t *)take(nq * 8);
+    t.lslot = (int32_t *)take(nq * kRowsPerWG * 4);
+    t.la = (float *)take(nq * kRowsPerWG * Bm * 4);
+    t.partial = (float *)take((size_t)kGroups * Bm * d * 4);
+    t.arrive = (unsigned *)take(kSlices * 4);
     t.masks = (uint64_t *)take(Bm * words * 8);
-    t.umask = (uint64_t *)take(words * 8);
     t.slots = (int32_t *)take(f * 4);
     t.count = (int32_t *)take(64);
-    t.partial = (float *)take((size_t)kFfnGroups * Bm * d * 4);
-    t.bar = (unsigned *)take(64);
-    t.err = (int *)take(64);
     if (v) *v = t;
     return (size_t)(p - align_up(base, 256));
 }
@@ -113,7 +118,7 @@ asf_status asf_create_layer(const asf_layer_desc *desc, const asf_layer_weights 
         return ASF_ERR_ARG;
     {
         const int ws = desc->wtype == ASF_F16 ? 2 : 4;
-        if ((desc->d_model * ws) % 16 != 0 || (desc->pred_hidden * ws) % 16 != 0)
+        if ((desc->d_model * ws) % (16 * kSlices) != 0 || (desc->pred_hidden * ws) % 16 != 0)
             return ASF_ERR_ALIGN;
     }
     if (!desc_ok(*desc)) return ASF_ERR_SHAPE;
@@ -157,9 +162,7 @@ asf_status asf_create_layer(const asf_layer_desc *desc, const asf_layer_weights 
                               (size_t)dn_idx * d, s));
     chk(launch_gather_f32(w->b1, v.perm, f, v.b1, s));
     chk(launch_gather_f32(w->b2, nullptr, d, v.b2, s));
-    chk(hipMemsetAsync(v.bar, 0, 64, s));
-    chk(hipMemsetAsync(v.err, 0, 64, s));
-    L->fused = fused_supported(v);
+    chk(hipMemsetAsync(v.arrive, 0, kSlices * 4, s));
     if (e != hipSuccess) {
         delete L;
         return ASF_ERR_HIP;
@@ -181,9 +184,12 @@ asf_status asf_predict(const asf_layer *layer, const float *x, int32_t B, int32_
                        int32_t *n_active, uint64_t *token_masks, void *stream) {
     asf_status st = check_call(layer, x, B);
     if (st != ASF_OK) return st;
-    if (launch_predict(layer->v, x, B, active, n_active, token_masks, layer->tr(),
-                       (hipStream_t)stream) !=
-        hipSuccess)
+    const LayerView &v = layer->v;
+    hipStream_t s = (hipStream_t)stream;
+    if (launch_pred_l1(v, x, B, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
+    if (launch_score(v, x, B, false, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
+    if ((active || n_active || token_masks) &&
+        launch_list(v, B, active, n_active, token_masks, layer->tr(), s) != hipSuccess)
         return ASF_ERR_HIP;
     return ASF_OK;
 }
@@ -195,8 +201,11 @@ asf_status asf_sparse_ffn(const asf_layer *layer, const float *x, int32_t B,
     if (st != ASF_OK) return st;
     if (!y || (active && !n_active)) return ASF_ERR_ARG;
     if (!aligned16(y) || (residual && !aligned16(residual))) return ASF_ERR_ALIGN;
-    if (launch_ffn(layer->v, x, B, active ? 1 : 0, active, n_active, residual, y, layer->tr(),
-                   (hipStream_t)stream) != hipSuccess)
+    const LayerView &v = layer->v;
+    hipStream_t s = (hipStream_t)stream;
+    if (launch_fc1(v, x, B, active ? 1 : 0, active, n_active, layer->tr(), s) != hipSuccess)
+        return ASF_ERR_HIP;
+    if (launch_fc2(v, B, active != nullptr, residual, y, layer->tr(), s) != hipSuccess)
         return ASF_ERR_HIP;
     return ASF_OK;
 }
@@ -208,17 +217,13 @@ asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
     if (st != ASF_OK) return st;
     if (!y) return ASF_ERR_ARG;
     if (!aligned16(y) || (residual && !aligned16(residual))) return ASF_ERR_ALIGN;
+    const LayerView &v = layer->v;
     hipStream_t s = (hipStream_t)stream;
-    if (layer->fused && B == 1) {
-        if (launch_decode_fused(layer->v, x, residual, y, active, n_active, layer->tr(), s) !=
-            hipSuccess)
-            return ASF_ERR_HIP;
-        return ASF_OK;
-    }
-    if (launch_predict(layer->v, x, B, active, n_active, nullptr, layer->tr(), s) != hipSuccess)
-        return ASF_ERR_HIP;
-    if (launch_ffn(layer->v, x, B, 0, nullptr, nullptr, residual, y, layer->tr(), s) !=
-        hipSuccess)
+    if (launch_pred_l1(v, x, B, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
+    if (launch_score(v, x, B, true, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
+    if (launch_fc2(v, B, false, residual, y, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
+    if ((active || n_active) &&
+        launch_list(v, B, active, n_active, nullptr, layer->tr(), s) != hipSuccess)
         return ASF_ERR_HIP;
     return ASF_OK;
 }
@@ -229,21 +234,13 @@ asf_status asf_dense_ffn_ref(const asf_layer *layer, const float *x, int32_t B,
     if (st != ASF_OK) return st;
     if (!y) return ASF_ERR_ARG;
     if (!aligned16(y) || (residual && !aligned16(residual))) return ASF_ERR_ALIGN;
-    if (launch_ffn(layer->v, x, B, 2, nullptr, nullptr, residual, y, layer->tr(),
-                   (hipStream_t)stream) != hipSuccess)
+    const LayerView &v = layer->v;
+    hipStream_t s = (hipStream_t)stream;
+    if (launch_fc1(v, x, B, 2, nullptr, nullptr, layer->tr(), s) != hipSuccess)
         return ASF_ERR_HIP;
+    if (launch_fc2(v, B, false, residual, y, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
     return ASF_OK;
 }
-
-asf_status asf_layer_read_error(const asf_layer *layer, int32_t *flags, int32_t clear,
-                                void *stream) {
-    if (!layer || !flags) return ASF_ERR_ARG;
-    if (launch_read_error(layer->v, flags, clear ? 1 : 0, (hipStream_t)stream) != hipSuccess)
-        return ASF_ERR_HIP;
-    return ASF_OK;
-}
-
-int32_t asf_layer_is_fused(const asf_layer *layer) { return layer && layer->fused ? 1 : 0; }
 
 asf_status asf_layer_set_trace(asf_layer *layer, void *const *events, int32_t n) {
     if (!layer || n < 0 || n > ASF_K_COUNT) return ASF_ERR_ARG;

@@ -10,21 +10,28 @@
 
 namespace asf {
 
-// Workgroups of the fused FFN kernel: one per compute unit of an MI355X.
-// Each owns one float32 partial of y, summed by the reduction kernel.
-constexpr int kFfnGroups = 256;
-constexpr int kFfnThreads = 512;
+constexpr int kThreads = 512;     // workgroup size of the step kernels (8 waves)
+constexpr int kRowsPerWG = 64;    // neuron slots owned by one scoring workgroup
+constexpr int kSlices = 16;       // FC2: output slices
+constexpr int kGroups = 16;       // FC2: neuron groups (partials per output)
 constexpr int kMaxBatch = 32;
-constexpr int kMaxFfn = 65536;  // compaction handles up to 1024 mask words
+constexpr int kMaxFfn = 65536;    // the list kernel handles up to 1024 mask words
 
 // Device view of a created layer, carved out of the caller's storage.
+//
+// Neuron work is split over nq = ceil(f / 64) "owner" workgroups: owner q
+// holds the slots q, q + nq, q + 2*nq, ... (64 of them, bit i of its mask
+// word is slot q + nq*i).  With a hot-first neuron table every owner gets
+// the same mix of hot and cold neurons, so per-owner work stays balanced
+// without a global prefix sum.
 struct LayerView {
     int d, f, H, max_batch, gated, wtype;
     float threshold;
     int ws;        // bytes per weight element
     int cd;        // 16-byte chunks per d-long weight row
     int ch;        // 16-byte chunks per H-long weight row
-    int words;     // 64-bit mask words: ceil(f / 64)
+    int words;     // 64-bit words of a slot-ordered mask: ceil(f / 64)
+    int nq;        // owner workgroups (== words)
     int nmat;      // matrices per neuron bundle: 2 (up, down) or 3 (gate, up, down)
 
     // weights in the library layout
@@ -39,19 +46,27 @@ struct LayerView {
     int32_t *inv;      // [f] original id -> slot
 
     // per-call scratch
-    float *h;          // [max_batch][H]
-    uint64_t *masks;   // [max_batch][words] per-token masks, slot order
-    uint64_t *umask;   // [words] union mask
-    int32_t *slots;    // [f] compacted union list, ascending slot
-    int32_t *count;    // [1] its length
-    float *partial;    // [kFfnGroups][max_batch][d]
-    unsigned *bar;     // [2] grid barrier: arrivals, generation
-    int *err;          // [1] device error bits (1: a grid barrier wait timed out)
+    float *h;          // [max_batch][H]           predictor hidden activations
+    uint64_t *wbits;   // [max_batch][nq]          per-token owner bits
+    uint64_t *ubits;   // [nq]                     union over the batch
+    uint64_t *vbits;   // [nq]                     entries listed by each owner
+    int32_t *lslot;    // [nq][64]                 their slots (ascending bit)
+    float *la;         // [nq][64][max_batch]      their FC1 activations
+    float *partial;    // [kGroups][max_batch][d]  FC2 partial sums
+    unsigned *arrive;  // [kSlices]                FC2 arrivals per slice
+    uint64_t *masks;   // [max_batch][words]       slot-ordered token masks
+    int32_t *slots;    // [f]                      ascending active slots
+    int32_t *count;    // [1]                      their number
 };
 
 size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v);
 
-// ---- launchers (asf_kernels.hip); each returns the hipError_t of its launch
+// Optional HIP events recorded around each kernel (2 per asf_kernel_id).
+struct Trace {
+    hipEvent_t ev[2 * ASF_K_COUNT];
+};
+
+// ---- create-time layout kernels
 hipError_t launch_perm_rows(const void *src, int chunks_per_row, const int32_t *perm, int nrows,
                             void *dst, size_t dst_stride_chunks, size_t dst_off_chunks,
                             hipStream_t s);
@@ -62,27 +77,25 @@ hipError_t launch_invert(const int32_t *perm, int f, int32_t *inv, hipStream_t s
 hipError_t launch_gather_f32(const float *src, const int32_t *perm, int n, float *dst,
                              hipStream_t s);
 
-// Optional HIP events recorded around each kernel (2 per asf_kernel_id).
-struct Trace {
-    hipEvent_t ev[2 * ASF_K_COUNT];
-};
-
-hipError_t launch_predict(const LayerView &L, const float *x, int B, int32_t *active_ids,
-                          int32_t *n_active, uint64_t *token_masks, const Trace *tr,
+// ---- step kernels
+// predictor layer 1: h = ReLU(P1 x + c1)
+hipError_t launch_pred_l1(const LayerView &L, const float *x, int B, const Trace *tr,
                           hipStream_t s);
-
-// list_mode: 0 = L.slots/L.count (last prediction), 1 = caller's original ids,
-//            2 = every neuron (dense)
-hipError_t launch_ffn(const LayerView &L, const float *x, int B, int list_mode,
-                      const int32_t *ids, const int32_t *n_ids, const float *resid, float *y,
+// predictor layer 2 + threshold into owner bits; with fc1, each owner also
+// runs FC1 over its union-active neurons (the decode-step form)
+hipError_t launch_score(const LayerView &L, const float *x, int B, bool fc1, const Trace *tr,
+                        hipStream_t s);
+// FC1 over a neuron set without scoring: mode 0 = union of the last
+// prediction, 1 = caller's original ids, 2 = every neuron
+hipError_t launch_fc1(const LayerView &L, const float *x, int B, int mode, const int32_t *ids,
+                      const int32_t *n_ids, const Trace *tr, hipStream_t s);
+// FC2 over the owners' lists + per-slice reduction into y; listed: the
+// entries' slots come from the list (caller ids) rather than the owner bits
+hipError_t launch_fc2(const LayerView &L, int B, bool listed, const float *resid, float *y,
                       const Trace *tr, hipStream_t s);
-
-// Fused one-launch decode step (B = 1, fp16 weights).
-bool fused_supported(const LayerView &L);
-hipError_t launch_decode_fused(const LayerView &L, const float *x, const float *resid, float *y,
-                               int32_t *active_ids, int32_t *n_active, const Trace *tr,
-                               hipStream_t s);
-hipError_t launch_read_error(const LayerView &L, int32_t *out, int clear, hipStream_t s);
+// slot-ordered outputs of the last prediction: token masks, ascending list
+hipError_t launch_list(const LayerView &L, int B, int32_t *active_ids, int32_t *n_active,
+                       uint64_t *token_masks, const Trace *tr, hipStream_t s);
 
 }  // namespace asf
 
@@ -90,6 +103,5 @@ struct asf_layer {
     asf::LayerView v;
     asf::Trace trace;
     bool tracing;
-    bool fused;  // the one-launch decode kernel fits this device and shape
     const asf::Trace *tr() const { return tracing ? &trace : nullptr; }
 };

@@ -1,28 +1,32 @@
 // asf_kernels.hip -- gfx950 kernels of the activation-sparse FFN decode path.
 //
-// Steps of one decode step of one layer:
-//   pred_l1   h = ReLU(P1 x + c1)                  dense GEMV, one wave per row
-//   pred_l2   s = P2 h + c2, bit = s > theta      dense GEMV over slot-ordered rows;
-//             64 rows -> one uint64 mask word      8 rows per wave, 8 waves per word
-//   compact   union of the tokens' masks, popcount + prefix sum -> ascending
-//             slot list (and original ids through the neuron table)
-//   ffn       per active neuron: FC1 dot of its up row with x (+b1, ReLU; or the
-//             ReLU-gated form), then AXPY of its down column into y; each
-//             workgroup owns a float32 partial of y
-//   reduce    y = residual + b2 + sum of the partials, in a fixed order
+// A decode step of one layer is three kernels; the kernel boundaries are the
+// grid-wide synchronisation points (on MI355X a boundary costs ~1.6 us inside
+// a HIP graph, far less than any in-kernel grid barrier):
 //
-// The steps exist as separate kernels (asf_predict, asf_sparse_ffn) and fused
-// into one cooperative kernel per decode step (k_decode) that separates them
-// with grid barriers and issues the loads of its predictor layer-2 rows before
-// the first barrier, so the whole predictor streams from HBM at once.  Both
-// forms share the per-row, per-neuron and per-tile device code below, so they
-// produce the same bits.
+//   pred_l1      h = ReLU(P1 x + c1)                           dense GEMV
+//   score_fc1    per owner workgroup q (slots q, q+nq, ...):   dense GEMV over
+//                s = P2 h + c2, bit = s > theta                the owner's P2
+//                then FC1 of its union-active neurons:         rows; gathered
+//                a = ReLU(W_up[slot] . x + b1) (or the gated   up rows
+//                form), listed with their slots
+//   fc2          y = b2 + residual + sum_j a_j * W_down[:, j]: 16 output
+//                slices x 16 neuron groups; each workgroup reads 512-byte
+//                segments of the listed down columns; the last of the 16
+//                groups to finish a slice sums the 16 partials (fixed order)
 //
-// All weight reads are whole 16-byte chunks (64 lanes x 16 B = 1 KiB per wave
-// instruction) of contiguous rows: an active neuron's up row and down column
-// sit back to back in one bundle, so its bytes form one contiguous run
-// ("LLM模型之PowerInfer1.0", "其他" question 3: load the active columns of the
-// down projection contiguously and skip the inactive ones).
+// The owner split balances FC1 without a global prefix sum: with a hot-first
+// neuron table, owner q holds ranks q, q+nq, q+2nq, ..., so every owner gets
+// the same mix of always-on and rarely-on neurons.  The hottest slot of each
+// owner (slot q) has its up row loaded before scoring, overlapping the P2
+// stream (and so is the next-hottest, slot q + nq); each is used only if
+// that neuron is predicted active.
+//
+// Weight reads are whole 16-byte chunks of contiguous rows (a wave load
+// instruction covers 1 KiB); an active neuron's up row and down column sit in
+// one bundle ("LLM模型之PowerInfer1.0", "其他" question 3: load the active
+// columns of the down projection contiguously, skip the inactive ones).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,9 +38,11 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kWaves = kFfnThreads / 64;       // waves per 512-thread workgroup
-constexpr int kL2Rows = 8;                     // predictor layer-2 rows per wave
-constexpr uint64_t kSpinTicks = 100000000ull;  // 1 s of the 100 MHz realtime clock
+constexpr int kWaves = kThreads / 64;
+constexpr int kL2Rows = kRowsPerWG / kWaves;  // predictor layer-2 rows per wave (8)
+constexpr int kFc2Batch = 8;                  // FC2 entries in flight per thread
+constexpr int kSpecRows = 2;                  // FC1 rows loaded before scoring, per owner
+constexpr int kMaxProducers = kMaxFfn / kRowsPerWG / kGroups + 1;
 
 // elements per 16-byte chunk: 8 binary16 or 4 binary32
 template <int WT> struct Elt { static constexpr int E = WT ? 8 : 4; };
@@ -74,40 +80,36 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// ---------------------------------------------------------------- grid barrier
-// Sense-reversing barrier over the workgroups of a cooperative launch (all
-// co-resident).  bar[0] counts arrivals, bar[1] is the generation.  Each wave
-// first waits for its own stores; thread 0 then arrives with an acquire-
-// release RMW (one L2 write-back per workgroup), the last arrival resets the
-// count and bumps the generation (release), and the others poll the
-// generation with relaxed loads and take one acquire fence when it moves.
-// Waits are bounded: after about a second without progress the error word
-// gets bit 0 and the wait ends, so a fault in the protocol cannot hang the
-// device.
-__device__ void grid_sync(unsigned *bar, unsigned nblocks, int *err) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned gen = __hip_atomic_load(bar + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned arrived =
-            __hip_atomic_fetch_add(bar, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        if (arrived + 1u == nblocks) {
-            __hip_atomic_store(bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_fetch_add(bar + 1, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            const uint64_t t0 = wall_clock64();
-            while (__hip_atomic_load(bar + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
-                __builtin_amdgcn_s_sleep(1);
-                if (wall_clock64() - t0 > kSpinTicks) {
-                    atomicOr(err, 1);
-                    break;
-                }
-            }
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        }
+// Sums eight per-lane values v[0..7] (one per row) over the 64 lanes of a
+// wave at once: three halving exchanges (lane bit 5, 4, 3 choose which half
+// of the remaining rows a lane keeps) leave lane L with row (L >> 3) & 7
+// summed over 8 lanes, and three butterfly steps finish the sum over the 8
+// lanes holding that row.  Ten shuffles instead of 6 per row.
+__device__ __forceinline__ float rows8_sum(const float (&v)[8], int lane) {
+    float a[4], b[2];
+    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float send = b5 ? v[k] : v[4 + k], keep = b5 ? v[4 + k] : v[k];
+        a[k] = keep + __shfl_xor(send, 32, 64);
     }
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const float send = b4 ? a[k] : a[2 + k], keep = b4 ? a[2 + k] : a[k];
+        b[k] = keep + __shfl_xor(send, 16, 64);
+    }
+    float c;
+    {
+        const float send = b3 ? b[0] : b[1], keep = b3 ? b[1] : b[0];
+        c = keep + __shfl_xor(send, 8, 64);
+    }
+    c += __shfl_xor(c, 4, 64);
+    c += __shfl_xor(c, 2, 64);
+    c += __shfl_xor(c, 1, 64);
+    return c;
 }
+
+__device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
 // ---------------------------------------------------------------- layout
 __global__ void k_perm_rows(const u32x4 *__restrict__ src, int C, const int32_t *__restrict__ perm,
@@ -165,177 +167,570 @@ __global__ void k_gather_f32(const float *__restrict__ src, const int32_t *__res
     }
 }
 
-// ---------------------------------------------------------------- predictor
-// One row of predictor layer 1, computed by one wave for every token:
-// lane l holds chunks l, l+64, ... of the row; h[b][row] = max(0, sum + c1).
+// ---------------------------------------------------------------- predictor layer 1
+// WPR waves share one row of P1 (wave part p of row r takes chunks p*64 + lane
+// + 64*WPR*i); the WPR wave sums are added in part order, then c1, then ReLU.
 template <int WT, int CPL, int BT>
-__device__ __forceinline__ void l1_row(const u32x4 *__restrict__ P1, const float *__restrict__ c1,
-                                       const float *__restrict__ x, int B, int d, int H, int row,
-                                       float *__restrict__ h, int lane) {
+__global__ __launch_bounds__(kThreads) void k_pred_l1(const u32x4 *__restrict__ P1,
+                                                      const float *__restrict__ c1,
+                                                      const float *__restrict__ x, int B, int d,
+                                                      int H, int wpr, float *__restrict__ h) {
     constexpr int E = Elt<WT>::E;
+    __shared__ float red[kWaves][BT];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rpw = kWaves / wpr;
+    const int row = blockIdx.x * rpw + wave / wpr, part = wave % wpr;
     const int C = d / E;
-    const u32x4 *prow = P1 + (size_t)row * C;
+    const bool live = row < H;
+    // every load is issued unconditionally from a clamped address, so all of
+    // them are in flight before the first wait; out-of-range chunks are
+    // zeroed when used
+    const int rowc = live ? row : H - 1;
     u32x4 w[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-        const int c = lane + 64 * i;
-        w[i] = c < C ? prow[c] : u32x4{0u, 0u, 0u, 0u};
+        const int c = part * 64 + lane + 64 * wpr * i;
+        w[i] = P1[(size_t)rowc * C + (c < C ? c : C - 1)];
     }
-    const float bias = c1[row];
+    float xv[BT][CPL][E];
+    auto load_x = [&](int b0) {
+#pragma unroll
+        for (int t = 0; t < BT; ++t)
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int c = part * 64 + lane + 64 * wpr * i;
+                const int tt = (BT == 1 || b0 + t < B) ? b0 + t : b0;
+                load_f32<E>(x + (size_t)tt * d + (size_t)(c < C ? c : C - 1) * E, xv[t][i]);
+            }
+    };
+    load_x(0);
     for (int b0 = 0; b0 < B; b0 += BT) {
         float acc[BT];
 #pragma unroll
         for (int t = 0; t < BT; ++t) acc[t] = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            const int c = lane + 64 * i;
-            if (c < C) {
+            const int c = part * 64 + lane + 64 * wpr * i;
+            if (live && c < C) {
                 float wv[E];
                 unpack<WT>(w[i], wv);
 #pragma unroll
-                for (int t = 0; t < BT; ++t) {
-                    if (BT == 1 || b0 + t < B) {
-                        float xv[E];
-                        load_f32<E>(x + (size_t)(b0 + t) * d + (size_t)c * E, xv);
+                for (int t = 0; t < BT; ++t)
 #pragma unroll
-                        for (int e = 0; e < E; ++e) acc[t] = fmaf(wv[e], xv[e], acc[t]);
-                    }
-                }
+                    for (int e = 0; e < E; ++e) acc[t] = fmaf(wv[e], xv[t][i][e], acc[t]);
             }
         }
+        if (b0 + BT < B) load_x(b0 + BT);
 #pragma unroll
         for (int t = 0; t < BT; ++t) {
-            const float s = wave_sum(acc[t]) + bias;
-            if (lane == 0 && (BT == 1 || b0 + t < B)) h[(size_t)(b0 + t) * H + row] = fmaxf(s, 0.0f);
+            const float sum = wave_sum(acc[t]);
+            if (lane == 0) red[wave][t] = sum;
         }
+        __syncthreads();
+        if ((int)threadIdx.x < rpw * BT) {
+            const int rl = threadIdx.x / BT, t = threadIdx.x % BT;
+            const int r = blockIdx.x * rpw + rl;
+            if (r < H && (BT == 1 || b0 + t < B)) {
+                float sum = 0.0f;
+                for (int p = 0; p < wpr; ++p) sum += red[rl * wpr + p][t];
+                h[(size_t)(b0 + t) * H + r] = fmaxf(sum + c1[r], 0.0f);
+            }
+        }
+        __syncthreads();
     }
 }
 
-// Loads of the kL2Rows predictor layer-2 rows slot0 .. slot0+7 of one wave
-// (lane l holds chunks l, l+64, ... of each row) and of their biases.
+// ---------------------------------------------------------------- predictor layer 2
+// Owner q, wave w scores the slots of bits i = 8w .. 8w+7 (slot q + nq*i);
+// lane l holds chunks l, l+64, ... of each row.  Loads are unconditional from
+// clamped addresses (rows past f read row f-1 and are discarded later), so
+// the whole wave's rows are in flight at once.
 template <int CPL>
-__device__ __forceinline__ void l2_load(const u32x4 *__restrict__ P2, const float *__restrict__ c2,
-                                        int f, int C, int slot0, int lane,
-                                        u32x4 (&w)[kL2Rows][CPL], float (&bias)[kL2Rows]) {
+__device__ __forceinline__ void l2_load(const u32x4 *__restrict__ P2, int f, int C, int q, int nq,
+                                        int wave, int lane, u32x4 (&w)[kL2Rows][CPL]) {
 #pragma unroll
     for (int j = 0; j < kL2Rows; ++j) {
-        const int slot = slot0 + j;
+        int slot = q + nq * (wave * kL2Rows + j);
+        slot = slot < f ? slot : f - 1;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + 64 * i;
-            w[j][i] = (slot < f && c < C) ? P2[(size_t)slot * C + c] : u32x4{0u, 0u, 0u, 0u};
+            w[j][i] = P2[(size_t)slot * C + (c < C ? c : C - 1)];
         }
-        bias[j] = slot < f ? c2[slot] : 0.0f;
     }
 }
 
-// Scores of those rows for tokens b0 .. b0+BT-1 against h; bit j of bits[t]
-// is set when s(slot0 + j) > theta for token b0 + t.
+// bits[t] bit j set when the score of row j of this wave exceeds theta for
+// token b0 + t.  Lane L ends with row r = (L >> 3) & 7 and adds that row's
+// bias, loaded per lane.
 template <int WT, int CPL, int BT>
 __device__ __forceinline__ void l2_bits(const u32x4 (&w)[kL2Rows][CPL],
-                                        const float (&bias)[kL2Rows], const float *__restrict__ h,
-                                        int b0, int B, int H, int f, int slot0, float theta,
-                                        int lane, uint32_t (&bits)[BT]) {
+                                        const float *__restrict__ c2, const float *__restrict__ h,
+                                        int b0, int B, int H, int f, int q, int nq, int wave,
+                                        float theta, int lane, uint32_t (&bits)[BT]) {
     constexpr int E = Elt<WT>::E;
     const int C = H / E;
+    const int r = (lane >> 3) & 7;
+    const int slot_r = q + nq * (wave * kL2Rows + r);
+    const bool valid_r = slot_r < f;
+    const float bias_r = c2[valid_r ? slot_r : f - 1];
     float hv[BT][CPL][E];
 #pragma unroll
     for (int t = 0; t < BT; ++t)
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + 64 * i;
-            if (c < C && (BT == 1 || b0 + t < B))
-                load_f32<E>(h + (size_t)(b0 + t) * H + (size_t)c * E, hv[t][i]);
-            else
-#pragma unroll
-                for (int e = 0; e < E; ++e) hv[t][i][e] = 0.0f;
+            const int tt = (BT == 1 || b0 + t < B) ? b0 + t : b0;
+            load_f32<E>(h + (size_t)tt * H + (size_t)(c < C ? c : C - 1) * E, hv[t][i]);
         }
+    float acc[BT][kL2Rows];
 #pragma unroll
-    for (int t = 0; t < BT; ++t) bits[t] = 0u;
+    for (int t = 0; t < BT; ++t)
 #pragma unroll
-    for (int j = 0; j < kL2Rows; ++j) {
-        float acc[BT];
+        for (int j = 0; j < kL2Rows; ++j) acc[t][j] = 0.0f;
 #pragma unroll
-        for (int t = 0; t < BT; ++t) acc[t] = 0.0f;
+    for (int i = 0; i < CPL; ++i) {
+        if (lane + 64 * i < C) {
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            float wv[E];
-            unpack<WT>(w[j][i], wv);
+            for (int j = 0; j < kL2Rows; ++j) {
+                float wv[E];
+                unpack<WT>(w[j][i], wv);
 #pragma unroll
-            for (int t = 0; t < BT; ++t)
+                for (int t = 0; t < BT; ++t)
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[t] = fmaf(wv[e], hv[t][i][e], acc[t]);
+                    for (int e = 0; e < E; ++e) acc[t][j] = fmaf(wv[e], hv[t][i][e], acc[t][j]);
+            }
         }
+    }
 #pragma unroll
-        for (int t = 0; t < BT; ++t) {
-            const float s = wave_sum(acc[t]) + bias[j];
-            if (slot0 + j < f && s > theta) bits[t] |= 1u << j;
-        }
+    for (int t = 0; t < BT; ++t) {
+        const float sc = rows8_sum(acc[t], lane) + bias_r;
+        const uint64_t m = __ballot(valid_r && sc > theta);
+        uint32_t b = 0;
+#pragma unroll
+        for (int j = 0; j < kL2Rows; ++j) b |= (uint32_t)((m >> (8 * j)) & 1ull) << j;
+        bits[t] = b;
     }
 }
 
-// Layer 1 as a kernel: one wave per hidden unit, 4 waves per workgroup.
-template <int WT, int CPL, int BT>
-__global__ __launch_bounds__(256) void k_pred_l1(const u32x4 *__restrict__ P1,
-                                                 const float *__restrict__ c1,
-                                                 const float *__restrict__ x, int B, int d, int H,
-                                                 float *__restrict__ h) {
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= H) return;
-    l1_row<WT, CPL, BT>(P1, c1, x, B, d, H, row, h, threadIdx.x & 63);
+// ---------------------------------------------------------------- FC1
+struct Fc1Out {
+    uint64_t *vbits;
+    int32_t *lslot;
+    float *la;
+    int max_batch;
+};
+
+// a for one neuron whose rows (up, and gate when gated) are in registers:
+// lane l holds chunks l, l+64, ... (C chunks in all); lane 0 writes a for
+// every token to a_out[t].
+template <int WT, bool GATED, int CPL>
+__device__ __forceinline__ void fc1_neuron(const u32x4 (&wu)[CPL], const u32x4 (&wg)[CPL], int C,
+                                           const float *__restrict__ x, int B, int d, float bias,
+                                           int lane, float *__restrict__ a_out) {
+    constexpr int E = Elt<WT>::E;
+    for (int t = 0; t < B; ++t) {
+        float au = 0.0f, ag = 0.0f;
+        float xv[CPL][E];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            load_f32<E>(x + (size_t)t * d + (size_t)(c < C ? c : C - 1) * E, xv[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            if (c < C) {
+                float vu[E];
+                unpack<WT>(wu[i], vu);
+#pragma unroll
+                for (int e = 0; e < E; ++e) au = fmaf(vu[e], xv[i][e], au);
+                if constexpr (GATED) {
+                    float vg[E];
+                    unpack<WT>(wg[i], vg);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) ag = fmaf(vg[e], xv[i][e], ag);
+                }
+            }
+        }
+        const float su = wave_sum(au);
+        float a;
+        if constexpr (GATED) {
+            const float sg = wave_sum(ag);
+            a = fmaxf(sg + bias, 0.0f) * su;
+        } else {
+            a = fmaxf(su + bias, 0.0f);
+        }
+        if (lane == 0) a_out[t] = a;
+    }
 }
 
-// Layer 2 + threshold as a kernel: workgroup = one 64-slot mask word, wave w
-// scores slots 8w .. 8w+7 of it.
-template <int WT, int CPL, int BT>
-__global__ __launch_bounds__(kFfnThreads) void k_pred_l2(const u32x4 *__restrict__ P2,
-                                                         const float *__restrict__ c2,
-                                                         const float *__restrict__ h, int B, int H,
-                                                         int f, int words, float theta,
-                                                         uint64_t *__restrict__ masks) {
-    constexpr int E = Elt<WT>::E;
+template <bool GATED, int CPL>
+__device__ __forceinline__ void load_fc1_rows(const u32x4 *__restrict__ bundles, size_t bstride,
+                                              int C, int slot, int lane, u32x4 (&wu)[CPL],
+                                              u32x4 (&wg)[CPL]) {
+    const u32x4 *bp = bundles + (size_t)slot * bstride;
+    constexpr int UP = GATED ? 1 : 0;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = lane + 64 * i;
+        const int cc = c < C ? c : C - 1;
+        wu[i] = bp[(size_t)UP * C + cc];
+        if constexpr (GATED) wg[i] = bp[cc];
+        else wg[i] = zero4();
+    }
+}
+
+// FC1 of owner q over its valid entries (bit i of `valid`, slot slot_of(i)):
+// wave w takes entries i = w, w+8, ...; the entry of rank r (r-th set bit)
+// is listed at lslot[q][r], la[q][r][0..B).  When spec is set, wave w's
+// registers spu/spg already hold the rows of slot_of(w).
+template <int WT, bool GATED, int CPL, class SlotOf>
+__device__ __forceinline__ void owner_fc1(int q, uint64_t valid, SlotOf slot_of,
+                                          const u32x4 *__restrict__ bundles, size_t bstride,
+                                          int C, const float *__restrict__ b1,
+                                          const float *__restrict__ x, int B, int d, Fc1Out o,
+                                          bool spec, const u32x4 (&spu)[CPL],
+                                          const u32x4 (&spg)[CPL], int wave, int lane) {
+    for (int k = 0; k < kRowsPerWG / kWaves; ++k) {
+        const int i = wave + kWaves * k;
+        if (!((valid >> i) & 1ull)) continue;
+        const int slot = slot_of(i);
+        const int rank = __popcll(valid & ((1ull << i) - 1ull));
+        u32x4 wu[CPL], wg[CPL];
+        if (k == 0 && spec) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                wu[c] = spu[c];
+                wg[c] = spg[c];
+            }
+        } else {
+            load_fc1_rows<GATED, CPL>(bundles, bstride, C, slot, lane, wu, wg);
+        }
+        const float bias = b1[slot];
+        const size_t e = (size_t)q * kRowsPerWG + rank;
+        fc1_neuron<WT, GATED, CPL>(wu, wg, C, x, B, d, bias, lane, o.la + e * o.max_batch);
+        if (lane == 0) o.lslot[e] = slot;
+    }
+}
+
+struct ScoreParams {
+    const u32x4 *p2;
+    const float *c2;
+    const float *h;
+    int B, H, f;
+    float theta;
+    uint64_t *wbits;  // [B][nq]
+    uint64_t *ubits;  // [nq]
+    // FC1 (decode-step form)
+    const u32x4 *bundles;
+    size_t bstride;   // chunks per bundle
+    int cd;           // chunks per d row
+    const float *b1;
+    const float *x;
+    int d;
+    Fc1Out out;
+};
+
+// Owner workgroup q: score its 64 slots for every token, store per-token and
+// union owner bits; with FC1, then list its union-active neurons with a.
+template <int WT, int CPL2, int BT, bool FC1, bool GATED, int CPL1>
+__global__ __launch_bounds__(kThreads) void k_score(ScoreParams p) {
     __shared__ uint32_t bits_lds[BT][kWaves];
+    __shared__ uint64_t u_lds;
+    const int q = blockIdx.x, nq = gridDim.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int word = blockIdx.x;
-    const int slot0 = word * 64 + wave * kL2Rows;
-    u32x4 w[kL2Rows][CPL];
-    float bias[kL2Rows];
-    l2_load<CPL>(P2, c2, f, H / E, slot0, lane, w, bias);
-    for (int b0 = 0; b0 < B; b0 += BT) {
+    u32x4 w2[kL2Rows][CPL2];
+    l2_load<CPL2>(p.p2, p.f, p.H / Elt<WT>::E, q, nq, wave, lane, w2);
+    // speculative FC1 rows of the owner's kSpecRows hottest slots (bit i =
+    // wave, slot q + nq*wave), in flight while P2 streams
+    u32x4 spu[FC1 ? CPL1 : 1], spg[FC1 ? CPL1 : 1];
+    const int spec_slot = q + nq * wave;
+    const bool spec = FC1 && wave < kSpecRows && spec_slot < p.f;
+    if constexpr (FC1) {
+        if (spec) load_fc1_rows<GATED, CPL1>(p.bundles, p.bstride, p.cd, spec_slot, lane, spu, spg);
+    }
+    uint64_t u = 0;
+    for (int b0 = 0; b0 < p.B; b0 += BT) {
         uint32_t bits[BT];
-        l2_bits<WT, CPL, BT>(w, bias, h, b0, B, H, f, slot0, theta, lane, bits);
+        l2_bits<WT, CPL2, BT>(w2, p.c2, p.h, b0, p.B, p.H, p.f, q, nq, wave, p.theta, lane,
+                              bits);
         if (lane == 0) {
 #pragma unroll
             for (int t = 0; t < BT; ++t) bits_lds[t][wave] = bits[t];
         }
         __syncthreads();
-        if (threadIdx.x < BT && (BT == 1 || b0 + (int)threadIdx.x < B)) {
-            const int t = threadIdx.x;
-            uint64_t m = 0;
+        if (threadIdx.x == 0) {
 #pragma unroll
-            for (int q = 0; q < kWaves; ++q) m |= (uint64_t)bits_lds[t][q] << (kL2Rows * q);
-            masks[(size_t)(b0 + t) * words + word] = m;
+            for (int t = 0; t < BT; ++t) {
+                if (BT == 1 || b0 + t < p.B) {
+                    uint64_t m = 0;
+#pragma unroll
+                    for (int w = 0; w < kWaves; ++w) m |= (uint64_t)bits_lds[t][w] << (kL2Rows * w);
+                    p.wbits[(size_t)(b0 + t) * nq + q] = m;
+                    u |= m;
+                }
+            }
         }
         __syncthreads();
     }
+    if (threadIdx.x == 0) {
+        p.ubits[q] = u;
+        u_lds = u;
+        if (FC1) p.out.vbits[q] = u;
+    }
+    __syncthreads();
+    if constexpr (FC1) {
+        auto slot_of = [&](int i) { return q + nq * i; };
+        owner_fc1<WT, GATED, CPL1>(q, u_lds, slot_of, p.bundles, p.bstride, p.cd, p.b1, p.x, p.B,
+                                   p.d, p.out, spec, spu, spg, wave, lane);
+    }
 }
 
-// Compaction as a kernel: one workgroup of 1024 threads; thread t owns mask
-// word t.  Union over the batch, popcount, exclusive prefix sum, then each
-// thread writes its set bits in ascending slot order at its offset.
-__global__ __launch_bounds__(1024) void k_compact(const uint64_t *__restrict__ masks, int B,
-                                                  int words, const int32_t *__restrict__ perm,
-                                                  uint64_t *__restrict__ umask,
-                                                  int32_t *__restrict__ slots,
-                                                  int32_t *__restrict__ count,
-                                                  int32_t *__restrict__ active_ids,
-                                                  int32_t *__restrict__ n_active) {
+struct Fc1Params {
+    const u32x4 *bundles;
+    size_t bstride;
+    int cd;
+    const float *b1;
+    const float *x;
+    int B, d, f;
+    int mode;              // 0 union of last prediction, 1 caller ids, 2 all
+    const uint64_t *ubits;
+    const int32_t *ids;
+    const int32_t *n_ids;
+    const int32_t *inv;
+    Fc1Out out;
+};
+
+// FC1 over a neuron set, owner q taking entries q, q+nq, ... (mode 0/2: slot
+// q + nq*i; mode 1: caller id number q + nq*i mapped to its slot).
+template <int WT, bool GATED, int CPL1>
+__global__ __launch_bounds__(kThreads) void k_fc1(Fc1Params p) {
+    __shared__ int slot_lds[kRowsPerWG];
+    __shared__ uint64_t valid_lds;
+    const int q = blockIdx.x, nq = gridDim.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (threadIdx.x < kRowsPerWG) {
+        const int i = threadIdx.x;
+        int slot = -1;
+        if (p.mode == 1) {
+            int n = *p.n_ids;
+            n = n < 0 ? 0 : (n > p.f ? p.f : n);
+            const int e = q + nq * i;
+            if (e < n) {
+                const int id = p.ids[e];
+                slot = (unsigned)id < (unsigned)p.f ? p.inv[id] : -1;
+                if ((unsigned)slot >= (unsigned)p.f) slot = -1;
+            }
+        } else {
+            const int s = q + nq * i;
+            if (s < p.f && (p.mode == 2 || ((p.ubits[q] >> i) & 1ull))) slot = s;
+        }
+        slot_lds[i] = slot;
+        const uint64_t b = __ballot(slot >= 0);
+        if (i == 0) valid_lds = b;
+    }
+    __syncthreads();
+    const uint64_t valid = valid_lds;
+    if (threadIdx.x == 0) p.out.vbits[q] = valid;
+    u32x4 none[CPL1];
+#pragma unroll
+    for (int c = 0; c < CPL1; ++c) none[c] = zero4();
+    auto slot_of = [&](int i) { return slot_lds[i]; };
+    owner_fc1<WT, GATED, CPL1>(q, valid, slot_of, p.bundles, p.bstride, p.cd, p.b1, p.x, p.B, p.d,
+                               p.out, false, none, none, wave, lane);
+}
+
+// ---------------------------------------------------------------- FC2
+struct Fc2Params {
+    const u32x4 *bundles;
+    size_t bstride;      // chunks per bundle
+    int dn_off;          // chunk offset of the down column in a bundle
+    const uint64_t *vbits;
+    const int32_t *lslot;
+    int listed;          // 0: entry i of owner q is slot q + nq*i; 1: slot from lslot
+    const float *la;
+    int max_batch;
+    int nq, d, B;
+    const float *b2;
+    const float *resid;
+    float *y;
+    float *partial;      // [kGroups][B][d]
+    unsigned *arrive;    // [kSlices]
+};
+
+// Workgroup (slice s, group g): output elements [s*W, (s+1)*W), W = d/16,
+// over the neurons listed by owners g, g+16, g+32, ...  The owners' valid-bit
+// words are loaded once (in parallel) and prefix-summed in LDS; entry e of
+// the group is bit i of owner q with rank r, its slot q + nq*i (or lslot) and
+// its activations la[q][r].  Threads form NL neuron lanes x CL chunk lanes
+// (CL = W/E); a neuron lane walks entries nl, nl+NL, ... in batches of
+// kFc2Batch loads.  The NL lane sums are added in lane order into this
+// group's partial; the last group to arrive at the slice adds the 16 partials
+// in group order, then b2, then the residual.
+template <int WT, int BT>
+__global__ __launch_bounds__(kThreads) void k_fc2(Fc2Params p) {
+    constexpr int E = Elt<WT>::E;
+    __shared__ uint64_t vb[kMaxProducers];
+    __shared__ int pre[kMaxProducers + 1];
+    __shared__ int2 tab[kMaxProducers * kRowsPerWG];  // entry -> (slot, list index)
+    __shared__ float red[kThreads * E];
+    __shared__ int last_lds;
+    const int s = blockIdx.x % kSlices, g = blockIdx.x / kSlices;
+    const int W = p.d / kSlices, CL = W / E, NL = kThreads / CL;
+    const int tid = threadIdx.x, nl = tid / CL, cl = tid % CL;
+    const bool lane_ok = nl < NL;
+    const int np = g < p.nq ? (p.nq - g + kGroups - 1) / kGroups : 0;
+    // owner words of this group (np <= 64) and their popcount prefix, by wave 0
+    if (tid < np) vb[tid] = p.vbits[g + kGroups * tid];
+    __syncthreads();
+    if (tid < 64) {
+        const int c = tid < np ? __popcll(vb[tid]) : 0;
+        int incl = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(incl, o, 64);
+            if (tid >= o) incl += v;
+        }
+        if (tid < np) pre[tid] = incl - c;
+        if (tid == 63) pre[np] = incl;
+    }
+    __syncthreads();
+    const int ng = pre[np];
+    // entry table: entry pre[k] + r is the r-th listed neuron of owner
+    // g + 16k (bit i of its word); built in one parallel pass
+    for (int idx = tid; idx < np * kRowsPerWG; idx += kThreads) {
+        const int k = idx / kRowsPerWG, i = idx % kRowsPerWG;
+        const uint64_t m = vb[k];
+        if ((m >> i) & 1ull) {
+            const int r = __popcll(m & ((1ull << i) - 1ull));
+            const int q = g + kGroups * k;
+            const int ent = q * kRowsPerWG + r;
+            tab[pre[k] + r] = make_int2(p.listed ? p.lslot[ent] : q + p.nq * i, ent);
+        }
+    }
+    __syncthreads();
+    const u32x4 *segbase = p.bundles + p.dn_off + (size_t)s * CL + cl;
+
+    for (int b0 = 0; b0 < p.B; b0 += BT) {
+        float yacc[BT][E];
+#pragma unroll
+        for (int t = 0; t < BT; ++t)
+#pragma unroll
+            for (int e = 0; e < E; ++e) yacc[t][e] = 0.0f;
+        if (lane_ok) {
+            for (int e0 = nl; e0 < ng; e0 += NL * kFc2Batch) {
+                int slot[kFc2Batch];
+                size_t ent[kFc2Batch];
+#pragma unroll
+                for (int k = 0; k < kFc2Batch; ++k) {
+                    const int e = e0 + NL * k;
+                    const int2 te = tab[e < ng ? e : ng - 1];
+                    slot[k] = te.x;
+                    ent[k] = (size_t)te.y;
+                }
+                // all of the batch's loads back to back (addresses are valid
+                // for every k; entries past ng are dropped below)
+                u32x4 v[kFc2Batch];
+                float a[kFc2Batch][BT];
+#pragma unroll
+                for (int k = 0; k < kFc2Batch; ++k) {
+                    v[k] = segbase[(size_t)slot[k] * p.bstride];
+#pragma unroll
+                    for (int t = 0; t < BT; ++t) {
+                        const int tt = (BT == 1 || b0 + t < p.B) ? b0 + t : b0;
+                        a[k][t] = p.la[ent[k] * p.max_batch + tt];
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < kFc2Batch; ++k) {
+                    if (e0 + NL * k >= ng) continue;
+                    float vd[E];
+                    unpack<WT>(v[k], vd);
+#pragma unroll
+                    for (int t = 0; t < BT; ++t)
+#pragma unroll
+                        for (int e = 0; e < E; ++e) yacc[t][e] = fmaf(a[k][t], vd[e], yacc[t][e]);
+                }
+            }
+        }
+        // sum the neuron lanes (fixed order) into this group's partial
+#pragma unroll
+        for (int t = 0; t < BT; ++t) {
+            if (lane_ok)
+#pragma unroll
+                for (int e = 0; e < E; ++e) red[nl * W + cl * E + e] = yacc[t][e];
+            __syncthreads();
+            if (BT == 1 || b0 + t < p.B) {
+                for (int w = tid; w < W; w += kThreads) {
+                    float sum = 0.0f;
+                    for (int l = 0; l < NL; ++l) sum += red[l * W + w];
+                    p.partial[((size_t)g * p.B + b0 + t) * p.d + (size_t)s * W + w] = sum;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    // arrive at the slice; the last of the kGroups groups reduces it
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const unsigned old =
+            __hip_atomic_fetch_add(p.arrive + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = old == (unsigned)(kGroups - 1);
+        if (last) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            __hip_atomic_store(p.arrive + s, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        last_lds = last;
+    }
+    __syncthreads();
+    if (last_lds) {
+        for (int idx = tid; idx < p.B * W; idx += kThreads) {
+            const int b = idx / W, w = idx % W;
+            const size_t m = (size_t)s * W + w;
+            float sum = 0.0f;
+#pragma unroll
+            for (int gg = 0; gg < kGroups; ++gg) sum += p.partial[((size_t)gg * p.B + b) * p.d + m];
+            sum += p.b2[m];
+            if (p.resid) sum += p.resid[(size_t)b * p.d + m];
+            p.y[(size_t)b * p.d + m] = sum;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- list
+// Slot-ordered outputs from the owner bits: thread t builds slot word t
+// (slots 64t .. 64t+63; slot s is bit s / nq of owner s % nq), writes the
+// per-token masks, and the ascending list of union-active slots / ids.
+__global__ __launch_bounds__(1024) void k_list(const uint64_t *__restrict__ ubits,
+                                               const uint64_t *__restrict__ wbits, int B, int f,
+                                               int nq, int words, const int32_t *__restrict__ perm,
+                                               uint64_t *__restrict__ token_masks,
+                                               int32_t *__restrict__ slots,
+                                               int32_t *__restrict__ count,
+                                               int32_t *__restrict__ active_ids,
+                                               int32_t *__restrict__ n_active) {
     __shared__ int wave_tot[16];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     uint64_t u = 0;
     if (t < words) {
-        for (int b = 0; b < B; ++b) u |= masks[(size_t)b * words + t];
-        umask[t] = u;
+        for (int j = 0; j < 64; ++j) {
+            const int s = t * 64 + j;
+            if (s < f && ((ubits[s % nq] >> (s / nq)) & 1ull)) u |= 1ull << j;
+        }
+        if (token_masks) {
+            for (int b = 0; b < B; ++b) {
+                uint64_t m = 0;
+                for (int j = 0; j < 64; ++j) {
+                    const int s = t * 64 + j;
+                    if (s < f && ((wbits[(size_t)b * nq + s % nq] >> (s / nq)) & 1ull))
+                        m |= 1ull << j;
+                }
+                token_masks[(size_t)b * words + t] = m;
+            }
+        }
     }
     const int c = __popcll(u);
     int incl = c;
@@ -347,14 +742,14 @@ __global__ __launch_bounds__(1024) void k_compact(const uint64_t *__restrict__ m
     if (lane == 63) wave_tot[wave] = incl;
     __syncthreads();
     int base = 0;
-    for (int q = 0; q < wave; ++q) base += wave_tot[q];
+    for (int k = 0; k < wave; ++k) base += wave_tot[k];
     int off = base + incl - c;
     while (u) {
         const int j = __ffsll((unsigned long long)u) - 1;
         u &= u - 1;
-        const int slot = t * 64 + j;
-        slots[off] = slot;
-        if (active_ids) active_ids[off] = perm[slot];
+        const int s = t * 64 + j;
+        slots[off] = s;
+        if (active_ids) active_ids[off] = perm[s];
         ++off;
     }
     if (t == (int)blockDim.x - 1) {
@@ -364,389 +759,12 @@ __global__ __launch_bounds__(1024) void k_compact(const uint64_t *__restrict__ m
     }
 }
 
-// ---------------------------------------------------------------- FFN
-// One workgroup's share of the FFN: the neurons at list positions g, g+G, ...
-// (slot_of(q) gives the slot of the q-th of them, or -1 to skip).  Threads
-// split each neuron's rows into 16-byte chunks (thread t owns chunks t,
-// t+NT, ...).  Neurons go in batches of NB: all their chunk loads are issued,
-// per-thread partial dots are reduced across the wave and then across the
-// waves through LDS, and each thread adds a * down-column into the partial
-// of y it owns.  The partial is written to partial_g [B][d].
-template <int WT, bool GATED, int CPT, int BT, class SlotOf>
-__device__ __forceinline__ void ffn_wg(const u32x4 *__restrict__ bundles,
-                                       const float *__restrict__ b1, const float *__restrict__ x,
-                                       int B, int d, int nmine, SlotOf slot_of,
-                                       float *__restrict__ partial_g) {
-    constexpr int E = Elt<WT>::E;
-    constexpr int NMAT = GATED ? 3 : 2;
-    constexpr int NB = (CPT * (GATED ? 3 : 2) * (BT > 1 ? 2 : 1) > 4) ? 4 : 8;
-    constexpr int UP = GATED ? 1 : 0, DN = NMAT - 1;
-    __shared__ float red[2][NB][BT][kWaves];
-
-    const int tid = threadIdx.x, NT = blockDim.x, nw = NT >> 6, lane = tid & 63, wave = tid >> 6;
-    const int C = d / E;
-    const size_t bstride = (size_t)NMAT * C;
-
-    for (int b0 = 0; b0 < B; b0 += BT) {
-        float xv[BT][CPT][E], yacc[BT][CPT][E];
-#pragma unroll
-        for (int t = 0; t < BT; ++t)
-#pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-                const int c = tid + NT * i;
-#pragma unroll
-                for (int e = 0; e < E; ++e) yacc[t][i][e] = 0.0f;
-                if (c < C && (BT == 1 || b0 + t < B))
-                    load_f32<E>(x + (size_t)(b0 + t) * d + (size_t)c * E, xv[t][i]);
-                else
-#pragma unroll
-                    for (int e = 0; e < E; ++e) xv[t][i][e] = 0.0f;
-            }
-
-        for (int q0 = 0; q0 < nmine; q0 += NB) {
-            int slot[NB];
-#pragma unroll
-            for (int k = 0; k < NB; ++k) slot[k] = (q0 + k < nmine) ? slot_of(q0 + k) : -1;
-            u32x4 wu[NB][CPT], wd[NB][CPT], wg[GATED ? NB : 1][CPT];
-#pragma unroll
-            for (int k = 0; k < NB; ++k)
-#pragma unroll
-                for (int i = 0; i < CPT; ++i) {
-                    const int c = tid + NT * i;
-                    const bool ok = slot[k] >= 0 && c < C;
-                    const u32x4 *bp = bundles + (size_t)(ok ? slot[k] : 0) * bstride + c;
-                    const u32x4 z = {0u, 0u, 0u, 0u};
-                    wu[k][i] = ok ? bp[(size_t)UP * C] : z;
-                    wd[k][i] = ok ? bp[(size_t)DN * C] : z;
-                    if constexpr (GATED) wg[k][i] = ok ? bp[0] : z;
-                }
-            // partial dots
-#pragma unroll
-            for (int k = 0; k < NB; ++k) {
-                float pu[BT], pg[BT];
-#pragma unroll
-                for (int t = 0; t < BT; ++t) pu[t] = pg[t] = 0.0f;
-#pragma unroll
-                for (int i = 0; i < CPT; ++i) {
-                    float vu[E];
-                    unpack<WT>(wu[k][i], vu);
-#pragma unroll
-                    for (int t = 0; t < BT; ++t)
-#pragma unroll
-                        for (int e = 0; e < E; ++e) pu[t] = fmaf(vu[e], xv[t][i][e], pu[t]);
-                    if constexpr (GATED) {
-                        float vg[E];
-                        unpack<WT>(wg[k][i], vg);
-#pragma unroll
-                        for (int t = 0; t < BT; ++t)
-#pragma unroll
-                            for (int e = 0; e < E; ++e) pg[t] = fmaf(vg[e], xv[t][i][e], pg[t]);
-                    }
-                }
-#pragma unroll
-                for (int t = 0; t < BT; ++t) {
-                    const float su = wave_sum(pu[t]);
-                    float sg = 0.0f;
-                    if constexpr (GATED) sg = wave_sum(pg[t]);
-                    if (lane == 0) {
-                        red[0][k][t][wave] = su;
-                        red[1][k][t][wave] = sg;
-                    }
-                }
-            }
-            __syncthreads();
-            float a[NB][BT];
-#pragma unroll
-            for (int k = 0; k < NB; ++k) {
-                const float bias = slot[k] >= 0 ? b1[slot[k]] : 0.0f;
-#pragma unroll
-                for (int t = 0; t < BT; ++t) {
-                    float su = 0.0f, sg = 0.0f;
-                    for (int w = 0; w < nw; ++w) {
-                        su += red[0][k][t][w];
-                        if constexpr (GATED) sg += red[1][k][t][w];
-                    }
-                    float av;
-                    if constexpr (GATED)
-                        av = fmaxf(sg + bias, 0.0f) * su;
-                    else
-                        av = fmaxf(su + bias, 0.0f);
-                    a[k][t] = slot[k] >= 0 ? av : 0.0f;
-                }
-            }
-            __syncthreads();
-            // AXPY of the down columns
-#pragma unroll
-            for (int k = 0; k < NB; ++k)
-#pragma unroll
-                for (int i = 0; i < CPT; ++i) {
-                    float vd[E];
-                    unpack<WT>(wd[k][i], vd);
-#pragma unroll
-                    for (int t = 0; t < BT; ++t)
-#pragma unroll
-                        for (int e = 0; e < E; ++e)
-                            yacc[t][i][e] = fmaf(a[k][t], vd[e], yacc[t][i][e]);
-                }
-        }
-        // this workgroup's partial of y
-#pragma unroll
-        for (int t = 0; t < BT; ++t)
-#pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-                const int c = tid + NT * i;
-                if (c < C && (BT == 1 || b0 + t < B)) {
-                    float4 *dst = reinterpret_cast<float4 *>(partial_g + (size_t)(b0 + t) * d +
-                                                             (size_t)c * E);
-#pragma unroll
-                    for (int k = 0; k < E / 4; ++k)
-                        dst[k] = make_float4(yacc[t][i][4 * k], yacc[t][i][4 * k + 1],
-                                             yacc[t][i][4 * k + 2], yacc[t][i][4 * k + 3]);
-                }
-            }
-    }
-}
-
-// FFN as a kernel over a list: list_mode 0 = slots, 1 = original ids (mapped
-// through the inverse neuron table, out-of-range ids skipped), 2 = all slots.
-template <int WT, bool GATED, int CPT, int BT>
-__global__ __launch_bounds__(kFfnThreads) void k_ffn(
-    const u32x4 *__restrict__ bundles, const float *__restrict__ b1, const float *__restrict__ x,
-    int B, int d, int f, int list_mode, const int32_t *__restrict__ list,
-    const int32_t *__restrict__ list_count, const int32_t *__restrict__ inv,
-    float *__restrict__ partial) {
-    const int G = gridDim.x, g = blockIdx.x;
-    int n;
-    if (list_mode == 2) {
-        n = f;
-    } else {
-        n = *list_count;
-        n = n < 0 ? 0 : (n > f ? f : n);
-    }
-    const int nmine = n > g ? (n - g + G - 1) / G : 0;
-    auto slot_of = [&](int q) -> int {
-        const int j = g + G * q;
-        int s;
-        if (list_mode == 2) {
-            s = j;
-        } else if (list_mode == 0) {
-            s = list[j];
-        } else {
-            const int id = list[j];
-            s = ((unsigned)id < (unsigned)f) ? inv[id] : -1;
-        }
-        return ((unsigned)s < (unsigned)f) ? s : -1;
-    };
-    ffn_wg<WT, GATED, CPT, BT>(bundles, b1, x, B, d, nmine, slot_of,
-                               partial + (size_t)g * B * d);
-}
-
-// ---------------------------------------------------------------- reduction
-// One tile of 32 outputs of one token: y[b][m] = (sum over workgroups g of
-// partial[g][b][m]) + b2[m] + resid[b][m].  Threads 0..255 work (8 groups of
-// 32; group q sums g = q, q+8, ... in ascending order), all threads of the
-// workgroup must call it.
-__device__ __forceinline__ void reduce_tile(const float *__restrict__ partial, int G, int B, int d,
-                                            const float *__restrict__ b2, const float *resid,
-                                            float *y, int tile, float (&red)[8][32]) {
-    constexpr int KMAX = kFfnGroups / 8;
-    const int tiles = (d + 31) / 32;
-    const int b = tile / tiles, m = (tile % tiles) * 32 + (threadIdx.x & 31);
-    const int grp = threadIdx.x >> 5;
-    if (threadIdx.x < 256) {
-        float v[KMAX];
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            const int g = grp + 8 * k;
-            v[k] = (g < G && m < d) ? partial[((size_t)g * B + b) * d + m] : 0.0f;
-        }
-        float acc = 0.0f;
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) acc += v[k];
-        red[grp][threadIdx.x & 31] = acc;
-    }
-    __syncthreads();
-    if (grp == 0 && m < d) {
-        float s = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) s += red[q][threadIdx.x];
-        s += b2[m];
-        if (resid) s += resid[(size_t)b * d + m];
-        y[(size_t)b * d + m] = s;
-    }
-    __syncthreads();
-}
-
-__global__ __launch_bounds__(256) void k_reduce(const float *__restrict__ partial, int G, int B,
-                                                int d, const float *__restrict__ b2,
-                                                const float *resid, float *y) {
-    __shared__ float red[8][32];
-    reduce_tile(partial, G, B, d, b2, resid, y, blockIdx.x, red);
-}
-
-// ---------------------------------------------------------------- fused step
-struct DecodeParams {
-    const u32x4 *p1;
-    const float *c1;
-    const u32x4 *p2;
-    const float *c2;
-    const u32x4 *bundles;
-    const float *b1;
-    const float *b2;
-    const int32_t *perm;
-    int d, f, H, words;
-    float theta;
-    const float *x;
-    const float *resid;
-    float *y;
-    float *h;
-    uint64_t *masks;
-    uint64_t *umask;
-    int32_t *slots;
-    int32_t *count;
-    float *partial;
-    unsigned *bar;
-    int *err;
-    int32_t *active_ids;
-    int32_t *n_active;
-};
-
-// One decode step of one token (B = 1) in one cooperative launch of
-// kFfnGroups workgroups x kFfnThreads threads.  Phases, split by grid
-// barriers: (1) predictor layer 1, with the layer-2 rows of this workgroup's
-// first mask word already in flight; (2) layer 2 + threshold -> mask words;
-// (3) every workgroup rebuilds the prefix sums of the mask words in LDS,
-// finds the slots at its list positions g, g+G, ... by binary search, writes
-// them to the active list, and runs its FFN share; (4) reduction tiles.
-template <int WT, int CPL1, int CPL2, bool GATED, int CPT>
-__global__ __launch_bounds__(kFfnThreads) void k_decode(DecodeParams p) {
-    constexpr int E = Elt<WT>::E;
-    __shared__ uint64_t um[kMaxFfn / 64];
-    __shared__ int pre[kMaxFfn / 64 + 1];
-    __shared__ int wave_tot[kWaves];
-    __shared__ uint32_t bits_lds[kWaves];
-    __shared__ float red[8][32];
-    __shared__ int myslots[kMaxFfn / kFfnGroups];
-
-    const int G = gridDim.x, g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int GW = G * kWaves, gw = g * kWaves + wave;
-
-    // (0) layer-2 rows of the first word of this workgroup: loads in flight now
-    u32x4 w2[kL2Rows][CPL2];
-    float bias2[kL2Rows];
-    const int C2 = p.H / E;
-    if (g < p.words) l2_load<CPL2>(p.p2, p.c2, p.f, C2, g * 64 + wave * kL2Rows, lane, w2, bias2);
-
-    // (1) predictor layer 1
-    for (int row = gw; row < p.H; row += GW)
-        l1_row<WT, CPL1, 1>(p.p1, p.c1, p.x, 1, p.d, p.H, row, p.h, lane);
-    grid_sync(p.bar, G, p.err);
-
-    // (2) layer 2 + threshold
-    for (int q = g; q < p.words; q += G) {
-        const int slot0 = q * 64 + wave * kL2Rows;
-        if (q != g) l2_load<CPL2>(p.p2, p.c2, p.f, C2, slot0, lane, w2, bias2);
-        uint32_t bits[1];
-        l2_bits<WT, CPL2, 1>(w2, bias2, p.h, 0, 1, p.H, p.f, slot0, p.theta, lane, bits);
-        if (lane == 0) bits_lds[wave] = bits[0];
-        __syncthreads();
-        if (tid == 0) {
-            uint64_t m = 0;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) m |= (uint64_t)bits_lds[w] << (kL2Rows * w);
-            p.masks[q] = m;
-        }
-        __syncthreads();
-    }
-    grid_sync(p.bar, G, p.err);
-
-    // (3) compaction: prefix sums of the popcounts of all words (thread t owns
-    // words 2t and 2t+1)
-    const int w0 = 2 * tid;
-    const uint64_t m0 = w0 < p.words ? p.masks[w0] : 0ull;
-    const uint64_t m1 = w0 + 1 < p.words ? p.masks[w0 + 1] : 0ull;
-    if (w0 < p.words) um[w0] = m0;
-    if (w0 + 1 < p.words) um[w0 + 1] = m1;
-    const int loc = __popcll(m0) + __popcll(m1);
-    int incl = loc;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-    }
-    if (lane == 63) wave_tot[wave] = incl;
-    __syncthreads();
-    int base = 0, total = 0;
-    for (int w = 0; w < kWaves; ++w) {
-        if (w < wave) base += wave_tot[w];
-        total += wave_tot[w];
-    }
-    {
-        const int ex = base + incl - loc;
-        if (w0 < p.words) pre[w0] = ex;
-        if (w0 + 1 < p.words) pre[w0 + 1] = ex + __popcll(m0);
-    }
-    __syncthreads();
-    if (g == 0) {
-        for (int w = tid; w < p.words; w += blockDim.x) p.umask[w] = um[w];
-        if (tid == 0) {
-            *p.count = total;
-            if (p.n_active) *p.n_active = total;
-        }
-    }
-    // slots of this workgroup's list positions j = g + G*q: thread q finds
-    // the word holding the j-th set bit (binary search over the prefix sums)
-    // and the bit inside it; the slots go to LDS and to the active list
-    const int nmine = total > g ? (total - g + G - 1) / G : 0;
-    if (tid < nmine) {
-        const int j = g + G * tid;
-        int lo = 0, hi = p.words - 1;  // last word w with pre[w] <= j
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (pre[mid] <= j) lo = mid;
-            else hi = mid - 1;
-        }
-        uint64_t m = um[lo];
-        int r = j - pre[lo], off = 0;
-#pragma unroll
-        for (int step = 32; step >= 8; step >>= 1) {
-            const uint64_t low = m & ((1ull << step) - 1ull);
-            const int c = __popcll(low);
-            if (r >= c) {
-                r -= c;
-                m >>= step;
-                off += step;
-            } else {
-                m = low;
-            }
-        }
-        for (; r > 0; --r) m &= m - 1;
-        const int s = lo * 64 + off + __ffsll((unsigned long long)m) - 1;
-        myslots[tid] = s;
-        p.slots[j] = s;
-        if (p.active_ids) p.active_ids[j] = p.perm[s];
-    }
-    __syncthreads();
-    auto slot_of = [&](int q) -> int { return myslots[q]; };
-    ffn_wg<WT, GATED, CPT, 1>(p.bundles, p.b1, p.x, 1, p.d, nmine, slot_of,
-                              p.partial + (size_t)g * p.d);
-    grid_sync(p.bar, G, p.err);
-
-    // (4) reduction
-    const int tiles = (p.d + 31) / 32;
-    for (int t = g; t < tiles; t += G) reduce_tile(p.partial, G, 1, p.d, p.b2, p.resid, p.y, t, red);
-}
-
-__global__ void k_read_error(int *err, int32_t *out, int clear) {
-    if (threadIdx.x == 0) {
-        *out = *err;
-        if (clear) *err = 0;
-    }
-}
-
-inline void trace_mark(const Trace *tr, int k, int edge, hipStream_t s) {
-    if (tr && tr->ev[2 * k + edge]) (void)hipEventRecord(tr->ev[2 * k + edge], s);
-}
+// Traced launches carry their start/stop events on the dispatch packet itself
+// (hipExtLaunchKernelGGL), so the events time exactly the kernel.
+inline hipEvent_t ev_start(const Trace *tr, int k) { return tr ? tr->ev[2 * k] : nullptr; }
+inline hipEvent_t ev_stop(const Trace *tr, int k) { return tr ? tr->ev[2 * k + 1] : nullptr; }
+#define ASF_LAUNCH(KID, F, GRID, BLK, ...) \
+    hipExtLaunchKernelGGL(F, GRID, BLK, 0, s, ev_start(tr, KID), ev_stop(tr, KID), 0, __VA_ARGS__)
 
 inline int pow2_at_least(int v) {
     int p = 1;
@@ -791,180 +809,177 @@ hipError_t launch_gather_f32(const float *src, const int32_t *perm, int n, float
     return hipGetLastError();
 }
 
-template <int WT>
-static void dispatch_pred(const LayerView &L, const float *x, int B, uint64_t *masks,
-                          const Trace *tr, hipStream_t s) {
-    const int cpl1 = pow2_at_least((L.cd + 63) / 64);
-    const dim3 g1((L.H + 3) / 4), blk(256);
-    const u32x4 *P1 = (const u32x4 *)L.p1;
-#define ASF_L1(CPL, BT) \
-    hipLaunchKernelGGL((k_pred_l1<WT, CPL, BT>), g1, blk, 0, s, P1, L.c1, x, B, L.d, L.H, L.h)
-#define ASF_L1B(CPL) \
-    if (B == 1) ASF_L1(CPL, 1); else ASF_L1(CPL, 4);
-    trace_mark(tr, ASF_K_PRED_L1, 0, s);
-    switch (cpl1) {
-    case 1: ASF_L1B(1) break;
-    case 2: ASF_L1B(2) break;
-    case 4: ASF_L1B(4) break;
-    case 8: ASF_L1B(8) break;
-    default: ASF_L1B(16) break;
-    }
-    trace_mark(tr, ASF_K_PRED_L1, 1, s);
-#undef ASF_L1B
-#undef ASF_L1
-    const int cpl2 = pow2_at_least((L.ch + 63) / 64);
-    const dim3 g2(L.words), blk2(kFfnThreads);
-    const u32x4 *P2 = (const u32x4 *)L.p2;
-#define ASF_L2(CPL, BT)                                                                        \
-    hipLaunchKernelGGL((k_pred_l2<WT, CPL, BT>), g2, blk2, 0, s, P2, L.c2, L.h, B, L.H, L.f, \
-                       L.words, L.threshold, masks)
-#define ASF_L2B(CPL) \
-    if (B == 1) ASF_L2(CPL, 1); else ASF_L2(CPL, 4);
-    trace_mark(tr, ASF_K_PRED_L2, 0, s);
-    switch (cpl2) {
-    case 1: ASF_L2B(1) break;
-    case 2: ASF_L2B(2) break;
-    default: ASF_L2B(4) break;
-    }
-    trace_mark(tr, ASF_K_PRED_L2, 1, s);
-#undef ASF_L2B
-#undef ASF_L2
+// waves per predictor layer-1 row and the resulting chunks per lane
+static void l1_shape(const LayerView &L, int *wpr, int *cpl) {
+    int w = L.H >= 2048 ? 1 : pow2_at_least((2048 + L.H - 1) / L.H);
+    if (w > 8) w = 8;
+    while (w < 8 && (L.cd + 64 * w - 1) / (64 * w) > 8) w *= 2;
+    *wpr = w;
+    *cpl = pow2_at_least((L.cd + 64 * w - 1) / (64 * w));
 }
 
-hipError_t launch_predict(const LayerView &L, const float *x, int B, int32_t *active_ids,
-                          int32_t *n_active, uint64_t *token_masks, const Trace *tr,
+hipError_t launch_pred_l1(const LayerView &L, const float *x, int B, const Trace *tr,
                           hipStream_t s) {
-    uint64_t *masks = token_masks ? token_masks : L.masks;
-    if (L.wtype == ASF_F16)
-        dispatch_pred<1>(L, x, B, masks, tr, s);
-    else
-        dispatch_pred<0>(L, x, B, masks, tr, s);
-    trace_mark(tr, ASF_K_COMPACT, 0, s);
-    hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, s, (const uint64_t *)masks, B, L.words,
-                       (const int32_t *)L.perm, L.umask, L.slots, L.count, active_ids, n_active);
-    trace_mark(tr, ASF_K_COMPACT, 1, s);
+    int wpr, cpl;
+    l1_shape(L, &wpr, &cpl);
+    const int rpw = kWaves / wpr;
+    const dim3 grid((L.H + rpw - 1) / rpw), blk(kThreads);
+    const u32x4 *P1 = (const u32x4 *)L.p1;
+#define ASF_L1(WT, CPL, BT)                                                                 \
+    ASF_LAUNCH(ASF_K_PRED_L1, (k_pred_l1<WT, CPL, BT>), grid, blk, P1, L.c1, x, B, L.d, L.H,  \
+               wpr, L.h)
+#define ASF_L1C(WT, CPL) \
+    if (B == 1) ASF_L1(WT, CPL, 1); else ASF_L1(WT, CPL, 4);
+#define ASF_L1W(WT)                   \
+    switch (cpl) {                    \
+    case 1: ASF_L1C(WT, 1) break;     \
+    case 2: ASF_L1C(WT, 2) break;     \
+    case 4: ASF_L1C(WT, 4) break;     \
+    default: ASF_L1C(WT, 8) break;    \
+    }
+    if (L.wtype == ASF_F16) { ASF_L1W(1) } else { ASF_L1W(0) }
+#undef ASF_L1W
+#undef ASF_L1C
+#undef ASF_L1
     return hipGetLastError();
 }
 
-template <int WT, bool GATED>
-static void dispatch_ffn(const LayerView &L, const float *x, int B, int list_mode,
-                         const int32_t *list, const int32_t *cnt, hipStream_t s) {
-    constexpr int E = WT ? 8 : 4;
-    const int C = L.d / E;
-    const int cpt = (C + kFfnThreads - 1) / kFfnThreads;
-    const u32x4 *bp = (const u32x4 *)L.bundles;
-#define ASF_FFN(CPT, BT)                                                                     \
-    hipLaunchKernelGGL((k_ffn<WT, GATED, CPT, BT>), dim3(kFfnGroups), dim3(kFfnThreads), 0, \
-                       s, bp, L.b1, x, B, L.d, L.f, list_mode, list, cnt, L.inv,           \
-                       L.partial)
-    if (cpt <= 1) {
-        if (B == 1) ASF_FFN(1, 1); else ASF_FFN(1, 4);
-    } else {
-        if (B == 1) ASF_FFN(2, 1); else ASF_FFN(2, 4);
-    }
-#undef ASF_FFN
-}
+static Fc1Out fc1_out(const LayerView &L) { return Fc1Out{L.vbits, L.lslot, L.la, L.max_batch}; }
 
-hipError_t launch_ffn(const LayerView &L, const float *x, int B, int list_mode, const int32_t *ids,
-                      const int32_t *n_ids, const float *resid, float *y, const Trace *tr,
-                      hipStream_t s) {
-    const int32_t *list = list_mode == 0 ? L.slots : ids;
-    const int32_t *cnt = list_mode == 0 ? L.count : n_ids;
-    trace_mark(tr, ASF_K_FFN, 0, s);
-    if (L.wtype == ASF_F16) {
-        if (L.gated) dispatch_ffn<1, true>(L, x, B, list_mode, list, cnt, s);
-        else dispatch_ffn<1, false>(L, x, B, list_mode, list, cnt, s);
-    } else {
-        if (L.gated) dispatch_ffn<0, true>(L, x, B, list_mode, list, cnt, s);
-        else dispatch_ffn<0, false>(L, x, B, list_mode, list, cnt, s);
-    }
-    trace_mark(tr, ASF_K_FFN, 1, s);
-    const int tiles = (L.d + 31) / 32;
-    trace_mark(tr, ASF_K_REDUCE, 0, s);
-    hipLaunchKernelGGL(k_reduce, dim3(B * tiles), dim3(256), 0, s, (const float *)L.partial,
-                       kFfnGroups, B, L.d, (const float *)L.b2, resid, y);
-    trace_mark(tr, ASF_K_REDUCE, 1, s);
-    return hipGetLastError();
-}
-
-// ---------------------------------------------------------------- fused step
-// Kernel pointer of the fused decode kernel for a layer, or null when the
-// layer's shape has no fused variant (fp32 weights).
-static const void *decode_kernel(const LayerView &L) {
-    if (L.wtype != ASF_F16) return nullptr;
-    const int cpl1 = pow2_at_least((L.cd + 63) / 64);
-    const int cpl2 = pow2_at_least((L.ch + 63) / 64);
-    const int cpt = (L.cd + kFfnThreads - 1) / kFfnThreads;
-    if (cpl1 < 4 || cpl1 > 16 || cpl2 > 4 || cpt > 2) return nullptr;
-#define ASF_DK(C1, C2, CT)                                                                  \
-    return L.gated ? (const void *)&k_decode<1, C1, C2, true, CT>                         \
-                   : (const void *)&k_decode<1, C1, C2, false, CT>;
-#define ASF_DK2(C1, CT)              \
-    switch (cpl2) {                  \
-    case 1: ASF_DK(C1, 1, CT)        \
-    case 2: ASF_DK(C1, 2, CT)        \
-    default: ASF_DK(C1, 4, CT)       \
-    }
-    if (cpl1 == 4) { ASF_DK2(4, 1) }
-    if (cpl1 == 8) { ASF_DK2(8, 1) }
-    ASF_DK2(16, 2)
-#undef ASF_DK2
-#undef ASF_DK
-}
-
-bool fused_supported(const LayerView &L) {
-    const void *k = decode_kernel(L);
-    if (!k) return false;
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return false;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return false;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kFfnThreads, 0) != hipSuccess)
-        return false;
-    return (long)per_cu * cus >= kFfnGroups;
-}
-
-hipError_t launch_decode_fused(const LayerView &L, const float *x, const float *resid, float *y,
-                               int32_t *active_ids, int32_t *n_active, const Trace *tr,
-                               hipStream_t s) {
-    const void *k = decode_kernel(L);
-    if (!k) return hipErrorInvalidValue;
-    DecodeParams p;
-    p.p1 = (const u32x4 *)L.p1;
-    p.c1 = L.c1;
+hipError_t launch_score(const LayerView &L, const float *x, int B, bool fc1, const Trace *tr,
+                        hipStream_t s) {
+    ScoreParams p;
     p.p2 = (const u32x4 *)L.p2;
     p.c2 = L.c2;
-    p.bundles = (const u32x4 *)L.bundles;
-    p.b1 = L.b1;
-    p.b2 = L.b2;
-    p.perm = L.perm;
-    p.d = L.d;
-    p.f = L.f;
-    p.H = L.H;
-    p.words = L.words;
-    p.theta = L.threshold;
-    p.x = x;
-    p.resid = resid;
-    p.y = y;
     p.h = L.h;
-    p.masks = L.masks;
-    p.umask = L.umask;
-    p.slots = L.slots;
-    p.count = L.count;
-    p.partial = L.partial;
-    p.bar = L.bar;
-    p.err = L.err;
-    p.active_ids = active_ids;
-    p.n_active = n_active;
-    void *args[] = {&p};
-    trace_mark(tr, ASF_K_DECODE, 0, s);
-    hipError_t e = hipLaunchCooperativeKernel(k, dim3(kFfnGroups), dim3(kFfnThreads), args, 0, s);
-    trace_mark(tr, ASF_K_DECODE, 1, s);
-    return e != hipSuccess ? e : hipGetLastError();
+    p.B = B;
+    p.H = L.H;
+    p.f = L.f;
+    p.theta = L.threshold;
+    p.wbits = L.wbits;
+    p.ubits = L.ubits;
+    p.bundles = (const u32x4 *)L.bundles;
+    p.bstride = (size_t)L.nmat * L.cd;
+    p.cd = L.cd;
+    p.b1 = L.b1;
+    p.x = x;
+    p.d = L.d;
+    p.out = fc1_out(L);
+    const int cpl2 = pow2_at_least((L.ch + 63) / 64);
+    const int cpl1 = pow2_at_least((L.cd + 63) / 64);
+    const dim3 grid(L.nq), blk(kThreads);
+    const bool fused = fc1 && L.wtype == ASF_F16 && B == 1;
+    const int k = fused ? ASF_K_SCORE_FC1 : ASF_K_SCORE;
+    if (fused) {
+#define ASF_SF(C2, C1)                                                                          \
+    if (L.gated) ASF_LAUNCH(k, (k_score<1, C2, 1, true, true, C1>), grid, blk, p);              \
+    else ASF_LAUNCH(k, (k_score<1, C2, 1, true, false, C1>), grid, blk, p);
+#define ASF_SF1(C2)                   \
+    switch (cpl1) {                   \
+    case 1: ASF_SF(C2, 1) break;      \
+    case 2: ASF_SF(C2, 2) break;      \
+    case 4: ASF_SF(C2, 4) break;      \
+    case 8: ASF_SF(C2, 8) break;      \
+    default: ASF_SF(C2, 16) break;    \
+    }
+        switch (cpl2) {
+        case 1: ASF_SF1(1) break;
+        case 2: ASF_SF1(2) break;
+        default: ASF_SF1(4) break;
+        }
+#undef ASF_SF1
+#undef ASF_SF
+    } else {
+#define ASF_S(WT, C2)                                                                          \
+    if (B == 1) ASF_LAUNCH(k, (k_score<WT, C2, 1, false, false, 1>), grid, blk, p);            \
+    else ASF_LAUNCH(k, (k_score<WT, C2, 4, false, false, 1>), grid, blk, p);
+#define ASF_SW(WT)                  \
+    switch (cpl2) {                 \
+    case 1: ASF_S(WT, 1) break;     \
+    case 2: ASF_S(WT, 2) break;     \
+    default: ASF_S(WT, 4) break;    \
+    }
+        if (L.wtype == ASF_F16) { ASF_SW(1) } else { ASF_SW(0) }
+#undef ASF_SW
+#undef ASF_S
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !fc1 || fused) return e;
+    // the score-only kernel ran: FC1 of the union separately
+    return launch_fc1(L, x, B, 0, nullptr, nullptr, tr, s);
 }
 
-hipError_t launch_read_error(const LayerView &L, int32_t *out, int clear, hipStream_t s) {
-    hipLaunchKernelGGL(k_read_error, dim3(1), dim3(64), 0, s, L.err, out, clear);
+hipError_t launch_fc1(const LayerView &L, const float *x, int B, int mode, const int32_t *ids,
+                      const int32_t *n_ids, const Trace *tr, hipStream_t s) {
+    Fc1Params p;
+    p.bundles = (const u32x4 *)L.bundles;
+    p.bstride = (size_t)L.nmat * L.cd;
+    p.cd = L.cd;
+    p.b1 = L.b1;
+    p.x = x;
+    p.B = B;
+    p.d = L.d;
+    p.f = L.f;
+    p.mode = mode;
+    p.ubits = L.ubits;
+    p.ids = ids;
+    p.n_ids = n_ids;
+    p.inv = L.inv;
+    p.out = fc1_out(L);
+    const int cpl1 = pow2_at_least((L.cd + 63) / 64);
+    const dim3 grid(L.nq), blk(kThreads);
+#define ASF_F(WT, C1)                                                             \
+    if (L.gated) ASF_LAUNCH(ASF_K_FC1, (k_fc1<WT, true, C1>), grid, blk, p); \
+    else ASF_LAUNCH(ASF_K_FC1, (k_fc1<WT, false, C1>), grid, blk, p);
+#define ASF_FW(WT)                   \
+    switch (cpl1) {                  \
+    case 1: ASF_F(WT, 1) break;      \
+    case 2: ASF_F(WT, 2) break;      \
+    case 4: ASF_F(WT, 4) break;      \
+    case 8: ASF_F(WT, 8) break;      \
+    default: ASF_F(WT, 16) break;    \
+    }
+    if (L.wtype == ASF_F16) { ASF_FW(1) } else { ASF_FW(0) }
+#undef ASF_FW
+#undef ASF_F
+    return hipGetLastError();
+}
+
+hipError_t launch_fc2(const LayerView &L, int B, bool listed, const float *resid, float *y,
+                      const Trace *tr, hipStream_t s) {
+    Fc2Params p;
+    p.bundles = (const u32x4 *)L.bundles;
+    p.bstride = (size_t)L.nmat * L.cd;
+    p.dn_off = (L.nmat - 1) * L.cd;
+    p.vbits = L.vbits;
+    p.lslot = L.lslot;
+    p.listed = listed ? 1 : 0;
+    p.la = L.la;
+    p.max_batch = L.max_batch;
+    p.nq = L.nq;
+    p.d = L.d;
+    p.B = B;
+    p.b2 = L.b2;
+    p.resid = resid;
+    p.y = y;
+    p.partial = L.partial;
+    p.arrive = L.arrive;
+    const dim3 grid(kSlices * kGroups), blk(kThreads);
+    if (L.wtype == ASF_F16) {
+        if (B == 1) ASF_LAUNCH(ASF_K_FC2, (k_fc2<1, 1>), grid, blk, p);
+        else ASF_LAUNCH(ASF_K_FC2, (k_fc2<1, 4>), grid, blk, p);
+    } else {
+        if (B == 1) ASF_LAUNCH(ASF_K_FC2, (k_fc2<0, 1>), grid, blk, p);
+        else ASF_LAUNCH(ASF_K_FC2, (k_fc2<0, 4>), grid, blk, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_list(const LayerView &L, int B, int32_t *active_ids, int32_t *n_active,
+                       uint64_t *token_masks, const Trace *tr, hipStream_t s) {
+    ASF_LAUNCH(ASF_K_LIST, k_list, dim3(1), dim3(1024), (const uint64_t *)L.ubits,
+                       (const uint64_t *)L.wbits, B, L.f, L.nq, L.words, (const int32_t *)L.perm,
+                       token_masks, L.slots, L.count, active_ids, n_active);
     return hipGetLastError();
 }
 

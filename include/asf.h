@@ -82,8 +82,11 @@ typedef enum {
  *   threshold    logit threshold theta: neuron i is predicted active when
  *                its score s_i > theta (strict).  0 is the sigmoid-0.5
  *                decision of the pages' per-output binary classifier.
- * Alignment: d_model * sizeof(weight) and pred_hidden * sizeof(weight) must
- * be multiples of 16 bytes (d_model % 8 == 0 for ASF_F16, % 4 for ASF_F32). */
+ * Alignment: d_model * sizeof(weight) must be a multiple of 256 bytes
+ * (d_model % 128 == 0 for ASF_F16, % 64 for ASF_F32; the FC2 kernel splits
+ * d_model into 16 slices of whole 16-byte chunks) and pred_hidden *
+ * sizeof(weight) a multiple of 16 bytes.  Limits: d_model * sizeof(weight)
+ * <= 16 KiB, pred_hidden * sizeof(weight) <= 4 KiB. */
 typedef struct {
     int32_t d_model;
     int32_t d_ffn;
@@ -172,13 +175,9 @@ asf_status asf_sparse_ffn(const asf_layer *layer, const float *x, int32_t B,
 
 /* One decode step of one layer: asf_predict followed by asf_sparse_ffn over
  * the predicted union set, with no host round trip in between.  The optional
- * outputs are those of asf_predict.  For B == 1 with fp16 weights this is a
- * single cooperative kernel (all workgroups co-resident, grid barriers
- * between the predictor, threshold, compaction/FFN and reduction phases)
- * whose results are bit-identical to the separate calls; otherwise the
- * separate kernels run back to back.  A grid-barrier wait that makes no
- * progress for about a second is abandoned and reported through
- * asf_layer_read_error instead of hanging the device. */
+ * outputs are those of asf_predict.  Three kernels (predictor layer 1;
+ * layer 2 + threshold + FC1; FC2 + reduction); the results are bit-identical
+ * to asf_predict followed by asf_sparse_ffn with active == NULL. */
 asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
                            const float *residual, float *y, int32_t *active,
                            int32_t *n_active, void *stream);
@@ -187,14 +186,19 @@ asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
 asf_status asf_dense_ffn_ref(const asf_layer *layer, const float *x, int32_t B,
                              const float *residual, float *y, void *stream);
 
-/* Kernels of a decode step, in launch order (ids for asf_layer_set_trace). */
+/* Kernels behind the calls (ids for asf_layer_set_trace).
+ *   asf_predict       PRED_L1, SCORE, then LIST when an output is requested
+ *   asf_decode_step   PRED_L1, SCORE_FC1 (B == 1, fp16; else SCORE + FC1),
+ *                     FC2, then LIST when an output is requested
+ *   asf_sparse_ffn    FC1, FC2
+ *   asf_dense_ffn_ref FC1 (every neuron), FC2 */
 typedef enum {
-    ASF_K_PRED_L1 = 0, /* predictor layer 1 GEMV */
-    ASF_K_PRED_L2 = 1, /* predictor layer 2 GEMV + threshold -> mask words */
-    ASF_K_COMPACT = 2, /* union + prefix sum -> active list */
-    ASF_K_FFN = 3,     /* gathered FC1 (+ReLU) and FC2 AXPY -> partial sums */
-    ASF_K_REDUCE = 4,  /* partial sums + b2 + residual -> y */
-    ASF_K_DECODE = 5,  /* the one-launch decode step (all of the above fused) */
+    ASF_K_PRED_L1 = 0,   /* predictor layer 1 GEMV */
+    ASF_K_SCORE = 1,     /* predictor layer 2 GEMV + threshold -> mask bits */
+    ASF_K_SCORE_FC1 = 2, /* the same, then FC1 of the predicted neurons */
+    ASF_K_FC1 = 3,       /* FC1 (+ReLU) of a neuron set */
+    ASF_K_FC2 = 4,       /* FC2 column gather + reduction -> y */
+    ASF_K_LIST = 5,      /* slot-ordered masks and active list */
     ASF_K_COUNT = 6
 } asf_kernel_id;
 
@@ -205,16 +209,6 @@ typedef enum {
  * (NULL entries are skipped).  events == NULL or n == 0 turns tracing off.
  * The handles are borrowed: the caller creates and destroys them. */
 asf_status asf_layer_set_trace(asf_layer *layer, void *const *events, int32_t n);
-
-/* Device-side error bits of a layer (bit 0: a grid-barrier wait of the fused
- * decode kernel timed out, so that step's outputs are invalid).  Writes the
- * bits to the DEVICE int32 *flags, stream-ordered after earlier work, and
- * clears them when `clear` is nonzero. */
-asf_status asf_layer_read_error(const asf_layer *layer, int32_t *flags, int32_t clear,
-                                void *stream);
-
-/* 1 when asf_decode_step runs as the single fused kernel for B == 1. */
-int32_t asf_layer_is_fused(const asf_layer *layer);
 
 /* Human-readable name of a status code (static string). */
 const char *asf_status_string(asf_status s);

@@ -47,8 +47,10 @@ def test_storage_bytes_validation(asf):
     assert asf.storage_bytes(4096, 16384, 1024, 1, True, asf.F16) > ok        # gate matrix
     assert asf.storage_bytes(4096, 16385, 1024, 1, False, asf.F16) > ok       # ragged f
     assert asf.storage_bytes(4100, 16384, 1024, 1, False, asf.F16) == 0       # d % 8 != 0
+    assert asf.storage_bytes(4104, 16384, 1024, 1, False, asf.F16) == 0       # d % 128 != 0
     assert asf.storage_bytes(4096, 16384, 1020, 1, False, asf.F16) == 0       # H % 8 != 0
-    assert asf.storage_bytes(4092, 16384, 1024, 1, False, asf.F32) > 0        # fp32: d % 4
+    assert asf.storage_bytes(4032, 16384, 1024, 1, False, asf.F32) > 0        # fp32: d % 64
+    assert asf.storage_bytes(4092, 16384, 1024, 1, False, asf.F32) == 0
     assert asf.storage_bytes(4096, 16384, 1024, 0, False, asf.F16) == 0       # B range
     assert asf.storage_bytes(4096, 16384, 1024, 33, False, asf.F16) == 0
     assert asf.storage_bytes(4096, 65537, 1024, 1, False, asf.F16) == 0       # f limit
@@ -80,10 +82,10 @@ def test_create_layer_host_validation(asf):
                               lib.asf_layer_storage_bytes(ctypes.byref(gdesc)), None,
                               ctypes.byref(out))
     assert st == 5                                            # gated without w_gate
-    bad = asf.make_desc(260, 1024, 64, 1, False, asf.F16)
+    bad = asf.make_desc(264, 1024, 64, 1, False, asf.F16)
     st = lib.asf_create_layer(ctypes.byref(bad), ctypes.byref(w), None, fake, need, None,
                               ctypes.byref(out))
-    assert st == 3                                            # d*2 not a multiple of 16
+    assert st == 3                                            # d*2 not a multiple of 256
     w3 = asf.LayerWeights(None, None, None, fake, None, fake, None, fake, None)
     st = lib.asf_create_layer(ctypes.byref(desc), ctypes.byref(w3), None, fake, need, None,
                               ctypes.byref(out))

@@ -225,17 +225,15 @@ def test_deterministic_repeat():
 
 @pytest.mark.parametrize("d,f,H,gated", [(2048, 3000, 256, False), (2048, 2500, 512, True),
                                          (5120, 4160, 1024, False), (7168, 2048, 2048, False)])
-def test_fused_decode_kernel(orc, d, f, H, gated):
-    """The one-launch decode kernel (fp16, B = 1) across its register-tiling
-    variants: same bits as the separate predict + sparse_ffn kernels, oracle
-    parity, and no barrier timeouts."""
+def test_decode_step_tiling_variants(orc, d, f, H, gated):
+    """The decode-step kernels (fp16, B = 1) across their register-tiling
+    variants (d and H classes): same bits as predict + sparse_ffn, oracle
+    parity."""
     need_gpu()
     _, sh = wl.CONFIGS["llama7b_gated_relu" if gated else "opt6.7b_ffn"]
     L = wl.make_layer(wl.scaled_shape(sh, d, f, H), 500 + d + f)
     lay = asf().layer_from_numpy(L)
-    assert lay.fused
     x = wl.make_tokens(d, 5, 600 + f)
     worst = _run_tokens(orc, L, x, lay, "fused %dx%d H%d%s" % (d, f, H, " gated" if gated else ""),
                         check_dense=False)
-    assert lay.read_error() == 0
     assert worst <= TOL["f16"]
