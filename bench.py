@@ -21,6 +21,7 @@ import argparse
 import ctypes
 import json
 import os
+import re
 import sys
 import time
 
@@ -76,6 +77,38 @@ def bytes_model(sh, k_mean):
             + k_mean * (nmat * d * ws + 4) + d * 4 + d * 4)
     dense = f * (nmat * d * ws + 4) + d * 4 * 3
     return step, per, dense
+
+
+PROFILE = os.path.join(ROOT, "profiles", "decode_step_opt6.7b_4096x16384_fp16.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "activation_sparse_ffn_02_amd", "csrc", n)
+                  for n in ("asf_kernels.hip", "asf_internal.h")]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` (calibrated FETCH_SIZE + WRITE_SIZE)
+    from the committed counter summary, or None when that summary is missing
+    or was taken on kernel sources other than the ones built here."""
+    try:
+        text = open(PROFILE).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    k = rec.get("per_launch_bytes", {}).get(kernel)
+    return None if k is None else k["fetch"] + k["write"]
 
 
 class HipEvents:
@@ -243,17 +276,20 @@ def main():
     achieved = per_bytes[dname] / (kmean[dom] * 1e-3) / 1e9
     gpu_kernel_ms = float(kt.sum(axis=1).mean())
 
-    # dense comparator on the same ring
-    for i in range(20):
-        ring[i % args.ring].dense_ffn_ref(Xd[i % args.tokens], out=Y[i % args.ring])
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(args.dense_steps):
-        ring[i % args.ring].dense_ffn_ref(Xd[i % args.tokens], out=Y[i % args.ring])
-    e1.record()
-    torch.cuda.synchronize()
-    dense_ms = e0.elapsed_time(e1) / args.dense_steps
+    # dense comparator on the same ring (skipped with --dense-steps 0, e.g. for
+    # counter runs that must see the sparse step's kernels only)
+    dense_ms = None
+    if args.dense_steps > 0:
+        for i in range(20):
+            ring[i % args.ring].dense_ffn_ref(Xd[i % args.tokens], out=Y[i % args.ring])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.dense_steps):
+            ring[i % args.ring].dense_ffn_ref(Xd[i % args.tokens], out=Y[i % args.ring])
+        e1.record()
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / args.dense_steps
 
     tok_s = K / elapsed
     eff_gbs = step_bytes * K / elapsed / 1e9
@@ -285,11 +321,12 @@ def main():
         "traced_steps": len(traced_steps),
         "gpu_span_ms_per_step": gpu_span_ms / K,
         "dense_ms_per_step": dense_ms,
-        "dense_gbps": dense_bytes / (dense_ms * 1e-3) / 1e9,
-        "sparse_step_speedup_vs_dense": dense_ms / ms_per_step,
+        "dense_gbps": None if dense_ms is None else dense_bytes / (dense_ms * 1e-3) / 1e9,
+        "sparse_step_speedup_vs_dense": None if dense_ms is None else dense_ms / ms_per_step,
         "roofline": {"bound": "hbm", "kernel": dname, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None},
+                     "traffic": measured_traffic(dname),
+                     "algorithmic_bytes": per_bytes[dname]},
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(args, L, X)
