@@ -60,6 +60,8 @@ _lib.asf_sparse_ffn.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
 _lib.asf_sparse_ffn.restype = ctypes.c_int
 _lib.asf_decode_step.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
 _lib.asf_decode_step.restype = ctypes.c_int
+_lib.asf_stack_decode.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _i32, _i32, _vp, _vp, _vp]
+_lib.asf_stack_decode.restype = ctypes.c_int
 _lib.asf_dense_ffn_ref.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp]
 _lib.asf_dense_ffn_ref.restype = ctypes.c_int
 _lib.asf_layer_set_trace.argtypes = [_vp, ctypes.POINTER(ctypes.c_void_p), _i32]
@@ -263,6 +265,51 @@ class Layer:
             self.close()
         except Exception:
             pass
+
+
+class Stack:
+    """Layers run one after another in one call (asf_stack_decode):
+    x_{l+1} = FFN_l(x_l), plus x_l when ``residual``.  Holds references to the
+    layers; every layer must have the same d_model."""
+
+    def __init__(self, layers, residual: bool = False):
+        self.layers = list(layers)
+        if not self.layers:
+            raise ValueError("empty stack")
+        self.d_model = self.layers[0].d_model
+        self.device = self.layers[0].device
+        self.residual = 1 if residual else 0
+        self._arr = (_vp * len(self.layers))(*[l.handle for l in self.layers])
+        self._work = {}
+
+    def _work_for(self, B):
+        w = self._work.get(B)
+        if w is None:
+            w = torch.empty((B, self.d_model), dtype=torch.float32, device=self.device)
+            self._work[B] = w
+        return w
+
+    def decode(self, x, out=None, work=None, stream=None):
+        if x.dim() == 1:
+            x = x.unsqueeze(0)
+        B = x.shape[0]
+        if out is None:
+            out = torch.empty((B, self.d_model), dtype=torch.float32, device=self.device)
+        if work is None:
+            work = self._work_for(B)
+        _check(_lib.asf_stack_decode(self._arr, len(self.layers), _dev_ptr(x, torch.float32, "x"),
+                                     B, self.residual, _dev_ptr(out, torch.float32, "out"),
+                                     _dev_ptr(work, torch.float32, "work"), _stream(stream)),
+               "asf_stack_decode")
+        return out
+
+    def decode_raw(self, x_ptr: int, B: int, y_ptr: int, work_ptr: int,
+                   stream_handle: int) -> None:
+        """decode on raw device pointers and a raw stream handle."""
+        rc = _lib.asf_stack_decode(self._arr, len(self.layers), x_ptr, B, self.residual, y_ptr,
+                                   work_ptr, stream_handle)
+        if rc != ASF_OK:
+            raise AsfError(rc, "asf_stack_decode")
 
 
 def layer_from_numpy(L, device="cuda", max_batch: int = 1, threshold: float = 0.0,

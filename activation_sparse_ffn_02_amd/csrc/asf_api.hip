@@ -228,6 +228,48 @@ asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
     return ASF_OK;
 }
 
+asf_status asf_stack_decode(asf_layer *const *layers, int32_t n_layers, const float *x,
+                            int32_t B, int32_t residual, float *y, float *work, void *stream) {
+    if (!layers || n_layers < 1 || !x || !y || (residual != 0 && residual != 1))
+        return ASF_ERR_ARG;
+    if (n_layers > 1 && !work) return ASF_ERR_ARG;
+    if (!layers[0]) return ASF_ERR_ARG;
+    const int d = layers[0]->v.d;
+    for (int32_t l = 0; l < n_layers; ++l) {
+        const asf_layer *L = layers[l];
+        if (!L) return ASF_ERR_ARG;
+        if (L->v.d != d) return ASF_ERR_SHAPE;
+        if (B < 1 || B > L->v.max_batch) return ASF_ERR_SHAPE;
+        for (int32_t m = 0; m < l; ++m)
+            if (layers[m] == L) return ASF_ERR_ARG;
+    }
+    if (!aligned16(x) || !aligned16(y) || (work && !aligned16(work))) return ASF_ERR_ALIGN;
+    if (n_layers > 1) {
+        const uintptr_t bytes = (uintptr_t)B * d * 4;
+        auto overlap = [&](const void *a, const void *b) {
+            const uintptr_t p = (uintptr_t)a, q = (uintptr_t)b;
+            return p < q + bytes && q < p + bytes;
+        };
+        if (overlap(work, x) || overlap(work, y)) return ASF_ERR_ARG;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    // layer l writes y when (n_layers - 1 - l) is even, else work, so the
+    // last layer lands in y; layer 0 reads x, every later layer its
+    // predecessor's output
+    const float *in = x;
+    for (int32_t l = 0; l < n_layers; ++l) {
+        const LayerView &v = layers[l]->v;
+        const asf::Trace *tr = layers[l]->tr();
+        float *out = ((n_layers - 1 - l) % 2 == 0) ? y : work;
+        if (launch_pred_l1(v, in, B, tr, s) != hipSuccess) return ASF_ERR_HIP;
+        if (launch_score(v, in, B, true, tr, s) != hipSuccess) return ASF_ERR_HIP;
+        if (launch_fc2(v, B, false, residual ? in : nullptr, out, tr, s) != hipSuccess)
+            return ASF_ERR_HIP;
+        in = out;
+    }
+    return ASF_OK;
+}
+
 asf_status asf_dense_ffn_ref(const asf_layer *layer, const float *x, int32_t B,
                              const float *residual, float *y, void *stream) {
     asf_status st = check_call(layer, x, B);

@@ -703,7 +703,8 @@ __global__ __launch_bounds__(kThreads) void k_fc2(Fc2Params p) {
 // ---------------------------------------------------------------- list
 // Slot-ordered outputs from the owner bits: thread t builds slot word t
 // (slots 64t .. 64t+63; slot s is bit s / nq of owner s % nq), writes the
-// per-token masks, and the ascending list of union-active slots / ids.
+// per-token masks, and the ascending list of union-active slots / ids.  The
+// owner words are staged in LDS first (nq <= 1024).
 __global__ __launch_bounds__(1024) void k_list(const uint64_t *__restrict__ ubits,
                                                const uint64_t *__restrict__ wbits, int B, int f,
                                                int nq, int words, const int32_t *__restrict__ perm,
@@ -712,26 +713,31 @@ __global__ __launch_bounds__(1024) void k_list(const uint64_t *__restrict__ ubit
                                                int32_t *__restrict__ count,
                                                int32_t *__restrict__ active_ids,
                                                int32_t *__restrict__ n_active) {
+    __shared__ uint64_t ob[kMaxFfn / 64];
     __shared__ int wave_tot[16];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    uint64_t u = 0;
-    if (t < words) {
-        for (int j = 0; j < 64; ++j) {
-            const int s = t * 64 + j;
-            if (s < f && ((ubits[s % nq] >> (s / nq)) & 1ull)) u |= 1ull << j;
-        }
-        if (token_masks) {
-            for (int b = 0; b < B; ++b) {
-                uint64_t m = 0;
-                for (int j = 0; j < 64; ++j) {
-                    const int s = t * 64 + j;
-                    if (s < f && ((wbits[(size_t)b * nq + s % nq] >> (s / nq)) & 1ull))
-                        m |= 1ull << j;
-                }
-                token_masks[(size_t)b * words + t] = m;
+    auto build = [&]() {
+        uint64_t m = 0;
+        if (t < words) {
+            for (int j = 0; j < 64; ++j) {
+                const int s = t * 64 + j;
+                if (s < f && ((ob[s % nq] >> (s / nq)) & 1ull)) m |= 1ull << j;
             }
         }
+        return m;
+    };
+    if (token_masks) {
+        for (int b = 0; b < B; ++b) {
+            for (int i = t; i < nq; i += blockDim.x) ob[i] = wbits[(size_t)b * nq + i];
+            __syncthreads();
+            const uint64_t m = build();
+            if (t < words) token_masks[(size_t)b * words + t] = m;
+            __syncthreads();
+        }
     }
+    for (int i = t; i < nq; i += blockDim.x) ob[i] = ubits[i];
+    __syncthreads();
+    uint64_t u = build();
     const int c = __popcll(u);
     int incl = c;
 #pragma unroll

@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--trace-every", type=int, default=10,
                     help="record kernel events on every n-th timed step")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--stack-tokens", type=int, default=256,
+                    help="tokens through the 48-layer stack (0 skips the stack)")
+    ap.add_argument("--stack-warmup", type=int, default=8)
+    ap.add_argument("--stack-dense-tokens", type=int, default=8)
     return ap.parse_args()
 
 
@@ -164,6 +168,83 @@ def cpu_baseline(args, L, x):
     return {"value": done / dt, "unit": "tokens/s", "cores": int(n_thr), "kind": "oracle",
             "sample": "%d decode tokens of the same layer and token stream (fp64 predictor "
                       "+ FFN over the predicted set), %.1f s" % (done, dt)}
+
+
+def bench_stack(args, asf, torch, np, wl, dev, stream):
+    """The 48-layer OPT-30B-shaped stack (7168x28672 fp16, ~40 GB resident):
+    B = 1 tokens through all layers per asf_stack_decode call."""
+    from workload.gpu import stack_layer_device, stack_tokens
+    t0 = time.perf_counter()
+    layers, shapes = [], []
+    for l in range(wl.STACK_LAYERS):
+        DL = stack_layer_device(l, dev)
+        layers.append(asf.Layer(DL.w_up, DL.w_down, DL.p1, DL.p2, b1=DL.b1, b2=DL.b2, c2=DL.c2,
+                                neuron_table=DL.perm))
+        shapes.append(DL.shape)
+        del DL
+        torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    resident = sum(l.storage.numel() for l in layers)
+    log(args, "stack of %d layers, %.2f GB, built in %.1f s" % (len(layers), resident / 1e9,
+                                                             time.perf_counter() - t0))
+    st = asf.Stack(layers)
+    n = args.stack_tokens
+    X = torch.from_numpy(stack_tokens(n + args.stack_warmup)).to(dev)
+    Y = torch.empty((1, wl.STACK_D), dtype=torch.float32, device=dev)
+    work = torch.empty_like(Y)
+    sh_ = stream.cuda_stream
+    xs = [X[t].data_ptr() for t in range(X.shape[0])]
+    for t in range(args.stack_warmup):
+        st.decode_raw(xs[n + t], 1, Y.data_ptr(), work.data_ptr(), sh_)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(n):
+        st.decode_raw(xs[t], 1, Y.data_ptr(), work.data_ptr(), sh_)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # per-layer active counts of the same tokens (outside the timed region)
+    counts = torch.zeros((n, len(layers)), dtype=torch.int32, device=dev)
+    for t in range(n):
+        cur = X[t:t + 1]
+        for l, lay in enumerate(layers):
+            lay.predict(cur, n_active=counts[t, l:l + 1], want_list=False)
+            cur = lay.decode_step(cur)
+    torch.cuda.synchronize()
+    k = counts.double().mean(dim=0).cpu().numpy()
+    tok_bytes = sum(bytes_model(shapes[l], float(k[l]))[0] for l in range(len(layers)))
+    dense_bytes = sum(bytes_model(shapes[l], 0.0)[2] for l in range(len(layers)))
+    # dense comparator: every layer's dense FFN, chained, a few tokens
+    nd = args.stack_dense_tokens
+    dense_ms = None
+    if nd > 0:
+        cur = X[:1]
+        for l, lay in enumerate(layers):
+            cur = lay.dense_ffn_ref(cur)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for t in range(nd):
+            cur = X[t:t + 1]
+            for lay in layers:
+                cur = lay.dense_ffn_ref(cur)
+        torch.cuda.synchronize()
+        dense_ms = (time.perf_counter() - t1) * 1e3 / nd
+    ms_tok = elapsed * 1e3 / n
+    res = {
+        "workload": "OPT-30B-shaped FFN stack: 48 layers 7168x28672 fp16, predictors 7168->"
+                    "{512,1024,2048}->28672, activation 3%->15% by depth, batch 1",
+        "tokens": n, "tokens_per_s": n / elapsed, "ms_per_token": ms_tok,
+        "resident_gb": resident / 1e9,
+        "algorithmic_bytes_per_token": tok_bytes,
+        "effective_gbps": tok_bytes / (ms_tok * 1e-3) / 1e9,
+        "effective_frac_of_peak": tok_bytes / (ms_tok * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "active_frac_by_layer": [round(float(k[l]) / shapes[l].f, 4) for l in range(len(layers))],
+        "dense_ms_per_token": dense_ms,
+        "dense_gbps": None if dense_ms is None else dense_bytes / (dense_ms * 1e-3) / 1e9,
+        "speedup_vs_dense": None if dense_ms is None else dense_ms / ms_tok,
+    }
+    for lay in layers:
+        lay.close()
+    return res
 
 
 def main():
@@ -330,6 +411,11 @@ def main():
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(args, L, X)
+    if args.stack_tokens > 0:
+        del ring, Xd, Y
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        out["stack"] = bench_stack(args, asf, torch, np, wl, dev, stream)
     print(json.dumps(out), flush=True)
 
 

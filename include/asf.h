@@ -182,6 +182,24 @@ asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
                            const float *residual, float *y, int32_t *active,
                            int32_t *n_active, void *stream);
 
+/* One decode step of B tokens through a stack of layers, in order:
+ *   x_0 = x;  x_{l+1} = FFN_l(x_l) + (residual ? x_l : 0);  y = x_n
+ * where FFN_l is layer l's decode step (asf_decode_step: predictor, threshold,
+ * FC1 and FC2 over the predicted set).  The pages give every layer its own
+ * predictor, sized by that layer's skew ("LLM模型之PowerInfer1.0" §4.1), and
+ * run the layers one after another.
+ *   layers    HOST array of n_layers >= 1 handles, all with the same d_model
+ *             and max_batch >= B; a handle may appear once only (each layer's
+ *             scratch serves one step at a time)
+ *   x         DEVICE float32 [B][d_model], read only unless y == x
+ *   residual  0: x_{l+1} = FFN_l(x_l);  1: x_{l+1} = x_l + FFN_l(x_l)
+ *   y         DEVICE float32 [B][d_model]; may equal x
+ *   work      DEVICE float32 [B][d_model] scratch, overlapping neither x nor y
+ *             (may be NULL when n_layers == 1)
+ * Asynchronous on `stream`; launches the decode step's kernels per layer. */
+asf_status asf_stack_decode(asf_layer *const *layers, int32_t n_layers, const float *x,
+                            int32_t B, int32_t residual, float *y, float *work, void *stream);
+
 /* Dense comparator: the same FFN over all d_ffn neurons. */
 asf_status asf_dense_ffn_ref(const asf_layer *layer, const float *x, int32_t B,
                              const float *residual, float *y, void *stream);
@@ -204,10 +222,12 @@ typedef enum {
 
 /* Kernel tracing, for measuring each kernel with HIP events on the stream it
  * runs on.  `events` holds 2*n hipEvent_t handles (as void*), n <= ASF_K_COUNT:
- * events[2k] is recorded on the call's stream right before kernel k is
- * launched and events[2k+1] right after it, by every later call on this layer
- * (NULL entries are skipped).  events == NULL or n == 0 turns tracing off.
- * The handles are borrowed: the caller creates and destroys them. */
+ * every later call on this layer launches kernel k with events[2k] as its
+ * start and events[2k+1] as its stop event (hipExtLaunchKernelGGL: the
+ * dispatch itself takes the events, so their difference is the kernel's own
+ * duration); NULL entries are skipped.  events == NULL or n == 0 turns
+ * tracing off.  The handles are borrowed: the caller creates and destroys
+ * them. */
 asf_status asf_layer_set_trace(asf_layer *layer, void *const *events, int32_t n);
 
 /* Human-readable name of a status code (static string). */

@@ -21,7 +21,11 @@ def declared_functions():
 @pytest.fixture(scope="module")
 def asf():
     if not os.path.exists(LIB):
-        import activation_sparse_ffn_02_amd.build as b
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_asf_build", os.path.join(ROOT, "activation_sparse_ffn_02_amd", "build.py"))
+        b = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(b)
         b.build()
     import activation_sparse_ffn_02_amd as m
     return m

@@ -1,0 +1,146 @@
+"""GPU parity of the layer stack (asf_stack_decode).
+
+* The stack call equals the same layers' decode steps chained by hand, bit
+  for bit (same kernels, same inputs), with and without the residual.
+* Each layer's set and output agree with the oracle on that layer's actual
+  input (the previous layer's GPU output): sets bit-exact beyond the 1e-3
+  margin, per-token relative L2 <= 5e-3 (fp16 weights).
+* The full 48-layer OPT-30B-shaped stack (7168x28672 fp16, predictors of
+  512/1024/2048 hidden, ~40 GB resident) runs end to end; the oracle checks
+  layers 0, 23 and 47 (their weights are read back from the device).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workload as wl
+from gpu_util import TOL, asf, check_set, need_gpu, rel_l2, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _device_layers(shapes, seed0, keep=()):
+    """Create library layers from device-generated weights; keep host copies
+    of the layers whose index is in `keep` (for the oracle)."""
+    from workload.gpu import make_layer_device
+    m = asf()
+    layers, host = [], {}
+    for l, sh in enumerate(shapes):
+        DL = make_layer_device(sh, seed0 + l, torch.device("cuda"))
+        layers.append(m.Layer(DL.w_up, DL.w_down, DL.p1, DL.p2, w_gate=DL.w_gate, b1=DL.b1,
+                              b2=DL.b2, c1=DL.c1, c2=DL.c2, neuron_table=DL.perm))
+        if l in keep:
+            host[l] = DL.to_numpy()
+        del DL
+    torch.cuda.synchronize()
+    return layers, host
+
+
+def _check_layer(orc, L, xin, y_gpu, ids_gpu, label):
+    _, s_orc, _ = orc.predict(L.p1, L.c1, L.p2, L.c2, xin[None, :])
+    check_set(ids_gpu, s_orc[0], 0.0, L.perm, label)
+    y_orc = orc.ffn(L.w_up, L.w_down, xin, ids_gpu, b1=L.b1, b2=L.b2, W_gate=L.w_gate)
+    e = rel_l2(y_gpu, y_orc[0])
+    assert e <= TOL["f16"], "%s: rel-L2 %.3g" % (label, e)
+    return e
+
+
+@pytest.mark.parametrize("residual", [False, True])
+def test_small_stack_equals_chained_steps(orc, residual):
+    need_gpu()
+    d, f = 512, 2048
+    shapes = [wl.LayerShape(d, f, H, rho, "f16")
+              for H, rho in ((64, 0.03), (128, 0.08), (256, 0.15), (128, 0.10), (64, 0.05))]
+    layers, host = _device_layers(shapes, 700, keep=range(len(shapes)))
+    st = asf().Stack(layers, residual=residual)
+    x = wl.make_tokens(d, 3, 701)
+    for t in range(x.shape[0]):
+        xt = to_dev(x[t:t + 1])
+        y = st.decode(xt)
+        cur = xt
+        for l, lay in enumerate(layers):
+            act = torch.empty(f, dtype=torch.int32, device="cuda")
+            n = torch.empty(1, dtype=torch.int32, device="cuda")
+            nxt = lay.decode_step(cur, residual=cur if residual else None, active=act,
+                                  n_active=n)
+            torch.cuda.synchronize()
+            ids = act[:int(n.item())].cpu().numpy()
+            xin = cur.cpu().numpy()[0]
+            yl = nxt.cpu().numpy()[0] - (xin if residual else 0.0)
+            L = host[l]
+            _, s_orc, _ = orc.predict(L.p1, L.c1, L.p2, L.c2, xin[None, :])
+            check_set(ids, s_orc[0], 0.0, L.perm, "layer %d token %d" % (l, t))
+            y_orc = orc.ffn(L.w_up, L.w_down, xin, ids, b1=L.b1, b2=L.b2)
+            assert rel_l2(yl, y_orc[0]) <= TOL["f16"], (l, t)
+            cur = nxt
+        assert torch.equal(y, cur), "stack output differs from the chained steps"
+    # y may equal x (in place)
+    xt = to_dev(x[:1])
+    ref = st.decode(xt)
+    inplace = xt.clone()
+    st.decode(inplace, out=inplace)
+    assert torch.equal(inplace, ref)
+
+
+def test_stack_argument_errors():
+    need_gpu()
+    m = asf()
+    d, f = 256, 512
+    layers, _ = _device_layers([wl.LayerShape(d, f, 64, 0.1, "f16")] * 2, 720)
+    other, _ = _device_layers([wl.LayerShape(384, f, 64, 0.1, "f16")], 730)
+    x = torch.zeros((1, d), device="cuda")
+    with pytest.raises(m.AsfError):
+        m.Stack([layers[0], layers[0]]).decode(x)               # a layer twice
+    with pytest.raises(m.AsfError):
+        m.Stack([layers[0], other[0]]).decode(x)                # d mismatch
+    with pytest.raises(m.AsfError):
+        m.Stack(layers).decode(torch.zeros((2, d), device="cuda"))   # B > max_batch
+    st = m.Stack(layers)
+    buf = torch.zeros((2, d), device="cuda")
+    with pytest.raises(m.AsfError):
+        st.decode(buf[:1], out=buf[1:], work=buf[:1])           # work overlaps x
+
+
+def test_opt30b_stack_full_size(orc):
+    """48 layers of 7168x28672 fp16, 2 tokens; oracle on layers 0, 23, 47."""
+    need_gpu()
+    from workload.gpu import stack_layer_device
+    m = asf()
+    sampled = (0, 23, 47)
+    layers, host = [], {}
+    for l in range(wl.STACK_LAYERS):
+        DL = stack_layer_device(l, torch.device("cuda"))
+        layers.append(m.Layer(DL.w_up, DL.w_down, DL.p1, DL.p2, b1=DL.b1, b2=DL.b2,
+                              c2=DL.c2, neuron_table=DL.perm))
+        if l in sampled:
+            host[l] = DL.to_numpy()
+        del DL
+        torch.cuda.synchronize()
+    st = m.Stack(layers)
+    x = wl.make_tokens(wl.STACK_D, 2, 2003)
+    f = wl.STACK_F
+    for t in range(x.shape[0]):
+        xt = to_dev(x[t:t + 1])
+        y = st.decode(xt)
+        cur = xt
+        errs = []
+        for l, lay in enumerate(layers):
+            if l in sampled:
+                act = torch.empty(f, dtype=torch.int32, device="cuda")
+                n = torch.empty(1, dtype=torch.int32, device="cuda")
+                nxt = lay.decode_step(cur, active=act, n_active=n)
+                torch.cuda.synchronize()
+                ids = act[:int(n.item())].cpu().numpy()
+                errs.append(_check_layer(orc, host[l], cur.cpu().numpy()[0],
+                                         nxt.cpu().numpy()[0], ids,
+                                         "stack layer %d token %d" % (l, t)))
+                frac = ids.size / f
+                rho = wl.stack_layer_shape(l).rho
+                assert 0.5 * rho < frac < 2.0 * rho, (l, frac, rho)
+            else:
+                nxt = lay.decode_step(cur)
+            cur = nxt
+        assert torch.equal(y, cur)
+        rms = float(y.pow(2).mean().sqrt())
+        assert 0.5 < rms < 2.0, rms
+        print("token %d: sampled-layer rel-L2 %s, output rms %.3f" % (t, errs, rms))

@@ -68,3 +68,48 @@ def test_generator_is_deterministic():
     for k in ("w_up", "w_down", "b1", "b2", "p1", "p2", "c2", "perm"):
         assert np.array_equal(getattr(a, k), getattr(b, k))
     assert a.w_up.dtype == np.float16 and a.b1.dtype == np.float32
+
+
+def test_relu_second_moment_closed_form():
+    """E[ReLU(z)^2], z ~ N(mu, s^2), against Monte Carlo and two exact cases
+    (mu = 0 gives s^2/2; mu >> s gives mu^2 + s^2)."""
+    from workload.gpu import relu_second_moment
+    rng = np.random.Generator(np.random.PCG64(3))
+    mu = np.array([-2.0, -0.5, 0.0, 0.7, 1.5])
+    s = np.array([1.0, 0.3, 2.0, 1.2, 0.5])
+    z = rng.standard_normal((400000, 1)) * s + mu
+    mc = (np.maximum(z, 0.0) ** 2).mean(axis=0)
+    cf = relu_second_moment(mu, s)
+    assert np.all(np.abs(mc - cf) < 0.01 * (cf + 0.01)), (mc, cf)
+    assert abs(relu_second_moment(np.array([0.0]), np.array([3.0]))[0] - 4.5) < 1e-12
+    assert abs(relu_second_moment(np.array([40.0]), np.array([1.0]))[0] - 1601.0) < 1e-9
+
+
+def test_stack_generator_keeps_layer_inputs_calibrated(orc):
+    """Stack layers drawn by the device generator (here on the CPU device):
+    each layer fires at its rho on N(0,1) inputs, and chaining
+    x_{l+1} = FFN_l(x_l) over the predicted sets keeps the next layer's input
+    near unit RMS, so deeper layers still fire at their own rho."""
+    import torch
+    from workload.gpu import make_layer_device
+    d, f = 256, 2048
+    rhos, Hs = [0.03, 0.09, 0.15], [64, 128, 256]
+    x = wl.make_tokens(d, 64, 99).astype(np.float64)
+    for l, (rho, H) in enumerate(zip(rhos, Hs)):
+        sh = wl.LayerShape(d, f, H, rho, "f16")
+        DL = make_layer_device(sh, 500 + l, torch.device("cpu"))
+        L = DL.to_numpy()
+        assert L.w_up.dtype == np.float16 and L.w_down.shape == (d, f)
+        assert np.all(np.diff(L.p[L.perm]) <= 0)
+        xin = x.astype(np.float32)
+        rms_in = np.sqrt((xin.astype(np.float64) ** 2).mean())
+        assert 0.8 < rms_in < 1.2, (l, rms_in)
+        _, tm = orc.true_mask(L.w_up, xin, b1=L.b1)
+        assert abs(tm.mean() - rho) < 0.35 * rho + 0.005, (l, tm.mean(), rho)
+        _, _, act = orc.predict(L.p1, L.c1, L.p2, L.c2, xin)
+        ys = []
+        for t in range(xin.shape[0]):
+            ids = orc.active_list(act[t], L.perm)
+            ys.append(orc.ffn(L.w_up, L.w_down, xin[t:t + 1], ids, b1=L.b1, b2=L.b2)[0])
+        x = np.asarray(ys)
+    assert 0.75 < np.sqrt((x ** 2).mean()) < 1.2
