@@ -240,6 +240,124 @@ __global__ __launch_bounds__(kThreads) void k_pred_l1(const u32x4 *__restrict__ 
     }
 }
 
+// ---------------------------------------------------------------- single-token staging
+// The B = 1 kernels stage x (and h) in LDS once per workgroup; every wave reads
+// the chunk of x it needs from LDS right before the FMAs, so registers hold
+// only weight chunks and partial sums (no spills up to d = 8192 fp16).
+constexpr int kMaxDLds = 8192;   // floats of x (a d row is at most 16 KiB of weights)
+constexpr int kMaxHLds = 2048;   // floats of h
+
+// Each thread loads its float4s of a length-n fp32 vector (n % 4 == 0,
+// n <= 4 * kThreads * N4) from clamped addresses, then stores them to LDS.
+template <int N4>
+__device__ __forceinline__ void stage_load(const float *__restrict__ src, int n, float4 (&v)[N4]) {
+    const float4 *s4 = reinterpret_cast<const float4 *>(src);
+    const int n4 = n / 4;
+#pragma unroll
+    for (int i = 0; i < N4; ++i) {
+        const int idx = (int)threadIdx.x + kThreads * i;
+        v[i] = s4[idx < n4 ? idx : n4 - 1];
+    }
+}
+
+template <int N4>
+__device__ __forceinline__ void stage_store(float *dst, int n, const float4 (&v)[N4]) {
+    float4 *d4 = reinterpret_cast<float4 *>(dst);
+    const int n4 = n / 4;
+#pragma unroll
+    for (int i = 0; i < N4; ++i) {
+        const int idx = (int)threadIdx.x + kThreads * i;
+        if (idx < n4) d4[idx] = v[i];
+    }
+}
+
+// acc += chunk c of a weight row (in registers) . chunk c of an LDS vector
+template <int WT>
+__device__ __forceinline__ float dot_chunk_lds(const u32x4 w, const float *vs, int c, float acc) {
+    constexpr int E = Elt<WT>::E;
+    float wv[E];
+    unpack<WT>(w, wv);
+    const float4 *v4 = reinterpret_cast<const float4 *>(vs + c * E);
+#pragma unroll
+    for (int k = 0; k < E / 4; ++k) {
+        const float4 t = v4[k];
+        acc = fmaf(wv[4 * k + 0], t.x, acc);
+        acc = fmaf(wv[4 * k + 1], t.y, acc);
+        acc = fmaf(wv[4 * k + 2], t.z, acc);
+        acc = fmaf(wv[4 * k + 3], t.w, acc);
+    }
+    return acc;
+}
+
+// Predictor layer 1 for one token: WPR waves share a row of P1 (wave part p
+// takes chunks p*64 + lane + 64*WPR*i); x comes from LDS.  Sums: per lane in
+// chunk order, butterfly over the wave, then the parts in order, then c1,
+// then ReLU.
+template <int WT, int CPL>
+__global__ __launch_bounds__(kThreads) void k_pred1(const u32x4 *__restrict__ P1,
+                                                    const float *__restrict__ c1,
+                                                    const float *__restrict__ x, int d, int H,
+                                                    int wpr, float *__restrict__ h) {
+    constexpr int E = Elt<WT>::E;
+    // up to 8 chunks per lane the x chunks travel with the weight chunks in
+    // registers; beyond that x is staged in LDS
+    constexpr bool XLDS = CPL > 8;
+    __shared__ float xs[XLDS ? kMaxDLds : 4];
+    __shared__ float red[kWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rpw = kWaves / wpr;
+    const int row = blockIdx.x * rpw + wave / wpr, part = wave % wpr;
+    const int C = d / E;
+    const bool live = row < H;
+    const int rowc = live ? row : H - 1;
+    float4 xv[XLDS ? 4 : 1];
+    if constexpr (XLDS) stage_load<4>(x, d, xv);
+    u32x4 w[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = part * 64 + lane + 64 * wpr * i;
+        w[i] = P1[(size_t)rowc * C + (c < C ? c : C - 1)];
+    }
+    float acc = 0.0f;
+    if constexpr (XLDS) {
+        stage_store<4>(xs, d, xv);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = part * 64 + lane + 64 * wpr * i;
+            if (live && c < C) acc = dot_chunk_lds<WT>(w[i], xs, c, acc);
+        }
+    } else {
+        float xr[CPL][E];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = part * 64 + lane + 64 * wpr * i;
+            load_f32<E>(x + (size_t)(c < C ? c : C - 1) * E, xr[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = part * 64 + lane + 64 * wpr * i;
+            if (live && c < C) {
+                float wv[E];
+                unpack<WT>(w[i], wv);
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc = fmaf(wv[e], xr[i][e], acc);
+            }
+        }
+    }
+    const float sum = wave_sum(acc);
+    if (lane == 0) red[wave] = sum;
+    __syncthreads();
+    if ((int)threadIdx.x < rpw) {
+        const int r = blockIdx.x * rpw + threadIdx.x;
+        if (r < H) {
+            float t = 0.0f;
+            for (int pp = 0; pp < wpr; ++pp) t += red[threadIdx.x * wpr + pp];
+            h[r] = fmaxf(t + c1[r], 0.0f);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- predictor layer 2
 // Owner q, wave w scores the slots of bits i = 8w .. 8w+7 (slot q + nq*i);
 // lane l holds chunks l, l+64, ... of each row.  Loads are unconditional from
@@ -541,6 +659,232 @@ __global__ __launch_bounds__(kThreads) void k_fc1(Fc1Params p) {
                                p.out, false, none, none, wave, lane);
 }
 
+// ---------------------------------------------------------------- single-token score / FC1
+// FC1 of one neuron for one token with x in LDS; returns a (every lane).
+template <int WT, bool GATED, int CPL>
+__device__ __forceinline__ float fc1_one(const u32x4 (&wu)[CPL], const u32x4 (&wg)[CPL], int C,
+                                         const float *xs, float bias, int lane) {
+    float au = 0.0f, ag = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = lane + 64 * i;
+        if (c < C) {
+            au = dot_chunk_lds<WT>(wu[i], xs, c, au);
+            if constexpr (GATED) ag = dot_chunk_lds<WT>(wg[i], xs, c, ag);
+        }
+    }
+    const float su = wave_sum(au);
+    if constexpr (GATED) return fmaxf(wave_sum(ag) + bias, 0.0f) * su;
+    else return fmaxf(su + bias, 0.0f);
+}
+
+// FC1 of owner q's valid entries for one token (x in LDS): wave w takes
+// entries i = w + 8k for k >= k0; the entry of rank r (r-th set bit of
+// `valid`) is listed at lslot[q][r], la[q][r].
+template <int WT, bool GATED, int CPL>
+__device__ __forceinline__ void fc1_entry_1(int q, uint64_t valid, int i, int slot,
+                                            const u32x4 (&wu)[CPL], const u32x4 (&wg)[CPL],
+                                            int C, float bias, const float *xs, Fc1Out o,
+                                            int lane) {
+    const int rank = __popcll(valid & ((1ull << i) - 1ull));
+    const float a = fc1_one<WT, GATED, CPL>(wu, wg, C, xs, bias, lane);
+    if (lane == 0) {
+        const size_t e = (size_t)q * kRowsPerWG + rank;
+        o.la[e * o.max_batch] = a;
+        o.lslot[e] = slot;
+    }
+}
+
+template <int WT, bool GATED, int CPL, class SlotOf>
+__device__ __forceinline__ void owner_fc1_1(int q, uint64_t valid, SlotOf slot_of, int k0,
+                                            const u32x4 *__restrict__ bundles, size_t bstride,
+                                            int C, const float *__restrict__ b1, const float *xs,
+                                            Fc1Out o, int wave, int lane) {
+    for (int k = k0; k < kRowsPerWG / kWaves; ++k) {
+        const int i = wave + kWaves * k;
+        if (!((valid >> i) & 1ull)) continue;
+        const int slot = slot_of(i);
+        const float bias = b1[slot];
+        u32x4 wu[CPL], wg[CPL];
+        load_fc1_rows<GATED, CPL>(bundles, bstride, C, slot, lane, wu, wg);
+        fc1_entry_1<WT, GATED, CPL>(q, valid, i, slot, wu, wg, C, bias, xs, o, lane);
+    }
+}
+
+// registers per FC1 row set (up, and gate when gated), in 16-byte chunks
+template <bool GATED, int CPL1, bool SPEC = false> struct Fc1Regs {
+    static constexpr int chunks = CPL1 * (GATED ? 2 : 1);
+    // at most 128 VGPRs (4 waves per SIMD) while the rows fit beside the P2
+    // double buffer; more otherwise, and when the hottest rows are held
+    // through the scoring phase (used only when one workgroup per CU covers
+    // every owner)
+    static constexpr int waves_per_eu = (chunks <= 14 && !SPEC) ? 4 : 2;
+};
+
+// With at most 128 VGPRs (4 waves per SIMD) two workgroups fit on a CU, so
+// up to 512 owners (f <= 32768) run in one round.
+template <int WT, int CPL2, bool FC1, bool GATED, int CPL1, bool SPEC>
+__global__ __launch_bounds__(kThreads) __attribute__((
+    amdgpu_waves_per_eu(Fc1Regs<GATED, CPL1, SPEC>::waves_per_eu))) void k_score1(ScoreParams p) {
+    constexpr int E = Elt<WT>::E;
+    constexpr int RG = kL2Rows / CPL2;      // rows per group
+    constexpr int NG = CPL2;                // groups per wave
+    __shared__ float hs[kMaxHLds];
+    __shared__ float xs[FC1 ? kMaxDLds : 4];
+    __shared__ uint32_t bits_lds[kWaves];
+    __shared__ uint64_t u_lds;
+    const int q = blockIdx.x, nq = gridDim.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int C2 = p.H / E;
+    // staging loads first: their waits then leave the weight loads in flight
+    float4 hv[1];
+    stage_load<1>(p.h, p.H, hv);
+    float4 xv[FC1 ? 4 : 1];
+    if constexpr (FC1) stage_load<4>(p.x, p.d, xv);
+    u32x4 wb[2][RG][CPL2];
+    auto load_group = [&](int g, u32x4 (&dst)[RG][CPL2]) {
+#pragma unroll
+        for (int j = 0; j < RG; ++j) {
+            int slot = q + nq * (wave * kL2Rows + g * RG + j);
+            slot = slot < p.f ? slot : p.f - 1;
+#pragma unroll
+            for (int i = 0; i < CPL2; ++i) {
+                const int c = lane + 64 * i;
+                dst[j][i] = p.p2[(size_t)slot * C2 + (c < C2 ? c : C2 - 1)];
+            }
+        }
+    };
+    load_group(0, wb[0]);
+    if constexpr (NG > 1) load_group(1, wb[1]);
+    u32x4 spu[FC1 ? CPL1 : 1], spg[FC1 ? CPL1 : 1];
+    if constexpr (SPEC) {
+        const int spec_slot = q + nq * wave;
+        if (wave < kSpecRows && spec_slot < p.f)
+            load_fc1_rows<GATED, CPL1>(p.bundles, p.bstride, p.cd, spec_slot, lane, spu, spg);
+    }
+    stage_store<1>(hs, p.H, hv);
+    if constexpr (FC1) stage_store<4>(xs, p.d, xv);
+    __syncthreads();
+    // every row of the wave uses the same chunks of h: keep them in registers
+    float hr[CPL2][E];
+#pragma unroll
+    for (int i = 0; i < CPL2; ++i) {
+        const int c = lane + 64 * i;
+        const float4 *h4 = reinterpret_cast<const float4 *>(hs + (c < C2 ? c : 0) * E);
+#pragma unroll
+        for (int k = 0; k < E / 4; ++k) {
+            const float4 t = h4[k];
+            hr[i][4 * k + 0] = t.x;
+            hr[i][4 * k + 1] = t.y;
+            hr[i][4 * k + 2] = t.z;
+            hr[i][4 * k + 3] = t.w;
+        }
+    }
+    float acc[kL2Rows];
+#pragma unroll
+    for (int j = 0; j < kL2Rows; ++j) acc[j] = 0.0f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+#pragma unroll
+        for (int j = 0; j < RG; ++j)
+#pragma unroll
+            for (int i = 0; i < CPL2; ++i) {
+                const int c = lane + 64 * i;
+                if (c < C2) {
+                    float wv[E];
+                    unpack<WT>(wb[g & 1][j][i], wv);
+                    float a = acc[g * RG + j];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) a = fmaf(wv[e], hr[i][e], a);
+                    acc[g * RG + j] = a;
+                }
+            }
+        if (g + 2 < NG) load_group(g + 2, wb[g & 1]);
+    }
+    // lane L ends with row (L >> 3) & 7 of this wave
+    const int r = (lane >> 3) & 7;
+    const int slot_r = q + nq * (wave * kL2Rows + r);
+    const bool valid_r = slot_r < p.f;
+    const float sc = rows8_sum(acc, lane) + p.c2[valid_r ? slot_r : p.f - 1];
+    const uint64_t m = __ballot(valid_r && sc > p.theta);
+    if (lane == 0) {
+        uint32_t b = 0;
+#pragma unroll
+        for (int j = 0; j < kL2Rows; ++j) b |= (uint32_t)((m >> (8 * j)) & 1ull) << j;
+        bits_lds[wave] = b;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t u = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) u |= (uint64_t)bits_lds[w] << (kL2Rows * w);
+        p.wbits[q] = u;
+        p.ubits[q] = u;
+        if (FC1) p.out.vbits[q] = u;
+        u_lds = u;
+    }
+    __syncthreads();
+    if constexpr (FC1) {
+        const uint64_t valid = u_lds;
+        int k0 = 0;
+        if constexpr (SPEC) {
+            // waves below kSpecRows hold the rows of their first entry (bit
+            // i = wave, slot q + nq*wave) already
+            if (wave < kSpecRows) {
+                k0 = 1;
+                if ((valid >> wave) & 1ull) {
+                    const int slot = q + nq * wave;
+                    fc1_entry_1<WT, GATED, CPL1>(q, valid, wave, slot, spu, spg, p.cd,
+                                                 p.b1[slot], xs, p.out, lane);
+                }
+            }
+        }
+        auto slot_of = [&](int i) { return q + nq * i; };
+        owner_fc1_1<WT, GATED, CPL1>(q, valid, slot_of, k0, p.bundles, p.bstride, p.cd, p.b1, xs,
+                                     p.out, wave, lane);
+    }
+}
+
+// FC1 over a neuron set for one token (x staged in LDS); modes as k_fc1.
+template <int WT, bool GATED, int CPL1>
+__global__ __launch_bounds__(kThreads) __attribute__((
+    amdgpu_waves_per_eu(Fc1Regs<GATED, CPL1>::waves_per_eu))) void k_fc1_1(Fc1Params p) {
+    __shared__ float xs[kMaxDLds];
+    __shared__ int slot_lds[kRowsPerWG];
+    __shared__ uint64_t valid_lds;
+    const int q = blockIdx.x, nq = gridDim.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float4 xv[4];
+    stage_load<4>(p.x, p.d, xv);
+    if (threadIdx.x < kRowsPerWG) {
+        const int i = threadIdx.x;
+        int slot = -1;
+        if (p.mode == 1) {
+            int n = *p.n_ids;
+            n = n < 0 ? 0 : (n > p.f ? p.f : n);
+            const int e = q + nq * i;
+            if (e < n) {
+                const int id = p.ids[e];
+                slot = (unsigned)id < (unsigned)p.f ? p.inv[id] : -1;
+                if ((unsigned)slot >= (unsigned)p.f) slot = -1;
+            }
+        } else {
+            const int s = q + nq * i;
+            if (s < p.f && (p.mode == 2 || ((p.ubits[q] >> i) & 1ull))) slot = s;
+        }
+        slot_lds[i] = slot;
+        const uint64_t b = __ballot(slot >= 0);
+        if (i == 0) valid_lds = b;
+    }
+    stage_store<4>(xs, p.d, xv);
+    __syncthreads();
+    const uint64_t valid = valid_lds;
+    if (threadIdx.x == 0) p.out.vbits[q] = valid;
+    auto slot_of = [&](int i) { return slot_lds[i]; };
+    owner_fc1_1<WT, GATED, CPL1>(q, valid, slot_of, 0, p.bundles, p.bstride, p.cd, p.b1, xs,
+                                 p.out, wave, lane);
+}
+
 // ---------------------------------------------------------------- FC2
 struct Fc2Params {
     const u32x4 *bundles;
@@ -815,7 +1159,7 @@ hipError_t launch_gather_f32(const float *src, const int32_t *perm, int n, float
     return hipGetLastError();
 }
 
-// waves per predictor layer-1 row and the resulting chunks per lane
+// waves per predictor layer-1 row and the resulting chunks per lane (batched form)
 static void l1_shape(const LayerView &L, int *wpr, int *cpl) {
     int w = L.H >= 2048 ? 1 : pow2_at_least((2048 + L.H - 1) / L.H);
     if (w > 8) w = 8;
@@ -824,30 +1168,71 @@ static void l1_shape(const LayerView &L, int *wpr, int *cpl) {
     *cpl = pow2_at_least((L.cd + 64 * w - 1) / (64 * w));
 }
 
+// single-token form: rows per workgroup R = ceil(H / 256) (power of two, <= 8)
+// so that about 256 workgroups cover P1, waves per row 8 / R, at most 16
+// chunks per lane
+static void pred1_shape(const LayerView &L, int *wpr, int *cpl) {
+    int R = pow2_at_least((L.H + 255) / 256);
+    if (R > kWaves) R = kWaves;
+    int w = kWaves / R;
+    while (w < kWaves && (L.cd + 64 * w - 1) / (64 * w) > 16) w *= 2;
+    *wpr = w;
+    *cpl = pow2_at_least((L.cd + 64 * w - 1) / (64 * w));
+}
+
 hipError_t launch_pred_l1(const LayerView &L, const float *x, int B, const Trace *tr,
                           hipStream_t s) {
+    const u32x4 *P1 = (const u32x4 *)L.p1;
+    if (B == 1) {
+        int wpr, cpl;
+        pred1_shape(L, &wpr, &cpl);
+        const int rpw = kWaves / wpr;
+        const dim3 grid((L.H + rpw - 1) / rpw), blk(kThreads);
+#define ASF_P1(WT, CPL)                                                                        \
+    ASF_LAUNCH(ASF_K_PRED_L1, (k_pred1<WT, CPL>), grid, blk, P1, L.c1, x, L.d, L.H, wpr, L.h);
+#define ASF_P1W(WT)                  \
+    switch (cpl) {                   \
+    case 1: ASF_P1(WT, 1) break;     \
+    case 2: ASF_P1(WT, 2) break;     \
+    case 4: ASF_P1(WT, 4) break;     \
+    case 8: ASF_P1(WT, 8) break;     \
+    default: ASF_P1(WT, 16) break;   \
+    }
+        if (L.wtype == ASF_F16) { ASF_P1W(1) } else { ASF_P1W(0) }
+#undef ASF_P1W
+#undef ASF_P1
+        return hipGetLastError();
+    }
     int wpr, cpl;
     l1_shape(L, &wpr, &cpl);
     const int rpw = kWaves / wpr;
     const dim3 grid((L.H + rpw - 1) / rpw), blk(kThreads);
-    const u32x4 *P1 = (const u32x4 *)L.p1;
-#define ASF_L1(WT, CPL, BT)                                                                 \
-    ASF_LAUNCH(ASF_K_PRED_L1, (k_pred_l1<WT, CPL, BT>), grid, blk, P1, L.c1, x, B, L.d, L.H,  \
-               wpr, L.h)
-#define ASF_L1C(WT, CPL) \
-    if (B == 1) ASF_L1(WT, CPL, 1); else ASF_L1(WT, CPL, 4);
+#define ASF_L1(WT, CPL)                                                                         \
+    ASF_LAUNCH(ASF_K_PRED_L1, (k_pred_l1<WT, CPL, 4>), grid, blk, P1, L.c1, x, B, L.d, L.H,    \
+               wpr, L.h);
 #define ASF_L1W(WT)                   \
     switch (cpl) {                    \
-    case 1: ASF_L1C(WT, 1) break;     \
-    case 2: ASF_L1C(WT, 2) break;     \
-    case 4: ASF_L1C(WT, 4) break;     \
-    default: ASF_L1C(WT, 8) break;    \
+    case 1: ASF_L1(WT, 1) break;      \
+    case 2: ASF_L1(WT, 2) break;      \
+    case 4: ASF_L1(WT, 4) break;      \
+    default: ASF_L1(WT, 8) break;     \
     }
     if (L.wtype == ASF_F16) { ASF_L1W(1) } else { ASF_L1W(0) }
 #undef ASF_L1W
-#undef ASF_L1C
 #undef ASF_L1
     return hipGetLastError();
+}
+
+// chunks per lane for a d row, rounded up to an instantiated count
+static int fc1_cpl(int cd) {
+    const int c = (cd + 63) / 64;
+    if (c <= 2) return c < 1 ? 1 : c;
+    if (c <= 4) return 4;
+    if (c <= 8) return 8;
+    if (c <= 10) return 10;
+    if (c <= 12) return 12;
+    if (c <= 14) return 14;
+    return 16;
 }
 
 static Fc1Out fc1_out(const LayerView &L) { return Fc1Out{L.vbits, L.lslot, L.la, L.max_batch}; }
@@ -872,46 +1257,59 @@ hipError_t launch_score(const LayerView &L, const float *x, int B, bool fc1, con
     p.d = L.d;
     p.out = fc1_out(L);
     const int cpl2 = pow2_at_least((L.ch + 63) / 64);
-    const int cpl1 = pow2_at_least((L.cd + 63) / 64);
     const dim3 grid(L.nq), blk(kThreads);
-    const bool fused = fc1 && L.wtype == ASF_F16 && B == 1;
-    const int k = fused ? ASF_K_SCORE_FC1 : ASF_K_SCORE;
-    if (fused) {
-#define ASF_SF(C2, C1)                                                                          \
-    if (L.gated) ASF_LAUNCH(k, (k_score<1, C2, 1, true, true, C1>), grid, blk, p);              \
-    else ASF_LAUNCH(k, (k_score<1, C2, 1, true, false, C1>), grid, blk, p);
-#define ASF_SF1(C2)                   \
-    switch (cpl1) {                   \
-    case 1: ASF_SF(C2, 1) break;      \
-    case 2: ASF_SF(C2, 2) break;      \
-    case 4: ASF_SF(C2, 4) break;      \
-    case 8: ASF_SF(C2, 8) break;      \
-    default: ASF_SF(C2, 16) break;    \
+    if (B == 1) {
+        const int k = fc1 ? ASF_K_SCORE_FC1 : ASF_K_SCORE;
+        const int cpl1 = fc1_cpl(L.cd);
+        // the hottest rows are loaded before scoring when they fit (at most
+        // 8 chunks per lane of up and gate rows) and one workgroup per CU
+        // covers every owner
+        const bool spec = L.nq <= 256;
+#define ASF_S1F(WT, C2, G, C1)                                                                 \
+    if (spec && C1 * (G ? 2 : 1) <= 8)                                                         \
+        ASF_LAUNCH(k, (k_score1<WT, C2, true, G, C1, (C1 * (G ? 2 : 1) <= 8)>), grid, blk, p); \
+    else ASF_LAUNCH(k, (k_score1<WT, C2, true, G, C1, false>), grid, blk, p);
+#define ASF_S1G(WT, C2, C1) \
+    if (L.gated) { ASF_S1F(WT, C2, true, C1) } else { ASF_S1F(WT, C2, false, C1) }
+#define ASF_S1C(WT, C2)                  \
+    if (!fc1) {                          \
+        ASF_LAUNCH(k, (k_score1<WT, C2, false, false, 1, false>), grid, blk, p); \
+    } else switch (cpl1) {               \
+    case 1: ASF_S1G(WT, C2, 1) break;    \
+    case 2: ASF_S1G(WT, C2, 2) break;    \
+    case 4: ASF_S1G(WT, C2, 4) break;    \
+    case 8: ASF_S1G(WT, C2, 8) break;    \
+    case 10: ASF_S1G(WT, C2, 10) break;  \
+    case 12: ASF_S1G(WT, C2, 12) break;  \
+    case 14: ASF_S1G(WT, C2, 14) break;  \
+    default: ASF_S1G(WT, C2, 16) break;  \
     }
-        switch (cpl2) {
-        case 1: ASF_SF1(1) break;
-        case 2: ASF_SF1(2) break;
-        default: ASF_SF1(4) break;
-        }
-#undef ASF_SF1
-#undef ASF_SF
-    } else {
-#define ASF_S(WT, C2)                                                                          \
-    if (B == 1) ASF_LAUNCH(k, (k_score<WT, C2, 1, false, false, 1>), grid, blk, p);            \
-    else ASF_LAUNCH(k, (k_score<WT, C2, 4, false, false, 1>), grid, blk, p);
+#define ASF_S1W(WT)                  \
+    switch (cpl2) {                  \
+    case 1: ASF_S1C(WT, 1) break;    \
+    case 2: ASF_S1C(WT, 2) break;    \
+    default: ASF_S1C(WT, 4) break;   \
+    }
+        if (L.wtype == ASF_F16) { ASF_S1W(1) } else { ASF_S1W(0) }
+#undef ASF_S1W
+#undef ASF_S1C
+#undef ASF_S1G
+#undef ASF_S1F
+        return hipGetLastError();
+    }
+    // batched: score only, then FC1 of the union
+#define ASF_S(WT, C2) ASF_LAUNCH(ASF_K_SCORE, (k_score<WT, C2, 4, false, false, 1>), grid, blk, p);
 #define ASF_SW(WT)                  \
     switch (cpl2) {                 \
     case 1: ASF_S(WT, 1) break;     \
     case 2: ASF_S(WT, 2) break;     \
     default: ASF_S(WT, 4) break;    \
     }
-        if (L.wtype == ASF_F16) { ASF_SW(1) } else { ASF_SW(0) }
+    if (L.wtype == ASF_F16) { ASF_SW(1) } else { ASF_SW(0) }
 #undef ASF_SW
 #undef ASF_S
-    }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !fc1 || fused) return e;
-    // the score-only kernel ran: FC1 of the union separately
+    if (e != hipSuccess || !fc1) return e;
     return launch_fc1(L, x, B, 0, nullptr, nullptr, tr, s);
 }
 
@@ -932,8 +1330,29 @@ hipError_t launch_fc1(const LayerView &L, const float *x, int B, int mode, const
     p.n_ids = n_ids;
     p.inv = L.inv;
     p.out = fc1_out(L);
-    const int cpl1 = pow2_at_least((L.cd + 63) / 64);
     const dim3 grid(L.nq), blk(kThreads);
+    if (B == 1) {
+        const int cpl1 = fc1_cpl(L.cd);
+#define ASF_F1(WT, C1)                                                            \
+    if (L.gated) ASF_LAUNCH(ASF_K_FC1, (k_fc1_1<WT, true, C1>), grid, blk, p); \
+    else ASF_LAUNCH(ASF_K_FC1, (k_fc1_1<WT, false, C1>), grid, blk, p);
+#define ASF_F1W(WT)                  \
+    switch (cpl1) {                  \
+    case 1: ASF_F1(WT, 1) break;     \
+    case 2: ASF_F1(WT, 2) break;     \
+    case 4: ASF_F1(WT, 4) break;     \
+    case 8: ASF_F1(WT, 8) break;     \
+    case 10: ASF_F1(WT, 10) break;   \
+    case 12: ASF_F1(WT, 12) break;   \
+    case 14: ASF_F1(WT, 14) break;   \
+    default: ASF_F1(WT, 16) break;   \
+    }
+        if (L.wtype == ASF_F16) { ASF_F1W(1) } else { ASF_F1W(0) }
+#undef ASF_F1W
+#undef ASF_F1
+        return hipGetLastError();
+    }
+    const int cpl1 = pow2_at_least((L.cd + 63) / 64);
 #define ASF_F(WT, C1)                                                             \
     if (L.gated) ASF_LAUNCH(ASF_K_FC1, (k_fc1<WT, true, C1>), grid, blk, p); \
     else ASF_LAUNCH(ASF_K_FC1, (k_fc1<WT, false, C1>), grid, blk, p);
