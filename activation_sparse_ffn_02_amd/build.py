@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libasf.so")
-SOURCES = ["asf_api.hip", "asf_kernels.hip"]
+SOURCES = ["asf_api.hip", "asf_kernels.hip", "asf_batched.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -16,6 +16,7 @@ constexpr int kSlices = 16;       // FC2: output slices
 constexpr int kGroups = 16;       // FC2: neuron groups (partials per output)
 constexpr int kMaxBatch = 32;
 constexpr int kMaxFfn = 65536;    // the list kernel handles up to 1024 mask words
+constexpr int kArrive = 64;       // arrival counters (FC2 slices, predictor row tiles)
 
 // Device view of a created layer, carved out of the caller's storage.
 //
@@ -53,7 +54,9 @@ struct LayerView {
     int32_t *lslot;    // [nq][64]                 their slots (ascending bit)
     float *la;         // [nq][64][max_batch]      their FC1 activations
     float *partial;    // [kGroups][max_batch][d]  FC2 partial sums
-    unsigned *arrive;  // [kSlices]                FC2 arrivals per slice
+    unsigned *arrive;  // [kArrive]                FC2 arrivals per slice
+    float *pred_part;  // [ceil(H/32)][8][32*32]   batched predictor partial tiles
+    unsigned *pred_arrive;  // [kArrive]           their arrivals per row tile
     uint64_t *masks;   // [max_batch][words]       slot-ordered token masks
     int32_t *slots;    // [f]                      ascending active slots
     int32_t *count;    // [1]                      their number
@@ -93,6 +96,15 @@ hipError_t launch_fc1(const LayerView &L, const float *x, int B, int mode, const
 // entries' slots come from the list (caller ids) rather than the owner bits
 hipError_t launch_fc2(const LayerView &L, int B, bool listed, const float *resid, float *y,
                       const Trace *tr, hipStream_t s);
+// batched forms on the matrix cores (B >= 2, fp16 weights)
+int pred_mm_splits(int d);
+hipError_t launch_pred_mm(const LayerView &L, const float *x, int B, const Trace *tr,
+                          hipStream_t s);
+hipError_t launch_score_mm(const LayerView &L, int B, const Trace *tr, hipStream_t s);
+hipError_t launch_fc1_mm(const LayerView &L, const float *x, int B, int mode, const int32_t *ids,
+                         const int32_t *n_ids, const Trace *tr, hipStream_t s);
+hipError_t launch_fc2_mm(const LayerView &L, int B, bool listed, const float *resid, float *y,
+                         const Trace *tr, hipStream_t s);
 // slot-ordered outputs of the last prediction: token masks, ascending list
 hipError_t launch_list(const LayerView &L, int B, int32_t *active_ids, int32_t *n_active,
                        uint64_t *token_masks, const Trace *tr, hipStream_t s);

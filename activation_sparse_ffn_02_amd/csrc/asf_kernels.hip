@@ -1203,6 +1203,7 @@ hipError_t launch_pred_l1(const LayerView &L, const float *x, int B, const Trace
 #undef ASF_P1
         return hipGetLastError();
     }
+    if (L.wtype == ASF_F16) return launch_pred_mm(L, x, B, tr, s);
     int wpr, cpl;
     l1_shape(L, &wpr, &cpl);
     const int rpw = kWaves / wpr;
@@ -1298,6 +1299,11 @@ hipError_t launch_score(const LayerView &L, const float *x, int B, bool fc1, con
         return hipGetLastError();
     }
     // batched: score only, then FC1 of the union
+    if (L.wtype == ASF_F16) {
+        const hipError_t e = launch_score_mm(L, B, tr, s);
+        if (e != hipSuccess || !fc1) return e;
+        return launch_fc1(L, x, B, 0, nullptr, nullptr, tr, s);
+    }
 #define ASF_S(WT, C2) ASF_LAUNCH(ASF_K_SCORE, (k_score<WT, C2, 4, false, false, 1>), grid, blk, p);
 #define ASF_SW(WT)                  \
     switch (cpl2) {                 \
@@ -1352,6 +1358,7 @@ hipError_t launch_fc1(const LayerView &L, const float *x, int B, int mode, const
 #undef ASF_F1
         return hipGetLastError();
     }
+    if (L.wtype == ASF_F16) return launch_fc1_mm(L, x, B, mode, ids, n_ids, tr, s);
     const int cpl1 = pow2_at_least((L.cd + 63) / 64);
 #define ASF_F(WT, C1)                                                             \
     if (L.gated) ASF_LAUNCH(ASF_K_FC1, (k_fc1<WT, true, C1>), grid, blk, p); \
@@ -1389,6 +1396,7 @@ hipError_t launch_fc2(const LayerView &L, int B, bool listed, const float *resid
     p.y = y;
     p.partial = L.partial;
     p.arrive = L.arrive;
+    if (B > 1 && L.wtype == ASF_F16) return launch_fc2_mm(L, B, listed, resid, y, tr, s);
     const dim3 grid(kSlices * kGroups), blk(kThreads);
     if (L.wtype == ASF_F16) {
         if (B == 1) ASF_LAUNCH(ASF_K_FC2, (k_fc2<1, 1>), grid, blk, p);

@@ -51,6 +51,9 @@ def parse():
                     help="tokens through the 48-layer stack (0 skips the stack)")
     ap.add_argument("--stack-warmup", type=int, default=8)
     ap.add_argument("--stack-dense-tokens", type=int, default=8)
+    ap.add_argument("--batches", type=int, nargs="*", default=[1, 4, 16, 32],
+                    help="batch sizes of the batched-union workload (none skips it)")
+    ap.add_argument("--batched-ring", type=int, default=3)
     return ap.parse_args()
 
 
@@ -247,6 +250,88 @@ def bench_stack(args, asf, torch, np, wl, dev, stream):
     return res
 
 
+def bench_batched(args, asf, torch, np, wl, dev, stream):
+    """Batched decode on the OPT-13B-shaped layer (5120x20480 fp16, predictor
+    5120->1024->20480, ~5% active per token): B tokens per step share the
+    union of their predicted sets.  1000 // B steps per batch size over a ring
+    of layer copies; the dense comparators are this library's dense FFN and
+    torch's fp16 GEMMs (hipBLASLt) of the same shape."""
+    name = "opt13b_batched"
+    L = wl.config_layer(name)
+    sh = L.shape
+    X = torch.from_numpy(wl.config_tokens(name, 1000)).to(dev)
+
+    def up(a):
+        return None if a is None else torch.from_numpy(a).to(dev)
+    w_up, w_down = up(L.w_up), up(L.w_down)
+    orig = dict(p1=up(L.p1), p2=up(L.p2), b1=up(L.b1), b2=up(L.b2), c2=up(L.c2),
+                neuron_table=up(L.perm))
+    ring = [asf.Layer(w_up, w_down, orig["p1"], orig["p2"], b1=orig["b1"], b2=orig["b2"],
+                      c2=orig["c2"], neuron_table=orig["neuron_table"], max_batch=32)
+            for _ in range(args.batched_ring)]
+    torch.cuda.synchronize()
+    del orig
+    sh_ = stream.cuda_stream
+    out = []
+    for B in args.batches:
+        steps = 1000 // B
+        Y = torch.empty((args.batched_ring, B, sh.d), dtype=torch.float32, device=dev)
+        xs = [X[i * B:(i + 1) * B].data_ptr() for i in range(steps)]
+        ys = [Y[r].data_ptr() for r in range(args.batched_ring)]
+        for i in range(min(10, steps)):
+            ring[i % len(ring)].decode_step_raw(xs[i], B, ys[i % len(ring)], sh_)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ring[i % len(ring)].decode_step_raw(xs[i], B, ys[i % len(ring)], sh_)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        counts = torch.zeros(steps, dtype=torch.int32, device=dev)
+        for i in range(steps):
+            ring[0].predict(X[i * B:(i + 1) * B], n_active=counts[i:i + 1], want_list=False)
+        torch.cuda.synchronize()
+        k = float(counts.double().mean())
+        step_bytes, _, dense_bytes = bytes_model(sh, k)
+        nd = max(5, min(50, steps))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ring[0].dense_ffn_ref(X[:B])
+        e0.record()
+        for i in range(nd):
+            ring[i % len(ring)].dense_ffn_ref(X[i * B:(i + 1) * B], out=Y[i % len(ring)])
+        e1.record()
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / nd
+        # torch fp16 GEMMs of the same shape (context)
+        xh = X[:B].half()
+        bh = torch.from_numpy(L.b1).to(dev).half()
+        for _ in range(3):
+            torch.nn.functional.linear(torch.relu(torch.nn.functional.linear(xh, w_up, bh)), w_down)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(nd):
+            xh = X[i * B:(i + 1) * B].half()
+            torch.nn.functional.linear(torch.relu(torch.nn.functional.linear(xh, w_up, bh)), w_down)
+        e1.record()
+        torch.cuda.synchronize()
+        torch_ms = e0.elapsed_time(e1) / nd
+        ms = el * 1e3 / steps
+        out.append({
+            "batch": B, "steps": steps, "tokens_per_s": B * steps / el, "ms_per_step": ms,
+            "union_frac": k / sh.f, "algorithmic_bytes_per_step": step_bytes,
+            "effective_gbps": step_bytes / (ms * 1e-3) / 1e9,
+            "effective_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "dense_ms_per_step": dense_ms, "dense_gbps": dense_bytes / (dense_ms * 1e-3) / 1e9,
+            "speedup_vs_dense": dense_ms / ms,
+            "torch_fp16_gemm_ms_per_step": torch_ms,
+        })
+        log(args, "batched B=%d: %.1f us/step, union %.3f" % (B, ms * 1e3, k / sh.f))
+    for lay in ring:
+        lay.close()
+    return {"workload": "OPT-13B-shaped FFN layer 5120x20480 fp16, predictor 5120->1024->20480, "
+                        "~5% active per token, batch union", "ring_layers": len(ring),
+            "by_batch": out}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -416,6 +501,10 @@ def main():
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         out["stack"] = bench_stack(args, asf, torch, np, wl, dev, stream)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    if args.batches:
+        out["batched"] = bench_batched(args, asf, torch, np, wl, dev, stream)
     print(json.dumps(out), flush=True)
 
 

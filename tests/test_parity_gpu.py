@@ -237,3 +237,75 @@ def test_decode_step_tiling_variants(orc, d, f, H, gated):
     worst = _run_tokens(orc, L, x, lay, "fused %dx%d H%d%s" % (d, f, H, " gated" if gated else ""),
                         check_dense=False)
     assert worst <= TOL["f16"]
+
+
+def _batched_check(orc, L, x, lay, label, check_dense=True, user_list=True):
+    """B tokens through the batched (matrix-core) path: per-token masks and
+    the union against the oracle's scores (margin rule); decode_step equal bit
+    for bit to predict + sparse_ffn; outputs against the oracle over the GPU's
+    union; a caller id list in any order; the dense comparator."""
+    B, f = x.shape[0], L.shape.f
+    xd = to_dev(x)
+    masks = torch.zeros((B, (f + 63) // 64), dtype=torch.int64, device="cuda")
+    active, n = lay.predict(xd, token_masks=masks)
+    y1 = lay.sparse_ffn(xd)
+    a2 = torch.empty_like(active)
+    n2 = torch.empty_like(n)
+    y2 = lay.decode_step(xd, active=a2, n_active=n2)
+    torch.cuda.synchronize()
+    k = int(n.item())
+    ids = active[:k].cpu().numpy()
+    assert int(n2.item()) == k and np.array_equal(a2[:k].cpu().numpy(), ids)
+    assert torch.equal(y1, y2), label + ": decode_step differs from predict + sparse_ffn"
+    _, s_orc, _ = orc.predict(L.p1, L.c1, L.p2, L.c2, x)
+    mw = masks.cpu().numpy().view(np.uint64)
+    bits = ((mw[:, :, None] >> np.arange(64, dtype=np.uint64)) & np.uint64(1)).reshape(B, -1)
+    bits = bits[:, :f].astype(bool)
+    amb = 0
+    for t in range(B):
+        amb += check_set(L.perm[np.nonzero(bits[t])[0]], s_orc[t], 0.0, L.perm,
+                         "%s tok %d" % (label, t))
+    assert np.array_equal(ids, L.perm[np.nonzero(bits.any(axis=0))[0]])
+    y_orc = orc.ffn(L.w_up, L.w_down, x, ids, b1=L.b1, b2=L.b2, W_gate=L.w_gate)
+    yg = y1.cpu().numpy()
+    worst = max(rel_l2(yg[t], y_orc[t]) for t in range(B))
+    assert worst <= TOL["f16"], "%s: rel-L2 %.3g" % (label, worst)
+    if user_list:
+        rng = np.random.default_rng(B)
+        sub = rng.permutation(ids)[: max(1, k // 2)].astype(np.int32)
+        yl = lay.sparse_ffn(xd, active=to_dev(sub), n_active=to_dev(np.array([sub.size], np.int32)))
+        yl_orc = orc.ffn(L.w_up, L.w_down, x, sub, b1=L.b1, b2=L.b2, W_gate=L.w_gate)
+        ylg = yl.cpu().numpy()
+        for t in range(B):
+            assert rel_l2(ylg[t], yl_orc[t]) <= TOL["f16"]
+    if check_dense:
+        yd = lay.dense_ffn_ref(xd).cpu().numpy()
+        yd_orc = orc.dense_ffn(L.w_up, L.w_down, x, b1=L.b1, b2=L.b2, W_gate=L.w_gate)
+        for t in range(B):
+            assert rel_l2(yd[t], yd_orc[t]) <= TOL["f16"]
+    print("%s: B=%d union %d (%.3f), worst rel-L2 %.3g, ambiguous flips %d"
+          % (label, B, k, k / f, worst, amb))
+
+
+@pytest.mark.parametrize("B,gated", [(3, False), (16, False), (5, True), (32, True)])
+def test_batched_matrix_core_path(orc, B, gated):
+    """Scaled layers with ragged tiles (d not a multiple of 256, H not of 64,
+    f not of 64) through the batched kernels."""
+    need_gpu()
+    _, sh = wl.CONFIGS["llama7b_gated_relu" if gated else "opt13b_batched"]
+    L = wl.make_layer(wl.scaled_shape(sh, 1152, 3000 + 7 * B, 200), 900 + B)
+    lay = asf().layer_from_numpy(L, max_batch=32)
+    x = wl.make_tokens(1152, B, 950 + B)
+    _batched_check(orc, L, x, lay, "mm %s" % ("gated" if gated else "plain"))
+
+
+def test_batched_full_size(orc):
+    """The OPT-13B-shaped layer (5120x20480 fp16, predictor 5120->1024->20480)
+    at batch 4 and 32."""
+    need_gpu()
+    L = wl.config_layer("opt13b_batched")
+    lay = asf().layer_from_numpy(L, max_batch=32)
+    X = wl.config_tokens("opt13b_batched", 36)
+    for B, off in ((4, 0), (32, 4)):
+        _batched_check(orc, L, X[off:off + B], lay, "opt13b B%d" % B, check_dense=(B == 4),
+                       user_list=(B == 32))
