@@ -65,6 +65,8 @@ size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v) {
     t.perm = (int32_t *)take(f * 4);
     t.inv = (int32_t *)take(f * 4);
     t.h = (float *)take(Bm * H * 4);
+    t.h16 = Bm > 1 ? (_Float16 *)take(2 * Bm * H * 2) : nullptr;
+    t.x16 = Bm > 1 ? (_Float16 *)take(Bm * d * 2) : nullptr;
     t.wbits = (uint64_t *)take(Bm * nq * 8);
     t.ubits = (uint64_t *)take(nq * 8);
     t.vbits = (uint64_t *)take(nq * 8);
@@ -78,6 +80,7 @@ size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v) {
     t.masks = (uint64_t *)take(Bm * words * 8);
     t.slots = (int32_t *)take(f * 4);
     t.count = (int32_t *)take(64);
+    t.rows = (int32_t *)take(64);
     if (v) *v = t;
     return (size_t)(p - align_up(base, 256));
 }

@@ -114,7 +114,9 @@ __global__ __launch_bounds__(kThreads) void k_pred_mm(const u32x4 *__restrict__ 
                                                       const float *__restrict__ x, int B, int d,
                                                       int H, int KS, float *__restrict__ part,
                                                       unsigned *__restrict__ arrive,
-                                                      float *__restrict__ h) {
+                                                      float *__restrict__ h,
+                                                      _Float16 *__restrict__ h16,
+                                                      _Float16 *__restrict__ x16) {
     __shared__ float red[kW][kTile * kTile];
     __shared__ int last_lds;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -156,6 +158,16 @@ __global__ __launch_bounds__(kThreads) void k_pred_mm(const u32x4 *__restrict__ 
         for (int w = 0; w < kW; ++w) sum += red[w][e];
         v[j] = sum;
     }
+    if (mt == 0) {
+        // x as fp16 for the FC1 of this step: this workgroup's k range
+        const int n8 = d / KS / 8;
+        for (int idx = tid; idx < B * n8; idx += kThreads) {
+            const int t = idx / n8, k = ks * (d / KS) + 8 * (idx % n8);
+            h8 hv, unused;
+            frag_f32<false>(x + (size_t)t * d + k, true, hv, unused);
+            *reinterpret_cast<h8 *>(x16 + (size_t)t * d + k) = hv;
+        }
+    }
     if (KS > 1) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
@@ -173,71 +185,167 @@ __global__ __launch_bounds__(kThreads) void k_pred_mm(const u32x4 *__restrict__ 
     for (int j = 0; j < 2; ++j) {
         const int e = tid + kThreads * j;
         const int r = kTile * mt + e / kTile, t = e % kTile;
-        if (r < H && t < B) h[(size_t)t * H + r] = fmaxf(v[j] + c1[r], 0.0f);
+        if (r < H && t < B) {
+            const float hv = fmaxf(v[j] + c1[r], 0.0f);
+            const _Float16 hi = (_Float16)hv;
+            h[(size_t)t * H + r] = hv;
+            h16[(size_t)t * H + r] = hi;
+            h16[(size_t)(B + t) * H + r] = (_Float16)(hv - (float)hi);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- weight tiles through LDS
+// A 32-row weight tile streams in chunks of 256 k (512 bytes of fp16 per
+// row, 16 KiB per chunk): thread t loads 16-byte chunks t%16 and t%16 + 16
+// of row t/16 (a wave instruction covers 4 rows x 256 contiguous bytes),
+// kPre chunks ahead in registers, and stores them to one of two LDS buffers
+// with the chunk index XOR-ed with row % 16, so that the fragment reads
+// (32 rows at one chunk) hit distinct banks.  Wave w multiplies MFMA steps
+// 2w and 2w+1 of every chunk (a k split across the waves; the 8 partial
+// tiles are added in wave order at the end).
+constexpr int kChunkK = 256;                 // k per chunk
+constexpr int kChunkC = kChunkK / 8;         // 16-byte chunks per row per chunk (32)
+constexpr int kPre = 4;                      // chunks in flight per thread
+
+__device__ __forceinline__ int swz(int row, int c) { return row * kChunkC + (c ^ (row & 15)); }
+
+// thread's two loads of chunk `ch` of a row whose first 16-byte chunk is at
+// `rp` (C chunks per row); chunks past C and dead rows give zeros
+__device__ __forceinline__ void tile_load(const u32x4 *rp, bool live, int C, int ch, int lc,
+                                          u32x4 &v0, u32x4 &v1) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int c0 = ch * kChunkC + lc, c1 = c0 + 16;
+    v0 = (live && c0 < C) ? rp[c0] : z;
+    v1 = (live && c1 < C) ? rp[c1] : z;
+}
+
+__device__ __forceinline__ void tile_store(u32x4 *buf, int lrow, int lc, const u32x4 &v0,
+                                           const u32x4 &v1) {
+    buf[swz(lrow, lc)] = v0;
+    buf[swz(lrow, lc + 16)] = v1;
+}
+
+// A fragment of step s (0..15) of a staged chunk: lane row l%32, k group l/32
+__device__ __forceinline__ h8 tile_frag(const u32x4 *buf, int s, int lane) {
+    const int row = lane & 31, c = 2 * s + (lane >> 5);
+    return __builtin_bit_cast(h8, buf[swz(row, c)]);
+}
+
+// Token fragment of step s of chunk ch: 8 consecutive fp16 at chunk
+// ch*32 + 2s + g of a token row (C chunks), zero past C or for dead tokens.
+__device__ __forceinline__ u32x4 tok_frag(const u32x4 *trow, bool tok, int C, int ch, int s,
+                                          int lane) {
+    const int c = ch * kChunkC + 2 * s + (lane >> 5);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    return (tok && c < C) ? trow[c] : z;
+}
+
+// The 8 wave partial tiles (red[w][row*32 + col]) of this workgroup summed in
+// wave order; thread tid owns elements tid and tid + 512.
+__device__ __forceinline__ void tile_sum(const float (*red)[kTile * kTile], float (&v)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int e = threadIdx.x + kThreads * j;
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kW; ++w) sum += red[w][e];
+        v[j] = sum;
     }
 }
 
 // ---------------------------------------------------------------- predictor layer 2
-// Owner q: rows i = 0..63 (slot q + nq*i) in two 32-row tiles; wave w takes
-// tile w & 1 and the (w >> 1)-th quarter of the 16-k steps over H.  The
-// quarter tiles are added in order, then c2; wave w ballots tokens w, w+8,
-// ... into the per-token owner words; the union is their OR.
+// Owner q: rows i = 0..63 (slot q + nq*i) in two 32-row tiles, each streamed
+// through LDS over k = H; h enters as fp16 hi + lo (two MFMAs per step).
+// Scores = tile sums + c2; wave w ballots tokens w, w+8, ... into the
+// per-token owner words; the union is their OR.
 __global__ __launch_bounds__(kThreads) void k_score_mm(const u32x4 *__restrict__ P2,
                                                        const float *__restrict__ c2,
-                                                       const float *__restrict__ h, int B, int H,
-                                                       int f, float theta,
+                                                       const _Float16 *__restrict__ h16, int B,
+                                                       int H, int f, float theta,
                                                        uint64_t *__restrict__ wbits,
                                                        uint64_t *__restrict__ ubits) {
+    __shared__ u32x4 abuf[2][kTile * kChunkC];
     __shared__ float red[kW][kTile * kTile];
+    __shared__ float sc[2 * kTile][kTile + 1];
     __shared__ uint64_t uw[kW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int q = blockIdx.x, nq = gridDim.x;
-    const int tile = wave & 1, quarter = wave >> 1;
-    const int g = lane >> 5, col = lane & 31;
-    const int C = H / 8;                              // 8-k chunks per row
-    const int nst = (C + 1) / 2;                      // 16-k steps (the last may be half)
-    const int st_beg = quarter * nst / 4, st_end = (quarter + 1) * nst / 4;
-    int slot = q + nq * (kTile * tile + col);
-    slot = slot < f ? slot : f - 1;
-    const u32x4 *arow = P2 + (size_t)slot * C;
+    const int C = H / 8;
+    const int nch = (C + kChunkC - 1) / kChunkC;
+    const int nit = 2 * nch;                      // (tile, chunk) pairs
+    const int lrow = tid / 16, lc = tid % 16;
+    const u32x4 *rp[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        int slot = q + nq * (kTile * t + lrow);
+        slot = slot < f ? slot : f - 1;
+        rp[t] = P2 + (size_t)slot * C;
+    }
+    const int col = lane & 31;
     const bool tok = col < B;
-    const float *hrow = h + (size_t)(tok ? col : 0) * H;
-    f32x16 acc = zero16();
-    for (int s0 = st_beg; s0 < st_end; s0 += kSteps) {
-        u32x4 a[kSteps];
-        h8 bh[kSteps], bl[kSteps];
+    const u32x4 *hhi = reinterpret_cast<const u32x4 *>(h16 + (size_t)(tok ? col : 0) * H);
+    const u32x4 *hlo = reinterpret_cast<const u32x4 *>(h16 + (size_t)(B + (tok ? col : 0)) * H);
+    u32x4 ra[kPre][2];
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            const int st = s0 + s < st_end ? s0 + s : st_end - 1;
-            const int c = 2 * st + g;
-            const bool in = c < C;
-            const int cc = in ? c : C - 1;
-            a[s] = in ? arow[cc] : u32x4{0u, 0u, 0u, 0u};
-            frag_f32<true>(hrow + 8 * cc, tok && in, bh[s], bl[s]);
-        }
+    for (int u = 0; u < kPre; ++u) {
+        const int it = u < nit ? u : nit - 1;
+        tile_load(rp[it / nch], true, C, it % nch, lc, ra[u][0], ra[u][1]);
+    }
+    f32x16 acc0 = zero16(), acc1 = zero16();
+    for (int it0 = 0; it0 < nit; it0 += kPre) {
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            if (s0 + s < st_end) {
-                const h8 av = __builtin_bit_cast(h8, a[s]);
-                acc = mfma(av, bh[s], acc);
-                acc = mfma(av, bl[s], acc);
+        for (int u = 0; u < kPre; ++u) {
+            const int it = it0 + u;
+            if (it < nit) {
+                const int buf = it & 1;
+                tile_store(abuf[buf], lrow, lc, ra[u][0], ra[u][1]);
+                const int nx = it + kPre < nit ? it + kPre : nit - 1;
+                tile_load(rp[nx / nch], true, C, nx % nch, lc, ra[u][0], ra[u][1]);
+                const int ch = it % nch;
+                u32x4 bh[2], bl[2];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    bh[k] = tok_frag(hhi, tok, C, ch, 2 * wave + k, lane);
+                    bl[k] = tok_frag(hlo, tok, C, ch, 2 * wave + k, lane);
+                }
+                __syncthreads();
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const h8 av = tile_frag(abuf[buf], 2 * wave + k, lane);
+                    if (it < nch) {
+                        acc0 = mfma(av, __builtin_bit_cast(h8, bh[k]), acc0);
+                        acc0 = mfma(av, __builtin_bit_cast(h8, bl[k]), acc0);
+                    } else {
+                        acc1 = mfma(av, __builtin_bit_cast(h8, bh[k]), acc1);
+                        acc1 = mfma(av, __builtin_bit_cast(h8, bl[k]), acc1);
+                    }
+                }
             }
         }
     }
-    tile_to_lds(red[wave], acc, lane);
+    // tile sums -> sc[i][t]
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        __syncthreads();
+        tile_to_lds(red[wave], t == 0 ? acc0 : acc1, lane);
+        __syncthreads();
+        float v[2];
+        tile_sum(red, v);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int e = tid + kThreads * j;
+            sc[kTile * t + e / kTile][e % kTile] = v[j];
+        }
+    }
     __syncthreads();
-    // score of row i (0..63), token t: tiles i / 32, quarters in order
     const int i = lane;
     const int slot_i = q + nq * i;
     const bool valid_i = slot_i < f;
     const float bias = c2[valid_i ? slot_i : f - 1];
     uint64_t u = 0;
     for (int t = wave; t < B; t += kW) {
-        const int e = (i % kTile) * kTile + t, tl = i / kTile;
-        float sc = 0.0f;
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) sc += red[tl + 2 * qq][e];
-        const uint64_t m = __ballot(valid_i && sc + bias > theta);
+        const uint64_t m = __ballot(valid_i && sc[i][t] + bias > theta);
         if (lane == 0) wbits[(size_t)t * nq + q] = m;
         u |= m;
     }
@@ -258,105 +366,210 @@ struct Fc1MmParams {
     int cd;              // chunks per d row
     const float *b1;
     const float *x;
-    int B, d, f;
+    const _Float16 *x16; // x as fp16 when taken from the predictor's copy
+    int B, d, f, nq;
     int mode;            // 0 union of the last prediction, 1 caller ids, 2 all
     const uint64_t *ubits;
     const int32_t *ids;
     const int32_t *n_ids;
     const int32_t *inv;
-    uint64_t *vbits;
-    int32_t *lslot;
-    float *la;
+    int32_t *lslot;      // [rows] slot of list row r (-1: a skipped caller id)
+    float *la;           // [rows][max_batch]
     int max_batch;
+    int32_t *rows;       // number of list rows
 };
 
-// Owner q: its listed neurons (rank r = r-th set bit) are rows of up to two
-// 32-row tiles; with one tile all 8 waves split k, with two each tile gets 4
-// waves.  Wave sums are added in k order; a = ReLU(up . x + b1) or, gated,
-// ReLU(gate . x + b1) * (up . x); written to la[q][r][t] and lslot[q][r].
-template <bool GATED>
+// Position of the r-th set bit of m (r < popcount(m)), by halving.
+__device__ __forceinline__ int nth_set_bit(uint64_t m, int r) {
+    int pos = 0;
+    int c = __popc((uint32_t)m);
+    if (r >= c) {
+        r -= c;
+        m >>= 32;
+        pos = 32;
+    }
+    uint32_t w = (uint32_t)m;
+    c = __popc(w & 0xffffu);
+    if (r >= c) { r -= c; w >>= 16; pos += 16; }
+    c = __popc(w & 0xffu);
+    if (r >= c) { r -= c; w >>= 8; pos += 8; }
+    c = __popc(w & 0xfu);
+    if (r >= c) { r -= c; w >>= 4; pos += 4; }
+    c = __popc(w & 0x3u);
+    if (r >= c) { r -= c; w >>= 2; pos += 2; }
+    if (r >= (int)(w & 1u)) pos += 1;
+    return pos;
+}
+
+// The FC1 list: mode 0 the union of the last prediction, owner by owner
+// (row r is the (r - pre[q])-th set bit i of owner q, slot q + nq*i, for the
+// owner with pre[q] <= r < pre[q+1], pre the popcount prefix); mode 1 the
+// caller's ids in list order; mode 2 every slot.  Workgroup b takes rows
+// 32b .. 32b+31 as one tile streamed through LDS over k = d; x enters as fp16.
+// a = ReLU(up . x + b1) (gated: ReLU(gate . x + b1) * (up . x)), written to
+// la[r][t] and lslot[r].
+template <bool GATED, bool X16>
 __global__ __launch_bounds__(kThreads) void k_fc1_mm(Fc1MmParams p) {
-    __shared__ int slot_lds[kRowsPerWG];
-    __shared__ int crow[kRowsPerWG];
-    __shared__ uint64_t valid_lds;
-    __shared__ float red[GATED ? 2 : 1][kW][kTile * kTile];
+    constexpr int NM = GATED ? 2 : 1;
+    __shared__ u32x4 abuf[NM][2][kTile * kChunkC];
+    __shared__ float red[kW][kTile * kTile];
+    __shared__ float gsum[GATED ? kTile * kTile : 1];
+    __shared__ uint64_t vb[kMaxFfn / 64];
+    __shared__ int pre[kMaxFfn / 64 + 1];
+    __shared__ int wave_tot[kW];
+    __shared__ int rslot[kTile];
+    __shared__ int nrows_lds;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int q = blockIdx.x, nq = gridDim.x;
-    if (tid < kRowsPerWG) {
-        const int i = tid;
-        int slot = -1;
-        if (p.mode == 1) {
-            int n = *p.n_ids;
-            n = n < 0 ? 0 : (n > p.f ? p.f : n);
-            const int e = q + nq * i;
-            if (e < n) {
-                const int id = p.ids[e];
-                slot = (unsigned)id < (unsigned)p.f ? p.inv[id] : -1;
-                if ((unsigned)slot >= (unsigned)p.f) slot = -1;
-            }
-        } else {
-            const int s = q + nq * i;
-            if (s < p.f && (p.mode == 2 || ((p.ubits[q] >> i) & 1ull))) slot = s;
+    const int r0 = kTile * blockIdx.x;
+    // ---- the list's length and this tile's slots
+    if (p.mode == 0) {
+        const int nq = p.nq;
+        for (int q = tid; q < nq; q += kThreads) vb[q] = p.ubits[q];
+        __syncthreads();
+        const int q0 = 2 * tid, q1 = 2 * tid + 1;
+        const int c0 = q0 < nq ? __popcll(vb[q0]) : 0, c1 = q1 < nq ? __popcll(vb[q1]) : 0;
+        const int sum = c0 + c1;
+        int incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += v;
         }
-        slot_lds[i] = slot;
-        const uint64_t b = __ballot(slot >= 0);
-        if (slot >= 0) crow[__popcll(b & ((1ull << i) - 1ull))] = slot;
-        if (i == 0) valid_lds = b;
+        if (lane == 63) wave_tot[wave] = incl;
+        __syncthreads();
+        int base = 0;
+        for (int w = 0; w < wave; ++w) base += wave_tot[w];
+        const int excl = base + incl - sum;
+        if (q0 < nq) pre[q0] = excl;
+        if (q1 < nq) pre[q1] = excl + c0;
+        if (tid == kThreads - 1) {
+            pre[nq] = base + incl;
+            nrows_lds = base + incl;
+        }
+        __syncthreads();
+        if (tid < kTile) {
+            const int r = r0 + tid;
+            int slot = -1;
+            if (r < nrows_lds) {
+                int lo = 0, hi = nq;                 // largest q with pre[q] <= r
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (pre[mid] <= r) lo = mid;
+                    else hi = mid;
+                }
+                slot = lo + nq * nth_set_bit(vb[lo], r - pre[lo]);
+            }
+            rslot[tid] = slot;
+        }
+    } else {
+        if (tid == 0) {
+            int n = p.f;
+            if (p.mode == 1) {
+                n = *p.n_ids;
+                n = n < 0 ? 0 : (n > p.f ? p.f : n);
+            }
+            nrows_lds = n;
+        }
+        __syncthreads();
+        if (tid < kTile) {
+            const int r = r0 + tid;
+            int slot = -1;
+            if (r < nrows_lds) {
+                if (p.mode == 2) {
+                    slot = r;
+                } else {
+                    const int id = p.ids[r];
+                    slot = (unsigned)id < (unsigned)p.f ? p.inv[id] : -1;
+                    if ((unsigned)slot >= (unsigned)p.f) slot = -1;
+                }
+            }
+            rslot[tid] = slot;
+        }
     }
     __syncthreads();
-    const uint64_t valid = valid_lds;
-    if (tid == 0) p.vbits[q] = valid;
-    const int n = __popcll(valid);
-    if (n == 0) return;
-    const int ntiles = (n + kTile - 1) / kTile;
-    const int tile = wave % ntiles, nk = kW / ntiles, kp = wave / ntiles;
-    const int g = lane >> 5, col = lane & 31;
-    const int r = kTile * tile + col;
-    const bool live = r < n;
-    const int slot = crow[live ? r : 0];
+    const int nrows = nrows_lds;
+    if (blockIdx.x == 0 && tid == 0) *p.rows = nrows;
+    if (r0 >= nrows) return;
+    // ---- the tile over k = d
+    const int C = p.cd;
+    const int nch = (C + kChunkC - 1) / kChunkC;
+    const int lrow = tid / 16, lc = tid % 16;
+    const int myslot = rslot[lrow];
+    const bool live = myslot >= 0;
     constexpr int UP = GATED ? 1 : 0;
-    const u32x4 *bp = p.bundles + (size_t)slot * p.bstride;
+    const u32x4 *bp = p.bundles + (size_t)(live ? myslot : 0) * p.bstride;
+    const u32x4 *rpu = bp + (size_t)UP * C, *rpg = bp;
+    const int col = lane & 31;
     const bool tok = col < p.B;
     const float *xrow = p.x + (size_t)(tok ? col : 0) * p.d;
-    const int nst = p.cd / 2;                         // 16-k steps (cd is even)
-    const int st_beg = kp * nst / nk, st_end = (kp + 1) * nst / nk;
-    f32x16 acc = zero16(), accg = zero16();
-    for (int s0 = st_beg; s0 < st_end; s0 += kSteps) {
-        u32x4 a[kSteps], ag[kSteps];
-        h8 bx[kSteps], unused[kSteps];
+    const u32x4 *xr16 = reinterpret_cast<const u32x4 *>(p.x16 + (size_t)(tok ? col : 0) * p.d);
+    u32x4 ra[kPre][NM][2];
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            const int st = s0 + s < st_end ? s0 + s : st_end - 1;
-            const int c = 2 * st + g;
-            a[s] = live ? bp[(size_t)UP * p.cd + c] : u32x4{0u, 0u, 0u, 0u};
-            if constexpr (GATED) ag[s] = live ? bp[c] : u32x4{0u, 0u, 0u, 0u};
-            frag_f32<false>(xrow + 8 * c, tok, bx[s], unused[s]);
-        }
+    for (int u = 0; u < kPre; ++u) {
+        const int ch = u < nch ? u : nch - 1;
+        tile_load(rpu, live, C, ch, lc, ra[u][0][0], ra[u][0][1]);
+        if constexpr (GATED) tile_load(rpg, live, C, ch, lc, ra[u][NM - 1][0], ra[u][NM - 1][1]);
+    }
+    f32x16 accu = zero16(), accg = zero16();
+    for (int ch0 = 0; ch0 < nch; ch0 += kPre) {
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            if (s0 + s < st_end) {
-                acc = mfma(__builtin_bit_cast(h8, a[s]), bx[s], acc);
-                if constexpr (GATED) accg = mfma(__builtin_bit_cast(h8, ag[s]), bx[s], accg);
+        for (int u = 0; u < kPre; ++u) {
+            const int ch = ch0 + u;
+            if (ch < nch) {
+                const int buf = ch & 1;
+#pragma unroll
+                for (int m = 0; m < NM; ++m) tile_store(abuf[m][buf], lrow, lc, ra[u][m][0], ra[u][m][1]);
+                const int nx = ch + kPre < nch ? ch + kPre : nch - 1;
+                tile_load(rpu, live, C, nx, lc, ra[u][0][0], ra[u][0][1]);
+                if constexpr (GATED) tile_load(rpg, live, C, nx, lc, ra[u][NM - 1][0], ra[u][NM - 1][1]);
+                h8 bx[2];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    if constexpr (X16) {
+                        bx[k] = __builtin_bit_cast(h8, tok_frag(xr16, tok, C, ch, 2 * wave + k, lane));
+                    } else {
+                        const int c = ch * kChunkC + 2 * (2 * wave + k) + (lane >> 5);
+                        h8 unused;
+                        frag_f32<false>(xrow + 8 * (c < C ? c : C - 1), tok && c < C, bx[k], unused);
+                    }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    accu = mfma(tile_frag(abuf[0][buf], 2 * wave + k, lane), bx[k], accu);
+                    if constexpr (GATED)
+                        accg = mfma(tile_frag(abuf[NM - 1][buf], 2 * wave + k, lane), bx[k], accg);
+                }
             }
         }
     }
-    tile_to_lds(red[0][wave], acc, lane);
-    if constexpr (GATED) tile_to_lds(red[GATED ? 1 : 0][wave], accg, lane);
+    // ---- epilogue
+    float v[2];
+    if constexpr (GATED) {
+        __syncthreads();
+        tile_to_lds(red[wave], accg, lane);
+        __syncthreads();
+        tile_sum(red, v);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) gsum[tid + kThreads * j] = v[j];
+    }
     __syncthreads();
-    for (int e2 = tid; e2 < ntiles * kTile * kTile; e2 += kThreads) {
-        const int tl = e2 / (kTile * kTile), e = e2 % (kTile * kTile);
-        const int rr = kTile * tl + e / kTile, t = e % kTile;
-        if (rr >= n || t >= p.B) continue;
-        float su = 0.0f, sg = 0.0f;
-        for (int k = 0; k < nk; ++k) {
-            su += red[0][tl + ntiles * k][e];
-            if constexpr (GATED) sg += red[GATED ? 1 : 0][tl + ntiles * k][e];
+    tile_to_lds(red[wave], accu, lane);
+    __syncthreads();
+    tile_sum(red, v);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int e = tid + kThreads * j;
+        const int rr = e / kTile, t = e % kTile, r = r0 + rr;
+        if (r >= nrows || t >= p.B) continue;
+        const int sl = rslot[rr];
+        float a = 0.0f;
+        if (sl >= 0) {
+            if constexpr (GATED) a = fmaxf(gsum[e] + p.b1[sl], 0.0f) * v[j];
+            else a = fmaxf(v[j] + p.b1[sl], 0.0f);
         }
-        const int sl = crow[rr];
-        const float a = GATED ? fmaxf(sg + p.b1[sl], 0.0f) * su : fmaxf(su + p.b1[sl], 0.0f);
-        const size_t ent = (size_t)q * kRowsPerWG + rr;
-        p.la[ent * p.max_batch + t] = a;
-        if (t == 0) p.lslot[ent] = sl;
+        p.la[(size_t)r * p.max_batch + t] = a;
+        if (t == 0) p.lslot[r] = sl;
     }
 }
 
@@ -366,12 +579,11 @@ struct Fc2MmParams {
     size_t bstride;      // chunks per bundle
     int dn_off;          // chunk offset of the down column in a bundle
     int cd;              // chunks per down column
-    const uint64_t *vbits;
     const int32_t *lslot;
-    int listed;
     const float *la;
+    const int32_t *rows;
     int max_batch;
-    int nq, d, B;
+    int d, B;
     const float *b2;
     const float *resid;
     float *y;
@@ -379,105 +591,77 @@ struct Fc2MmParams {
     unsigned *arrive;    // per slice
 };
 
-constexpr int kMaxProd = kMaxFfn / kRowsPerWG / kGroups + 1;
-constexpr int kFc2K = 16;                   // neurons per MFMA step
-constexpr int kWPitch = kSliceOut + 8;      // halfs per staged down row (16-byte multiple)
-constexpr int kAPitch = kFc2K + 8;          // halfs per staged token row of a
+constexpr int kFc2N = 64;                   // neurons per step (4 MFMA k-steps)
+constexpr int kWPitch = kSliceOut + 8;      // halfs per staged down row
+constexpr int kAPitch = kFc2N + 8;          // halfs per staged token row of a
+constexpr int kFc2Pre = 2;                  // steps in flight per thread
 
-// Workgroup (slice s, group g): outputs 256s .. 256s+255, neurons listed by
-// owners g, g+16, ...  Per step of 16 neurons each thread loads one 16-byte
-// chunk of one down segment (neuron tid / 32, chunk tid % 32) and one a
-// value (neuron tid / 32, token tid % 32), kSteps steps ahead; the step is
-// written to LDS (double buffered) and wave w multiplies tokens x its 32
-// outputs x 16 neurons, reading each lane's 8 neurons of one output column
-// transposed from LDS.  Group tiles meet in `partial`; the last group to
-// arrive at the slice adds the 16 in group order, then b2, then the residual.
+// Workgroup (slice s, group g): outputs 256s .. 256s+255 over list rows
+// [g*R/16, (g+1)*R/16).  Per step of 64 rows each thread loads four 16-byte
+// chunks of down segments (row tid/32 + 16j, chunk tid%32) and four a values
+// (row tid/32 + 16j, token tid%32), kFc2Pre steps ahead; the step is staged
+// in LDS (double buffered) and wave w multiplies tokens x its 32 outputs x
+// 64 rows, reading each lane's 8 rows of one output column transposed.
+// Group tiles meet in `partial`; the last group to arrive at the slice adds
+// the 16 in group order, then b2, then the residual.
 __global__ __launch_bounds__(kThreads) void k_fc2_mm(Fc2MmParams p) {
-    __shared__ uint64_t vb[kMaxProd];
-    __shared__ int pre[kMaxProd + 1];
-    __shared__ int2 tab[kMaxProd * kRowsPerWG];
-    __shared__ __attribute__((aligned(16))) _Float16 wl[2][kFc2K * kWPitch];
+    __shared__ __attribute__((aligned(16))) _Float16 wl[2][kFc2N * kWPitch];
     __shared__ __attribute__((aligned(16))) _Float16 al[2][kTile * kAPitch];
     __shared__ int last_lds;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nslice = gridDim.x / kGroups;
     const int s = blockIdx.x % nslice, g = blockIdx.x / nslice;
-    const int np = g < p.nq ? (p.nq - g + kGroups - 1) / kGroups : 0;
-    if (tid < np) vb[tid] = p.vbits[g + kGroups * tid];
-    __syncthreads();
-    if (tid < 64) {
-        const int c = tid < np ? __popcll(vb[tid]) : 0;
-        int incl = c;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int v = __shfl_up(incl, o, 64);
-            if (tid >= o) incl += v;
-        }
-        if (tid < np) pre[tid] = incl - c;
-        if (tid == 63) pre[np] = incl;
-    }
-    __syncthreads();
-    const int ng = pre[np];
-    for (int idx = tid; idx < np * kRowsPerWG; idx += kThreads) {
-        const int k = idx / kRowsPerWG, i = idx % kRowsPerWG;
-        const uint64_t m = vb[k];
-        if ((m >> i) & 1ull) {
-            const int r = __popcll(m & ((1ull << i) - 1ull));
-            const int q = g + kGroups * k;
-            const int ent = q * kRowsPerWG + r;
-            tab[pre[k] + r] = make_int2(p.listed ? p.lslot[ent] : q + p.nq * i, ent);
-        }
-    }
-    __syncthreads();
-    // this thread's share of every step: down chunk (neuron ln, chunk lc) and
-    // a (neuron ln, token lc)
+    const int R = *p.rows;
+    const int rb = (int)((long long)R * g / kGroups), re = (int)((long long)R * (g + 1) / kGroups);
+    const int nst = (re - rb + kFc2N - 1) / kFc2N;
     const int ln = tid / kTile, lc = tid % kTile;
-    const int chunk = s * (kSliceOut / 8) + lc;        // chunk of the down column
+    const int chunk = s * (kSliceOut / 8) + lc;
     const bool cin = chunk < p.cd;
     const u32x4 *dbase = p.bundles + p.dn_off + (cin ? chunk : 0);
     const bool tok_a = lc < p.B;
-    const int nst = (ng + kFc2K - 1) / kFc2K;
-    u32x4 rv[kSteps];
-    float ra[kSteps];
-    auto load_step = [&](int st, u32x4 &v, float &a) {
-        const int e = st * kFc2K + ln;
-        const bool in = st < nst && e < ng;
-        const int2 te = tab[in ? e : 0];
-        v = (in && cin) ? dbase[(size_t)te.x * p.bstride] : u32x4{0u, 0u, 0u, 0u};
-        a = (in && tok_a) ? p.la[(size_t)te.y * p.max_batch + lc] : 0.0f;
+    u32x4 rv[kFc2Pre][4];
+    float ra[kFc2Pre][4];
+    auto load_step = [&](int st, u32x4 (&v)[4], float (&a)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = rb + st * kFc2N + ln + 16 * j;
+            const bool in = st < nst && r < re;
+            const int sl = in ? p.lslot[r] : -1;
+            const bool ok = sl >= 0;
+            v[j] = (ok && cin) ? dbase[(size_t)sl * p.bstride] : u32x4{0u, 0u, 0u, 0u};
+            a[j] = (ok && tok_a) ? p.la[(size_t)r * p.max_batch + lc] : 0.0f;
+        }
     };
-    auto stage = [&](int buf, const u32x4 &v, float a) {
-        *reinterpret_cast<u32x4 *>(&wl[buf][ln * kWPitch + 8 * lc]) = v;
-        al[buf][lc * kAPitch + ln] = (_Float16)a;
+    auto stage = [&](int buf, const u32x4 (&v)[4], const float (&a)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            *reinterpret_cast<u32x4 *>(&wl[buf][(ln + 16 * j) * kWPitch + 8 * lc]) = v[j];
+            al[buf][lc * kAPitch + ln + 16 * j] = (_Float16)a[j];
+        }
     };
     const int gk = lane >> 5, col = lane & 31;
-    const int jw = kTile * wave + col;                 // output column within the slice
+    const int jw = kTile * wave + col;
     f32x16 acc = zero16();
-    if (ng > 0) {
+    if (nst > 0) {
 #pragma unroll
-        for (int u = 0; u < kSteps; ++u) load_step(u, rv[u], ra[u]);
-        stage(0, rv[0], ra[0]);
-        load_step(kSteps, rv[0], ra[0]);
-        __syncthreads();
-        for (int st0 = 0; st0 < nst; st0 += kSteps) {
+        for (int u = 0; u < kFc2Pre; ++u) load_step(u, rv[u], ra[u]);
+        for (int st0 = 0; st0 < nst; st0 += kFc2Pre) {
 #pragma unroll
-            for (int u = 0; u < kSteps; ++u) {
+            for (int u = 0; u < kFc2Pre; ++u) {
                 const int st = st0 + u;
                 if (st < nst) {
-                    const int nu = (u + 1) % kSteps;
-                    if (st + 1 < nst) {
-                        stage((st + 1) & 1, rv[nu], ra[nu]);
-                        load_step(st + 1 + kSteps, rv[nu], ra[nu]);
-                    }
                     const int buf = st & 1;
-                    h8 av, bv;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        av[j] = al[buf][col * kAPitch + 8 * gk + j];
-                        bv[j] = wl[buf][(8 * gk + j) * kWPitch + jw];
-                    }
-                    acc = mfma(av, bv, acc);
+                    stage(buf, rv[u], ra[u]);
+                    load_step(st + kFc2Pre, rv[u], ra[u]);
                     __syncthreads();
+#pragma unroll
+                    for (int k = 0; k < kFc2N / 16; ++k) {
+                        const h8 av = *reinterpret_cast<const h8 *>(&al[buf][col * kAPitch + 16 * k + 8 * gk]);
+                        h8 bv;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) bv[j] = wl[buf][(16 * k + 8 * gk + j) * kWPitch + jw];
+                        acc = mfma(av, bv, acc);
+                    }
                 }
             }
         }
@@ -490,15 +674,35 @@ __global__ __launch_bounds__(kThreads) void k_fc2_mm(Fc2MmParams p) {
         if (t < p.B && m < p.d) p.partial[((size_t)g * p.B + t) * p.d + m] = acc[i];
     }
     if (!arrive_last(p.arrive + s, (unsigned)kGroups, &last_lds)) return;
-    for (int idx = tid; idx < p.B * kSliceOut; idx += kThreads) {
-        const int t = idx / kSliceOut, m = kSliceOut * s + idx % kSliceOut;
+    // four outputs per item; per output: groups in order, then b2, then the
+    // residual
+    constexpr int n4 = kSliceOut / 4;
+    for (int idx = tid; idx < p.B * n4; idx += kThreads) {
+        const int t = idx / n4, m = kSliceOut * s + 4 * (idx % n4);
         if (m >= p.d) continue;
-        float sum = 0.0f;
+        float4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int gg = 0; gg < kGroups; ++gg) sum += p.partial[((size_t)gg * p.B + t) * p.d + m];
-        sum += p.b2[m];
-        if (p.resid) sum += p.resid[(size_t)t * p.d + m];
-        p.y[(size_t)t * p.d + m] = sum;
+        for (int gg = 0; gg < kGroups; ++gg) {
+            const float4 v =
+                *reinterpret_cast<const float4 *>(p.partial + ((size_t)gg * p.B + t) * p.d + m);
+            sum.x += v.x;
+            sum.y += v.y;
+            sum.z += v.z;
+            sum.w += v.w;
+        }
+        const float4 bb = *reinterpret_cast<const float4 *>(p.b2 + m);
+        sum.x += bb.x;
+        sum.y += bb.y;
+        sum.z += bb.z;
+        sum.w += bb.w;
+        if (p.resid) {
+            const float4 rr = *reinterpret_cast<const float4 *>(p.resid + (size_t)t * p.d + m);
+            sum.x += rr.x;
+            sum.y += rr.y;
+            sum.z += rr.z;
+            sum.w += rr.w;
+        }
+        *reinterpret_cast<float4 *>(p.y + (size_t)t * p.d + m) = sum;
     }
 }
 
@@ -521,54 +725,59 @@ hipError_t launch_pred_mm(const LayerView &L, const float *x, int B, const Trace
                           hipStream_t s) {
     const int mt = (L.H + kTile - 1) / kTile, ks = pred_mm_splits(L.d);
     ASF_LAUNCH(ASF_K_PRED_L1, k_pred_mm, dim3(mt * ks), dim3(kThreads), (const u32x4 *)L.p1, L.c1,
-               x, B, L.d, L.H, ks, L.pred_part, L.pred_arrive, L.h);
+               x, B, L.d, L.H, ks, L.pred_part, L.pred_arrive, L.h, L.h16, L.x16);
     return hipGetLastError();
 }
 
 hipError_t launch_score_mm(const LayerView &L, int B, const Trace *tr, hipStream_t s) {
     ASF_LAUNCH(ASF_K_SCORE, k_score_mm, dim3(L.nq), dim3(kThreads), (const u32x4 *)L.p2, L.c2,
-               L.h, B, L.H, L.f, L.threshold, L.wbits, L.ubits);
+               (const _Float16 *)L.h16, B, L.H, L.f, L.threshold, L.wbits, L.ubits);
     return hipGetLastError();
 }
 
 hipError_t launch_fc1_mm(const LayerView &L, const float *x, int B, int mode, const int32_t *ids,
-                         const int32_t *n_ids, const Trace *tr, hipStream_t s) {
+                         const int32_t *n_ids, bool x16, const Trace *tr, hipStream_t s) {
     Fc1MmParams p;
     p.bundles = (const u32x4 *)L.bundles;
     p.bstride = (size_t)L.nmat * L.cd;
     p.cd = L.cd;
     p.b1 = L.b1;
     p.x = x;
+    p.x16 = L.x16;
     p.B = B;
     p.d = L.d;
     p.f = L.f;
+    p.nq = L.nq;
     p.mode = mode;
     p.ubits = L.ubits;
     p.ids = ids;
     p.n_ids = n_ids;
     p.inv = L.inv;
-    p.vbits = L.vbits;
     p.lslot = L.lslot;
     p.la = L.la;
     p.max_batch = L.max_batch;
-    if (L.gated) ASF_LAUNCH(ASF_K_FC1, k_fc1_mm<true>, dim3(L.nq), dim3(kThreads), p);
-    else ASF_LAUNCH(ASF_K_FC1, k_fc1_mm<false>, dim3(L.nq), dim3(kThreads), p);
+    p.rows = L.rows;
+    const dim3 grid((L.f + kTile - 1) / kTile);     // the list has at most f rows
+#define ASF_FM(G)                                                                \
+    if (x16) ASF_LAUNCH(ASF_K_FC1, (k_fc1_mm<G, true>), grid, dim3(kThreads), p); \
+    else ASF_LAUNCH(ASF_K_FC1, (k_fc1_mm<G, false>), grid, dim3(kThreads), p);
+    if (L.gated) { ASF_FM(true) } else { ASF_FM(false) }
+#undef ASF_FM
     return hipGetLastError();
 }
 
 hipError_t launch_fc2_mm(const LayerView &L, int B, bool listed, const float *resid, float *y,
                          const Trace *tr, hipStream_t s) {
+    (void)listed;   // the batched list always carries its slots
     Fc2MmParams p;
     p.bundles = (const u32x4 *)L.bundles;
     p.bstride = (size_t)L.nmat * L.cd;
     p.dn_off = (L.nmat - 1) * L.cd;
     p.cd = L.cd;
-    p.vbits = L.vbits;
     p.lslot = L.lslot;
-    p.listed = listed ? 1 : 0;
     p.la = L.la;
+    p.rows = L.rows;
     p.max_batch = L.max_batch;
-    p.nq = L.nq;
     p.d = L.d;
     p.B = B;
     p.b2 = L.b2;

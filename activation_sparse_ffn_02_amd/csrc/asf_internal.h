@@ -48,11 +48,15 @@ struct LayerView {
 
     // per-call scratch
     float *h;          // [max_batch][H]           predictor hidden activations
+    _Float16 *h16;     // [2][max_batch][H]        h as fp16 hi, lo (batched form)
+    _Float16 *x16;     // [max_batch][d]           x as fp16 (batched form)
     uint64_t *wbits;   // [max_batch][nq]          per-token owner bits
     uint64_t *ubits;   // [nq]                     union over the batch
     uint64_t *vbits;   // [nq]                     entries listed by each owner
-    int32_t *lslot;    // [nq][64]                 their slots (ascending bit)
-    float *la;         // [nq][64][max_batch]      their FC1 activations
+    int32_t *lslot;    // [nq][64]                 their slots (ascending bit); batched
+                       //                          form: [rows] in list order
+    float *la;         // [nq][64][max_batch]      their FC1 activations; batched
+                       //                          form: [rows][max_batch]
     float *partial;    // [kGroups][max_batch][d]  FC2 partial sums
     unsigned *arrive;  // [kArrive]                FC2 arrivals per slice
     float *pred_part;  // [ceil(H/32)][8][32*32]   batched predictor partial tiles
@@ -60,6 +64,7 @@ struct LayerView {
     uint64_t *masks;   // [max_batch][words]       slot-ordered token masks
     int32_t *slots;    // [f]                      ascending active slots
     int32_t *count;    // [1]                      their number
+    int32_t *rows;     // [1]                      rows of the batched FC1 list
 };
 
 size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v);
@@ -101,8 +106,9 @@ int pred_mm_splits(int d);
 hipError_t launch_pred_mm(const LayerView &L, const float *x, int B, const Trace *tr,
                           hipStream_t s);
 hipError_t launch_score_mm(const LayerView &L, int B, const Trace *tr, hipStream_t s);
+// x16: take x as fp16 from L.x16 (written by launch_pred_mm for the same x)
 hipError_t launch_fc1_mm(const LayerView &L, const float *x, int B, int mode, const int32_t *ids,
-                         const int32_t *n_ids, const Trace *tr, hipStream_t s);
+                         const int32_t *n_ids, bool x16, const Trace *tr, hipStream_t s);
 hipError_t launch_fc2_mm(const LayerView &L, int B, bool listed, const float *resid, float *y,
                          const Trace *tr, hipStream_t s);
 // slot-ordered outputs of the last prediction: token masks, ascending list

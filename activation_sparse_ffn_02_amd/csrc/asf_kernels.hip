@@ -1302,7 +1302,7 @@ hipError_t launch_score(const LayerView &L, const float *x, int B, bool fc1, con
     if (L.wtype == ASF_F16) {
         const hipError_t e = launch_score_mm(L, B, tr, s);
         if (e != hipSuccess || !fc1) return e;
-        return launch_fc1(L, x, B, 0, nullptr, nullptr, tr, s);
+        return launch_fc1_mm(L, x, B, 0, nullptr, nullptr, true, tr, s);
     }
 #define ASF_S(WT, C2) ASF_LAUNCH(ASF_K_SCORE, (k_score<WT, C2, 4, false, false, 1>), grid, blk, p);
 #define ASF_SW(WT)                  \
@@ -1358,7 +1358,7 @@ hipError_t launch_fc1(const LayerView &L, const float *x, int B, int mode, const
 #undef ASF_F1
         return hipGetLastError();
     }
-    if (L.wtype == ASF_F16) return launch_fc1_mm(L, x, B, mode, ids, n_ids, tr, s);
+    if (L.wtype == ASF_F16) return launch_fc1_mm(L, x, B, mode, ids, n_ids, false, tr, s);
     const int cpl1 = pow2_at_least((L.cd + 63) / 64);
 #define ASF_F(WT, C1)                                                             \
     if (L.gated) ASF_LAUNCH(ASF_K_FC1, (k_fc1<WT, true, C1>), grid, blk, p); \
