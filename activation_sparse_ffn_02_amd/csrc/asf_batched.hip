@@ -195,85 +195,101 @@ __global__ __launch_bounds__(kThreads) void k_pred_mm(const u32x4 *__restrict__ 
     }
 }
 
-// ---------------------------------------------------------------- weight tiles through LDS
-// A 32-row weight tile streams in chunks of 256 k (512 bytes of fp16 per
-// row, 16 KiB per chunk): thread t loads 16-byte chunks t%16 and t%16 + 16
-// of row t/16 (a wave instruction covers 4 rows x 256 contiguous bytes),
-// kPre chunks ahead in registers, and stores them to one of two LDS buffers
-// with the chunk index XOR-ed with row % 16, so that the fragment reads
-// (32 rows at one chunk) hit distinct banks.  Wave w multiplies MFMA steps
-// 2w and 2w+1 of every chunk (a k split across the waves; the 8 partial
-// tiles are added in wave order at the end).
-constexpr int kChunkK = 256;                 // k per chunk
-constexpr int kChunkC = kChunkK / 8;         // 16-byte chunks per row per chunk (32)
+// ---------------------------------------------------------------- operand tiles through LDS
+// Both operands of a 32-row x 32-token x k product stream through LDS in
+// chunks of CW 16-byte chunks (8*CW k) per row: the weight tile (32 rows)
+// and the token tile (32 token rows of fp16).  Thread t loads chunk t%16
+// (and t%16 + 16) of row t/16, so a wave instruction covers 4 rows x 256
+// contiguous bytes.  Loads run kPre chunks ahead into registers, always
+// from clamped addresses and zeroed afterwards (a load under a lane
+// condition makes the compiler wait for every outstanding load before the
+// next LDS store, which would cancel the prefetch).  A chunk is stored to one
+// of two LDS buffers with the 16-byte chunk index XOR-ed with row % 16, so a
+// fragment read (32 rows at one chunk) hits distinct banks.  Wave w
+// multiplies its CW/16 of the CW/2 MFMA steps of every chunk: a k split over
+// the waves, whose 8 partial tiles are added in wave order at the end.
 constexpr int kPre = 4;                      // chunks in flight per thread
 
-__device__ __forceinline__ int swz(int row, int c) { return row * kChunkC + (c ^ (row & 15)); }
+template <int CW> struct Geo {
+    static constexpr int LPT = CW / 16;      // loads per thread per tile chunk
+    static constexpr int SPW = CW / 16;      // MFMA steps per wave per chunk
+    static constexpr int ELEMS = kTile * CW; // 16-byte elements per tile chunk
+};
 
-// thread's two loads of chunk `ch` of a row whose first 16-byte chunk is at
-// `rp` (C chunks per row); chunks past C and dead rows give zeros
-__device__ __forceinline__ void tile_load(const u32x4 *rp, bool live, int C, int ch, int lc,
-                                          u32x4 &v0, u32x4 &v1) {
+template <int CW> __device__ __forceinline__ int swz(int row, int c) {
+    return row * CW + (c ^ (row & 15));
+}
+
+__device__ __forceinline__ u32x4 sel4(bool keep, const u32x4 v) {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    const int c0 = ch * kChunkC + lc, c1 = c0 + 16;
-    v0 = (live && c0 < C) ? rp[c0] : z;
-    v1 = (live && c1 < C) ? rp[c1] : z;
+    return keep ? v : z;
 }
 
-__device__ __forceinline__ void tile_store(u32x4 *buf, int lrow, int lc, const u32x4 &v0,
-                                           const u32x4 &v1) {
-    buf[swz(lrow, lc)] = v0;
-    buf[swz(lrow, lc + 16)] = v1;
+// this thread's loads of chunk ch of the row at rp (a valid row of C
+// chunks), from clamped addresses; the values are zeroed only when stored
+// (st_chunk), a ring period later, so that no instruction touches them
+// before then
+template <int CW>
+__device__ __forceinline__ void ld_chunk(const u32x4 *rp, int C, int ch, int lc,
+                                         u32x4 (&v)[Geo<CW>::LPT]) {
+#pragma unroll
+    for (int j = 0; j < Geo<CW>::LPT; ++j) {
+        const int c = ch * CW + lc + 16 * j;
+        v[j] = rp[c < C ? c : C - 1];
+    }
 }
 
-// A fragment of step s (0..15) of a staged chunk: lane row l%32, k group l/32
-__device__ __forceinline__ h8 tile_frag(const u32x4 *buf, int s, int lane) {
-    const int row = lane & 31, c = 2 * s + (lane >> 5);
-    return __builtin_bit_cast(h8, buf[swz(row, c)]);
+// stores chunk ch of this thread's row, zero for chunks past C or a dead row
+template <int CW>
+__device__ __forceinline__ void st_chunk(u32x4 *buf, int lrow, int lc, bool live, int C, int ch,
+                                         const u32x4 (&v)[Geo<CW>::LPT]) {
+#pragma unroll
+    for (int j = 0; j < Geo<CW>::LPT; ++j) {
+        const int c = ch * CW + lc + 16 * j;
+        buf[swz<CW>(lrow, lc + 16 * j)] = sel4(live && c < C, v[j]);
+    }
 }
 
-// Token fragment of step s of chunk ch: 8 consecutive fp16 at chunk
-// ch*32 + 2s + g of a token row (C chunks), zero past C or for dead tokens.
-__device__ __forceinline__ u32x4 tok_frag(const u32x4 *trow, bool tok, int C, int ch, int s,
-                                          int lane) {
-    const int c = ch * kChunkC + 2 * s + (lane >> 5);
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    return (tok && c < C) ? trow[c] : z;
+// fragment of step s of a staged chunk: lane row l%32, k group l/32
+template <int CW>
+__device__ __forceinline__ h8 frag(const u32x4 *buf, int s, int lane) {
+    return __builtin_bit_cast(h8, buf[swz<CW>(lane & 31, 2 * s + (lane >> 5))]);
 }
 
-// The 8 wave partial tiles (red[w][row*32 + col]) of this workgroup summed in
-// wave order; thread tid owns elements tid and tid + 512.
-__device__ __forceinline__ void tile_sum(const float (*red)[kTile * kTile], float (&v)[2]) {
+// The 8 wave partial tiles (red[w*1024 + row*32 + col]) summed in wave
+// order; thread tid owns elements tid and tid + 512.
+__device__ __forceinline__ void tile_sum(const float *red, float (&v)[2]) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int e = threadIdx.x + kThreads * j;
         float sum = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kW; ++w) sum += red[w][e];
+        for (int w = 0; w < kW; ++w) sum += red[w * kTile * kTile + e];
         v[j] = sum;
     }
 }
 
 // ---------------------------------------------------------------- predictor layer 2
 // Owner q: rows i = 0..63 (slot q + nq*i) in two 32-row tiles, each streamed
-// through LDS over k = H; h enters as fp16 hi + lo (two MFMAs per step).
-// Scores = tile sums + c2; wave w ballots tokens w, w+8, ... into the
-// per-token owner words; the union is their OR.
+// with the token tiles of h (fp16 hi and lo, two MFMAs per step) over k = H in
+// chunks of 128 k.  Scores = tile sums + c2; wave w ballots tokens w, w+8, ...
+// into the per-token owner words; the union is their OR.
 __global__ __launch_bounds__(kThreads) void k_score_mm(const u32x4 *__restrict__ P2,
                                                        const float *__restrict__ c2,
                                                        const _Float16 *__restrict__ h16, int B,
                                                        int H, int f, float theta,
                                                        uint64_t *__restrict__ wbits,
                                                        uint64_t *__restrict__ ubits) {
-    __shared__ u32x4 abuf[2][kTile * kChunkC];
-    __shared__ float red[kW][kTile * kTile];
+    constexpr int CW = 16;
+    constexpr int EL = Geo<CW>::ELEMS;
+    __shared__ u32x4 smem[2 * 3 * EL];               // [buffer][A, h hi, h lo] chunks; later the wave tiles
     __shared__ float sc[2 * kTile][kTile + 1];
     __shared__ uint64_t uw[kW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int q = blockIdx.x, nq = gridDim.x;
     const int C = H / 8;
-    const int nch = (C + kChunkC - 1) / kChunkC;
-    const int nit = 2 * nch;                      // (tile, chunk) pairs
+    const int nch = (C + CW - 1) / CW;
+    const int nit = 2 * nch;                         // (tile, chunk) pairs
     const int lrow = tid / 16, lc = tid % 16;
     const u32x4 *rp[2];
 #pragma unroll
@@ -282,53 +298,51 @@ __global__ __launch_bounds__(kThreads) void k_score_mm(const u32x4 *__restrict__
         slot = slot < f ? slot : f - 1;
         rp[t] = P2 + (size_t)slot * C;
     }
-    const int col = lane & 31;
-    const bool tok = col < B;
-    const u32x4 *hhi = reinterpret_cast<const u32x4 *>(h16 + (size_t)(tok ? col : 0) * H);
-    const u32x4 *hlo = reinterpret_cast<const u32x4 *>(h16 + (size_t)(B + (tok ? col : 0)) * H);
-    u32x4 ra[kPre][2];
+    const bool tokr = lrow < B;
+    const u32x4 *hhi = reinterpret_cast<const u32x4 *>(h16 + (size_t)(tokr ? lrow : 0) * H);
+    const u32x4 *hlo = reinterpret_cast<const u32x4 *>(h16 + (size_t)(B + (tokr ? lrow : 0)) * H);
+    // iterations past nit load zeros (the loop body stays free of branches, so
+    // the ring registers carry over without copies that would wait)
+    u32x4 ra[kPre][3][1];
+    auto load = [&](int it, u32x4 (&v)[3][1]) {
+        const int t = it / nch < 1 ? 0 : 1, ch = it < nit ? it % nch : 0;
+        ld_chunk<CW>(rp[t], C, ch, lc, v[0]);
+        ld_chunk<CW>(hhi, C, ch, lc, v[1]);
+        ld_chunk<CW>(hlo, C, ch, lc, v[2]);
+    };
 #pragma unroll
-    for (int u = 0; u < kPre; ++u) {
-        const int it = u < nit ? u : nit - 1;
-        tile_load(rp[it / nch], true, C, it % nch, lc, ra[u][0], ra[u][1]);
-    }
+    for (int u = 0; u < kPre; ++u) load(u, ra[u]);
     f32x16 acc0 = zero16(), acc1 = zero16();
     for (int it0 = 0; it0 < nit; it0 += kPre) {
 #pragma unroll
         for (int u = 0; u < kPre; ++u) {
             const int it = it0 + u;
-            if (it < nit) {
-                const int buf = it & 1;
-                tile_store(abuf[buf], lrow, lc, ra[u][0], ra[u][1]);
-                const int nx = it + kPre < nit ? it + kPre : nit - 1;
-                tile_load(rp[nx / nch], true, C, nx % nch, lc, ra[u][0], ra[u][1]);
-                const int ch = it % nch;
-                u32x4 bh[2], bl[2];
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    bh[k] = tok_frag(hhi, tok, C, ch, 2 * wave + k, lane);
-                    bl[k] = tok_frag(hlo, tok, C, ch, 2 * wave + k, lane);
-                }
-                __syncthreads();
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const h8 av = tile_frag(abuf[buf], 2 * wave + k, lane);
-                    if (it < nch) {
-                        acc0 = mfma(av, __builtin_bit_cast(h8, bh[k]), acc0);
-                        acc0 = mfma(av, __builtin_bit_cast(h8, bl[k]), acc0);
-                    } else {
-                        acc1 = mfma(av, __builtin_bit_cast(h8, bh[k]), acc1);
-                        acc1 = mfma(av, __builtin_bit_cast(h8, bl[k]), acc1);
-                    }
-                }
+            const bool in = it < nit;
+            const int ch = in ? it % nch : 0;
+            u32x4 *bufp = smem + (u & 1) * 3 * EL;
+            st_chunk<CW>(bufp, lrow, lc, in, C, ch, ra[u][0]);
+            st_chunk<CW>(bufp + EL, lrow, lc, in && tokr, C, ch, ra[u][1]);
+            st_chunk<CW>(bufp + 2 * EL, lrow, lc, in && tokr, C, ch, ra[u][2]);
+            load(it + kPre, ra[u]);
+            __syncthreads();
+            const h8 av = frag<CW>(bufp, wave, lane);
+            const h8 bh = frag<CW>(bufp + EL, wave, lane);
+            const h8 bl = frag<CW>(bufp + 2 * EL, wave, lane);
+            if (it < nch) {
+                acc0 = mfma(av, bh, acc0);
+                acc0 = mfma(av, bl, acc0);
+            } else {
+                acc1 = mfma(av, bh, acc1);
+                acc1 = mfma(av, bl, acc1);
             }
         }
     }
     // tile sums -> sc[i][t]
+    float *red = reinterpret_cast<float *>(smem);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         __syncthreads();
-        tile_to_lds(red[wave], t == 0 ? acc0 : acc1, lane);
+        tile_to_lds(red + wave * kTile * kTile, t == 0 ? acc0 : acc1, lane);
         __syncthreads();
         float v[2];
         tile_sum(red, v);
@@ -365,8 +379,7 @@ struct Fc1MmParams {
     size_t bstride;      // chunks per bundle
     int cd;              // chunks per d row
     const float *b1;
-    const float *x;
-    const _Float16 *x16; // x as fp16 when taken from the predictor's copy
+    const _Float16 *x16; // x as fp16 [B][d]
     int B, d, f, nq;
     int mode;            // 0 union of the last prediction, 1 caller ids, 2 all
     const uint64_t *ubits;
@@ -401,20 +414,26 @@ __device__ __forceinline__ int nth_set_bit(uint64_t m, int r) {
     return pos;
 }
 
+// x -> fp16 [B][d] (for FC1 calls that follow no predictor pass)
+__global__ void k_to_f16(const float *__restrict__ x, int n, _Float16 *__restrict__ x16) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+        x16[i] = (_Float16)x[i];
+}
+
 // The FC1 list: mode 0 the union of the last prediction, owner by owner
 // (row r is the (r - pre[q])-th set bit i of owner q, slot q + nq*i, for the
 // owner with pre[q] <= r < pre[q+1], pre the popcount prefix); mode 1 the
 // caller's ids in list order; mode 2 every slot.  Workgroup b takes rows
-// 32b .. 32b+31 as one tile streamed through LDS over k = d; x enters as fp16.
-// a = ReLU(up . x + b1) (gated: ReLU(gate . x + b1) * (up . x)), written to
-// la[r][t] and lslot[r].
-template <bool GATED, bool X16>
+// 32b .. 32b+31 as one tile streamed with the token tile of x (fp16) over
+// k = d in chunks of 256 k.  a = ReLU(up . x + b1) (gated: ReLU(gate . x +
+// b1) * (up . x)), written to la[r][t] and lslot[r].
+template <bool GATED>
 __global__ __launch_bounds__(kThreads) void k_fc1_mm(Fc1MmParams p) {
-    constexpr int NM = GATED ? 2 : 1;
-    __shared__ u32x4 abuf[NM][2][kTile * kChunkC];
-    __shared__ float red[kW][kTile * kTile];
+    constexpr int CW = 32;
+    constexpr int EL = Geo<CW>::ELEMS;
+    constexpr int NT = GATED ? 3 : 2;                // staged tiles: [gate,] up, x
+    __shared__ u32x4 smem[2 * NT * EL];              // chunks; before: owner words; after: wave tiles
     __shared__ float gsum[GATED ? kTile * kTile : 1];
-    __shared__ uint64_t vb[kMaxFfn / 64];
     __shared__ int pre[kMaxFfn / 64 + 1];
     __shared__ int wave_tot[kW];
     __shared__ int rslot[kTile];
@@ -423,6 +442,7 @@ __global__ __launch_bounds__(kThreads) void k_fc1_mm(Fc1MmParams p) {
     const int r0 = kTile * blockIdx.x;
     // ---- the list's length and this tile's slots
     if (p.mode == 0) {
+        uint64_t *vb = reinterpret_cast<uint64_t *>(smem);
         const int nq = p.nq;
         for (int q = tid; q < nq; q += kThreads) vb[q] = p.ubits[q];
         __syncthreads();
@@ -492,69 +512,59 @@ __global__ __launch_bounds__(kThreads) void k_fc1_mm(Fc1MmParams p) {
     if (r0 >= nrows) return;
     // ---- the tile over k = d
     const int C = p.cd;
-    const int nch = (C + kChunkC - 1) / kChunkC;
+    const int nch = (C + CW - 1) / CW;
     const int lrow = tid / 16, lc = tid % 16;
     const int myslot = rslot[lrow];
     const bool live = myslot >= 0;
     constexpr int UP = GATED ? 1 : 0;
     const u32x4 *bp = p.bundles + (size_t)(live ? myslot : 0) * p.bstride;
     const u32x4 *rpu = bp + (size_t)UP * C, *rpg = bp;
-    const int col = lane & 31;
-    const bool tok = col < p.B;
-    const float *xrow = p.x + (size_t)(tok ? col : 0) * p.d;
-    const u32x4 *xr16 = reinterpret_cast<const u32x4 *>(p.x16 + (size_t)(tok ? col : 0) * p.d);
-    u32x4 ra[kPre][NM][2];
+    const bool tokr = lrow < p.B;
+    const u32x4 *xr = reinterpret_cast<const u32x4 *>(p.x16 + (size_t)(tokr ? lrow : 0) * p.d);
+    // chunks past nch load zeros (chunk indices past C are clamped and
+    // zeroed), so the loop body stays free of branches and the ring registers
+    // carry over without copies that would wait
+    u32x4 ra[kPre][NT][Geo<CW>::LPT];
+    auto load = [&](int ch, u32x4 (&v)[NT][Geo<CW>::LPT]) {
+        ld_chunk<CW>(rpu, C, ch, lc, v[0]);
+        ld_chunk<CW>(xr, C, ch, lc, v[1]);
+        if constexpr (GATED) ld_chunk<CW>(rpg, C, ch, lc, v[NT - 1]);
+    };
 #pragma unroll
-    for (int u = 0; u < kPre; ++u) {
-        const int ch = u < nch ? u : nch - 1;
-        tile_load(rpu, live, C, ch, lc, ra[u][0][0], ra[u][0][1]);
-        if constexpr (GATED) tile_load(rpg, live, C, ch, lc, ra[u][NM - 1][0], ra[u][NM - 1][1]);
-    }
+    for (int u = 0; u < kPre; ++u) load(u, ra[u]);
     f32x16 accu = zero16(), accg = zero16();
     for (int ch0 = 0; ch0 < nch; ch0 += kPre) {
 #pragma unroll
         for (int u = 0; u < kPre; ++u) {
             const int ch = ch0 + u;
-            if (ch < nch) {
-                const int buf = ch & 1;
+            u32x4 *bufp = smem + (u & 1) * NT * EL;
+            st_chunk<CW>(bufp, lrow, lc, live, C, ch, ra[u][0]);
+            st_chunk<CW>(bufp + EL, lrow, lc, tokr, C, ch, ra[u][1]);
+            if constexpr (GATED) st_chunk<CW>(bufp + (NT - 1) * EL, lrow, lc, live, C, ch, ra[u][NT - 1]);
+            load(ch + kPre, ra[u]);
+            __syncthreads();
 #pragma unroll
-                for (int m = 0; m < NM; ++m) tile_store(abuf[m][buf], lrow, lc, ra[u][m][0], ra[u][m][1]);
-                const int nx = ch + kPre < nch ? ch + kPre : nch - 1;
-                tile_load(rpu, live, C, nx, lc, ra[u][0][0], ra[u][0][1]);
-                if constexpr (GATED) tile_load(rpg, live, C, nx, lc, ra[u][NM - 1][0], ra[u][NM - 1][1]);
-                h8 bx[2];
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    if constexpr (X16) {
-                        bx[k] = __builtin_bit_cast(h8, tok_frag(xr16, tok, C, ch, 2 * wave + k, lane));
-                    } else {
-                        const int c = ch * kChunkC + 2 * (2 * wave + k) + (lane >> 5);
-                        h8 unused;
-                        frag_f32<false>(xrow + 8 * (c < C ? c : C - 1), tok && c < C, bx[k], unused);
-                    }
-                }
-                __syncthreads();
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    accu = mfma(tile_frag(abuf[0][buf], 2 * wave + k, lane), bx[k], accu);
-                    if constexpr (GATED)
-                        accg = mfma(tile_frag(abuf[NM - 1][buf], 2 * wave + k, lane), bx[k], accg);
-                }
+            for (int k = 0; k < Geo<CW>::SPW; ++k) {
+                const int st = Geo<CW>::SPW * wave + k;
+                const h8 bx = frag<CW>(bufp + EL, st, lane);
+                accu = mfma(frag<CW>(bufp, st, lane), bx, accu);
+                if constexpr (GATED) accg = mfma(frag<CW>(bufp + (NT - 1) * EL, st, lane), bx, accg);
             }
         }
     }
     // ---- epilogue
+    float *red = reinterpret_cast<float *>(smem);
     float v[2];
     if constexpr (GATED) {
         __syncthreads();
-        tile_to_lds(red[wave], accg, lane);
+        tile_to_lds(red + wave * kTile * kTile, accg, lane);
         __syncthreads();
         tile_sum(red, v);
 #pragma unroll
         for (int j = 0; j < 2; ++j) gsum[tid + kThreads * j] = v[j];
     }
     __syncthreads();
-    tile_to_lds(red[wave], accu, lane);
+    tile_to_lds(red + wave * kTile * kTile, accu, lane);
     __syncthreads();
     tile_sum(red, v);
 #pragma unroll
@@ -587,33 +597,39 @@ struct Fc2MmParams {
     const float *b2;
     const float *resid;
     float *y;
-    float *partial;      // [kGroups][B][d]
+    float *partial;      // [groups][B][d]
     unsigned *arrive;    // per slice
+    int groups;          // list-row ranges (<= kGroups)
 };
 
 constexpr int kFc2N = 64;                   // neurons per step (4 MFMA k-steps)
 constexpr int kWPitch = kSliceOut + 8;      // halfs per staged down row
 constexpr int kAPitch = kFc2N + 8;          // halfs per staged token row of a
-constexpr int kFc2Pre = 2;                  // steps in flight per thread
+constexpr int kFc2Pre = 4;                  // steps in flight per thread
+constexpr int kFc2Rows = 8192;              // list rows per group (f <= 65536, >= 8 groups)
 
 // Workgroup (slice s, group g): outputs 256s .. 256s+255 over list rows
-// [g*R/16, (g+1)*R/16).  Per step of 64 rows each thread loads four 16-byte
+// [g*R/G, (g+1)*R/G).  Per step of 64 rows each thread loads four 16-byte
 // chunks of down segments (row tid/32 + 16j, chunk tid%32) and four a values
 // (row tid/32 + 16j, token tid%32), kFc2Pre steps ahead; the step is staged
 // in LDS (double buffered) and wave w multiplies tokens x its 32 outputs x
 // 64 rows, reading each lane's 8 rows of one output column transposed.
 // Group tiles meet in `partial`; the last group to arrive at the slice adds
-// the 16 in group order, then b2, then the residual.
+// the G in group order, then b2, then the residual.
 __global__ __launch_bounds__(kThreads) void k_fc2_mm(Fc2MmParams p) {
     __shared__ __attribute__((aligned(16))) _Float16 wl[2][kFc2N * kWPitch];
     __shared__ __attribute__((aligned(16))) _Float16 al[2][kTile * kAPitch];
+    __shared__ int rslot[kFc2Rows];
     __shared__ int last_lds;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nslice = gridDim.x / kGroups;
+    const int G = p.groups;
+    const int nslice = gridDim.x / G;
     const int s = blockIdx.x % nslice, g = blockIdx.x / nslice;
     const int R = *p.rows;
-    const int rb = (int)((long long)R * g / kGroups), re = (int)((long long)R * (g + 1) / kGroups);
+    const int rb = (int)((long long)R * g / G), re = (int)((long long)R * (g + 1) / G);
     const int nst = (re - rb + kFc2N - 1) / kFc2N;
+    for (int i = tid; i < re - rb; i += kThreads) rslot[i] = p.lslot[rb + i];
+    __syncthreads();
     const int ln = tid / kTile, lc = tid % kTile;
     const int chunk = s * (kSliceOut / 8) + lc;
     const bool cin = chunk < p.cd;
@@ -621,22 +637,31 @@ __global__ __launch_bounds__(kThreads) void k_fc2_mm(Fc2MmParams p) {
     const bool tok_a = lc < p.B;
     u32x4 rv[kFc2Pre][4];
     float ra[kFc2Pre][4];
+    // the group's list slots are staged in LDS, so a step's down-segment
+    // loads do not wait on a load of their slot
+    // loads from clamped addresses; the values are zeroed only when staged,
+    // a ring period later, so that no instruction touches them before then
+    auto row_ok = [&](int st, int j) {                   // branch free (bitwise and)
+        const int rl = st * kFc2N + ln + 16 * j;              // row within the group
+        const bool in = (st < nst) & (rb + rl < re);
+        return in & (rslot[in ? rl : 0] >= 0);
+    };
     auto load_step = [&](int st, u32x4 (&v)[4], float (&a)[4]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int r = rb + st * kFc2N + ln + 16 * j;
-            const bool in = st < nst && r < re;
-            const int sl = in ? p.lslot[r] : -1;
-            const bool ok = sl >= 0;
-            v[j] = (ok && cin) ? dbase[(size_t)sl * p.bstride] : u32x4{0u, 0u, 0u, 0u};
-            a[j] = (ok && tok_a) ? p.la[(size_t)r * p.max_batch + lc] : 0.0f;
+            const int rl = st * kFc2N + ln + 16 * j;
+            const bool in = (st < nst) & (rb + rl < re);
+            const int sl = rslot[in ? rl : 0];
+            v[j] = dbase[(size_t)(sl >= 0 ? sl : 0) * p.bstride];
+            a[j] = p.la[(size_t)(in ? rb + rl : rb) * p.max_batch + (tok_a ? lc : 0)];
         }
     };
-    auto stage = [&](int buf, const u32x4 (&v)[4], const float (&a)[4]) {
+    auto stage = [&](int st, int buf, const u32x4 (&v)[4], const float (&a)[4]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            *reinterpret_cast<u32x4 *>(&wl[buf][(ln + 16 * j) * kWPitch + 8 * lc]) = v[j];
-            al[buf][lc * kAPitch + ln + 16 * j] = (_Float16)a[j];
+            const bool ok = row_ok(st, j);
+            *reinterpret_cast<u32x4 *>(&wl[buf][(ln + 16 * j) * kWPitch + 8 * lc]) = sel4(ok & cin, v[j]);
+            al[buf][lc * kAPitch + ln + 16 * j] = (_Float16)((ok & tok_a) ? a[j] : 0.0f);
         }
     };
     const int gk = lane >> 5, col = lane & 31;
@@ -645,23 +670,23 @@ __global__ __launch_bounds__(kThreads) void k_fc2_mm(Fc2MmParams p) {
     if (nst > 0) {
 #pragma unroll
         for (int u = 0; u < kFc2Pre; ++u) load_step(u, rv[u], ra[u]);
+        // steps past nst stage zeros: the loop body stays free of branches, so
+        // the ring registers carry over without copies that would wait
         for (int st0 = 0; st0 < nst; st0 += kFc2Pre) {
 #pragma unroll
             for (int u = 0; u < kFc2Pre; ++u) {
                 const int st = st0 + u;
-                if (st < nst) {
-                    const int buf = st & 1;
-                    stage(buf, rv[u], ra[u]);
-                    load_step(st + kFc2Pre, rv[u], ra[u]);
-                    __syncthreads();
+                const int buf = u & 1;
+                stage(st, buf, rv[u], ra[u]);
+                load_step(st + kFc2Pre, rv[u], ra[u]);
+                __syncthreads();
 #pragma unroll
-                    for (int k = 0; k < kFc2N / 16; ++k) {
-                        const h8 av = *reinterpret_cast<const h8 *>(&al[buf][col * kAPitch + 16 * k + 8 * gk]);
-                        h8 bv;
+                for (int k = 0; k < kFc2N / 16; ++k) {
+                    const h8 av = *reinterpret_cast<const h8 *>(&al[buf][col * kAPitch + 16 * k + 8 * gk]);
+                    h8 bv;
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) bv[j] = wl[buf][(16 * k + 8 * gk + j) * kWPitch + jw];
-                        acc = mfma(av, bv, acc);
-                    }
+                    for (int j = 0; j < 8; ++j) bv[j] = wl[buf][(16 * k + 8 * gk + j) * kWPitch + jw];
+                    acc = mfma(av, bv, acc);
                 }
             }
         }
@@ -673,7 +698,7 @@ __global__ __launch_bounds__(kThreads) void k_fc2_mm(Fc2MmParams p) {
         const int m = kSliceOut * s + jw;
         if (t < p.B && m < p.d) p.partial[((size_t)g * p.B + t) * p.d + m] = acc[i];
     }
-    if (!arrive_last(p.arrive + s, (unsigned)kGroups, &last_lds)) return;
+    if (!arrive_last(p.arrive + s, (unsigned)G, &last_lds)) return;
     // four outputs per item; per output: groups in order, then b2, then the
     // residual
     constexpr int n4 = kSliceOut / 4;
@@ -681,8 +706,7 @@ __global__ __launch_bounds__(kThreads) void k_fc2_mm(Fc2MmParams p) {
         const int t = idx / n4, m = kSliceOut * s + 4 * (idx % n4);
         if (m >= p.d) continue;
         float4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int gg = 0; gg < kGroups; ++gg) {
+        for (int gg = 0; gg < G; ++gg) {
             const float4 v =
                 *reinterpret_cast<const float4 *>(p.partial + ((size_t)gg * p.B + t) * p.d + m);
             sum.x += v.x;
@@ -737,12 +761,17 @@ hipError_t launch_score_mm(const LayerView &L, int B, const Trace *tr, hipStream
 
 hipError_t launch_fc1_mm(const LayerView &L, const float *x, int B, int mode, const int32_t *ids,
                          const int32_t *n_ids, bool x16, const Trace *tr, hipStream_t s) {
+    if (!x16) {
+        // x as fp16 first (the predictor writes this copy in a decode step)
+        const int n = B * L.d;
+        hipLaunchKernelGGL(k_to_f16, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024),
+                           dim3(256), 0, s, x, n, L.x16);
+    }
     Fc1MmParams p;
     p.bundles = (const u32x4 *)L.bundles;
     p.bstride = (size_t)L.nmat * L.cd;
     p.cd = L.cd;
     p.b1 = L.b1;
-    p.x = x;
     p.x16 = L.x16;
     p.B = B;
     p.d = L.d;
@@ -758,11 +787,8 @@ hipError_t launch_fc1_mm(const LayerView &L, const float *x, int B, int mode, co
     p.max_batch = L.max_batch;
     p.rows = L.rows;
     const dim3 grid((L.f + kTile - 1) / kTile);     // the list has at most f rows
-#define ASF_FM(G)                                                                \
-    if (x16) ASF_LAUNCH(ASF_K_FC1, (k_fc1_mm<G, true>), grid, dim3(kThreads), p); \
-    else ASF_LAUNCH(ASF_K_FC1, (k_fc1_mm<G, false>), grid, dim3(kThreads), p);
-    if (L.gated) { ASF_FM(true) } else { ASF_FM(false) }
-#undef ASF_FM
+    if (L.gated) ASF_LAUNCH(ASF_K_FC1, k_fc1_mm<true>, grid, dim3(kThreads), p);
+    else ASF_LAUNCH(ASF_K_FC1, k_fc1_mm<false>, grid, dim3(kThreads), p);
     return hipGetLastError();
 }
 
@@ -785,8 +811,12 @@ hipError_t launch_fc2_mm(const LayerView &L, int B, bool listed, const float *re
     p.y = y;
     p.partial = L.partial;
     p.arrive = L.arrive;
+    // one workgroup per CU covers the grid: groups = 256 / slices, at most 16
     const int nslice = (L.d + kSliceOut - 1) / kSliceOut;
-    ASF_LAUNCH(ASF_K_FC2, k_fc2_mm, dim3(nslice * kGroups), dim3(kThreads), p);
+    int G = 256 / nslice;
+    G = G < 1 ? 1 : (G > kGroups ? kGroups : G);
+    p.groups = G;
+    ASF_LAUNCH(ASF_K_FC2, k_fc2_mm, dim3(nslice * G), dim3(kThreads), p);
     return hipGetLastError();
 }
 
