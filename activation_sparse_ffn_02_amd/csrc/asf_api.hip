@@ -57,7 +57,7 @@ size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v) {
     t.nmat = nmat;
     t.p1 = (void *)take(H * d * ws);
     t.c1 = (float *)take(H * 4);
-    t.p2 = (void *)take(f * H * ws);
+    t.p2 = (void *)take(nq * kRowsPerWG * H * ws);   // owner-major rows, padded to nq*64
     t.c2 = (float *)take(f * 4);
     t.bundles = (void *)take(f * nmat * d * ws);
     t.b1 = (float *)take(f * 4);
@@ -156,14 +156,15 @@ asf_status asf_create_layer(const asf_layer_desc *desc, const asf_layer_weights 
     // predictor: layer 1 as given, layer 2 rows and bias in slot order
     chk(hipMemcpyAsync(v.p1, w->p1, (size_t)H * d * ws, hipMemcpyDeviceToDevice, s));
     chk(launch_gather_f32(w->c1, nullptr, H, v.c1, s));
-    chk(launch_perm_rows(w->p2, v.ch, v.perm, f, v.p2, v.ch, 0, s));
+    chk(hipMemsetAsync(v.p2, 0, (size_t)v.nq * kRowsPerWG * H * ws, s));
+    chk(launch_perm_rows(w->p2, v.ch, v.perm, f, v.p2, v.ch, 0, v.nq, s));
     chk(launch_gather_f32(w->c2, v.perm, f, v.c2, s));
     // neuron bundles: [gate,] up row, down column (W_down transposed), slot order
     const size_t bstride_chunks = (size_t)v.nmat * v.cd;
     const int up_idx = v.gated ? 1 : 0, dn_idx = v.nmat - 1;
-    if (v.gated) chk(launch_perm_rows(w->w_gate, v.cd, v.perm, f, v.bundles, bstride_chunks, 0, s));
+    if (v.gated) chk(launch_perm_rows(w->w_gate, v.cd, v.perm, f, v.bundles, bstride_chunks, 0, 0, s));
     chk(launch_perm_rows(w->w_up, v.cd, v.perm, f, v.bundles, bstride_chunks,
-                         (size_t)up_idx * v.cd, s));
+                         (size_t)up_idx * v.cd, 0, s));
     chk(launch_transpose_perm(w->w_down, d, f, ws, v.inv, v.bundles, (size_t)v.nmat * d,
                               (size_t)dn_idx * d, s));
     chk(launch_gather_f32(w->b1, v.perm, f, v.b1, s));

@@ -293,11 +293,7 @@ __global__ __launch_bounds__(kThreads) void k_score_mm(const u32x4 *__restrict__
     const int lrow = tid / 16, lc = tid % 16;
     const u32x4 *rp[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        int slot = q + nq * (kTile * t + lrow);
-        slot = slot < f ? slot : f - 1;
-        rp[t] = P2 + (size_t)slot * C;
-    }
+    for (int t = 0; t < 2; ++t) rp[t] = P2 + (size_t)(q * kRowsPerWG + kTile * t + lrow) * C;   // owner-major rows
     const bool tokr = lrow < B;
     const u32x4 *hhi = reinterpret_cast<const u32x4 *>(h16 + (size_t)(tokr ? lrow : 0) * H);
     const u32x4 *hlo = reinterpret_cast<const u32x4 *>(h16 + (size_t)(B + (tokr ? lrow : 0)) * H);

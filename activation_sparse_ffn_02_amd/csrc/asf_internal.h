@@ -38,7 +38,8 @@ struct LayerView {
     // weights in the library layout
     void *p1;          // [H][d]            predictor layer 1 (as given)
     float *c1;         // [H]
-    void *p2;          // [f][H]            predictor layer 2, rows in slot order
+    void *p2;          // [nq*64][H]        predictor layer 2, owner-major: slot q + nq*i
+                       //                   at row q*64 + i (rows past f are zero)
     float *c2;         // [f]               slot order
     void *bundles;     // [f][nmat][d]      per slot: (gate,) up row, down column
     float *b1;         // [f]               slot order (gate bias when gated)
@@ -75,9 +76,10 @@ struct Trace {
 };
 
 // ---- create-time layout kernels
+// owner_major = nq > 0: slot r = q + nq*i goes to row q*64 + i
 hipError_t launch_perm_rows(const void *src, int chunks_per_row, const int32_t *perm, int nrows,
                             void *dst, size_t dst_stride_chunks, size_t dst_off_chunks,
-                            hipStream_t s);
+                            int owner_major, hipStream_t s);
 hipError_t launch_transpose_perm(const void *wdown, int d, int f, int ws, const int32_t *inv,
                                  void *bundles, size_t bundle_stride_elems,
                                  size_t dst_off_elems, hipStream_t s);

@@ -112,15 +112,19 @@ __device__ __forceinline__ float rows8_sum(const float (&v)[8], int lane) {
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
 // ---------------------------------------------------------------- layout
+// dst row of slot r: r, or with owner_major = nq > 0 the row q*64 + i of
+// slot r = q + nq*i (each owner's 64 rows contiguous)
 __global__ void k_perm_rows(const u32x4 *__restrict__ src, int C, const int32_t *__restrict__ perm,
-                            int nrows, u32x4 *__restrict__ dst, size_t dstride, size_t doff) {
+                            int nrows, u32x4 *__restrict__ dst, size_t dstride, size_t doff,
+                            int owner_major) {
     const size_t total = (size_t)nrows * C;
     for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
          idx += (size_t)gridDim.x * blockDim.x) {
         const int r = (int)(idx / C), c = (int)(idx % C);
         int sr = perm ? perm[r] : r;
         if ((unsigned)sr >= (unsigned)nrows) sr = r;
-        dst[(size_t)r * dstride + doff + c] = src[(size_t)sr * C + c];
+        const int dr = owner_major > 0 ? (r % owner_major) * kRowsPerWG + r / owner_major : r;
+        dst[(size_t)dr * dstride + doff + c] = src[(size_t)sr * C + c];
     }
 }
 
@@ -310,6 +314,9 @@ __global__ __launch_bounds__(kThreads) void k_pred1(const u32x4 *__restrict__ P1
     const int C = d / E;
     const bool live = row < H;
     const int rowc = live ? row : H - 1;
+    // the bias of the row this thread finishes (threads < rpw), loaded early
+    const int rfin = blockIdx.x * rpw + (int)threadIdx.x;
+    const float c1v = c1[rfin < H ? rfin : H - 1];
     float4 xv[XLDS ? 4 : 1];
     if constexpr (XLDS) stage_load<4>(x, d, xv);
     u32x4 w[CPL];
@@ -353,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void k_pred1(const u32x4 *__restrict__ P1
         if (r < H) {
             float t = 0.0f;
             for (int pp = 0; pp < wpr; ++pp) t += red[threadIdx.x * wpr + pp];
-            h[r] = fmaxf(t + c1[r], 0.0f);
+            h[r] = fmaxf(t + c1v, 0.0f);
         }
     }
 }
@@ -368,12 +375,11 @@ __device__ __forceinline__ void l2_load(const u32x4 *__restrict__ P2, int f, int
                                         int wave, int lane, u32x4 (&w)[kL2Rows][CPL]) {
 #pragma unroll
     for (int j = 0; j < kL2Rows; ++j) {
-        int slot = q + nq * (wave * kL2Rows + j);
-        slot = slot < f ? slot : f - 1;
+        const int row = q * kRowsPerWG + wave * kL2Rows + j;   // owner-major P2 row
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + 64 * i;
-            w[j][i] = P2[(size_t)slot * C + (c < C ? c : C - 1)];
+            w[j][i] = P2[(size_t)row * C + (c < C ? c : C - 1)];
         }
     }
 }
@@ -745,12 +751,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((
     auto load_group = [&](int g, u32x4 (&dst)[RG][CPL2]) {
 #pragma unroll
         for (int j = 0; j < RG; ++j) {
-            int slot = q + nq * (wave * kL2Rows + g * RG + j);
-            slot = slot < p.f ? slot : p.f - 1;
+            const int row = q * kRowsPerWG + wave * kL2Rows + g * RG + j;   // owner-major
 #pragma unroll
             for (int i = 0; i < CPL2; ++i) {
                 const int c = lane + 64 * i;
-                dst[j][i] = p.p2[(size_t)slot * C2 + (c < C2 ? c : C2 - 1)];
+                dst[j][i] = p.p2[(size_t)row * C2 + (c < C2 ? c : C2 - 1)];
             }
         }
     };
@@ -1126,11 +1131,11 @@ inline int pow2_at_least(int v) {
 
 // ================================================================ launchers
 hipError_t launch_perm_rows(const void *src, int C, const int32_t *perm, int nrows, void *dst,
-                            size_t dstride, size_t doff, hipStream_t s) {
+                            size_t dstride, size_t doff, int owner_major, hipStream_t s) {
     const size_t total = (size_t)nrows * C;
     const int blocks = (int)((total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192);
     hipLaunchKernelGGL(k_perm_rows, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, s,
-                       (const u32x4 *)src, C, perm, nrows, (u32x4 *)dst, dstride, doff);
+                       (const u32x4 *)src, C, perm, nrows, (u32x4 *)dst, dstride, doff, owner_major);
     return hipGetLastError();
 }
 
