@@ -73,6 +73,7 @@ size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v) {
     t.lslot = (int32_t *)take(nq * kRowsPerWG * 4);
     t.la = (float *)take(nq * kRowsPerWG * Bm * 4);
     t.partial = (float *)take((size_t)kGroups * Bm * d * 4);
+    t.part1 = (float *)take(nq * d * 4);
     t.arrive = (unsigned *)take(kArrive * 4);
     // batched predictor partial tiles (row tiles x up to 8 k-splits x 32x32)
     t.pred_part = Bm > 1 ? (float *)take(((H + 31) / 32) * 8 * 1024 * 4) : nullptr;
@@ -86,6 +87,14 @@ size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v) {
 }
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// FC2 after launch_score with FC1: a single token's owner rows are already
+// formed (launch_fc2_sum adds them); batches go through the owner lists
+static hipError_t launch_fc2_step(const LayerView &v, int B, const float *resid, float *y,
+                                  const Trace *tr, hipStream_t s) {
+    if (B == 1) return launch_fc2_sum(v, resid, y, tr, s);
+    return launch_fc2(v, B, false, resid, y, tr, s);
+}
 
 }  // namespace asf
 
@@ -229,7 +238,7 @@ asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
     hipStream_t s = (hipStream_t)stream;
     if (launch_pred_l1(v, x, B, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
     if (launch_score(v, x, B, true, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
-    if (launch_fc2(v, B, false, residual, y, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
+    if (launch_fc2_step(v, B, residual, y, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
     if ((active || n_active) &&
         launch_list(v, B, active, n_active, nullptr, layer->tr(), s) != hipSuccess)
         return ASF_ERR_HIP;
@@ -271,7 +280,7 @@ asf_status asf_stack_decode(asf_layer *const *layers, int32_t n_layers, const fl
         float *out = ((n_layers - 1 - l) % 2 == 0) ? y : work;
         if (launch_pred_l1(v, in, B, tr, s) != hipSuccess) return ASF_ERR_HIP;
         if (launch_score(v, in, B, true, tr, s) != hipSuccess) return ASF_ERR_HIP;
-        if (launch_fc2(v, B, false, residual ? in : nullptr, out, tr, s) != hipSuccess)
+        if (launch_fc2_step(v, B, residual ? in : nullptr, out, tr, s) != hipSuccess)
             return ASF_ERR_HIP;
         in = out;
     }

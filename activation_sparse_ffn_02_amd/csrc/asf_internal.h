@@ -59,6 +59,7 @@ struct LayerView {
     float *la;         // [nq][64][max_batch]      their FC1 activations; batched
                        //                          form: [rows][max_batch]
     float *partial;    // [kGroups][max_batch][d]  FC2 partial sums
+    float *part1;      // [d/16][nq][16]           single-token FC2 rows per owner
     unsigned *arrive;  // [kArrive]                FC2 arrivals per slice
     float *pred_part;  // [ceil(H/32)][8][32*32]   batched predictor partial tiles
     unsigned *pred_arrive;  // [kArrive]           their arrivals per row tile
@@ -103,6 +104,10 @@ hipError_t launch_fc1(const LayerView &L, const float *x, int B, int mode, const
 // entries' slots come from the list (caller ids) rather than the owner bits
 hipError_t launch_fc2(const LayerView &L, int B, bool listed, const float *resid, float *y,
                       const Trace *tr, hipStream_t s);
+// single token, after launch_score with FC1: y = sum over owners of their
+// FC2 rows (part1) + b2 (+ resid)
+hipError_t launch_fc2_sum(const LayerView &L, const float *resid, float *y, const Trace *tr,
+                          hipStream_t s);
 // batched forms on the matrix cores (B >= 2, fp16 weights)
 int pred_mm_splits(int d);
 hipError_t launch_pred_mm(const LayerView &L, const float *x, int B, const Trace *tr,

@@ -264,15 +264,16 @@ __device__ __forceinline__ void stage_load(const float *__restrict__ src, int n,
     }
 }
 
-template <int N4>
-__device__ __forceinline__ void stage_store(float *dst, int n, const float4 (&v)[N4]) {
+// Every thread stores (no guard: the LDS array holds N4 * kThreads float4,
+// and places past n get copies of the last float4, never read), so the
+// staging loads stay where they were issued instead of sinking into a
+// guarded store behind a full wait.
+template <int N4, int NF>
+__device__ __forceinline__ void stage_store(float (&dst)[NF], const float4 (&v)[N4]) {
+    static_assert(NF >= N4 * 4 * kThreads, "LDS staging array too small");
     float4 *d4 = reinterpret_cast<float4 *>(dst);
-    const int n4 = n / 4;
 #pragma unroll
-    for (int i = 0; i < N4; ++i) {
-        const int idx = (int)threadIdx.x + kThreads * i;
-        if (idx < n4) d4[idx] = v[i];
-    }
+    for (int i = 0; i < N4; ++i) d4[(int)threadIdx.x + kThreads * i] = v[i];
 }
 
 // acc += chunk c of a weight row (in registers) . chunk c of an LDS vector
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void k_pred1(const u32x4 *__restrict__ P1
     }
     float acc = 0.0f;
     if constexpr (XLDS) {
-        stage_store<4>(xs, d, xv);
+        stage_store<4>(xs, xv);
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
@@ -554,6 +555,10 @@ struct ScoreParams {
     const float *x;
     int d;
     Fc1Out out;
+    // single-token FC2 partial rows: [d/16][nq][16], owner q's sum over its
+    // listed neurons of a * (down column), 16 outputs per slice
+    int dn_off;       // chunk offset of the down column in a bundle
+    float *part1;
 };
 
 // Owner workgroup q: score its 64 slots for every token, store per-token and
@@ -686,18 +691,20 @@ __device__ __forceinline__ float fc1_one(const u32x4 (&wu)[CPL], const u32x4 (&w
 
 // FC1 of owner q's valid entries for one token (x in LDS): wave w takes
 // entries i = w + 8k for k >= k0; the entry of rank r (r-th set bit of
-// `valid`) is listed at lslot[q][r], la[q][r].
+// `valid`) is listed at lslot[q][r], la[q][r], and at a_lds[r] when a_lds
+// is given.
 template <int WT, bool GATED, int CPL>
 __device__ __forceinline__ void fc1_entry_1(int q, uint64_t valid, int i, int slot,
                                             const u32x4 (&wu)[CPL], const u32x4 (&wg)[CPL],
                                             int C, float bias, const float *xs, Fc1Out o,
-                                            int lane) {
+                                            float *a_lds, int lane) {
     const int rank = __popcll(valid & ((1ull << i) - 1ull));
     const float a = fc1_one<WT, GATED, CPL>(wu, wg, C, xs, bias, lane);
     if (lane == 0) {
         const size_t e = (size_t)q * kRowsPerWG + rank;
         o.la[e * o.max_batch] = a;
         o.lslot[e] = slot;
+        if (a_lds) a_lds[rank] = a;
     }
 }
 
@@ -705,7 +712,7 @@ template <int WT, bool GATED, int CPL, class SlotOf>
 __device__ __forceinline__ void owner_fc1_1(int q, uint64_t valid, SlotOf slot_of, int k0,
                                             const u32x4 *__restrict__ bundles, size_t bstride,
                                             int C, const float *__restrict__ b1, const float *xs,
-                                            Fc1Out o, int wave, int lane) {
+                                            Fc1Out o, float *a_lds, int wave, int lane) {
     for (int k = k0; k < kRowsPerWG / kWaves; ++k) {
         const int i = wave + kWaves * k;
         if (!((valid >> i) & 1ull)) continue;
@@ -713,7 +720,7 @@ __device__ __forceinline__ void owner_fc1_1(int q, uint64_t valid, SlotOf slot_o
         const float bias = b1[slot];
         u32x4 wu[CPL], wg[CPL];
         load_fc1_rows<GATED, CPL>(bundles, bstride, C, slot, lane, wu, wg);
-        fc1_entry_1<WT, GATED, CPL>(q, valid, i, slot, wu, wg, C, bias, xs, o, lane);
+        fc1_entry_1<WT, GATED, CPL>(q, valid, i, slot, wu, wg, C, bias, xs, o, a_lds, lane);
     }
 }
 
@@ -727,6 +734,50 @@ template <bool GATED, int CPL1, bool SPEC = false> struct Fc1Regs {
     static constexpr int waves_per_eu = (chunks <= 14 && !SPEC) ? 4 : 2;
 };
 
+// Chunks t, t + 512, ... (thread t) of the down columns of the next N
+// entries of `m` (ascending bits, slot q + nq*bit; past the last entry the
+// owner's slot q); returns m without those entries.
+template <int N, int CPT>
+__device__ __forceinline__ uint64_t load_down(u32x4 (&dv)[N][CPT], uint64_t m,
+                                              const u32x4 *__restrict__ dn, size_t bstride, int q,
+                                              int nq, int cd) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const int i = m ? __builtin_ctzll(m) : 0;
+        m &= m - 1ull;
+        const u32x4 *bp = dn + (size_t)(q + nq * i) * bstride;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int c = threadIdx.x + kThreads * j;
+            dv[n][j] = bp[c < cd ? c : cd - 1];
+        }
+    }
+    return m;
+}
+
+// acc += a[n0 + n] * dv[n] for the entries below cnt, in entry order
+template <int WT, int N, int CPT>
+__device__ __forceinline__ void fma_down(const u32x4 (&dv)[N][CPT], int n0, int cnt,
+                                         const float *a_lds, float (&acc)[CPT][Elt<WT>::E]) {
+    constexpr int E = Elt<WT>::E;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const float a = n0 + n < cnt ? a_lds[(n0 + n) & (kRowsPerWG - 1)] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            float vd[E];
+            unpack<WT>(dv[n][j], vd);
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[j][e] = fmaf(a, vd[e], acc[j][e]);
+        }
+    }
+}
+
+// Single-token owner workgroup q: scores of its 64 slots, owner bits; with
+// FC1, a of its listed neurons and then the owner's FC2 partial row (its
+// listed neurons' a times their down columns, added in rank order), which
+// k_fc2_sum adds over owners.  The down columns sit right after the up rows
+// in each bundle, so every listed neuron costs one contiguous bundle read.
 // With at most 128 VGPRs (4 waves per SIMD) two workgroups fit on a CU, so
 // up to 512 owners (f <= 32768) run in one round.
 template <int WT, int CPL2, bool FC1, bool GATED, int CPL1, bool SPEC>
@@ -739,6 +790,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((
     __shared__ float xs[FC1 ? kMaxDLds : 4];
     __shared__ uint32_t bits_lds[kWaves];
     __shared__ uint64_t u_lds;
+    __shared__ float a_lds[FC1 ? kRowsPerWG : 1];
     const int q = blockIdx.x, nq = gridDim.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int C2 = p.H / E;
@@ -762,13 +814,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((
     load_group(0, wb[0]);
     if constexpr (NG > 1) load_group(1, wb[1]);
     u32x4 spu[FC1 ? CPL1 : 1], spg[FC1 ? CPL1 : 1];
+    float spec_bias = 0.0f;
     if constexpr (SPEC) {
         const int spec_slot = q + nq * wave;
+        spec_bias = p.b1[spec_slot < p.f ? spec_slot : p.f - 1];
         if (wave < kSpecRows && spec_slot < p.f)
             load_fc1_rows<GATED, CPL1>(p.bundles, p.bstride, p.cd, spec_slot, lane, spu, spg);
     }
-    stage_store<1>(hs, p.H, hv);
-    if constexpr (FC1) stage_store<4>(xs, p.d, xv);
+    stage_store<1>(hs, hv);
+    if constexpr (FC1) stage_store<4>(xs, xv);
     __syncthreads();
     // every row of the wave uses the same chunks of h: keep them in registers
     float hr[CPL2][E];
@@ -831,6 +885,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((
     __syncthreads();
     if constexpr (FC1) {
         const uint64_t valid = u_lds;
+        const int cnt = __popcll(valid);
+        // FC2 of this owner's listed neurons: thread t takes chunks t, t + 512
+        // of the down columns.  The chunks of the first PF entries (rank
+        // order) are loaded now, beside the FC1 rows; the rest in batches
+        // of PF2 once the FC1 rows are no longer held.  PF is cut where the
+        // FC1 rows leave no registers under the 128-VGPR cap.
+        constexpr int CPT = (CPL1 + 7) / 8;      // d-row chunks per thread
+        constexpr int PF2 = 8 / CPT;
+        constexpr bool kTight = Fc1Regs<GATED, CPL1, SPEC>::waves_per_eu == 4 && CPT == 2;
+        constexpr int PF = kTight ? (CPL1 >= 12 ? 0 : 2) : PF2;   // no spills
+        const u32x4 *dn = p.bundles + p.dn_off;
+        u32x4 dv[PF > 0 ? PF : 1][CPT];
+        uint64_t rest = valid;
+        if constexpr (PF > 0) rest = load_down<PF, CPT>(dv, valid, dn, p.bstride, q, nq, p.cd);
         int k0 = 0;
         if constexpr (SPEC) {
             // waves below kSpecRows hold the rows of their first entry (bit
@@ -840,13 +908,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((
                 if ((valid >> wave) & 1ull) {
                     const int slot = q + nq * wave;
                     fc1_entry_1<WT, GATED, CPL1>(q, valid, wave, slot, spu, spg, p.cd,
-                                                 p.b1[slot], xs, p.out, lane);
+                                                 spec_bias, xs, p.out, a_lds, lane);
                 }
             }
         }
         auto slot_of = [&](int i) { return q + nq * i; };
         owner_fc1_1<WT, GATED, CPL1>(q, valid, slot_of, k0, p.bundles, p.bstride, p.cd, p.b1, xs,
-                                     p.out, wave, lane);
+                                     p.out, a_lds, wave, lane);
+        __syncthreads();
+        float acc2[CPT][E];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j)
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc2[j][e] = 0.0f;
+        if constexpr (PF > 0) fma_down<WT, PF, CPT>(dv, 0, cnt, a_lds, acc2);
+        for (int n0 = PF; n0 < cnt; n0 += PF2) {
+            u32x4 dv2[PF2][CPT];
+            rest = load_down<PF2, CPT>(dv2, rest, dn, p.bstride, q, nq, p.cd);
+            fma_down<WT, PF2, CPT>(dv2, n0, cnt, a_lds, acc2);
+        }
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int c = threadIdx.x + kThreads * j;
+            if (c < p.cd) {
+                const int o = c * E;
+                float4 *dst = reinterpret_cast<float4 *>(p.part1 + ((size_t)(o >> 4) * nq + q) * 16 + (o & 15));
+#pragma unroll
+                for (int k = 0; k < E / 4; ++k)
+                    dst[k] = make_float4(acc2[j][4 * k], acc2[j][4 * k + 1], acc2[j][4 * k + 2],
+                                         acc2[j][4 * k + 3]);
+            }
+        }
     }
 }
 
@@ -881,13 +973,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((
         const uint64_t b = __ballot(slot >= 0);
         if (i == 0) valid_lds = b;
     }
-    stage_store<4>(xs, p.d, xv);
+    stage_store<4>(xs, xv);
     __syncthreads();
     const uint64_t valid = valid_lds;
     if (threadIdx.x == 0) p.out.vbits[q] = valid;
     auto slot_of = [&](int i) { return slot_lds[i]; };
     owner_fc1_1<WT, GATED, CPL1>(q, valid, slot_of, 0, p.bundles, p.bstride, p.cd, p.b1, xs,
-                                 p.out, wave, lane);
+                                 p.out, nullptr, wave, lane);
 }
 
 // ---------------------------------------------------------------- FC2
@@ -1046,6 +1138,55 @@ __global__ __launch_bounds__(kThreads) void k_fc2(Fc2Params p) {
             if (p.resid) sum += p.resid[(size_t)b * p.d + m];
             p.y[(size_t)b * p.d + m] = sum;
         }
+    }
+}
+
+// ---------------------------------------------------------------- single-token FC2 sum
+// Workgroup s finishes outputs [16s, 16s + 16) from the owners' partial rows
+// (slice-major, [d/16][nq][16]): thread t = 4g + c reads float4 column c of
+// owners g, g + 128, ... and adds them in that order; the 128 owner lanes
+// are then added in a fixed order (32 in sequence, then 4 in a fixed pair
+// tree), then b2, then the residual.
+constexpr int kSumQ = kMaxFfn / kRowsPerWG / (kThreads / 4);   // owners per thread, at most
+
+__global__ __launch_bounds__(kThreads) void k_fc2_sum(const float *__restrict__ part, int nq,
+                                                      const float *__restrict__ b2,
+                                                      const float *__restrict__ resid,
+                                                      float *__restrict__ y) {
+    __shared__ float4 red[kThreads];
+    const int s = blockIdx.x, tid = threadIdx.x;
+    const int c = tid & 3, g = tid >> 2;
+    const float4 *src = reinterpret_cast<const float4 *>(part + (size_t)s * nq * 16);
+    const int o = tid & 15;
+    const float bv = b2[16 * s + o];
+    const float rv = resid ? resid[16 * s + o] : 0.0f;
+    float4 v[kSumQ];
+#pragma unroll
+    for (int k = 0; k < kSumQ; ++k) {
+        const int q = g + (kThreads / 4) * k;
+        v[k] = src[(size_t)(q < nq ? q : nq - 1) * 4 + c];
+    }
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int k = 0; k < kSumQ; ++k) {
+        if (g + (kThreads / 4) * k < nq) {
+            acc.x += v[k].x;
+            acc.y += v[k].y;
+            acc.z += v[k].z;
+            acc.w += v[k].w;
+        }
+    }
+    red[tid] = acc;
+    __syncthreads();
+    if (tid < 64) {
+        // lane: output o, quarter u of the 128 owner lanes
+        const int u = tid >> 4;
+        const float *rf = reinterpret_cast<const float *>(red);
+        float sum = 0.0f;
+        for (int gg = 32 * u; gg < 32 * u + 32; ++gg) sum += rf[(gg * 4 + (o >> 2)) * 4 + (o & 3)];
+        sum += __shfl_down(sum, 16, 64);   // u + (u + 1) for u = 0, 2
+        const float hi = __shfl_down(sum, 32, 64);
+        if (tid < 16) y[16 * s + o] = (sum + hi) + bv + rv;
     }
 }
 
@@ -1262,6 +1403,8 @@ hipError_t launch_score(const LayerView &L, const float *x, int B, bool fc1, con
     p.x = x;
     p.d = L.d;
     p.out = fc1_out(L);
+    p.dn_off = (L.nmat - 1) * L.cd;
+    p.part1 = L.part1;
     const int cpl2 = pow2_at_least((L.ch + 63) / 64);
     const dim3 grid(L.nq), blk(kThreads);
     if (B == 1) {
@@ -1379,6 +1522,14 @@ hipError_t launch_fc1(const LayerView &L, const float *x, int B, int mode, const
     if (L.wtype == ASF_F16) { ASF_FW(1) } else { ASF_FW(0) }
 #undef ASF_FW
 #undef ASF_F
+    return hipGetLastError();
+}
+
+hipError_t launch_fc2_sum(const LayerView &L, const float *resid, float *y, const Trace *tr,
+                          hipStream_t s) {
+    const dim3 grid(L.d / 16), blk(kThreads);
+    ASF_LAUNCH(ASF_K_FC2, k_fc2_sum, grid, blk, (const float *)L.part1, L.nq, (const float *)L.b2,
+               resid, y);
     return hipGetLastError();
 }
 

@@ -69,12 +69,16 @@ def bytes_model(sh, k_mean):
     ws = 2 if sh.wdtype == "f16" else 4
     nmat = 3 if sh.gated else 2
     words = (f + 63) // 64
+    # single-token decode step: the score/FC1 kernel also reads the listed
+    # down columns (FC2 into per-owner rows); the FC2 kernel adds the owner
+    # rows (implementation traffic, not counted) with b2 into y
     per = {
         "pred_l1": H * d * ws + H * 4 + d * 4 + H * 4,
         "score": f * H * ws + f * 4 + H * 4 + words * 8,
-        "score_fc1": f * H * ws + f * 4 + H * 4 + words * 8 + k_mean * (d * ws + 4) + d * 4,
+        "score_fc1": (f * H * ws + f * 4 + H * 4 + words * 8 + k_mean * (d * ws + 4) + d * 4
+                      + k_mean * d * ws),
         "fc1": k_mean * (d * ws + 4) + d * 4,
-        "fc2": k_mean * d * ws + d * 4 * 2,
+        "fc2": d * 4 * 2,
         "list": words * 8 + k_mean * 4,
     }
     if sh.gated:

@@ -213,9 +213,11 @@ asf_status asf_dense_ffn_ref(const asf_layer *layer, const float *x, int32_t B,
 typedef enum {
     ASF_K_PRED_L1 = 0,   /* predictor layer 1 GEMV */
     ASF_K_SCORE = 1,     /* predictor layer 2 GEMV + threshold -> mask bits */
-    ASF_K_SCORE_FC1 = 2, /* the same, then FC1 of the predicted neurons */
+    ASF_K_SCORE_FC1 = 2, /* the same, then FC1 of the predicted neurons; for one
+                            token also their FC2 into one row per owner */
     ASF_K_FC1 = 3,       /* FC1 (+ReLU) of a neuron set */
-    ASF_K_FC2 = 4,       /* FC2 column gather + reduction -> y */
+    ASF_K_FC2 = 4,       /* FC2 column gather + reduction -> y; for one token in a
+                            decode step, the sum of the owner rows -> y */
     ASF_K_LIST = 5,      /* slot-ordered masks and active list */
     ASF_K_COUNT = 6
 } asf_kernel_id;
