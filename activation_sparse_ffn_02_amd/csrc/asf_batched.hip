@@ -388,28 +388,6 @@ struct Fc1MmParams {
     int32_t *rows;       // number of list rows
 };
 
-// Position of the r-th set bit of m (r < popcount(m)), by halving.
-__device__ __forceinline__ int nth_set_bit(uint64_t m, int r) {
-    int pos = 0;
-    int c = __popc((uint32_t)m);
-    if (r >= c) {
-        r -= c;
-        m >>= 32;
-        pos = 32;
-    }
-    uint32_t w = (uint32_t)m;
-    c = __popc(w & 0xffffu);
-    if (r >= c) { r -= c; w >>= 16; pos += 16; }
-    c = __popc(w & 0xffu);
-    if (r >= c) { r -= c; w >>= 8; pos += 8; }
-    c = __popc(w & 0xfu);
-    if (r >= c) { r -= c; w >>= 4; pos += 4; }
-    c = __popc(w & 0x3u);
-    if (r >= c) { r -= c; w >>= 2; pos += 2; }
-    if (r >= (int)(w & 1u)) pos += 1;
-    return pos;
-}
-
 // x -> fp16 [B][d] (for FC1 calls that follow no predictor pass)
 __global__ void k_to_f16(const float *__restrict__ x, int n, _Float16 *__restrict__ x16) {
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)

@@ -18,6 +18,28 @@ constexpr int kMaxBatch = 32;
 constexpr int kMaxFfn = 65536;    // the list kernel handles up to 1024 mask words
 constexpr int kArrive = 64;       // arrival counters (FC2 slices, predictor row tiles)
 
+// Position of the r-th set bit of m (r < popcount(m)), by halving.
+__device__ __forceinline__ int nth_set_bit(uint64_t m, int r) {
+    int pos = 0;
+    int c = __popc((uint32_t)m);
+    if (r >= c) {
+        r -= c;
+        m >>= 32;
+        pos = 32;
+    }
+    uint32_t w = (uint32_t)m;
+    c = __popc(w & 0xffffu);
+    if (r >= c) { r -= c; w >>= 16; pos += 16; }
+    c = __popc(w & 0xffu);
+    if (r >= c) { r -= c; w >>= 8; pos += 8; }
+    c = __popc(w & 0xfu);
+    if (r >= c) { r -= c; w >>= 4; pos += 4; }
+    c = __popc(w & 0x3u);
+    if (r >= c) { r -= c; w >>= 2; pos += 2; }
+    if (r >= (int)(w & 1u)) pos += 1;
+    return pos;
+}
+
 // Device view of a created layer, carved out of the caller's storage.
 //
 // Neuron work is split over nq = ceil(f / 64) "owner" workgroups: owner q

@@ -888,33 +888,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((
         const int cnt = __popcll(valid);
         // FC2 of this owner's listed neurons: thread t takes chunks t, t + 512
         // of the down columns.  The chunks of the first PF entries (rank
-        // order) are loaded now, beside the FC1 rows; the rest in batches
-        // of PF2 once the FC1 rows are no longer held.  PF is cut where the
-        // FC1 rows leave no registers under the 128-VGPR cap.
+        // order) are loaded now, beside the FC1 rows, and with a 256-VGPR
+        // budget those of the next PFB too when the owner lists more; the
+        // rest in batches of PF2 once the FC1 rows are no longer held.  PF is
+        // cut where the FC1 rows leave no registers under the 128-VGPR cap.
         constexpr int CPT = (CPL1 + 7) / 8;      // d-row chunks per thread
         constexpr int PF2 = 8 / CPT;
-        constexpr bool kTight = Fc1Regs<GATED, CPL1, SPEC>::waves_per_eu == 4 && CPT == 2;
+        constexpr bool kWide = Fc1Regs<GATED, CPL1, SPEC>::waves_per_eu == 2;
+        constexpr bool kTight = !kWide && CPT == 2;
         constexpr int PF = kTight ? (CPL1 >= 12 ? 0 : 2) : PF2;   // no spills
+        constexpr int PFB = (kWide && Fc1Regs<GATED, CPL1>::chunks + 2 * PF * CPT <= 32) ? PF : 0;
         const u32x4 *dn = p.bundles + p.dn_off;
         u32x4 dv[PF > 0 ? PF : 1][CPT];
+        u32x4 dvb[PFB > 0 ? PFB : 1][CPT];
         uint64_t rest = valid;
         if constexpr (PF > 0) rest = load_down<PF, CPT>(dv, valid, dn, p.bstride, q, nq, p.cd);
-        int k0 = 0;
+        if constexpr (PFB > 0)
+            if (cnt > PF) rest = load_down<PFB, CPT>(dvb, rest, dn, p.bstride, q, nq, p.cd);
+        // FC1 balanced by rank: with SPEC, bit b < kSpecRows (rows held) is
+        // wave b's; the other entries, ranked among themselves, go to waves
+        // off, off + 1, ... round the 8 waves
+        constexpr int off = SPEC ? kSpecRows : 0;
         if constexpr (SPEC) {
-            // waves below kSpecRows hold the rows of their first entry (bit
-            // i = wave, slot q + nq*wave) already
-            if (wave < kSpecRows) {
-                k0 = 1;
-                if ((valid >> wave) & 1ull) {
-                    const int slot = q + nq * wave;
-                    fc1_entry_1<WT, GATED, CPL1>(q, valid, wave, slot, spu, spg, p.cd,
-                                                 spec_bias, xs, p.out, a_lds, lane);
-                }
+            if (wave < kSpecRows && ((valid >> wave) & 1ull)) {
+                const int slot = q + nq * wave;
+                fc1_entry_1<WT, GATED, CPL1>(q, valid, wave, slot, spu, spg, p.cd, spec_bias, xs,
+                                             p.out, a_lds, lane);
             }
         }
-        auto slot_of = [&](int i) { return q + nq * i; };
-        owner_fc1_1<WT, GATED, CPL1>(q, valid, slot_of, k0, p.bundles, p.bstride, p.cd, p.b1, xs,
-                                     p.out, a_lds, wave, lane);
+        const uint64_t mr = SPEC ? (valid & ~((1ull << kSpecRows) - 1ull)) : valid;
+        const int nr = __popcll(mr);
+        for (int r = (wave - off + kWaves) % kWaves; r < nr; r += kWaves) {
+            const int i = nth_set_bit(mr, r);
+            const int slot = q + nq * i;
+            const float bias = p.b1[slot];
+            u32x4 wu[CPL1], wg[CPL1];
+            load_fc1_rows<GATED, CPL1>(p.bundles, p.bstride, p.cd, slot, lane, wu, wg);
+            fc1_entry_1<WT, GATED, CPL1>(q, valid, i, slot, wu, wg, p.cd, bias, xs, p.out, a_lds,
+                                         lane);
+        }
         __syncthreads();
         float acc2[CPT][E];
 #pragma unroll
@@ -922,7 +934,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((
 #pragma unroll
             for (int e = 0; e < E; ++e) acc2[j][e] = 0.0f;
         if constexpr (PF > 0) fma_down<WT, PF, CPT>(dv, 0, cnt, a_lds, acc2);
-        for (int n0 = PF; n0 < cnt; n0 += PF2) {
+        if constexpr (PFB > 0)
+            if (cnt > PF) fma_down<WT, PFB, CPT>(dvb, PF, cnt, a_lds, acc2);
+        for (int n0 = PF + PFB; n0 < cnt; n0 += PF2) {
             u32x4 dv2[PF2][CPT];
             rest = load_down<PF2, CPT>(dv2, rest, dn, p.bstride, q, nq, p.cd);
             fma_down<WT, PF2, CPT>(dv2, n0, cnt, a_lds, acc2);
