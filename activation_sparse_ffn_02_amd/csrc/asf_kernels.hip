@@ -1,26 +1,32 @@
-// asf_kernels.hip -- gfx950 kernels of the activation-sparse FFN decode path.
+// asf_kernels.hip -- gfx950 kernels of the activation-sparse FFN decode path
+// (vector form; the batched matrix-core form is asf_batched.hip).
 //
-// A decode step of one layer is three kernels; the kernel boundaries are the
-// grid-wide synchronisation points (on MI355X a boundary costs ~1.6 us inside
-// a HIP graph, far less than any in-kernel grid barrier):
+// A single-token decode step of one layer is three kernels; the kernel
+// boundaries are the grid-wide synchronisation points (on MI355X a boundary
+// costs ~1.7 us, less than any in-kernel grid barrier):
 //
-//   pred_l1      h = ReLU(P1 x + c1)                           dense GEMV
-//   score_fc1    per owner workgroup q (slots q, q+nq, ...):   dense GEMV over
-//                s = P2 h + c2, bit = s > theta                the owner's P2
-//                then FC1 of its union-active neurons:         rows; gathered
-//                a = ReLU(W_up[slot] . x + b1) (or the gated   up rows
+//   k_pred1      h = ReLU(P1 x + c1)                           dense GEMV
+//   k_score1     per owner workgroup q (slots q, q+nq, ...):
+//                s = P2 h + c2, bit = s > theta                its 64 P2 rows
+//                FC1 of its predicted neurons:                 their up rows
+//                a = ReLU(W_up[slot] . x + b1) (or the gated
 //                form), listed with their slots
-//   fc2          y = b2 + residual + sum_j a_j * W_down[:, j]: 16 output
-//                slices x 16 neuron groups; each workgroup reads 512-byte
-//                segments of the listed down columns; the last of the 16
-//                groups to finish a slice sums the 16 partials (fixed order)
+//                FC2 of the same neurons into one fp32 row     their down
+//                of d outputs: sum over them of a * column     columns
+//   k_fc2_sum    y = b2 (+ residual) + sum over owners of their rows, in
+//                owner order
 //
-// The owner split balances FC1 without a global prefix sum: with a hot-first
-// neuron table, owner q holds ranks q, q+nq, q+2nq, ..., so every owner gets
-// the same mix of always-on and rarely-on neurons.  The hottest slot of each
-// owner (slot q) has its up row loaded before scoring, overlapping the P2
-// stream (and so is the next-hottest, slot q + nq); each is used only if
-// that neuron is predicted active.
+// The owner split balances FC1/FC2 without a global prefix sum: with a
+// hot-first neuron table, owner q holds ranks q, q+nq, q+2nq, ..., so every
+// owner gets the same mix of always-on and rarely-on neurons.  The two
+// hottest slots of each owner have their up rows loaded before scoring,
+// overlapping the P2 stream; each is used only if that neuron is predicted
+// active.
+//
+// The other entry points use the same building blocks: FC1 over a set
+// (k_fc1_1 for one token, k_fc1 for token chunks of 4) and the grouped FC2
+// (k_fc2: 16 output slices x 16 neuron groups, the last group at a slice
+// sums the partials in fixed order).
 //
 // Weight reads are whole 16-byte chunks of contiguous rows (a wave load
 // instruction covers 1 KiB); an active neuron's up row and down column sit in

@@ -96,11 +96,17 @@ KERNEL_SOURCES = [os.path.join(ROOT, "activation_sparse_ffn_02_amd", "csrc", n)
 
 
 def kernel_source_hash():
+    """SHA-256 of the kernel sources with comments and blank space removed, so
+    that a comment edit keeps counters taken on the same code valid."""
     import hashlib
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as fh:
-            h.update(fh.read())
+        with open(p, encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = re.sub(r"\s+", " ", text)
+        h.update(text.encode("utf-8"))
     return h.hexdigest()
 
 
