@@ -77,7 +77,6 @@ size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v) {
     t.arrive = (unsigned *)take(kArrive * 4);
     // batched predictor partial tiles (row tiles x up to 8 k-splits x 32x32)
     t.pred_part = Bm > 1 ? (float *)take(((H + 31) / 32) * 8 * 1024 * 4) : nullptr;
-    t.pred_arrive = (unsigned *)take(kArrive * 4);
     t.masks = (uint64_t *)take(Bm * words * 8);
     t.slots = (int32_t *)take(f * 4);
     t.count = (int32_t *)take(64);
@@ -179,7 +178,6 @@ asf_status asf_create_layer(const asf_layer_desc *desc, const asf_layer_weights 
     chk(launch_gather_f32(w->b1, v.perm, f, v.b1, s));
     chk(launch_gather_f32(w->b2, nullptr, d, v.b2, s));
     chk(hipMemsetAsync(v.arrive, 0, kArrive * 4, s));
-    chk(hipMemsetAsync(v.pred_arrive, 0, kArrive * 4, s));
     if (e != hipSuccess) {
         delete L;
         return ASF_ERR_HIP;

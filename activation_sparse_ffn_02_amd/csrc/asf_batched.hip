@@ -8,12 +8,15 @@
 // i of lane l holds D[8(i/4) + 4(l/32) + i%4][l % 32].
 //
 //   predictor layer 1   rows of P1 x tokens, k = d, split over workgroups;
-//                       the last workgroup of a row tile adds the partials
+//                       a second kernel adds the partials (many workgroups:
+//                       a last-arriver reduction costs an L2 write-back and
+//                       an atomic round trip per workgroup, then a serial sum)
 //   predictor layer 2   per owner: its 64 slot rows x tokens, k = H; then
 //                       threshold and one ballot per token
 //   FC1                 per owner: its union rows (compacted) x tokens
 //   FC2                 tokens x outputs, k = the group's listed neurons;
-//                       down segments go through LDS to be read transposed
+//                       down segments go through LDS to be read transposed;
+//                       a second kernel adds the groups' partials
 //
 // The predictor feeds x and h to the MFMA as fp16 hi + lo halves (two
 // instructions per step), so its sums keep fp32 accuracy and the active
@@ -85,40 +88,15 @@ __device__ __forceinline__ void tile_to_lds(float *dst, const f32x16 &acc, int l
     for (int i = 0; i < 16; ++i) dst[acc_row(i, lane) * kTile + col] = acc[i];
 }
 
-// Agent-scope arrival of this workgroup at counter c (after every thread's
-// global stores); true for the last of `n` arrivals, which also resets it.
-__device__ __forceinline__ bool arrive_last(unsigned *c, unsigned n, int *flag_lds) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const unsigned old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int last = old == n - 1;
-        if (last) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        *flag_lds = last;
-    }
-    __syncthreads();
-    return *flag_lds != 0;
-}
-
 // ---------------------------------------------------------------- predictor layer 1
 // Workgroup (mt, ks): rows 32mt .. 32mt+31 of P1 over k in [ks*KW, (ks+1)*KW),
 // KW = d / KS; wave w takes the w-th eighth of that range.  Wave tiles are
-// added in wave order; with KS > 1 the KS workgroup tiles of a row tile meet
-// in `part` and the last to arrive adds them in ks order, then c1, then ReLU.
+// added in wave order into the workgroup's partial tile; k_pred_fin adds the
+// KS partial tiles of a row tile in ks order, then c1, then ReLU.
 __global__ __launch_bounds__(kThreads) void k_pred_mm(const u32x4 *__restrict__ P1,
-                                                      const float *__restrict__ c1,
                                                       const float *__restrict__ x, int B, int d,
-                                                      int H, int KS, float *__restrict__ part,
-                                                      unsigned *__restrict__ arrive,
-                                                      float *__restrict__ h,
-                                                      _Float16 *__restrict__ h16,
-                                                      _Float16 *__restrict__ x16) {
+                                                      int H, int KS, float *__restrict__ part) {
     __shared__ float red[kW][kTile * kTile];
-    __shared__ int last_lds;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int mt = blockIdx.x / KS, ks = blockIdx.x % KS;
     const int KWw = d / KS / kW;                  // k per wave, a multiple of 16
@@ -149,49 +127,43 @@ __global__ __launch_bounds__(kThreads) void k_pred_mm(const u32x4 *__restrict__ 
     }
     tile_to_lds(red[wave], acc, lane);
     __syncthreads();
-    float v[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int e = tid + kThreads * j;
         float sum = 0.0f;
 #pragma unroll
         for (int w = 0; w < kW; ++w) sum += red[w][e];
-        v[j] = sum;
+        part[((size_t)mt * KS + ks) * (kTile * kTile) + e] = sum;
     }
-    if (mt == 0) {
-        // x as fp16 for the FC1 of this step: this workgroup's k range
-        const int n8 = d / KS / 8;
-        for (int idx = tid; idx < B * n8; idx += kThreads) {
-            const int t = idx / n8, k = ks * (d / KS) + 8 * (idx % n8);
-            h8 hv, unused;
-            frag_f32<false>(x + (size_t)t * d + k, true, hv, unused);
-            *reinterpret_cast<h8 *>(x16 + (size_t)t * d + k) = hv;
-        }
+}
+
+// Element e of row tile mt (row 32mt + e/32, token e%32): the KS partial
+// tiles in ks order, then c1, then ReLU -> h and its fp16 hi/lo halves.  The
+// grid also converts x to fp16 for the FC1 of the step.
+__global__ __launch_bounds__(kThreads) void k_pred_fin(const float *__restrict__ part,
+                                                       const float *__restrict__ c1,
+                                                       const float *__restrict__ x, int B, int d,
+                                                       int H, int KS, float *__restrict__ h,
+                                                       _Float16 *__restrict__ h16,
+                                                       _Float16 *__restrict__ x16) {
+    const int gid = blockIdx.x * kThreads + threadIdx.x;
+    const int mt = gid / (kTile * kTile), e = gid % (kTile * kTile);
+    const int r = kTile * mt + e / kTile, t = e % kTile;
+    if (r < H && t < B) {
+        const float *pp = part + (size_t)mt * KS * (kTile * kTile) + e;
+        float sum = 0.0f;
+        for (int ks = 0; ks < KS; ++ks) sum += pp[(size_t)ks * (kTile * kTile)];
+        const float hv = fmaxf(sum + c1[r], 0.0f);
+        const _Float16 hi = (_Float16)hv;
+        h[(size_t)t * H + r] = hv;
+        h16[(size_t)t * H + r] = hi;
+        h16[(size_t)(B + t) * H + r] = (_Float16)(hv - (float)hi);
     }
-    if (KS > 1) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            part[((size_t)mt * KS + ks) * (kTile * kTile) + tid + kThreads * j] = v[j];
-        if (!arrive_last(arrive + mt, (unsigned)KS, &last_lds)) return;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            float sum = 0.0f;
-            for (int kk = 0; kk < KS; ++kk)
-                sum += part[((size_t)mt * KS + kk) * (kTile * kTile) + tid + kThreads * j];
-            v[j] = sum;
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int e = tid + kThreads * j;
-        const int r = kTile * mt + e / kTile, t = e % kTile;
-        if (r < H && t < B) {
-            const float hv = fmaxf(v[j] + c1[r], 0.0f);
-            const _Float16 hi = (_Float16)hv;
-            h[(size_t)t * H + r] = hv;
-            h16[(size_t)t * H + r] = hi;
-            h16[(size_t)(B + t) * H + r] = (_Float16)(hv - (float)hi);
-        }
+    const int n8 = B * d / 8;
+    for (int i = gid; i < n8; i += gridDim.x * kThreads) {
+        h8 hv, unused;
+        frag_f32<false>(x + (size_t)8 * i, true, hv, unused);
+        *reinterpret_cast<h8 *>(x16 + (size_t)8 * i) = hv;
     }
 }
 
@@ -406,6 +378,7 @@ __global__ __launch_bounds__(kThreads) void k_fc1_mm(Fc1MmParams p) {
     constexpr int CW = 32;
     constexpr int EL = Geo<CW>::ELEMS;
     constexpr int NT = GATED ? 3 : 2;                // staged tiles: [gate,] up, x
+    constexpr int PRE = kPre;                        // chunks in flight per thread
     __shared__ u32x4 smem[2 * NT * EL];              // chunks; before: owner words; after: wave tiles
     __shared__ float gsum[GATED ? kTile * kTile : 1];
     __shared__ int pre[kMaxFfn / 64 + 1];
@@ -482,8 +455,12 @@ __global__ __launch_bounds__(kThreads) void k_fc1_mm(Fc1MmParams p) {
     }
     __syncthreads();
     const int nrows = nrows_lds;
-    if (blockIdx.x == 0 && tid == 0) *p.rows = nrows;
-    if (r0 >= nrows) return;
+    // (the list length is stored after the tile: a global store in flight
+    // would make the compiler wait for every load of the ring)
+    if (r0 >= nrows) {
+        if (blockIdx.x == 0 && tid == 0) *p.rows = nrows;
+        return;
+    }
     // ---- the tile over k = d
     const int C = p.cd;
     const int nch = (C + CW - 1) / CW;
@@ -498,24 +475,24 @@ __global__ __launch_bounds__(kThreads) void k_fc1_mm(Fc1MmParams p) {
     // chunks past nch load zeros (chunk indices past C are clamped and
     // zeroed), so the loop body stays free of branches and the ring registers
     // carry over without copies that would wait
-    u32x4 ra[kPre][NT][Geo<CW>::LPT];
+    u32x4 ra[PRE][NT][Geo<CW>::LPT];
     auto load = [&](int ch, u32x4 (&v)[NT][Geo<CW>::LPT]) {
         ld_chunk<CW>(rpu, C, ch, lc, v[0]);
         ld_chunk<CW>(xr, C, ch, lc, v[1]);
         if constexpr (GATED) ld_chunk<CW>(rpg, C, ch, lc, v[NT - 1]);
     };
 #pragma unroll
-    for (int u = 0; u < kPre; ++u) load(u, ra[u]);
+    for (int u = 0; u < PRE; ++u) load(u, ra[u]);
     f32x16 accu = zero16(), accg = zero16();
-    for (int ch0 = 0; ch0 < nch; ch0 += kPre) {
+    auto pass = [&](int ch0) {
 #pragma unroll
-        for (int u = 0; u < kPre; ++u) {
+        for (int u = 0; u < PRE; ++u) {
             const int ch = ch0 + u;
             u32x4 *bufp = smem + (u & 1) * NT * EL;
             st_chunk<CW>(bufp, lrow, lc, live, C, ch, ra[u][0]);
             st_chunk<CW>(bufp + EL, lrow, lc, tokr, C, ch, ra[u][1]);
             if constexpr (GATED) st_chunk<CW>(bufp + (NT - 1) * EL, lrow, lc, live, C, ch, ra[u][NT - 1]);
-            load(ch + kPre, ra[u]);
+            load(ch + PRE, ra[u]);
             __syncthreads();
 #pragma unroll
             for (int k = 0; k < Geo<CW>::SPW; ++k) {
@@ -525,7 +502,13 @@ __global__ __launch_bounds__(kThreads) void k_fc1_mm(Fc1MmParams p) {
                 if constexpr (GATED) accg = mfma(frag<CW>(bufp + (NT - 1) * EL, st, lane), bx, accg);
             }
         }
-    }
+    };
+    // the first pass is peeled (nch >= 1): the loop is then entered from a
+    // copy of its own body, with the ring's loads in the loop's order, so the
+    // wait at the loop head can stay fine-grained (entered from the prologue
+    // it would have to wait for every load in flight, on every pass)
+    pass(0);
+    for (int ch0 = PRE; ch0 < nch; ch0 += PRE) pass(ch0);
     // ---- epilogue
     float *red = reinterpret_cast<float *>(smem);
     float v[2];
@@ -555,6 +538,7 @@ __global__ __launch_bounds__(kThreads) void k_fc1_mm(Fc1MmParams p) {
         p.la[(size_t)r * p.max_batch + t] = a;
         if (t == 0) p.lslot[r] = sl;
     }
+    if (blockIdx.x == 0 && tid == 0) *p.rows = nrows;
 }
 
 // ---------------------------------------------------------------- FC2
@@ -572,7 +556,6 @@ struct Fc2MmParams {
     const float *resid;
     float *y;
     float *partial;      // [groups][B][d]
-    unsigned *arrive;    // per slice
     int groups;          // list-row ranges (<= kGroups)
 };
 
@@ -588,13 +571,12 @@ constexpr int kFc2Rows = 8192;              // list rows per group (f <= 65536, 
 // (row tid/32 + 16j, token tid%32), kFc2Pre steps ahead; the step is staged
 // in LDS (double buffered) and wave w multiplies tokens x its 32 outputs x
 // 64 rows, reading each lane's 8 rows of one output column transposed.
-// Group tiles meet in `partial`; the last group to arrive at the slice adds
-// the G in group order, then b2, then the residual.
+// Group tiles go to `partial`; k_fc2_fin adds the G in group order, then b2,
+// then the residual.
 __global__ __launch_bounds__(kThreads) void k_fc2_mm(Fc2MmParams p) {
     __shared__ __attribute__((aligned(16))) _Float16 wl[2][kFc2N * kWPitch];
     __shared__ __attribute__((aligned(16))) _Float16 al[2][kTile * kAPitch];
     __shared__ int rslot[kFc2Rows];
-    __shared__ int last_lds;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = p.groups;
     const int nslice = gridDim.x / G;
@@ -646,7 +628,7 @@ __global__ __launch_bounds__(kThreads) void k_fc2_mm(Fc2MmParams p) {
         for (int u = 0; u < kFc2Pre; ++u) load_step(u, rv[u], ra[u]);
         // steps past nst stage zeros: the loop body stays free of branches, so
         // the ring registers carry over without copies that would wait
-        for (int st0 = 0; st0 < nst; st0 += kFc2Pre) {
+        auto pass = [&](int st0) {
 #pragma unroll
             for (int u = 0; u < kFc2Pre; ++u) {
                 const int st = st0 + u;
@@ -663,45 +645,52 @@ __global__ __launch_bounds__(kThreads) void k_fc2_mm(Fc2MmParams p) {
                     acc = mfma(av, bv, acc);
                 }
             }
-        }
+        };
+        // first pass peeled: the loop is entered from a copy of its body, so
+        // the wait at its head need not cover every load in flight
+        pass(0);
+        for (int st0 = kFc2Pre; st0 < nst; st0 += kFc2Pre) pass(st0);
     }
-    // group tile -> partial; the last group at this slice reduces
+    // group tile -> partial (k_fc2_fin adds the groups)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int t = acc_row(i, lane);
         const int m = kSliceOut * s + jw;
         if (t < p.B && m < p.d) p.partial[((size_t)g * p.B + t) * p.d + m] = acc[i];
     }
-    if (!arrive_last(p.arrive + s, (unsigned)G, &last_lds)) return;
-    // four outputs per item; per output: groups in order, then b2, then the
-    // residual
-    constexpr int n4 = kSliceOut / 4;
-    for (int idx = tid; idx < p.B * n4; idx += kThreads) {
-        const int t = idx / n4, m = kSliceOut * s + 4 * (idx % n4);
-        if (m >= p.d) continue;
-        float4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int gg = 0; gg < G; ++gg) {
-            const float4 v =
-                *reinterpret_cast<const float4 *>(p.partial + ((size_t)gg * p.B + t) * p.d + m);
-            sum.x += v.x;
-            sum.y += v.y;
-            sum.z += v.z;
-            sum.w += v.w;
-        }
-        const float4 bb = *reinterpret_cast<const float4 *>(p.b2 + m);
-        sum.x += bb.x;
-        sum.y += bb.y;
-        sum.z += bb.z;
-        sum.w += bb.w;
-        if (p.resid) {
-            const float4 rr = *reinterpret_cast<const float4 *>(p.resid + (size_t)t * p.d + m);
-            sum.x += rr.x;
-            sum.y += rr.y;
-            sum.z += rr.z;
-            sum.w += rr.w;
-        }
-        *reinterpret_cast<float4 *>(p.y + (size_t)t * p.d + m) = sum;
+}
+
+// Four outputs per thread: y[t][m..m+3] = the G group partials in group
+// order, then b2, then the residual.
+__global__ __launch_bounds__(256) void k_fc2_fin(const float *__restrict__ partial, int G, int B,
+                                                 int d, const float *__restrict__ b2,
+                                                 const float *__restrict__ resid,
+                                                 float *__restrict__ y) {
+    const int d4 = d / 4;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= B * d4) return;
+    const int t = idx / d4, m = 4 * (idx % d4);
+    float4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int gg = 0; gg < G; ++gg) {
+        const float4 v = *reinterpret_cast<const float4 *>(partial + ((size_t)gg * B + t) * d + m);
+        sum.x += v.x;
+        sum.y += v.y;
+        sum.z += v.z;
+        sum.w += v.w;
     }
+    const float4 bb = *reinterpret_cast<const float4 *>(b2 + m);
+    sum.x += bb.x;
+    sum.y += bb.y;
+    sum.z += bb.z;
+    sum.w += bb.w;
+    if (resid) {
+        const float4 rr = *reinterpret_cast<const float4 *>(resid + (size_t)t * d + m);
+        sum.x += rr.x;
+        sum.y += rr.y;
+        sum.z += rr.z;
+        sum.w += rr.w;
+    }
+    *reinterpret_cast<float4 *>(y + (size_t)t * d + m) = sum;
 }
 
 inline hipEvent_t ev_start(const Trace *tr, int k) { return tr ? tr->ev[2 * k] : nullptr; }
@@ -722,8 +711,14 @@ int pred_mm_splits(int d) {
 hipError_t launch_pred_mm(const LayerView &L, const float *x, int B, const Trace *tr,
                           hipStream_t s) {
     const int mt = (L.H + kTile - 1) / kTile, ks = pred_mm_splits(L.d);
-    ASF_LAUNCH(ASF_K_PRED_L1, k_pred_mm, dim3(mt * ks), dim3(kThreads), (const u32x4 *)L.p1, L.c1,
-               x, B, L.d, L.H, ks, L.pred_part, L.pred_arrive, L.h, L.h16, L.x16);
+    // the traced interval spans both kernels
+    hipExtLaunchKernelGGL(k_pred_mm, dim3(mt * ks), dim3(kThreads), 0, s,
+                          ev_start(tr, ASF_K_PRED_L1), nullptr, 0u, (const u32x4 *)L.p1, x, B,
+                          L.d, L.H, ks, L.pred_part);
+    const int nfin = mt * (kTile * kTile) / kThreads;
+    hipExtLaunchKernelGGL(k_pred_fin, dim3(nfin), dim3(kThreads), 0, s, nullptr,
+                          ev_stop(tr, ASF_K_PRED_L1), 0u, (const float *)L.pred_part, L.c1, x, B,
+                          L.d, L.H, ks, L.h, L.h16, L.x16);
     return hipGetLastError();
 }
 
@@ -784,13 +779,18 @@ hipError_t launch_fc2_mm(const LayerView &L, int B, bool listed, const float *re
     p.resid = resid;
     p.y = y;
     p.partial = L.partial;
-    p.arrive = L.arrive;
     // one workgroup per CU covers the grid: groups = 256 / slices, at most 16
     const int nslice = (L.d + kSliceOut - 1) / kSliceOut;
     int G = 256 / nslice;
     G = G < 1 ? 1 : (G > kGroups ? kGroups : G);
     p.groups = G;
-    ASF_LAUNCH(ASF_K_FC2, k_fc2_mm, dim3(nslice * G), dim3(kThreads), p);
+    // the traced interval spans both kernels
+    hipExtLaunchKernelGGL(k_fc2_mm, dim3(nslice * G), dim3(kThreads), 0, s,
+                          ev_start(tr, ASF_K_FC2), nullptr, 0u, p);
+    const int n4 = B * (L.d / 4);
+    hipExtLaunchKernelGGL(k_fc2_fin, dim3((n4 + 255) / 256), dim3(256), 0, s, nullptr,
+                          ev_stop(tr, ASF_K_FC2), 0u, (const float *)L.partial, G, B, L.d, L.b2,
+                          resid, y);
     return hipGetLastError();
 }
 

@@ -84,7 +84,6 @@ struct LayerView {
     float *part1;      // [d/16][nq][16]           single-token FC2 rows per owner
     unsigned *arrive;  // [kArrive]                FC2 arrivals per slice
     float *pred_part;  // [ceil(H/32)][8][32*32]   batched predictor partial tiles
-    unsigned *pred_arrive;  // [kArrive]           their arrivals per row tile
     uint64_t *masks;   // [max_batch][words]       slot-ordered token masks
     int32_t *slots;    // [f]                      ascending active slots
     int32_t *count;    // [1]                      their number
