@@ -254,14 +254,14 @@ __global__ __launch_bounds__(kThreads) void k_score_mm(const u32x4 *__restrict__
                                                        uint64_t *__restrict__ ubits) {
     constexpr int CW = 16;
     constexpr int EL = Geo<CW>::ELEMS;
-    __shared__ u32x4 smem[2 * 3 * EL];               // [buffer][A, h hi, h lo] chunks; later the wave tiles
+    constexpr int PRE = 2;                           // chunk stages in flight per thread
+    __shared__ u32x4 smem[2 * 4 * EL];               // [buffer][A0, A1, h hi, h lo] chunks; later the wave tiles
     __shared__ float sc[2 * kTile][kTile + 1];
     __shared__ uint64_t uw[kW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int q = blockIdx.x, nq = gridDim.x;
     const int C = H / 8;
     const int nch = (C + CW - 1) / CW;
-    const int nit = 2 * nch;                         // (tile, chunk) pairs
     const int lrow = tid / 16, lc = tid % 16;
     const u32x4 *rp[2];
 #pragma unroll
@@ -269,42 +269,45 @@ __global__ __launch_bounds__(kThreads) void k_score_mm(const u32x4 *__restrict__
     const bool tokr = lrow < B;
     const u32x4 *hhi = reinterpret_cast<const u32x4 *>(h16 + (size_t)(tokr ? lrow : 0) * H);
     const u32x4 *hlo = reinterpret_cast<const u32x4 *>(h16 + (size_t)(B + (tokr ? lrow : 0)) * H);
-    // iterations past nit load zeros (the loop body stays free of branches, so
-    // the ring registers carry over without copies that would wait)
-    u32x4 ra[kPre][3][1];
-    auto load = [&](int it, u32x4 (&v)[3][1]) {
-        const int t = it / nch < 1 ? 0 : 1, ch = it < nit ? it % nch : 0;
-        ld_chunk<CW>(rp[t], C, ch, lc, v[0]);
-        ld_chunk<CW>(hhi, C, ch, lc, v[1]);
-        ld_chunk<CW>(hlo, C, ch, lc, v[2]);
+    // a chunk stage carries both row tiles of the owner and the h chunk they
+    // share; stages past nch load clamped and store zeros (the loop body stays
+    // free of branches, so the ring registers carry over without copies that
+    // would wait)
+    u32x4 ra[PRE][4][1];
+    auto load = [&](int ch, u32x4 (&v)[4][1]) {
+        ld_chunk<CW>(rp[0], C, ch, lc, v[0]);
+        ld_chunk<CW>(rp[1], C, ch, lc, v[1]);
+        ld_chunk<CW>(hhi, C, ch, lc, v[2]);
+        ld_chunk<CW>(hlo, C, ch, lc, v[3]);
     };
 #pragma unroll
-    for (int u = 0; u < kPre; ++u) load(u, ra[u]);
+    for (int u = 0; u < PRE; ++u) load(u, ra[u]);
     f32x16 acc0 = zero16(), acc1 = zero16();
-    for (int it0 = 0; it0 < nit; it0 += kPre) {
+    auto pass = [&](int ch0) {
 #pragma unroll
-        for (int u = 0; u < kPre; ++u) {
-            const int it = it0 + u;
-            const bool in = it < nit;
-            const int ch = in ? it % nch : 0;
-            u32x4 *bufp = smem + (u & 1) * 3 * EL;
-            st_chunk<CW>(bufp, lrow, lc, in, C, ch, ra[u][0]);
-            st_chunk<CW>(bufp + EL, lrow, lc, in && tokr, C, ch, ra[u][1]);
-            st_chunk<CW>(bufp + 2 * EL, lrow, lc, in && tokr, C, ch, ra[u][2]);
-            load(it + kPre, ra[u]);
+        for (int u = 0; u < PRE; ++u) {
+            const int ch = ch0 + u;
+            u32x4 *bufp = smem + (u & 1) * 4 * EL;     // consecutive stages alternate buffers
+            st_chunk<CW>(bufp, lrow, lc, true, C, ch, ra[u][0]);
+            st_chunk<CW>(bufp + EL, lrow, lc, true, C, ch, ra[u][1]);
+            st_chunk<CW>(bufp + 2 * EL, lrow, lc, tokr, C, ch, ra[u][2]);
+            st_chunk<CW>(bufp + 3 * EL, lrow, lc, tokr, C, ch, ra[u][3]);
+            load(ch + PRE, ra[u]);
             __syncthreads();
-            const h8 av = frag<CW>(bufp, wave, lane);
-            const h8 bh = frag<CW>(bufp + EL, wave, lane);
-            const h8 bl = frag<CW>(bufp + 2 * EL, wave, lane);
-            if (it < nch) {
-                acc0 = mfma(av, bh, acc0);
-                acc0 = mfma(av, bl, acc0);
-            } else {
-                acc1 = mfma(av, bh, acc1);
-                acc1 = mfma(av, bl, acc1);
-            }
+            const h8 a0 = frag<CW>(bufp, wave, lane);
+            const h8 a1 = frag<CW>(bufp + EL, wave, lane);
+            const h8 bh = frag<CW>(bufp + 2 * EL, wave, lane);
+            const h8 bl = frag<CW>(bufp + 3 * EL, wave, lane);
+            acc0 = mfma(a0, bh, acc0);
+            acc0 = mfma(a0, bl, acc0);
+            acc1 = mfma(a1, bh, acc1);
+            acc1 = mfma(a1, bl, acc1);
         }
-    }
+    };
+    // first pass peeled: the loop is entered from a copy of its body, so the
+    // wait at its head need not cover every load in flight
+    pass(0);
+    for (int ch0 = PRE; ch0 < nch; ch0 += PRE) pass(ch0);
     // tile sums -> sc[i][t]
     float *red = reinterpret_cast<float *>(smem);
 #pragma unroll
