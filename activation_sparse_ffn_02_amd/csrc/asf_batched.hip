@@ -40,6 +40,7 @@ constexpr int kW = kThreads / 64;   // waves per workgroup
 constexpr int kTile = 32;           // rows / tokens / outputs of one MFMA tile
 constexpr int kSteps = 8;           // 16-k steps whose loads are in flight per wave
 constexpr int kSliceOut = kTile * kW;  // FC2 outputs per workgroup (256)
+constexpr int kMaxSplit = 8;        // predictor layer 1: k split over at most 8 workgroups
 
 __device__ __forceinline__ f32x16 mfma(const h8 a, const h8 b, const f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -150,9 +151,15 @@ __global__ __launch_bounds__(kThreads) void k_pred_fin(const float *__restrict__
     const int mt = gid / (kTile * kTile), e = gid % (kTile * kTile);
     const int r = kTile * mt + e / kTile, t = e % kTile;
     if (r < H && t < B) {
+        // all KS loads in flight (unrolled to the largest split, clamped)
         const float *pp = part + (size_t)mt * KS * (kTile * kTile) + e;
+        float pv[kMaxSplit];
+#pragma unroll
+        for (int ks = 0; ks < kMaxSplit; ++ks) pv[ks] = pp[(size_t)(ks < KS ? ks : 0) * (kTile * kTile)];
         float sum = 0.0f;
-        for (int ks = 0; ks < KS; ++ks) sum += pp[(size_t)ks * (kTile * kTile)];
+#pragma unroll
+        for (int ks = 0; ks < kMaxSplit; ++ks)
+            if (ks < KS) sum += pv[ks];
         const float hv = fmaxf(sum + c1[r], 0.0f);
         const _Float16 hi = (_Float16)hv;
         h[(size_t)t * H + r] = hv;
@@ -673,13 +680,20 @@ __global__ __launch_bounds__(256) void k_fc2_fin(const float *__restrict__ parti
     const int idx = blockIdx.x * 256 + threadIdx.x;
     if (idx >= B * d4) return;
     const int t = idx / d4, m = 4 * (idx % d4);
+    // all G loads in flight (unrolled to kGroups, clamped)
+    float4 pv[kGroups];
+#pragma unroll
+    for (int gg = 0; gg < kGroups; ++gg)
+        pv[gg] = *reinterpret_cast<const float4 *>(partial + ((size_t)(gg < G ? gg : 0) * B + t) * d + m);
     float4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int gg = 0; gg < G; ++gg) {
-        const float4 v = *reinterpret_cast<const float4 *>(partial + ((size_t)gg * B + t) * d + m);
-        sum.x += v.x;
-        sum.y += v.y;
-        sum.z += v.z;
-        sum.w += v.w;
+#pragma unroll
+    for (int gg = 0; gg < kGroups; ++gg) {
+        if (gg < G) {
+            sum.x += pv[gg].x;
+            sum.y += pv[gg].y;
+            sum.z += pv[gg].z;
+            sum.w += pv[gg].w;
+        }
     }
     const float4 bb = *reinterpret_cast<const float4 *>(b2 + m);
     sum.x += bb.x;
@@ -703,10 +717,11 @@ inline hipEvent_t ev_stop(const Trace *tr, int k) { return tr ? tr->ev[2 * k + 1
 
 }  // namespace
 
-// split of the predictor's k over workgroups: the largest power of two <= 8
-// with d a multiple of 128 * KS (every wave then takes a multiple of 16 k)
+// split of the predictor's k over workgroups: the largest power of two <=
+// kMaxSplit with d a multiple of 128 * KS (every wave then takes a multiple
+// of 16 k)
 int pred_mm_splits(int d) {
-    int ks = 8;
+    int ks = kMaxSplit;
     while (ks > 1 && d % (128 * ks) != 0) ks >>= 1;
     return ks;
 }
