@@ -60,6 +60,8 @@ _lib.asf_sparse_ffn.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
 _lib.asf_sparse_ffn.restype = ctypes.c_int
 _lib.asf_decode_step.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
 _lib.asf_decode_step.restype = ctypes.c_int
+_lib.asf_exact_ffn.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
+_lib.asf_exact_ffn.restype = ctypes.c_int
 _lib.asf_stack_decode.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _i32, _i32, _vp, _vp, _vp]
 _lib.asf_stack_decode.restype = ctypes.c_int
 _lib.asf_dense_ffn_ref.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp]
@@ -238,6 +240,26 @@ class Layer:
                                   stream_handle)
         if rc != ASF_OK:
             raise AsfError(rc, "asf_decode_step")
+
+    def exact_ffn(self, x, residual=None, out=None, active=None, n_active=None, stream=None):
+        """asf_exact_ffn: one token through the FFN over its true active set
+        (every pre-activation computed, no predictor)."""
+        x = self._x(x)
+        B = x.shape[0]
+        out = self._out(out, B)
+        _check(_lib.asf_exact_ffn(self._h, _dev_ptr(x, torch.float32, "x"), B,
+                                  _dev_ptr(residual, torch.float32, "residual"),
+                                  _dev_ptr(out, torch.float32, "out"),
+                                  _dev_ptr(active, torch.int32, "active"),
+                                  _dev_ptr(n_active, torch.int32, "n_active"), _stream(stream)),
+               "asf_exact_ffn")
+        return out
+
+    def exact_ffn_raw(self, x_ptr: int, y_ptr: int, stream_handle: int) -> None:
+        """exact_ffn of one token on raw device pointers and a raw stream handle."""
+        rc = _lib.asf_exact_ffn(self._h, x_ptr, 1, None, y_ptr, None, None, stream_handle)
+        if rc != ASF_OK:
+            raise AsfError(rc, "asf_exact_ffn")
 
     def dense_ffn_ref(self, x, residual=None, out=None, stream=None):
         x = self._x(x)

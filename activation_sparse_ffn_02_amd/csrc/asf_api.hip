@@ -243,6 +243,24 @@ asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
     return ASF_OK;
 }
 
+asf_status asf_exact_ffn(const asf_layer *layer, const float *x, int32_t B,
+                         const float *residual, float *y, int32_t *active, int32_t *n_active,
+                         void *stream) {
+    asf_status st = check_call(layer, x, B);
+    if (st != ASF_OK) return st;
+    if (!y) return ASF_ERR_ARG;
+    if (B != 1) return ASF_ERR_UNSUPPORTED;
+    if (!aligned16(y) || (residual && !aligned16(residual))) return ASF_ERR_ALIGN;
+    const LayerView &v = layer->v;
+    hipStream_t s = (hipStream_t)stream;
+    if (launch_exact1(v, x, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
+    if (launch_fc2_sum(v, residual, y, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
+    if ((active || n_active) &&
+        launch_list(v, 1, active, n_active, nullptr, layer->tr(), s) != hipSuccess)
+        return ASF_ERR_HIP;
+    return ASF_OK;
+}
+
 asf_status asf_stack_decode(asf_layer *const *layers, int32_t n_layers, const float *x,
                             int32_t B, int32_t residual, float *y, float *work, void *stream) {
     if (!layers || n_layers < 1 || !x || !y || (residual != 0 && residual != 1))

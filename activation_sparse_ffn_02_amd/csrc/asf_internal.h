@@ -129,6 +129,10 @@ hipError_t launch_fc2(const LayerView &L, int B, bool listed, const float *resid
 // FC2 rows (part1) + b2 (+ resid)
 hipError_t launch_fc2_sum(const LayerView &L, const float *resid, float *y, const Trace *tr,
                           hipStream_t s);
+// exact mask, one token: the pre-activation of every neuron, the true set
+// (z + b1 > 0) into the owner words, and the owner FC2 rows (then
+// launch_fc2_sum)
+hipError_t launch_exact1(const LayerView &L, const float *x, const Trace *tr, hipStream_t s);
 // batched forms on the matrix cores (B >= 2, fp16 weights)
 int pred_mm_splits(int d);
 hipError_t launch_pred_mm(const LayerView &L, const float *x, int B, const Trace *tr,

@@ -962,6 +962,121 @@ __global__ __launch_bounds__(kThreads) __attribute__((
     }
 }
 
+// ---------------------------------------------------------------- exact mask, single token
+// No predictor: owner workgroup q computes the pre-activation z_i + b1 of
+// each of its 64 slots from the first row of the bundle (the up row, or the
+// gate row when gated), so the set is the true one: z_i + b1 > 0 (strict,
+// the FFN's own ReLU decides; "Técnicas dispersas…", section "Viabilidad de
+// la sparsidad de activación").  Wave w takes bits w, w+8, ...; the bits'
+// ballot is the owner's mask (stored as its owner words, so the list call
+// works as after a prediction).  Gated: a = (g + b1) * (up . x) for the
+// active bits, their up rows spread over the waves by rank; plain: a = z + b1.
+// Then the owner's FC2 row, as in k_score1.  Every mask row is read; only
+// the active neurons' down columns (and up rows when gated) are.
+template <int WT, bool GATED, int CPL1>
+__global__ __launch_bounds__(kThreads) __attribute__((
+    amdgpu_waves_per_eu(Fc1Regs<GATED, CPL1>::waves_per_eu))) void k_exact1(ScoreParams p) {
+    constexpr int E = Elt<WT>::E;
+    __shared__ float xs[kMaxDLds];
+    __shared__ float zb[kRowsPerWG];      // z + b1 of bit i (0 past f)
+    __shared__ float a_lds[kRowsPerWG];   // a of the active bits, by rank
+    __shared__ uint64_t m_lds;
+    const int q = blockIdx.x, nq = gridDim.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int C = p.cd;
+    float4 xv[4];
+    stage_load<4>(p.x, p.d, xv);
+    stage_store<4>(xs, xv);
+    __syncthreads();
+    for (int k = 0; k < kRowsPerWG / kWaves; ++k) {
+        const int i = wave + kWaves * k;
+        const int slot = q + nq * i;
+        const bool ok = slot < p.f;
+        const int sl = ok ? slot : p.f - 1;
+        const float bias = p.b1[sl];
+        const u32x4 *bp = p.bundles + (size_t)sl * p.bstride;   // mask row: chunk 0 of the bundle
+        u32x4 w[CPL1];
+#pragma unroll
+        for (int c = 0; c < CPL1; ++c) {
+            const int cc = lane + 64 * c;
+            w[c] = bp[cc < C ? cc : C - 1];
+        }
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL1; ++c) {
+            const int cc = lane + 64 * c;
+            if (cc < C) acc = dot_chunk_lds<WT>(w[c], xs, cc, acc);
+        }
+        const float z = wave_sum(acc) + bias;
+        if (lane == 0) zb[i] = ok ? z : 0.0f;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const uint64_t m = __ballot(zb[threadIdx.x] > 0.0f);
+        if (threadIdx.x == 0) {
+            m_lds = m;
+            p.wbits[q] = m;
+            p.ubits[q] = m;
+            p.out.vbits[q] = m;
+        }
+    }
+    __syncthreads();
+    const uint64_t m = m_lds;
+    const int cnt = __popcll(m);
+    constexpr int CPT = (CPL1 + 7) / 8;      // d-row chunks per thread
+    constexpr int PF = 8 / CPT;
+    const u32x4 *dn = p.bundles + p.dn_off;
+    u32x4 dv[PF][CPT];
+    uint64_t rest = load_down<PF, CPT>(dv, m, dn, p.bstride, q, nq, C);
+    if constexpr (GATED) {
+        for (int r = wave; r < cnt; r += kWaves) {
+            const int i = nth_set_bit(m, r);
+            const u32x4 *bp = p.bundles + (size_t)(q + nq * i) * p.bstride + C;   // up row
+            u32x4 w[CPL1];
+#pragma unroll
+            for (int c = 0; c < CPL1; ++c) {
+                const int cc = lane + 64 * c;
+                w[c] = bp[cc < C ? cc : C - 1];
+            }
+            float acc = 0.0f;
+#pragma unroll
+            for (int c = 0; c < CPL1; ++c) {
+                const int cc = lane + 64 * c;
+                if (cc < C) acc = dot_chunk_lds<WT>(w[c], xs, cc, acc);
+            }
+            const float u = wave_sum(acc);
+            if (lane == 0) a_lds[r] = zb[i] * u;
+        }
+    } else {
+        if (threadIdx.x < 64 && ((m >> threadIdx.x) & 1ull))
+            a_lds[__popcll(m & ((1ull << threadIdx.x) - 1ull))] = zb[threadIdx.x];
+    }
+    __syncthreads();
+    float acc2[CPT][E];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc2[j][e] = 0.0f;
+    fma_down<WT, PF, CPT>(dv, 0, cnt, a_lds, acc2);
+    for (int n0 = PF; n0 < cnt; n0 += PF) {
+        u32x4 dv2[PF][CPT];
+        rest = load_down<PF, CPT>(dv2, rest, dn, p.bstride, q, nq, C);
+        fma_down<WT, PF, CPT>(dv2, n0, cnt, a_lds, acc2);
+    }
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int c = threadIdx.x + kThreads * j;
+        if (c < C) {
+            const int o = c * E;
+            float4 *dst = reinterpret_cast<float4 *>(p.part1 + ((size_t)(o >> 4) * nq + q) * 16 + (o & 15));
+#pragma unroll
+            for (int k = 0; k < E / 4; ++k)
+                dst[k] = make_float4(acc2[j][4 * k], acc2[j][4 * k + 1], acc2[j][4 * k + 2],
+                                     acc2[j][4 * k + 3]);
+        }
+    }
+}
+
 // FC1 over a neuron set for one token (x staged in LDS); modes as k_fc1.
 template <int WT, bool GATED, int CPL1>
 __global__ __launch_bounds__(kThreads) __attribute__((
@@ -1550,6 +1665,42 @@ hipError_t launch_fc2_sum(const LayerView &L, const float *resid, float *y, cons
     const dim3 grid(L.d / 16), blk(kThreads);
     ASF_LAUNCH(ASF_K_FC2, k_fc2_sum, grid, blk, (const float *)L.part1, L.nq, (const float *)L.b2,
                resid, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_exact1(const LayerView &L, const float *x, const Trace *tr, hipStream_t s) {
+    ScoreParams p = {};
+    p.f = L.f;
+    p.wbits = L.wbits;
+    p.ubits = L.ubits;
+    p.bundles = (const u32x4 *)L.bundles;
+    p.bstride = (size_t)L.nmat * L.cd;
+    p.cd = L.cd;
+    p.b1 = L.b1;
+    p.x = x;
+    p.d = L.d;
+    p.out = fc1_out(L);
+    p.dn_off = (L.nmat - 1) * L.cd;
+    p.part1 = L.part1;
+    const dim3 grid(L.nq), blk(kThreads);
+    const int cpl1 = fc1_cpl(L.cd);
+#define ASF_EX(WT, C1)                                                              \
+    if (L.gated) ASF_LAUNCH(ASF_K_FC1, (k_exact1<WT, true, C1>), grid, blk, p);  \
+    else ASF_LAUNCH(ASF_K_FC1, (k_exact1<WT, false, C1>), grid, blk, p);
+#define ASF_EXW(WT)                  \
+    switch (cpl1) {                  \
+    case 1: ASF_EX(WT, 1) break;     \
+    case 2: ASF_EX(WT, 2) break;     \
+    case 4: ASF_EX(WT, 4) break;     \
+    case 8: ASF_EX(WT, 8) break;     \
+    case 10: ASF_EX(WT, 10) break;   \
+    case 12: ASF_EX(WT, 12) break;   \
+    case 14: ASF_EX(WT, 14) break;   \
+    default: ASF_EX(WT, 16) break;   \
+    }
+    if (L.wtype == ASF_F16) { ASF_EXW(1) } else { ASF_EXW(0) }
+#undef ASF_EXW
+#undef ASF_EX
     return hipGetLastError();
 }
 

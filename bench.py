@@ -467,6 +467,39 @@ def main():
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1) / args.dense_steps
 
+    # exact-mask mode (no predictor, every pre-activation, the true set) on the
+    # same ring and tokens, timed like the dense comparator
+    exact = None
+    if args.dense_steps > 0:
+        ne = args.dense_steps
+        n_true = torch.zeros(ne, dtype=torch.int32, device=dev)
+        act = torch.empty(sh.f, dtype=torch.int32, device=dev)
+        for i in range(ne):
+            ring[i % args.ring].exact_ffn(Xd[i % args.tokens], out=Y[i % args.ring], active=act,
+                                          n_active=n_true[i:i + 1])
+        torch.cuda.synchronize()
+        k_true = float(n_true.float().mean().item())
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(ne):
+            ring[i % args.ring].exact_ffn_raw(xs[i % args.tokens], ys[i % args.ring], sh_)
+        e1.record()
+        torch.cuda.synchronize()
+        ex_ms = e0.elapsed_time(e1) / ne
+        ws = 2 if sh.wdtype == "f16" else 4
+        # every mask row (+ b1), the true set's down columns (and up rows when
+        # gated), x, b2, y
+        ex_bytes = (sh.f * (sh.d * ws + 4) + k_true * sh.d * ws * (2 if sh.gated else 1)
+                    + sh.d * 4 * 3)
+        exact = {"ms_per_step": ex_ms, "true_active_mean": k_true,
+                 "true_active_frac": k_true / sh.f, "algorithmic_bytes_per_step": ex_bytes,
+                 "effective_gbps": ex_bytes / (ex_ms * 1e-3) / 1e9,
+                 "effective_frac_of_peak": ex_bytes / (ex_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "speedup_vs_dense": None if dense_ms is None else dense_ms / ex_ms,
+                 "byte_ceiling_vs_dense": dense_bytes / ex_bytes}
+        log(args, "exact-mask mode: %.1f us per step, true set %.1f%%" % (ex_ms * 1e3,
+                                                                        100 * k_true / sh.f))
+
     tok_s = K / elapsed
     eff_gbs = step_bytes * K / elapsed / 1e9
     out = {
@@ -499,6 +532,7 @@ def main():
         "dense_ms_per_step": dense_ms,
         "dense_gbps": None if dense_ms is None else dense_bytes / (dense_ms * 1e-3) / 1e9,
         "sparse_step_speedup_vs_dense": None if dense_ms is None else dense_ms / ms_per_step,
+        "exact_mask": exact,
         "roofline": {"bound": "hbm", "kernel": dname, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(dname),

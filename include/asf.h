@@ -175,9 +175,12 @@ asf_status asf_sparse_ffn(const asf_layer *layer, const float *x, int32_t B,
 
 /* One decode step of one layer: asf_predict followed by asf_sparse_ffn over
  * the predicted union set, with no host round trip in between.  The optional
- * outputs are those of asf_predict.  Three kernels (predictor layer 1;
- * layer 2 + threshold + FC1; FC2 + reduction); the results are bit-identical
- * to asf_predict followed by asf_sparse_ffn with active == NULL. */
+ * outputs are those of asf_predict.  One token: three kernels (predictor
+ * layer 1; layer 2 + threshold + FC1 + each owner's FC2 into one row; the
+ * sum of the owner rows); the set equals asf_predict's and y equals
+ * asf_predict + asf_sparse_ffn up to the order of the fp32 additions.
+ * B >= 2: the batched kernels, bit-identical to asf_predict followed by
+ * asf_sparse_ffn with active == NULL.  Repeated calls give identical bits. */
 asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
                            const float *residual, float *y, int32_t *active,
                            int32_t *n_active, void *stream);
@@ -204,12 +207,35 @@ asf_status asf_stack_decode(asf_layer *const *layers, int32_t n_layers, const fl
 asf_status asf_dense_ffn_ref(const asf_layer *layer, const float *x, int32_t B,
                              const float *residual, float *y, void *stream);
 
+/* Exact-mask FFN of one token, without the predictor: every neuron's
+ * pre-activation z_i = W_up[i] . x + b1_i (W_gate when gated) is computed,
+ * the set is the true one, {i : z_i > 0}, and FC2 reads only that set's down
+ * columns (the gated form also only its up rows):
+ *   y = residual + b2 + sum_{z_i > 0} a_i W_down[:, i]
+ * which equals the dense FFN (ReLU(z) is 0 off the set) up to the order of
+ * the fp32 additions.  The pages rest the method on this exact zero pattern
+ * of the ReLU ("Técnicas dispersas para una aceleración 100X…", section
+ * "Viabilidad de la sparsidad de activación"); it reads all of W_up (W_gate)
+ * and the active fraction of W_down.
+ *   x, residual, y   as asf_sparse_ffn, with B == 1 (ASF_ERR_UNSUPPORTED
+ *                    otherwise)
+ *   active, n_active DEVICE int32 [d_ffn] / [1], or NULL: the true set as
+ *                    original ids in ascending stored (slot) order, as
+ *                    asf_predict gives its set
+ * Kernels: FC1 (pre-activations, mask, gated up rows, owner FC2 rows), FC2
+ * (sum of the owner rows), then LIST when an output is requested. */
+asf_status asf_exact_ffn(const asf_layer *layer, const float *x, int32_t B,
+                         const float *residual, float *y, int32_t *active, int32_t *n_active,
+                         void *stream);
+
 /* Kernels behind the calls (ids for asf_layer_set_trace).
  *   asf_predict       PRED_L1, SCORE, then LIST when an output is requested
  *   asf_decode_step   PRED_L1, SCORE_FC1 (B == 1, fp16; else SCORE + FC1),
  *                     FC2, then LIST when an output is requested
  *   asf_sparse_ffn    FC1, FC2
- *   asf_dense_ffn_ref FC1 (every neuron), FC2 */
+ *   asf_dense_ffn_ref FC1 (every neuron), FC2
+ *   asf_exact_ffn     FC1 (pre-activations, true set, owner FC2 rows), FC2
+ *                     (sum of the owner rows), then LIST when requested */
 typedef enum {
     ASF_K_PRED_L1 = 0,   /* predictor layer 1 GEMV */
     ASF_K_SCORE = 1,     /* predictor layer 2 GEMV + threshold -> mask bits */

@@ -34,7 +34,8 @@ def asf():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("asf_layer_storage_bytes", "asf_create_layer", "asf_destroy_layer", "asf_predict",
-              "asf_sparse_ffn", "asf_dense_ffn_ref", "asf_decode_step", "asf_status_string"):
+              "asf_sparse_ffn", "asf_dense_ffn_ref", "asf_decode_step", "asf_exact_ffn",
+              "asf_stack_decode", "asf_status_string"):
         assert n in names
 
 
@@ -103,6 +104,7 @@ def test_calls_reject_null_handle(asf):
     assert lib.asf_sparse_ffn(None, fake, 1, None, None, None, fake, None) == 1
     assert lib.asf_decode_step(None, fake, 1, None, fake, None, None, None) == 1
     assert lib.asf_dense_ffn_ref(None, fake, 1, None, fake, None) == 1
+    assert lib.asf_exact_ffn(None, fake, 1, None, fake, None, None, None) == 1
     lib.asf_destroy_layer(None)
     assert lib.asf_status_string(0) == b"ok"
     assert lib.asf_status_string(4) == b"storage too small"
