@@ -62,6 +62,10 @@ _lib.asf_decode_step.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
 _lib.asf_decode_step.restype = ctypes.c_int
 _lib.asf_exact_ffn.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
 _lib.asf_exact_ffn.restype = ctypes.c_int
+_lib.asf_profile_activations.argtypes = [_vp, _vp, _i32, _vp, _vp]
+_lib.asf_profile_activations.restype = ctypes.c_int
+_lib.asf_hot_first_table.argtypes = [_vp, _i32, _vp, _vp]
+_lib.asf_hot_first_table.restype = ctypes.c_int
 _lib.asf_stack_decode.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _i32, _i32, _vp, _vp, _vp]
 _lib.asf_stack_decode.restype = ctypes.c_int
 _lib.asf_dense_ffn_ref.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp]
@@ -261,6 +265,19 @@ class Layer:
         if rc != ASF_OK:
             raise AsfError(rc, "asf_exact_ffn")
 
+    def profile_activations(self, x, counts=None, stream=None):
+        """asf_profile_activations: add each token's true active set (by
+        original id) into `counts` (uint32 viewed as int32 [d_ffn]; zeros when
+        not given); returns counts."""
+        x = self._x(x)
+        if counts is None:
+            counts = torch.zeros(self.d_ffn, dtype=torch.int32, device=x.device)
+        _check(_lib.asf_profile_activations(self._h, _dev_ptr(x, torch.float32, "x"), x.shape[0],
+                                            _dev_ptr(counts, torch.int32, "counts"),
+                                            _stream(stream)),
+               "asf_profile_activations")
+        return counts
+
     def dense_ffn_ref(self, x, residual=None, out=None, stream=None):
         x = self._x(x)
         B = x.shape[0]
@@ -332,6 +349,17 @@ class Stack:
                                    work_ptr, stream_handle)
         if rc != ASF_OK:
             raise AsfError(rc, "asf_stack_decode")
+
+
+def hot_first_table(counts, stream=None):
+    """asf_hot_first_table: int32 [d_ffn] table (slot -> original id), most
+    frequently active first, ties by smaller id, from device counts."""
+    f = counts.numel()
+    table = torch.empty(f, dtype=torch.int32, device=counts.device)
+    _check(_lib.asf_hot_first_table(_dev_ptr(counts, torch.int32, "counts"), f,
+                                    _dev_ptr(table, torch.int32, "table"), _stream(stream)),
+           "asf_hot_first_table")
+    return table
 
 
 def layer_from_numpy(L, device="cuda", max_batch: int = 1, threshold: float = 0.0,

@@ -253,10 +253,32 @@ asf_status asf_exact_ffn(const asf_layer *layer, const float *x, int32_t B,
     if (!aligned16(y) || (residual && !aligned16(residual))) return ASF_ERR_ALIGN;
     const LayerView &v = layer->v;
     hipStream_t s = (hipStream_t)stream;
-    if (launch_exact1(v, x, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
+    if (launch_exact1(v, x, false, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
     if (launch_fc2_sum(v, residual, y, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
     if ((active || n_active) &&
         launch_list(v, 1, active, n_active, nullptr, layer->tr(), s) != hipSuccess)
+        return ASF_ERR_HIP;
+    return ASF_OK;
+}
+
+asf_status asf_profile_activations(const asf_layer *layer, const float *x, int32_t n,
+                                   uint32_t *counts, void *stream) {
+    if (!layer || !x || !counts || n < 0) return ASF_ERR_ARG;
+    if (!aligned16(x)) return ASF_ERR_ALIGN;
+    const LayerView &v = layer->v;
+    hipStream_t s = (hipStream_t)stream;
+    for (int32_t t = 0; t < n; ++t) {
+        if (launch_exact1(v, x + (size_t)t * v.d, true, nullptr, s) != hipSuccess)
+            return ASF_ERR_HIP;
+        if (launch_count_bits(v, counts, s) != hipSuccess) return ASF_ERR_HIP;
+    }
+    return ASF_OK;
+}
+
+asf_status asf_hot_first_table(const uint32_t *counts, int32_t d_ffn, int32_t *table,
+                               void *stream) {
+    if (!counts || !table || d_ffn <= 0 || d_ffn > kMaxFfn) return ASF_ERR_ARG;
+    if (launch_rank_table(counts, d_ffn, table, (hipStream_t)stream) != hipSuccess)
         return ASF_ERR_HIP;
     return ASF_OK;
 }

@@ -132,7 +132,12 @@ hipError_t launch_fc2_sum(const LayerView &L, const float *resid, float *y, cons
 // exact mask, one token: the pre-activation of every neuron, the true set
 // (z + b1 > 0) into the owner words, and the owner FC2 rows (then
 // launch_fc2_sum)
-hipError_t launch_exact1(const LayerView &L, const float *x, const Trace *tr, hipStream_t s);
+hipError_t launch_exact1(const LayerView &L, const float *x, bool mask_only, const Trace *tr,
+                         hipStream_t s);
+// activation profiler: counts[perm[s]] += bit s of the single-token owner
+// words (L.wbits); hot-first table by ranking (count desc, id asc)
+hipError_t launch_count_bits(const LayerView &L, uint32_t *counts, hipStream_t s);
+hipError_t launch_rank_table(const uint32_t *counts, int f, int32_t *table, hipStream_t s);
 // batched forms on the matrix cores (B >= 2, fp16 weights)
 int pred_mm_splits(int d);
 hipError_t launch_pred_mm(const LayerView &L, const float *x, int B, const Trace *tr,

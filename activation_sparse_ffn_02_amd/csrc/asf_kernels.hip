@@ -1021,6 +1021,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((
         }
     }
     __syncthreads();
+    if (!p.part1) return;   // mask only (the activation profiler)
     const uint64_t m = m_lds;
     const int cnt = __popcll(m);
     constexpr int CPT = (CPL1 + 7) / 8;      // d-row chunks per thread
@@ -1323,6 +1324,39 @@ __global__ __launch_bounds__(kThreads) void k_fc2_sum(const float *__restrict__ 
         const float hi = __shfl_down(sum, 32, 64);
         if (tid < 16) y[16 * s + o] = (sum + hi) + bv + rv;
     }
+}
+
+// ---------------------------------------------------------------- activation profiler
+// counts[perm[s]] += bit s of the owner words of the last single-token pass
+// (slot s = q + nq*i is bit i of word q)
+__global__ __launch_bounds__(256) void k_count_bits(const uint64_t *__restrict__ words, int f,
+                                                    int nq, const int32_t *__restrict__ perm,
+                                                    uint32_t *__restrict__ counts) {
+    const int sl = blockIdx.x * 256 + threadIdx.x;
+    if (sl >= f) return;
+    if ((words[sl % nq] >> (sl / nq)) & 1ull) counts[perm[sl]] += 1u;
+}
+
+// Hot-first table by exact ranking: key_i = (count descending, id
+// ascending); neuron i goes to position #{j : key_j < key_i}, a permutation
+// because the keys are distinct.  Keys are compared in LDS tiles.
+constexpr int kRankTile = 1024;
+
+__global__ __launch_bounds__(kRankTile) void k_rank_table(const uint32_t *__restrict__ counts,
+                                                          int f, int32_t *__restrict__ table) {
+    __shared__ uint64_t kt[kRankTile];
+    const int i = blockIdx.x * kRankTile + threadIdx.x;
+    const uint64_t ki = i < f ? ((uint64_t)(0xffffffffu - counts[i]) << 32) | (uint32_t)i : ~0ull;
+    int rank = 0;
+    for (int j0 = 0; j0 < f; j0 += kRankTile) {
+        const int j = j0 + threadIdx.x;
+        kt[threadIdx.x] = j < f ? ((uint64_t)(0xffffffffu - counts[j]) << 32) | (uint32_t)j : ~0ull;
+        __syncthreads();
+        const int n = f - j0 < kRankTile ? f - j0 : kRankTile;
+        for (int t = 0; t < n; ++t) rank += kt[t] < ki;
+        __syncthreads();
+    }
+    if (i < f) table[rank] = i;
 }
 
 // ---------------------------------------------------------------- list
@@ -1668,7 +1702,8 @@ hipError_t launch_fc2_sum(const LayerView &L, const float *resid, float *y, cons
     return hipGetLastError();
 }
 
-hipError_t launch_exact1(const LayerView &L, const float *x, const Trace *tr, hipStream_t s) {
+hipError_t launch_exact1(const LayerView &L, const float *x, bool mask_only, const Trace *tr,
+                         hipStream_t s) {
     ScoreParams p = {};
     p.f = L.f;
     p.wbits = L.wbits;
@@ -1681,7 +1716,7 @@ hipError_t launch_exact1(const LayerView &L, const float *x, const Trace *tr, hi
     p.d = L.d;
     p.out = fc1_out(L);
     p.dn_off = (L.nmat - 1) * L.cd;
-    p.part1 = L.part1;
+    p.part1 = mask_only ? nullptr : L.part1;
     const dim3 grid(L.nq), blk(kThreads);
     const int cpl1 = fc1_cpl(L.cd);
 #define ASF_EX(WT, C1)                                                              \
@@ -1701,6 +1736,18 @@ hipError_t launch_exact1(const LayerView &L, const float *x, const Trace *tr, hi
     if (L.wtype == ASF_F16) { ASF_EXW(1) } else { ASF_EXW(0) }
 #undef ASF_EXW
 #undef ASF_EX
+    return hipGetLastError();
+}
+
+hipError_t launch_count_bits(const LayerView &L, uint32_t *counts, hipStream_t s) {
+    hipLaunchKernelGGL(k_count_bits, dim3((L.f + 255) / 256), dim3(256), 0, s,
+                       (const uint64_t *)L.wbits, L.f, L.nq, (const int32_t *)L.perm, counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_rank_table(const uint32_t *counts, int f, int32_t *table, hipStream_t s) {
+    hipLaunchKernelGGL(k_rank_table, dim3((f + kRankTile - 1) / kRankTile), dim3(kRankTile), 0, s,
+                       counts, f, table);
     return hipGetLastError();
 }
 

@@ -54,6 +54,11 @@ def parse():
     ap.add_argument("--batches", type=int, nargs="*", default=[1, 4, 16, 32],
                     help="batch sizes of the batched-union workload (none skips it)")
     ap.add_argument("--batched-ring", type=int, default=3)
+    ap.add_argument("--layout-steps", type=int, default=1000,
+                    help="decode steps per neuron-table variant (0 skips the layout ablation)")
+    ap.add_argument("--layout-ring", type=int, default=8)
+    ap.add_argument("--layout-calib", type=int, default=512,
+                    help="calibration tokens of the on-device activation profile")
     return ap.parse_args()
 
 
@@ -257,6 +262,59 @@ def bench_stack(args, asf, torch, np, wl, dev, stream):
     }
     for lay in layers:
         lay.close()
+    return res
+
+
+def bench_layout(args, asf, torch, np, wl, dev, stream):
+    """Neuron-table ablation on the benchmark layer: the decode step with the
+    identity table, with the hot-first table profiled on the device
+    (asf_profile_activations over calibration tokens, then
+    asf_hot_first_table), and with the generator's own hot-first table."""
+    import dataclasses
+    L = wl.config_layer(WORKLOAD)
+    sh = L.shape
+    t0 = time.perf_counter()
+    calib = torch.from_numpy(wl.config_calib_tokens(WORKLOAD, args.layout_calib)).to(dev)
+    ident = asf.layer_from_numpy(L, use_table=False)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    counts = ident.profile_activations(calib)
+    table = asf.hot_first_table(counts)
+    torch.cuda.synchronize()
+    prof_ms = (time.perf_counter() - t1) * 1e3
+    del ident
+    tab = table.cpu().numpy().astype(L.perm.dtype)
+    top = min(1000, sh.f)
+    overlap = len(set(tab[:top].tolist()) & set(L.perm[:top].tolist())) / top
+    X = torch.from_numpy(wl.config_tokens(WORKLOAD, args.tokens)).to(dev)
+    xs = [X[t:t + 1].data_ptr() for t in range(args.tokens)]
+    sh_ = stream.cuda_stream
+    res = {"workload": "OPT-6.7B-shaped layer 4096x16384 fp16, batch 1, ring of %d copies per table"
+                       % args.layout_ring,
+           "calibration_tokens": args.layout_calib, "profile_and_table_ms": prof_ms,
+           "profiled_top1000_overlap_with_generator": overlap}
+    variants = [("identity", dict(use_table=False), L),
+                ("profiled", {}, dataclasses.replace(L, perm=tab)),
+                ("generator", {}, L)]
+    for name, kw, LL in variants:
+        ring = [asf.layer_from_numpy(LL, **kw) for _ in range(args.layout_ring)]
+        Y = torch.empty((args.layout_ring, 1, sh.d), dtype=torch.float32, device=dev)
+        ys = [Y[r].data_ptr() for r in range(args.layout_ring)]
+        for i in range(50):
+            ring[i % len(ring)].decode_step_raw(xs[i % args.tokens], 1, ys[i % len(ring)], sh_)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.layout_steps):
+            ring[i % len(ring)].decode_step_raw(xs[i % args.tokens], 1, ys[i % len(ring)], sh_)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name + "_us_per_step"] = e0.elapsed_time(e1) * 1e3 / args.layout_steps
+        del ring, Y
+        torch.cuda.empty_cache()
+    log(args, "layout ablation (us per step): identity %.2f, profiled %.2f, generator %.2f; %.1f s"
+        % (res["identity_us_per_step"], res["profiled_us_per_step"], res["generator_us_per_step"],
+           time.perf_counter() - t0))
     return res
 
 
@@ -540,10 +598,14 @@ def main():
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(args, L, X)
-    if args.stack_tokens > 0:
-        del ring, Xd, Y
+    del ring, Xd, Y
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if args.layout_steps > 0:
+        out["layout"] = bench_layout(args, asf, torch, np, wl, dev, stream)
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
+    if args.stack_tokens > 0:
         out["stack"] = bench_stack(args, asf, torch, np, wl, dev, stream)
         torch.cuda.synchronize()
         torch.cuda.empty_cache()

@@ -228,6 +228,28 @@ asf_status asf_exact_ffn(const asf_layer *layer, const float *x, int32_t B,
                          const float *residual, float *y, int32_t *active, int32_t *n_active,
                          void *stream);
 
+/* Activation profiler, the offline half of the neuron table: for each of the
+ * n tokens of x, every neuron's true pre-activation is computed (as in
+ * asf_exact_ffn) and counts[id] is incremented for the neurons with z > 0,
+ * indexed by ORIGINAL id ("LLM模型之PowerInfer1.0" §5.1: the activation
+ * frequency of each neuron over a general dataset).  The layer's own table
+ * only fixes the storage order; create it with table == NULL to profile.
+ *   x       DEVICE float32 [n][d_model], n >= 0
+ *   counts  DEVICE uint32 [d_ffn], accumulated (the caller zeroes it first)
+ * Uses the layer's scratch like every other call; two small kernels per
+ * token, asynchronous on `stream`. */
+asf_status asf_profile_activations(const asf_layer *layer, const float *x, int32_t n,
+                                   uint32_t *counts, void *stream);
+
+/* Hot-first neuron table from activation counts: table[s] = the original id
+ * with the s-th largest count, ties broken by the smaller id -- the neuron
+ * impact of "LLM模型之PowerInfer1.0" §5.2 Eq. 1 (impact = activation
+ * frequency) in descending order, the layout asf_create_layer takes.
+ *   counts  DEVICE uint32 [d_ffn];  table  DEVICE int32 [d_ffn]
+ * d_ffn in 1 .. 65536.  One kernel (exact ranking), asynchronous. */
+asf_status asf_hot_first_table(const uint32_t *counts, int32_t d_ffn, int32_t *table,
+                               void *stream);
+
 /* Kernels behind the calls (ids for asf_layer_set_trace).
  *   asf_predict       PRED_L1, SCORE, then LIST when an output is requested
  *   asf_decode_step   PRED_L1, SCORE_FC1 (B == 1, fp16; else SCORE + FC1),

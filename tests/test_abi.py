@@ -105,6 +105,10 @@ def test_calls_reject_null_handle(asf):
     assert lib.asf_decode_step(None, fake, 1, None, fake, None, None, None) == 1
     assert lib.asf_dense_ffn_ref(None, fake, 1, None, fake, None) == 1
     assert lib.asf_exact_ffn(None, fake, 1, None, fake, None, None, None) == 1
+    assert lib.asf_profile_activations(None, fake, 1, fake, None) == 1
+    assert lib.asf_hot_first_table(None, 16, fake, None) == 1
+    assert lib.asf_hot_first_table(fake, 0, fake, None) == 1
+    assert lib.asf_hot_first_table(fake, 65537, fake, None) == 1
     lib.asf_destroy_layer(None)
     assert lib.asf_status_string(0) == b"ok"
     assert lib.asf_status_string(4) == b"storage too small"

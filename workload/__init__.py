@@ -157,6 +157,10 @@ def token_seed(config_index: int) -> int:
     return 2000 + config_index
 
 
+def calib_seed(config_index: int) -> int:
+    return 3000 + config_index
+
+
 def make_tokens(d: int, n: int, seed: int) -> np.ndarray:
     rng = np.random.Generator(np.random.PCG64(seed))
     return rng.standard_normal((n, d), dtype=np.float32)
@@ -170,6 +174,13 @@ def config_layer(name: str, layer: int = 0, shape: Optional[LayerShape] = None) 
 def config_tokens(name: str, n: int) -> np.ndarray:
     idx, sh = CONFIGS[name]
     return make_tokens(sh.d, n, token_seed(idx))
+
+
+def config_calib_tokens(name: str, n: int) -> np.ndarray:
+    """Calibration tokens (activation profiling), drawn apart from the
+    decode tokens."""
+    idx, sh = CONFIGS[name]
+    return make_tokens(sh.d, n, calib_seed(idx))
 
 
 def scaled_shape(shape: LayerShape, d: int, f: int, H: int) -> LayerShape:
