@@ -68,6 +68,8 @@ _lib.asf_hot_first_table.argtypes = [_vp, _i32, _vp, _vp]
 _lib.asf_hot_first_table.restype = ctypes.c_int
 _lib.asf_stack_decode.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _i32, _i32, _vp, _vp, _vp]
 _lib.asf_stack_decode.restype = ctypes.c_int
+_lib.asf_stack_decode_lookahead.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _i32, _vp, _vp, _vp]
+_lib.asf_stack_decode_lookahead.restype = ctypes.c_int
 _lib.asf_dense_ffn_ref.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp]
 _lib.asf_dense_ffn_ref.restype = ctypes.c_int
 _lib.asf_layer_set_trace.argtypes = [_vp, ctypes.POINTER(ctypes.c_void_p), _i32]
@@ -341,6 +343,30 @@ class Stack:
                                      _dev_ptr(work, torch.float32, "work"), _stream(stream)),
                "asf_stack_decode")
         return out
+
+    def decode_lookahead(self, x, out=None, work=None, stream=None):
+        """asf_stack_decode_lookahead: one token, layer l+1's set predicted
+        from layer l's input on a second stream."""
+        if x.dim() == 1:
+            x = x.unsqueeze(0)
+        if out is None:
+            out = torch.empty((1, self.d_model), dtype=torch.float32, device=self.device)
+        if work is None:
+            work = self._work_for(1)
+        _check(_lib.asf_stack_decode_lookahead(self._arr, len(self.layers),
+                                               _dev_ptr(x, torch.float32, "x"), self.residual,
+                                               _dev_ptr(out, torch.float32, "out"),
+                                               _dev_ptr(work, torch.float32, "work"),
+                                               _stream(stream)),
+               "asf_stack_decode_lookahead")
+        return out
+
+    def decode_lookahead_raw(self, x_ptr: int, y_ptr: int, work_ptr: int,
+                             stream_handle: int) -> None:
+        rc = _lib.asf_stack_decode_lookahead(self._arr, len(self.layers), x_ptr, self.residual,
+                                             y_ptr, work_ptr, stream_handle)
+        if rc != ASF_OK:
+            raise AsfError(rc, "asf_stack_decode_lookahead")
 
     def decode_raw(self, x_ptr: int, B: int, y_ptr: int, work_ptr: int,
                    stream_handle: int) -> None:

@@ -129,6 +129,10 @@ hipError_t launch_fc2(const LayerView &L, int B, bool listed, const float *resid
 // FC2 rows (part1) + b2 (+ resid)
 hipError_t launch_fc2_sum(const LayerView &L, const float *resid, float *y, const Trace *tr,
                           hipStream_t s);
+// one token over the set of the last prediction (the owner words): FC1 and
+// the owner FC2 rows, as the decode step does after its ballot (then
+// launch_fc2_sum)
+hipError_t launch_ffn1(const LayerView &L, const float *x, const Trace *tr, hipStream_t s);
 // exact mask, one token: the pre-activation of every neuron, the true set
 // (z + b1 > 0) into the owner words, and the owner FC2 rows (then
 // launch_fc2_sum)

@@ -779,6 +779,85 @@ __device__ __forceinline__ void fma_down(const u32x4 (&dv)[N][CPT], int n0, int 
     }
 }
 
+// FC1 of owner q's listed neurons (the bits of `valid`, slot q + nq*bit) and
+// the owner's FC2 row, one token, x in LDS.  With SPEC, waves below
+// kSpecRows already hold the rows (spu, spg) and bias of bit `wave`.
+template <int WT, bool GATED, int CPL1, bool SPEC>
+__device__ __forceinline__ void owner_ffn1(const ScoreParams &p, int q, int nq, uint64_t valid,
+                                           const float *xs, float *a_lds,
+                                           const u32x4 (&spu)[CPL1], const u32x4 (&spg)[CPL1],
+                                           float spec_bias, int wave, int lane) {
+    constexpr int E = Elt<WT>::E;
+    const int cnt = __popcll(valid);
+    // FC2 of this owner's listed neurons: thread t takes chunks t, t + 512
+    // of the down columns.  The chunks of the first PF entries (rank
+    // order) are loaded now, beside the FC1 rows, and with a 256-VGPR
+    // budget those of the next PFB too when the owner lists more; the
+    // rest in batches of PF2 once the FC1 rows are no longer held.  PF is
+    // cut where the FC1 rows leave no registers under the 128-VGPR cap.
+    constexpr int CPT = (CPL1 + 7) / 8;      // d-row chunks per thread
+    constexpr int PF2 = 8 / CPT;
+    constexpr bool kWide = Fc1Regs<GATED, CPL1, SPEC>::waves_per_eu == 2;
+    constexpr bool kTight = !kWide && CPT == 2;
+    constexpr int PF = kTight ? (CPL1 >= 12 ? 0 : 2) : PF2;   // no spills
+    constexpr int PFB = (kWide && Fc1Regs<GATED, CPL1>::chunks + 2 * PF * CPT <= 32) ? PF : 0;
+    const u32x4 *dn = p.bundles + p.dn_off;
+    u32x4 dv[PF > 0 ? PF : 1][CPT];
+    u32x4 dvb[PFB > 0 ? PFB : 1][CPT];
+    uint64_t rest = valid;
+    if constexpr (PF > 0) rest = load_down<PF, CPT>(dv, valid, dn, p.bstride, q, nq, p.cd);
+    if constexpr (PFB > 0)
+        if (cnt > PF) rest = load_down<PFB, CPT>(dvb, rest, dn, p.bstride, q, nq, p.cd);
+    // FC1 balanced by rank: with SPEC, bit b < kSpecRows (rows held) is
+    // wave b's; the other entries, ranked among themselves, go to waves
+    // off, off + 1, ... round the 8 waves
+    constexpr int off = SPEC ? kSpecRows : 0;
+    if constexpr (SPEC) {
+        if (wave < kSpecRows && ((valid >> wave) & 1ull)) {
+            const int slot = q + nq * wave;
+            fc1_entry_1<WT, GATED, CPL1>(q, valid, wave, slot, spu, spg, p.cd, spec_bias, xs,
+                                         p.out, a_lds, lane);
+        }
+    }
+    const uint64_t mr = SPEC ? (valid & ~((1ull << kSpecRows) - 1ull)) : valid;
+    const int nr = __popcll(mr);
+    for (int r = (wave - off + kWaves) % kWaves; r < nr; r += kWaves) {
+        const int i = nth_set_bit(mr, r);
+        const int slot = q + nq * i;
+        const float bias = p.b1[slot];
+        u32x4 wu[CPL1], wg[CPL1];
+        load_fc1_rows<GATED, CPL1>(p.bundles, p.bstride, p.cd, slot, lane, wu, wg);
+        fc1_entry_1<WT, GATED, CPL1>(q, valid, i, slot, wu, wg, p.cd, bias, xs, p.out, a_lds,
+                                     lane);
+    }
+    __syncthreads();
+    float acc2[CPT][E];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc2[j][e] = 0.0f;
+    if constexpr (PF > 0) fma_down<WT, PF, CPT>(dv, 0, cnt, a_lds, acc2);
+    if constexpr (PFB > 0)
+        if (cnt > PF) fma_down<WT, PFB, CPT>(dvb, PF, cnt, a_lds, acc2);
+    for (int n0 = PF + PFB; n0 < cnt; n0 += PF2) {
+        u32x4 dv2[PF2][CPT];
+        rest = load_down<PF2, CPT>(dv2, rest, dn, p.bstride, q, nq, p.cd);
+        fma_down<WT, PF2, CPT>(dv2, n0, cnt, a_lds, acc2);
+    }
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int c = threadIdx.x + kThreads * j;
+        if (c < p.cd) {
+            const int o = c * E;
+            float4 *dst = reinterpret_cast<float4 *>(p.part1 + ((size_t)(o >> 4) * nq + q) * 16 + (o & 15));
+#pragma unroll
+            for (int k = 0; k < E / 4; ++k)
+                dst[k] = make_float4(acc2[j][4 * k], acc2[j][4 * k + 1], acc2[j][4 * k + 2],
+                                     acc2[j][4 * k + 3]);
+        }
+    }
+}
+
 // Single-token owner workgroup q: scores of its 64 slots, owner bits; with
 // FC1, a of its listed neurons and then the owner's FC2 partial row (its
 // listed neurons' a times their down columns, added in rank order), which
@@ -889,77 +968,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((
         u_lds = u;
     }
     __syncthreads();
-    if constexpr (FC1) {
-        const uint64_t valid = u_lds;
-        const int cnt = __popcll(valid);
-        // FC2 of this owner's listed neurons: thread t takes chunks t, t + 512
-        // of the down columns.  The chunks of the first PF entries (rank
-        // order) are loaded now, beside the FC1 rows, and with a 256-VGPR
-        // budget those of the next PFB too when the owner lists more; the
-        // rest in batches of PF2 once the FC1 rows are no longer held.  PF is
-        // cut where the FC1 rows leave no registers under the 128-VGPR cap.
-        constexpr int CPT = (CPL1 + 7) / 8;      // d-row chunks per thread
-        constexpr int PF2 = 8 / CPT;
-        constexpr bool kWide = Fc1Regs<GATED, CPL1, SPEC>::waves_per_eu == 2;
-        constexpr bool kTight = !kWide && CPT == 2;
-        constexpr int PF = kTight ? (CPL1 >= 12 ? 0 : 2) : PF2;   // no spills
-        constexpr int PFB = (kWide && Fc1Regs<GATED, CPL1>::chunks + 2 * PF * CPT <= 32) ? PF : 0;
-        const u32x4 *dn = p.bundles + p.dn_off;
-        u32x4 dv[PF > 0 ? PF : 1][CPT];
-        u32x4 dvb[PFB > 0 ? PFB : 1][CPT];
-        uint64_t rest = valid;
-        if constexpr (PF > 0) rest = load_down<PF, CPT>(dv, valid, dn, p.bstride, q, nq, p.cd);
-        if constexpr (PFB > 0)
-            if (cnt > PF) rest = load_down<PFB, CPT>(dvb, rest, dn, p.bstride, q, nq, p.cd);
-        // FC1 balanced by rank: with SPEC, bit b < kSpecRows (rows held) is
-        // wave b's; the other entries, ranked among themselves, go to waves
-        // off, off + 1, ... round the 8 waves
-        constexpr int off = SPEC ? kSpecRows : 0;
-        if constexpr (SPEC) {
-            if (wave < kSpecRows && ((valid >> wave) & 1ull)) {
-                const int slot = q + nq * wave;
-                fc1_entry_1<WT, GATED, CPL1>(q, valid, wave, slot, spu, spg, p.cd, spec_bias, xs,
-                                             p.out, a_lds, lane);
-            }
-        }
-        const uint64_t mr = SPEC ? (valid & ~((1ull << kSpecRows) - 1ull)) : valid;
-        const int nr = __popcll(mr);
-        for (int r = (wave - off + kWaves) % kWaves; r < nr; r += kWaves) {
-            const int i = nth_set_bit(mr, r);
-            const int slot = q + nq * i;
-            const float bias = p.b1[slot];
-            u32x4 wu[CPL1], wg[CPL1];
-            load_fc1_rows<GATED, CPL1>(p.bundles, p.bstride, p.cd, slot, lane, wu, wg);
-            fc1_entry_1<WT, GATED, CPL1>(q, valid, i, slot, wu, wg, p.cd, bias, xs, p.out, a_lds,
-                                         lane);
-        }
-        __syncthreads();
-        float acc2[CPT][E];
+    if constexpr (FC1)
+        owner_ffn1<WT, GATED, CPL1, SPEC>(p, q, nq, u_lds, xs, a_lds, spu, spg, spec_bias, wave,
+                                          lane);
+}
+
+// FC1 + FC2 rows of one token over the set of the layer's last prediction
+// (its owner words), for the set predicted ahead of time (the look-ahead
+// stack) and for asf_sparse_ffn of one token over the last prediction: the
+// same per-owner work as k_score1 after its ballot, so the results match
+// the decode step bit for bit.
+template <int WT, bool GATED, int CPL1>
+__global__ __launch_bounds__(kThreads) __attribute__((
+    amdgpu_waves_per_eu(Fc1Regs<GATED, CPL1>::waves_per_eu))) void k_ffn1(ScoreParams p) {
+    __shared__ float xs[kMaxDLds];
+    __shared__ float a_lds[kRowsPerWG];
+    const int q = blockIdx.x, nq = gridDim.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float4 xv[4];
+    stage_load<4>(p.x, p.d, xv);
+    const uint64_t valid = p.ubits[q];
+    stage_store<4>(xs, xv);
+    if (threadIdx.x == 0) p.out.vbits[q] = valid;
+    __syncthreads();
+    u32x4 none[CPL1];
 #pragma unroll
-        for (int j = 0; j < CPT; ++j)
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc2[j][e] = 0.0f;
-        if constexpr (PF > 0) fma_down<WT, PF, CPT>(dv, 0, cnt, a_lds, acc2);
-        if constexpr (PFB > 0)
-            if (cnt > PF) fma_down<WT, PFB, CPT>(dvb, PF, cnt, a_lds, acc2);
-        for (int n0 = PF + PFB; n0 < cnt; n0 += PF2) {
-            u32x4 dv2[PF2][CPT];
-            rest = load_down<PF2, CPT>(dv2, rest, dn, p.bstride, q, nq, p.cd);
-            fma_down<WT, PF2, CPT>(dv2, n0, cnt, a_lds, acc2);
-        }
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            const int c = threadIdx.x + kThreads * j;
-            if (c < p.cd) {
-                const int o = c * E;
-                float4 *dst = reinterpret_cast<float4 *>(p.part1 + ((size_t)(o >> 4) * nq + q) * 16 + (o & 15));
-#pragma unroll
-                for (int k = 0; k < E / 4; ++k)
-                    dst[k] = make_float4(acc2[j][4 * k], acc2[j][4 * k + 1], acc2[j][4 * k + 2],
-                                         acc2[j][4 * k + 3]);
-            }
-        }
-    }
+    for (int c = 0; c < CPL1; ++c) none[c] = zero4();
+    owner_ffn1<WT, GATED, CPL1, false>(p, q, nq, valid, xs, a_lds, none, none, 0.0f, wave, lane);
 }
 
 // ---------------------------------------------------------------- exact mask, single token
@@ -1699,6 +1734,41 @@ hipError_t launch_fc2_sum(const LayerView &L, const float *resid, float *y, cons
     const dim3 grid(L.d / 16), blk(kThreads);
     ASF_LAUNCH(ASF_K_FC2, k_fc2_sum, grid, blk, (const float *)L.part1, L.nq, (const float *)L.b2,
                resid, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_ffn1(const LayerView &L, const float *x, const Trace *tr, hipStream_t s) {
+    ScoreParams p = {};
+    p.f = L.f;
+    p.ubits = L.ubits;
+    p.bundles = (const u32x4 *)L.bundles;
+    p.bstride = (size_t)L.nmat * L.cd;
+    p.cd = L.cd;
+    p.b1 = L.b1;
+    p.x = x;
+    p.d = L.d;
+    p.out = fc1_out(L);
+    p.dn_off = (L.nmat - 1) * L.cd;
+    p.part1 = L.part1;
+    const dim3 grid(L.nq), blk(kThreads);
+    const int cpl1 = fc1_cpl(L.cd);
+#define ASF_FF(WT, C1)                                                            \
+    if (L.gated) ASF_LAUNCH(ASF_K_FC1, (k_ffn1<WT, true, C1>), grid, blk, p);  \
+    else ASF_LAUNCH(ASF_K_FC1, (k_ffn1<WT, false, C1>), grid, blk, p);
+#define ASF_FFW(WT)                  \
+    switch (cpl1) {                  \
+    case 1: ASF_FF(WT, 1) break;     \
+    case 2: ASF_FF(WT, 2) break;     \
+    case 4: ASF_FF(WT, 4) break;     \
+    case 8: ASF_FF(WT, 8) break;     \
+    case 10: ASF_FF(WT, 10) break;   \
+    case 12: ASF_FF(WT, 12) break;   \
+    case 14: ASF_FF(WT, 14) break;   \
+    default: ASF_FF(WT, 16) break;   \
+    }
+    if (L.wtype == ASF_F16) { ASF_FFW(1) } else { ASF_FFW(0) }
+#undef ASF_FFW
+#undef ASF_FF
     return hipGetLastError();
 }
 

@@ -220,6 +220,16 @@ def bench_stack(args, asf, torch, np, wl, dev, stream):
         st.decode_raw(xs[t], 1, Y.data_ptr(), work.data_ptr(), sh_)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # the look-ahead form (layer l+1's set from layer l's input, predicted on
+    # a second stream while layer l's FC1/FC2 run), same tokens
+    for t in range(args.stack_warmup):
+        st.decode_lookahead_raw(xs[n + t], Y.data_ptr(), work.data_ptr(), sh_)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(n):
+        st.decode_lookahead_raw(xs[t], Y.data_ptr(), work.data_ptr(), sh_)
+    torch.cuda.synchronize()
+    elapsed_la = time.perf_counter() - t0
     # per-layer active counts of the same tokens (outside the timed region)
     counts = torch.zeros((n, len(layers)), dtype=torch.int32, device=dev)
     for t in range(n):
@@ -255,6 +265,8 @@ def bench_stack(args, asf, torch, np, wl, dev, stream):
         "algorithmic_bytes_per_token": tok_bytes,
         "effective_gbps": tok_bytes / (ms_tok * 1e-3) / 1e9,
         "effective_frac_of_peak": tok_bytes / (ms_tok * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "lookahead_tokens_per_s": n / elapsed_la,
+        "lookahead_ms_per_token": elapsed_la * 1e3 / n,
         "active_frac_by_layer": [round(float(k[l]) / shapes[l].f, 4) for l in range(len(layers))],
         "dense_ms_per_token": dense_ms,
         "dense_gbps": None if dense_ms is None else dense_bytes / (dense_ms * 1e-3) / 1e9,

@@ -162,13 +162,16 @@ asf_status asf_predict(const asf_layer *layer, const float *x, int32_t B,
  * with a_{b,i} the FC1 (gated) activation of neuron i for token b.
  *   x         DEVICE float32 [B][d_model]
  *   active    DEVICE int32 original ids (distinct, any order), or NULL to use
- *             the set of this layer's last asf_predict call
+ *             the layer's last set (of asf_predict, asf_decode_step or
+ *             asf_exact_ffn)
  *   n_active  DEVICE int32 [1] count of `active` (ignored when active == NULL;
  *             required otherwise)
  *   residual  DEVICE float32 [B][d_model] or NULL (= 0)
  *   y         DEVICE float32 [B][d_model]; may alias residual
  * For B > 1 every token computes every neuron of the set (the union of the
- * batch's sets when the set comes from asf_predict). */
+ * batch's sets when the set comes from asf_predict).  One token over the last
+ * set runs the decode step's own FC1 + FC2 kernels, so asf_predict followed
+ * by this call gives asf_decode_step's y bit for bit. */
 asf_status asf_sparse_ffn(const asf_layer *layer, const float *x, int32_t B,
                           const int32_t *active, const int32_t *n_active,
                           const float *residual, float *y, void *stream);
@@ -177,10 +180,9 @@ asf_status asf_sparse_ffn(const asf_layer *layer, const float *x, int32_t B,
  * the predicted union set, with no host round trip in between.  The optional
  * outputs are those of asf_predict.  One token: three kernels (predictor
  * layer 1; layer 2 + threshold + FC1 + each owner's FC2 into one row; the
- * sum of the owner rows); the set equals asf_predict's and y equals
- * asf_predict + asf_sparse_ffn up to the order of the fp32 additions.
- * B >= 2: the batched kernels, bit-identical to asf_predict followed by
- * asf_sparse_ffn with active == NULL.  Repeated calls give identical bits. */
+ * sum of the owner rows).  The results are bit-identical to asf_predict
+ * followed by asf_sparse_ffn with active == NULL, and repeated calls give
+ * identical bits. */
 asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
                            const float *residual, float *y, int32_t *active,
                            int32_t *n_active, void *stream);
@@ -202,6 +204,22 @@ asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
  * Asynchronous on `stream`; launches the decode step's kernels per layer. */
 asf_status asf_stack_decode(asf_layer *const *layers, int32_t n_layers, const float *x,
                             int32_t B, int32_t residual, float *y, float *work, void *stream);
+
+/* asf_stack_decode for one token with the look-ahead predictor (the
+ * asynchronous reading of DejaVu, "LLM模型之PowerInfer1.0" appendix "DejaVu",
+ * Eq. -2): layer l+1's set is predicted from layer l's INPUT, so its
+ * predictor streams on a second stream while layer l's FC1/FC2 run:
+ *   S_0 = predict_0(x_0);  S_l = predict_l(x_{l-1}) for l >= 1;
+ *   x_{l+1} = FFN_l(x_l over S_l) + (residual ? x_l : 0);  y = x_n
+ * Arguments as asf_stack_decode with B = 1.  The second stream and its
+ * events belong to the library (created on first use per device, kept until
+ * the process ends, default priority); the call returns once both streams
+ * are enqueued, and `stream` carries every result (it waits for the second
+ * stream's last prediction).  Per layer the results equal asf_predict on
+ * x_{l-1} followed by asf_sparse_ffn (active == NULL) on x_l, bit for bit. */
+asf_status asf_stack_decode_lookahead(asf_layer *const *layers, int32_t n_layers,
+                                      const float *x, int32_t residual, float *y, float *work,
+                                      void *stream);
 
 /* Dense comparator: the same FFN over all d_ffn neurons. */
 asf_status asf_dense_ffn_ref(const asf_layer *layer, const float *x, int32_t B,

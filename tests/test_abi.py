@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("asf_layer_storage_bytes", "asf_create_layer", "asf_destroy_layer", "asf_predict",
               "asf_sparse_ffn", "asf_dense_ffn_ref", "asf_decode_step", "asf_exact_ffn",
-              "asf_stack_decode", "asf_status_string"):
+              "asf_stack_decode", "asf_stack_decode_lookahead", "asf_profile_activations",
+              "asf_hot_first_table", "asf_status_string"):
         assert n in names
 
 

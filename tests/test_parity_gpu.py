@@ -16,9 +16,6 @@ from gpu_util import MARGIN, TOL, asf, check_set, need_gpu, rel_l2, to_dev
 
 pytestmark = pytest.mark.gpu
 
-# two fp32-accumulated sums of the same products in different orders
-REORDER_TOL = 1e-5
-
 
 def _run_tokens(orc, L, x, layer, label, check_dense=True, theta=0.0):
     """Per token: predict, decode_step, sparse_ffn on the GPU set, dense."""
@@ -40,11 +37,7 @@ def _run_tokens(orc, L, x, layer, label, check_dense=True, theta=0.0):
         k = int(n.item())
         ids = active[:k].cpu().numpy()
         assert int(n2.item()) == k and np.array_equal(a2[:k].cpu().numpy(), ids)
-        # the fused single-token step adds the same fp32 products in another
-        # order (owner rows, then owners) than sparse_ffn's FC2: equal up to
-        # fp32 reordering
-        e12 = rel_l2(y2.cpu().numpy()[0], y1.cpu().numpy()[0])
-        assert e12 <= REORDER_TOL, "decode_step vs predict + sparse_ffn: rel-L2 %.3g" % e12
+        assert torch.equal(y1, y2), "decode_step differs from predict + sparse_ffn"
         amb += check_set(ids, s_orc[t], theta, L.perm, "%s token %d" % (label, t))
         y_orc = orc.ffn(L.w_up, L.w_down, x[t], ids, b1=L.b1, b2=L.b2, W_gate=L.w_gate)
         e = max(rel_l2(y1.cpu().numpy()[0], y_orc[0]), rel_l2(y2.cpu().numpy()[0], y_orc[0]))
@@ -234,8 +227,8 @@ def test_deterministic_repeat():
                                          (5120, 4160, 1024, False), (7168, 2048, 2048, False)])
 def test_decode_step_tiling_variants(orc, d, f, H, gated):
     """The decode-step kernels (fp16, B = 1) across their register-tiling
-    variants (d and H classes): equal to predict + sparse_ffn up to fp32
-    reordering, oracle parity."""
+    variants (d and H classes): same bits as predict + sparse_ffn, oracle
+    parity."""
     need_gpu()
     _, sh = wl.CONFIGS["llama7b_gated_relu" if gated else "opt6.7b_ffn"]
     L = wl.make_layer(wl.scaled_shape(sh, d, f, H), 500 + d + f)

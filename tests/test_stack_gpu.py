@@ -5,6 +5,9 @@
 * Each layer's set and output agree with the oracle on that layer's actual
   input (the previous layer's GPU output): sets bit-exact beyond the 1e-3
   margin, per-token relative L2 <= 5e-3 (fp16 weights).
+* The look-ahead form (layer l's set predicted from layer l-1's input, on a
+  second stream) equals asf_predict + asf_sparse_ffn chained by hand on those
+  inputs, bit for bit, with oracle parity per layer.
 * The full 48-layer OPT-30B-shaped stack (7168x28672 fp16, predictors of
   512/1024/2048 hidden, ~40 GB resident) runs end to end; the oracle checks
   layers 0, 23 and 47 (their weights are read back from the device).
@@ -82,6 +85,49 @@ def test_small_stack_equals_chained_steps(orc, residual):
     assert torch.equal(inplace, ref)
 
 
+@pytest.mark.parametrize("residual", [False, True])
+def test_lookahead_stack_equals_chained_calls(orc, residual):
+    """Look-ahead reading: layer l's set is predicted from layer l-1's input
+    (layer 0's from its own).  The two-stream call equals asf_predict on
+    x_{l-1} then asf_sparse_ffn on x_l, chained by hand, bit for bit; each
+    layer's set and output agree with the oracle on those inputs."""
+    need_gpu()
+    d, f = 512, 2048
+    shapes = [wl.LayerShape(d, f, H, rho, "f16")
+              for H, rho in ((64, 0.03), (128, 0.08), (256, 0.15), (128, 0.10), (64, 0.05))]
+    layers, host = _device_layers(shapes, 760, keep=range(len(shapes)))
+    st = asf().Stack(layers, residual=residual)
+    x = wl.make_tokens(d, 3, 761)
+    for t in range(x.shape[0]):
+        xt = to_dev(x[t:t + 1])
+        y = st.decode_lookahead(xt)
+        prev, cur = xt, xt
+        for l, lay in enumerate(layers):
+            act = torch.empty(f, dtype=torch.int32, device="cuda")
+            n = torch.empty(1, dtype=torch.int32, device="cuda")
+            lay.predict(prev, active=act, n_active=n)
+            nxt = lay.sparse_ffn(cur, residual=cur if residual else None)
+            torch.cuda.synchronize()
+            ids = act[:int(n.item())].cpu().numpy()
+            xin, xpred = cur.cpu().numpy()[0], prev.cpu().numpy()[0]
+            L = host[l]
+            _, s_orc, _ = orc.predict(L.p1, L.c1, L.p2, L.c2, xpred[None, :])
+            check_set(ids, s_orc[0], 0.0, L.perm, "look-ahead layer %d token %d" % (l, t))
+            yl = nxt.cpu().numpy()[0] - (xin if residual else 0.0)
+            y_orc = orc.ffn(L.w_up, L.w_down, xin, ids, b1=L.b1, b2=L.b2)
+            assert rel_l2(yl, y_orc[0]) <= TOL["f16"], (l, t)
+            prev, cur = cur, nxt
+        assert torch.equal(y, cur), "look-ahead stack differs from the chained calls"
+    # in place (y == x), and a repeat gives the same bits
+    xt = to_dev(x[:1])
+    ref = st.decode_lookahead(xt)
+    again = st.decode_lookahead(xt)
+    inplace = xt.clone()
+    st.decode_lookahead(inplace, out=inplace)
+    torch.cuda.synchronize()
+    assert torch.equal(again, ref) and torch.equal(inplace, ref)
+
+
 def test_stack_argument_errors():
     need_gpu()
     m = asf()
@@ -99,6 +145,10 @@ def test_stack_argument_errors():
     buf = torch.zeros((2, d), device="cuda")
     with pytest.raises(m.AsfError):
         st.decode(buf[:1], out=buf[1:], work=buf[:1])           # work overlaps x
+    with pytest.raises(m.AsfError):
+        m.Stack([layers[0], layers[0]]).decode_lookahead(x)     # a layer twice
+    with pytest.raises(m.AsfError):
+        st.decode_lookahead(buf[:1], out=buf[1:], work=buf[:1])
 
 
 def test_opt30b_stack_full_size(orc):
