@@ -309,3 +309,26 @@ def test_batched_full_size(orc):
     for B, off in ((4, 0), (32, 4)):
         _batched_check(orc, L, X[off:off + B], lay, "opt13b B%d" % B, check_dense=(B == 4),
                        user_list=(B == 32))
+
+
+def test_max_ffn_size(orc):
+    """d_ffn at its maximum (65536: 1024 owners, 1024 mask words): the
+    single-token step, the batched step at max_batch = 32 and the exact-mask
+    mode against the oracle."""
+    need_gpu()
+    _, sh = wl.CONFIGS["opt6.7b_ffn"]
+    L = wl.make_layer(wl.scaled_shape(sh, 512, 65536, 128), 65536)
+    lay = asf().layer_from_numpy(L, max_batch=32)
+    x = wl.make_tokens(512, 32, 655)
+    worst = _run_tokens(orc, L, x[:2], lay, "f=65536", check_dense=False)
+    assert worst <= TOL["f16"]
+    _batched_check(orc, L, x, lay, "f=65536 B=32", check_dense=False, user_list=False)
+    pre, _ = orc.true_mask(L.w_up, x[:1], b1=L.b1)
+    act = torch.empty(L.shape.f, dtype=torch.int32, device="cuda")
+    n = torch.empty(1, dtype=torch.int32, device="cuda")
+    y = lay.exact_ffn(to_dev(x[:1]), active=act, n_active=n)
+    torch.cuda.synchronize()
+    ids = act[:int(n.item())].cpu().numpy()
+    check_set(ids, pre[0], 0.0, L.perm, "f=65536 exact")
+    y_orc = orc.dense_ffn(L.w_up, L.w_down, x[:1], b1=L.b1, b2=L.b2)
+    assert rel_l2(y.cpu().numpy()[0], y_orc[0]) <= TOL["f16"]
