@@ -346,7 +346,7 @@ class Stack:
 
     def decode_lookahead(self, x, out=None, work=None, stream=None):
         """asf_stack_decode_lookahead: one token, layer l+1's set predicted
-        from layer l's input on a second stream."""
+        from layer l's input, in the same launches as layer l's FFN."""
         if x.dim() == 1:
             x = x.unsqueeze(0)
         if out is None:

@@ -6,9 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
-#include <mutex>
 #include <new>
-#include <vector>
 
 #include "asf_internal.h"
 
@@ -291,44 +289,6 @@ asf_status asf_hot_first_table(const uint32_t *counts, int32_t d_ffn, int32_t *t
     return ASF_OK;
 }
 
-// A second stream and a pool of events per device for the look-ahead stack,
-// created on first use (host-side objects, default stream priority) and kept
-// until the process ends.  Enqueueing holds the lock, so calls from several
-// host threads do not share an event while it is in use.
-namespace {
-struct SideResources {
-    hipStream_t stream = nullptr;
-    std::vector<hipEvent_t> events;
-};
-constexpr int kMaxDevices = 64;
-std::mutex g_side_mutex;
-SideResources g_side[kMaxDevices];
-
-hipError_t side_resources(int n_events, hipStream_t *s2, hipEvent_t **ev) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    SideResources &r = g_side[dev];
-    if (!r.stream) {
-        e = hipStreamCreateWithFlags(&r.stream, hipStreamNonBlocking);
-        if (e != hipSuccess) {
-            r.stream = nullptr;
-            return e;
-        }
-    }
-    while ((int)r.events.size() < n_events) {
-        hipEvent_t h;
-        e = hipEventCreateWithFlags(&h, hipEventDisableTiming);
-        if (e != hipSuccess) return e;
-        r.events.push_back(h);
-    }
-    *s2 = r.stream;
-    *ev = r.events.data();
-    return hipSuccess;
-}
-}  // namespace
-
 static asf_status check_stack(asf_layer *const *layers, int32_t n_layers, const float *x,
                               int32_t B, int32_t residual, const float *y, const float *work) {
     if (!layers || n_layers < 1 || !x || !y || (residual != 0 && residual != 1))
@@ -384,41 +344,23 @@ asf_status asf_stack_decode_lookahead(asf_layer *const *layers, int32_t n_layers
     const asf_status st = check_stack(layers, n_layers, x, 1, residual, y, work);
     if (st != ASF_OK) return st;
     hipStream_t s = (hipStream_t)stream;
-    std::lock_guard<std::mutex> lock(g_side_mutex);
-    hipStream_t s2;
-    hipEvent_t *ev;
-    if (side_resources(2 * n_layers + 2, &s2, &ev) != hipSuccess) return ASF_ERR_HIP;
-    hipEvent_t *ev_in = ev, *ev_set = ev + n_layers + 1;
-    // layer 0's set from its own input; layer l+1's from layer l's input, on
-    // the second stream while layer l's FC1/FC2 run on `stream`
-    const float *in = x;
+    // layer 0's set from its own input
     {
         const LayerView &v = layers[0]->v;
         if (launch_pred_l1(v, x, 1, layers[0]->tr(), s) != hipSuccess ||
             launch_score(v, x, 1, false, layers[0]->tr(), s) != hipSuccess)
             return ASF_ERR_HIP;
     }
+    // layer l: its FC1/FC2 rows beside layer l+1's predictor layer 1 (both
+    // on layer l's input), then layer l+1's scores beside layer l's output
+    const float *in = x;
     for (int32_t l = 0; l < n_layers; ++l) {
         const LayerView &v = layers[l]->v;
+        const LayerView *vn = l + 1 < n_layers ? &layers[l + 1]->v : nullptr;
         float *out = ((n_layers - 1 - l) % 2 == 0) ? y : work;
-        if (l + 1 < n_layers) {
-            const LayerView &vn = layers[l + 1]->v;
-            const asf::Trace *trn = layers[l + 1]->tr();
-            if (hipEventRecord(ev_in[l], s) != hipSuccess ||
-                hipStreamWaitEvent(s2, ev_in[l], 0) != hipSuccess ||
-                launch_pred_l1(vn, in, 1, trn, s2) != hipSuccess ||
-                launch_score(vn, in, 1, false, trn, s2) != hipSuccess ||
-                hipEventRecord(ev_set[l + 1], s2) != hipSuccess)
-                return ASF_ERR_HIP;
-        }
-        // layer l's set (predicted on the second stream for l >= 1); layer 0
-        // writing in place (y == x) also waits for layer 1's predictor to
-        // have read x
-        const bool inplace = l == 0 && (const float *)out == in && n_layers > 1;
-        if ((l >= 1 || inplace) && hipStreamWaitEvent(s, ev_set[l >= 1 ? l : 1], 0) != hipSuccess)
-            return ASF_ERR_HIP;
-        if (launch_ffn1(v, in, layers[l]->tr(), s) != hipSuccess ||
-            launch_fc2_sum(v, residual ? in : nullptr, out, layers[l]->tr(), s) != hipSuccess)
+        if (launch_ffn1_pred1(v, vn, in, layers[l]->tr(), s) != hipSuccess ||
+            launch_score1_fc2sum(vn, v, residual ? in : nullptr, out, layers[l]->tr(), s) !=
+                hipSuccess)
             return ASF_ERR_HIP;
         in = out;
     }

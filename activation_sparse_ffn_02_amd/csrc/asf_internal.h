@@ -133,6 +133,13 @@ hipError_t launch_fc2_sum(const LayerView &L, const float *resid, float *y, cons
 // the owner FC2 rows, as the decode step does after its ballot (then
 // launch_fc2_sum)
 hipError_t launch_ffn1(const LayerView &L, const float *x, const Trace *tr, hipStream_t s);
+// one-stream look-ahead stack: layer L's FFN over its set with predictor
+// layer 1 of layer N on the same input x, then layer N's scores with layer
+// L's owner-row sum (N null: layer L's kernels alone)
+hipError_t launch_ffn1_pred1(const LayerView &L, const LayerView *N, const float *x,
+                             const Trace *tr, hipStream_t s);
+hipError_t launch_score1_fc2sum(const LayerView *N, const LayerView &L, const float *resid,
+                                float *y, const Trace *tr, hipStream_t s);
 // exact mask, one token: the pre-activation of every neuron, the true set
 // (z + b1 > 0) into the owner words, and the owner FC2 rows (then
 // launch_fc2_sum)

@@ -26,7 +26,9 @@
 // The other entry points use the same building blocks: FC1 over a set
 // (k_fc1_1 for one token, k_fc1 for token chunks of 4) and the grouped FC2
 // (k_fc2: 16 output slices x 16 neuron groups, the last group at a slice
-// sums the partials in fixed order).
+// sums the partials in fixed order).  The look-ahead stack runs two of the
+// per-workgroup bodies in one grid (k_ffn1_pred1, k_score1_fc2sum), so a
+// layer takes two launches and the next layer's predictor fills the tails.
 //
 // Weight reads are whole 16-byte chunks of contiguous rows (a wave load
 // instruction covers 1 KiB); an active neuron's up row and down column sit in
@@ -300,76 +302,75 @@ __device__ __forceinline__ float dot_chunk_lds(const u32x4 w, const float *vs, i
     return acc;
 }
 
-// Predictor layer 1 for one token: WPR waves share a row of P1 (wave part p
-// takes chunks p*64 + lane + 64*WPR*i); x comes from LDS.  Sums: per lane in
-// chunk order, butterfly over the wave, then the parts in order, then c1,
-// then ReLU.
-template <int WT, int CPL>
-__global__ __launch_bounds__(kThreads) void k_pred1(const u32x4 *__restrict__ P1,
-                                                    const float *__restrict__ c1,
-                                                    const float *__restrict__ x, int d, int H,
-                                                    int wpr, float *__restrict__ h) {
+// Predictor layer 1 for one token, workgroup `blk`: WPR waves share a row of
+// P1 (wave part p takes chunks p*64 + lane + 64*WPR*i, i < kPred1Cpl, WPR the
+// smallest power of two that covers the row so), with the x chunks loaded
+// beside the weight chunks.  Sums: per lane in chunk order, butterfly over
+// the wave, then the parts in order, then c1, then ReLU.
+constexpr int kPred1Cpl = 4;
+
+struct Pred1Args {
+    const u32x4 *P1;
+    const float *c1;
+    const float *x;
+    int d, H, wpr;
+    float *h;
+};
+
+template <int WT>
+__device__ __forceinline__ void pred1_block(const Pred1Args &a, int blk) {
     constexpr int E = Elt<WT>::E;
-    // up to 8 chunks per lane the x chunks travel with the weight chunks in
-    // registers; beyond that x is staged in LDS
-    constexpr bool XLDS = CPL > 8;
-    __shared__ float xs[XLDS ? kMaxDLds : 4];
+    constexpr int CPL = kPred1Cpl;
     __shared__ float red[kWaves];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wpr = a.wpr, H = a.H;
     const int rpw = kWaves / wpr;
-    const int row = blockIdx.x * rpw + wave / wpr, part = wave % wpr;
-    const int C = d / E;
+    const int row = blk * rpw + wave / wpr, part = wave % wpr;
+    const int C = a.d / E;
     const bool live = row < H;
     const int rowc = live ? row : H - 1;
     // the bias of the row this thread finishes (threads < rpw), loaded early
-    const int rfin = blockIdx.x * rpw + (int)threadIdx.x;
-    const float c1v = c1[rfin < H ? rfin : H - 1];
-    float4 xv[XLDS ? 4 : 1];
-    if constexpr (XLDS) stage_load<4>(x, d, xv);
+    const int rfin = blk * rpw + (int)threadIdx.x;
+    const float c1v = a.c1[rfin < H ? rfin : H - 1];
     u32x4 w[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = part * 64 + lane + 64 * wpr * i;
-        w[i] = P1[(size_t)rowc * C + (c < C ? c : C - 1)];
+        w[i] = a.P1[(size_t)rowc * C + (c < C ? c : C - 1)];
+    }
+    float xr[CPL][E];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = part * 64 + lane + 64 * wpr * i;
+        load_f32<E>(a.x + (size_t)(c < C ? c : C - 1) * E, xr[i]);
     }
     float acc = 0.0f;
-    if constexpr (XLDS) {
-        stage_store<4>(xs, xv);
-        __syncthreads();
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int c = part * 64 + lane + 64 * wpr * i;
-            if (live && c < C) acc = dot_chunk_lds<WT>(w[i], xs, c, acc);
-        }
-    } else {
-        float xr[CPL][E];
+    for (int i = 0; i < CPL; ++i) {
+        const int c = part * 64 + lane + 64 * wpr * i;
+        if (live && c < C) {
+            float wv[E];
+            unpack<WT>(w[i], wv);
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int c = part * 64 + lane + 64 * wpr * i;
-            load_f32<E>(x + (size_t)(c < C ? c : C - 1) * E, xr[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int c = part * 64 + lane + 64 * wpr * i;
-            if (live && c < C) {
-                float wv[E];
-                unpack<WT>(w[i], wv);
-#pragma unroll
-                for (int e = 0; e < E; ++e) acc = fmaf(wv[e], xr[i][e], acc);
-            }
+            for (int e = 0; e < E; ++e) acc = fmaf(wv[e], xr[i][e], acc);
         }
     }
     const float sum = wave_sum(acc);
     if (lane == 0) red[wave] = sum;
     __syncthreads();
     if ((int)threadIdx.x < rpw) {
-        const int r = blockIdx.x * rpw + threadIdx.x;
+        const int r = blk * rpw + threadIdx.x;
         if (r < H) {
             float t = 0.0f;
             for (int pp = 0; pp < wpr; ++pp) t += red[threadIdx.x * wpr + pp];
-            h[r] = fmaxf(t + c1v, 0.0f);
+            a.h[r] = fmaxf(t + c1v, 0.0f);
         }
     }
+}
+
+template <int WT>
+__global__ __launch_bounds__(kThreads) void k_pred1(Pred1Args a) {
+    pred1_block<WT>(a, blockIdx.x);
 }
 
 // ---------------------------------------------------------------- predictor layer 2
@@ -866,8 +867,7 @@ __device__ __forceinline__ void owner_ffn1(const ScoreParams &p, int q, int nq, 
 // With at most 128 VGPRs (4 waves per SIMD) two workgroups fit on a CU, so
 // up to 512 owners (f <= 32768) run in one round.
 template <int WT, int CPL2, bool FC1, bool GATED, int CPL1, bool SPEC>
-__global__ __launch_bounds__(kThreads) __attribute__((
-    amdgpu_waves_per_eu(Fc1Regs<GATED, CPL1, SPEC>::waves_per_eu))) void k_score1(ScoreParams p) {
+__device__ __forceinline__ void score1_block(const ScoreParams &p, int q, int nq) {
     constexpr int E = Elt<WT>::E;
     constexpr int RG = kL2Rows / CPL2;      // rows per group
     constexpr int NG = CPL2;                // groups per wave
@@ -876,7 +876,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((
     __shared__ uint32_t bits_lds[kWaves];
     __shared__ uint64_t u_lds;
     __shared__ float a_lds[FC1 ? kRowsPerWG : 1];
-    const int q = blockIdx.x, nq = gridDim.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int C2 = p.H / E;
     // staging loads first: their waits then leave the weight loads in flight
@@ -973,17 +972,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((
                                           lane);
 }
 
+template <int WT, int CPL2, bool FC1, bool GATED, int CPL1, bool SPEC>
+__global__ __launch_bounds__(kThreads) __attribute__((
+    amdgpu_waves_per_eu(Fc1Regs<GATED, CPL1, SPEC>::waves_per_eu))) void k_score1(ScoreParams p) {
+    score1_block<WT, CPL2, FC1, GATED, CPL1, SPEC>(p, blockIdx.x, gridDim.x);
+}
+
 // FC1 + FC2 rows of one token over the set of the layer's last prediction
 // (its owner words), for the set predicted ahead of time (the look-ahead
 // stack) and for asf_sparse_ffn of one token over the last prediction: the
 // same per-owner work as k_score1 after its ballot, so the results match
 // the decode step bit for bit.
 template <int WT, bool GATED, int CPL1>
-__global__ __launch_bounds__(kThreads) __attribute__((
-    amdgpu_waves_per_eu(Fc1Regs<GATED, CPL1>::waves_per_eu))) void k_ffn1(ScoreParams p) {
+__device__ __forceinline__ void ffn1_block(const ScoreParams &p, int q, int nq) {
     __shared__ float xs[kMaxDLds];
     __shared__ float a_lds[kRowsPerWG];
-    const int q = blockIdx.x, nq = gridDim.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     float4 xv[4];
     stage_load<4>(p.x, p.d, xv);
@@ -995,6 +998,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((
 #pragma unroll
     for (int c = 0; c < CPL1; ++c) none[c] = zero4();
     owner_ffn1<WT, GATED, CPL1, false>(p, q, nq, valid, xs, a_lds, none, none, 0.0f, wave, lane);
+}
+
+template <int WT, bool GATED, int CPL1>
+__global__ __launch_bounds__(kThreads) __attribute__((
+    amdgpu_waves_per_eu(Fc1Regs<GATED, CPL1>::waves_per_eu))) void k_ffn1(ScoreParams p) {
+    ffn1_block<WT, GATED, CPL1>(p, blockIdx.x, gridDim.x);
 }
 
 // ---------------------------------------------------------------- exact mask, single token
@@ -1320,12 +1329,22 @@ __global__ __launch_bounds__(kThreads) void k_fc2(Fc2Params p) {
 // tree), then b2, then the residual.
 constexpr int kSumQ = kMaxFfn / kRowsPerWG / (kThreads / 4);   // owners per thread, at most
 
-__global__ __launch_bounds__(kThreads) void k_fc2_sum(const float *__restrict__ part, int nq,
-                                                      const float *__restrict__ b2,
-                                                      const float *__restrict__ resid,
-                                                      float *__restrict__ y) {
+struct Fc2SumArgs {
+    const float *part;
+    int nq;
+    const float *b2;
+    const float *resid;
+    float *y;
+};
+
+__device__ __forceinline__ void fc2_sum_block(const Fc2SumArgs &a, int s) {
     __shared__ float4 red[kThreads];
-    const int s = blockIdx.x, tid = threadIdx.x;
+    const float *__restrict__ part = a.part;
+    const int nq = a.nq;
+    const float *__restrict__ b2 = a.b2;
+    const float *__restrict__ resid = a.resid;
+    float *__restrict__ y = a.y;
+    const int tid = threadIdx.x;
     const int c = tid & 3, g = tid >> 2;
     const float4 *src = reinterpret_cast<const float4 *>(part + (size_t)s * nq * 16);
     const int o = tid & 15;
@@ -1359,6 +1378,34 @@ __global__ __launch_bounds__(kThreads) void k_fc2_sum(const float *__restrict__ 
         const float hi = __shfl_down(sum, 32, 64);
         if (tid < 16) y[16 * s + o] = (sum + hi) + bv + rv;
     }
+}
+
+__global__ __launch_bounds__(kThreads) void k_fc2_sum(Fc2SumArgs a) { fc2_sum_block(a, blockIdx.x); }
+
+// ---------------------------------------------------------------- look-ahead stack on one stream
+// With layer l + 1's set predicted from layer l's input, each layer of the
+// stack is two launches, each running two kinds of workgroup side by side:
+//   k_ffn1_pred1      workgroups below nq: layer l's FC1 + owner FC2 rows
+//                     over its set (ffn1_block); the rest: predictor layer 1
+//                     of layer l + 1 on the same input (pred1_block)
+//   k_score1_fc2sum   workgroups below nq: layer l + 1's scores and owner
+//                     words (score1_block); the rest: layer l's output from
+//                     its owner rows (fc2_sum_block)
+// The long-running kind comes first in each grid and the short one fills
+// the CUs as they free up.  Each workgroup does exactly what it does in the
+// separate kernels, so results are theirs bit for bit.
+template <int WT, bool GATED, int CPL1>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    Fc1Regs<GATED, CPL1>::waves_per_eu))) void k_ffn1_pred1(ScoreParams p, int nq, Pred1Args a) {
+    if ((int)blockIdx.x < nq) ffn1_block<WT, GATED, CPL1>(p, blockIdx.x, nq);
+    else pred1_block<WT>(a, blockIdx.x - nq);
+}
+
+template <int WT, int CPL2>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    Fc1Regs<false, 1>::waves_per_eu))) void k_score1_fc2sum(ScoreParams p, int nq, Fc2SumArgs a) {
+    if ((int)blockIdx.x < nq) score1_block<WT, CPL2, false, false, 1, false>(p, blockIdx.x, nq);
+    else fc2_sum_block(a, blockIdx.x - nq);
 }
 
 // ---------------------------------------------------------------- activation profiler
@@ -1518,39 +1565,31 @@ static void l1_shape(const LayerView &L, int *wpr, int *cpl) {
     *cpl = pow2_at_least((L.cd + 64 * w - 1) / (64 * w));
 }
 
-// single-token form: rows per workgroup R = ceil(H / 256) (power of two, <= 8)
-// so that about 256 workgroups cover P1, waves per row 8 / R, at most 16
-// chunks per lane
-static void pred1_shape(const LayerView &L, int *wpr, int *cpl) {
-    int R = pow2_at_least((L.H + 255) / 256);
-    if (R > kWaves) R = kWaves;
-    int w = kWaves / R;
-    while (w < kWaves && (L.cd + 64 * w - 1) / (64 * w) > 16) w *= 2;
-    *wpr = w;
-    *cpl = pow2_at_least((L.cd + 64 * w - 1) / (64 * w));
+// single-token form: waves per row = the smallest power of two (<= 8) for
+// which a lane takes at most kPred1Cpl chunks; rows per workgroup 8 / that
+static int pred1_wpr(const LayerView &L) {
+    int w = 1;
+    while (w < kWaves && (L.cd + 64 * w - 1) / (64 * w) > kPred1Cpl) w *= 2;
+    return w;
+}
+
+static Pred1Args pred1_args(const LayerView &L, const float *x) {
+    return Pred1Args{(const u32x4 *)L.p1, L.c1, x, L.d, L.H, pred1_wpr(L), L.h};
+}
+
+static int pred1_blocks(const LayerView &L) {
+    const int rpw = kWaves / pred1_wpr(L);
+    return (L.H + rpw - 1) / rpw;
 }
 
 hipError_t launch_pred_l1(const LayerView &L, const float *x, int B, const Trace *tr,
                           hipStream_t s) {
     const u32x4 *P1 = (const u32x4 *)L.p1;
     if (B == 1) {
-        int wpr, cpl;
-        pred1_shape(L, &wpr, &cpl);
-        const int rpw = kWaves / wpr;
-        const dim3 grid((L.H + rpw - 1) / rpw), blk(kThreads);
-#define ASF_P1(WT, CPL)                                                                        \
-    ASF_LAUNCH(ASF_K_PRED_L1, (k_pred1<WT, CPL>), grid, blk, P1, L.c1, x, L.d, L.H, wpr, L.h);
-#define ASF_P1W(WT)                  \
-    switch (cpl) {                   \
-    case 1: ASF_P1(WT, 1) break;     \
-    case 2: ASF_P1(WT, 2) break;     \
-    case 4: ASF_P1(WT, 4) break;     \
-    case 8: ASF_P1(WT, 8) break;     \
-    default: ASF_P1(WT, 16) break;   \
-    }
-        if (L.wtype == ASF_F16) { ASF_P1W(1) } else { ASF_P1W(0) }
-#undef ASF_P1W
-#undef ASF_P1
+        const dim3 grid(pred1_blocks(L)), blk(kThreads);
+        const Pred1Args a = pred1_args(L, x);
+        if (L.wtype == ASF_F16) ASF_LAUNCH(ASF_K_PRED_L1, k_pred1<1>, grid, blk, a);
+        else ASF_LAUNCH(ASF_K_PRED_L1, k_pred1<0>, grid, blk, a);
         return hipGetLastError();
     }
     if (L.wtype == ASF_F16) return launch_pred_mm(L, x, B, tr, s);
@@ -1588,9 +1627,9 @@ static int fc1_cpl(int cd) {
 
 static Fc1Out fc1_out(const LayerView &L) { return Fc1Out{L.vbits, L.lslot, L.la, L.max_batch}; }
 
-hipError_t launch_score(const LayerView &L, const float *x, int B, bool fc1, const Trace *tr,
-                        hipStream_t s) {
-    ScoreParams p;
+// parameters of the owner kernels (scores, FC1, the owner FC2 rows) of layer L
+static ScoreParams score_params(const LayerView &L, const float *x, int B) {
+    ScoreParams p = {};
     p.p2 = (const u32x4 *)L.p2;
     p.c2 = L.c2;
     p.h = L.h;
@@ -1609,6 +1648,12 @@ hipError_t launch_score(const LayerView &L, const float *x, int B, bool fc1, con
     p.out = fc1_out(L);
     p.dn_off = (L.nmat - 1) * L.cd;
     p.part1 = L.part1;
+    return p;
+}
+
+hipError_t launch_score(const LayerView &L, const float *x, int B, bool fc1, const Trace *tr,
+                        hipStream_t s) {
+    const ScoreParams p = score_params(L, x, B);
     const int cpl2 = pow2_at_least((L.ch + 63) / 64);
     const dim3 grid(L.nq), blk(kThreads);
     if (B == 1) {
@@ -1732,24 +1777,13 @@ hipError_t launch_fc1(const LayerView &L, const float *x, int B, int mode, const
 hipError_t launch_fc2_sum(const LayerView &L, const float *resid, float *y, const Trace *tr,
                           hipStream_t s) {
     const dim3 grid(L.d / 16), blk(kThreads);
-    ASF_LAUNCH(ASF_K_FC2, k_fc2_sum, grid, blk, (const float *)L.part1, L.nq, (const float *)L.b2,
-               resid, y);
+    const Fc2SumArgs a{L.part1, L.nq, L.b2, resid, y};
+    ASF_LAUNCH(ASF_K_FC2, k_fc2_sum, grid, blk, a);
     return hipGetLastError();
 }
 
 hipError_t launch_ffn1(const LayerView &L, const float *x, const Trace *tr, hipStream_t s) {
-    ScoreParams p = {};
-    p.f = L.f;
-    p.ubits = L.ubits;
-    p.bundles = (const u32x4 *)L.bundles;
-    p.bstride = (size_t)L.nmat * L.cd;
-    p.cd = L.cd;
-    p.b1 = L.b1;
-    p.x = x;
-    p.d = L.d;
-    p.out = fc1_out(L);
-    p.dn_off = (L.nmat - 1) * L.cd;
-    p.part1 = L.part1;
+    const ScoreParams p = score_params(L, x, 1);
     const dim3 grid(L.nq), blk(kThreads);
     const int cpl1 = fc1_cpl(L.cd);
 #define ASF_FF(WT, C1)                                                            \
@@ -1772,21 +1806,59 @@ hipError_t launch_ffn1(const LayerView &L, const float *x, const Trace *tr, hipS
     return hipGetLastError();
 }
 
+hipError_t launch_ffn1_pred1(const LayerView &L, const LayerView *N, const float *x,
+                             const Trace *tr, hipStream_t s) {
+    if (!N || N->wtype != L.wtype) {
+        const hipError_t e = launch_ffn1(L, x, tr, s);
+        if (e != hipSuccess || !N) return e;
+        return launch_pred_l1(*N, x, 1, nullptr, s);
+    }
+    const ScoreParams p = score_params(L, x, 1);
+    const Pred1Args a = pred1_args(*N, x);
+    const dim3 grid(L.nq + pred1_blocks(*N)), blk(kThreads);
+    const int cpl1 = fc1_cpl(L.cd);
+#define ASF_FP(WT, C1)                                                                        \
+    if (L.gated) ASF_LAUNCH(ASF_K_FC1, (k_ffn1_pred1<WT, true, C1>), grid, blk, p, L.nq, a);  \
+    else ASF_LAUNCH(ASF_K_FC1, (k_ffn1_pred1<WT, false, C1>), grid, blk, p, L.nq, a);
+#define ASF_FPW(WT)                  \
+    switch (cpl1) {                  \
+    case 1: ASF_FP(WT, 1) break;     \
+    case 2: ASF_FP(WT, 2) break;     \
+    case 4: ASF_FP(WT, 4) break;     \
+    case 8: ASF_FP(WT, 8) break;     \
+    case 10: ASF_FP(WT, 10) break;   \
+    case 12: ASF_FP(WT, 12) break;   \
+    case 14: ASF_FP(WT, 14) break;   \
+    default: ASF_FP(WT, 16) break;   \
+    }
+    if (L.wtype == ASF_F16) { ASF_FPW(1) } else { ASF_FPW(0) }
+#undef ASF_FPW
+#undef ASF_FP
+    return hipGetLastError();
+}
+
+hipError_t launch_score1_fc2sum(const LayerView *N, const LayerView &L, const float *resid,
+                                float *y, const Trace *tr, hipStream_t s) {
+    if (!N) return launch_fc2_sum(L, resid, y, tr, s);
+    const ScoreParams p = score_params(*N, nullptr, 1);
+    const Fc2SumArgs a{L.part1, L.nq, L.b2, resid, y};
+    const dim3 grid(N->nq + L.d / 16), blk(kThreads);
+    const int cpl2 = pow2_at_least((N->ch + 63) / 64);
+#define ASF_SF(WT)                                                                                  \
+    switch (cpl2) {                                                                                 \
+    case 1: ASF_LAUNCH(ASF_K_FC2, (k_score1_fc2sum<WT, 1>), grid, blk, p, N->nq, a); break;      \
+    case 2: ASF_LAUNCH(ASF_K_FC2, (k_score1_fc2sum<WT, 2>), grid, blk, p, N->nq, a); break;      \
+    default: ASF_LAUNCH(ASF_K_FC2, (k_score1_fc2sum<WT, 4>), grid, blk, p, N->nq, a); break;     \
+    }
+    if (N->wtype == ASF_F16) { ASF_SF(1) } else { ASF_SF(0) }
+#undef ASF_SF
+    return hipGetLastError();
+}
+
 hipError_t launch_exact1(const LayerView &L, const float *x, bool mask_only, const Trace *tr,
                          hipStream_t s) {
-    ScoreParams p = {};
-    p.f = L.f;
-    p.wbits = L.wbits;
-    p.ubits = L.ubits;
-    p.bundles = (const u32x4 *)L.bundles;
-    p.bstride = (size_t)L.nmat * L.cd;
-    p.cd = L.cd;
-    p.b1 = L.b1;
-    p.x = x;
-    p.d = L.d;
-    p.out = fc1_out(L);
-    p.dn_off = (L.nmat - 1) * L.cd;
-    p.part1 = mask_only ? nullptr : L.part1;
+    ScoreParams p = score_params(L, x, 1);
+    if (mask_only) p.part1 = nullptr;
     const dim3 grid(L.nq), blk(kThreads);
     const int cpl1 = fc1_cpl(L.cd);
 #define ASF_EX(WT, C1)                                                              \

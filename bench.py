@@ -220,8 +220,8 @@ def bench_stack(args, asf, torch, np, wl, dev, stream):
         st.decode_raw(xs[t], 1, Y.data_ptr(), work.data_ptr(), sh_)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    # the look-ahead form (layer l+1's set from layer l's input, predicted on
-    # a second stream while layer l's FC1/FC2 run), same tokens
+    # the look-ahead form (layer l+1's set from layer l's input, predicted in
+    # the same launches as layer l's FC1/FC2), same tokens
     for t in range(args.stack_warmup):
         st.decode_lookahead_raw(xs[n + t], Y.data_ptr(), work.data_ptr(), sh_)
     torch.cuda.synchronize()

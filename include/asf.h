@@ -208,15 +208,16 @@ asf_status asf_stack_decode(asf_layer *const *layers, int32_t n_layers, const fl
 /* asf_stack_decode for one token with the look-ahead predictor (the
  * asynchronous reading of DejaVu, "LLM模型之PowerInfer1.0" appendix "DejaVu",
  * Eq. -2): layer l+1's set is predicted from layer l's INPUT, so its
- * predictor streams on a second stream while layer l's FC1/FC2 run:
+ * predictor runs beside layer l's FC1/FC2:
  *   S_0 = predict_0(x_0);  S_l = predict_l(x_{l-1}) for l >= 1;
  *   x_{l+1} = FFN_l(x_l over S_l) + (residual ? x_l : 0);  y = x_n
- * Arguments as asf_stack_decode with B = 1.  The second stream and its
- * events belong to the library (created on first use per device, kept until
- * the process ends, default priority); the call returns once both streams
- * are enqueued, and `stream` carries every result (it waits for the second
- * stream's last prediction).  Per layer the results equal asf_predict on
- * x_{l-1} followed by asf_sparse_ffn (active == NULL) on x_l, bit for bit. */
+ * Arguments as asf_stack_decode with B = 1.  Two launches per layer on
+ * `stream`: layer l's FC1/FC2 owner rows together with layer l+1's
+ * predictor layer 1, then layer l+1's scores together with layer l's
+ * output (layers of another weight type than their predecessor get their
+ * predictor layer 1 as a launch of its own).  Per layer the results equal
+ * asf_predict on x_{l-1} followed by asf_sparse_ffn (active == NULL) on
+ * x_l, bit for bit. */
 asf_status asf_stack_decode_lookahead(asf_layer *const *layers, int32_t n_layers,
                                       const float *x, int32_t residual, float *y, float *work,
                                       void *stream);
