@@ -5,9 +5,10 @@
 * Each layer's set and output agree with the oracle on that layer's actual
   input (the previous layer's GPU output): sets bit-exact beyond the 1e-3
   margin, per-token relative L2 <= 5e-3 (fp16 weights).
-* The look-ahead form (layer l's set predicted from layer l-1's input, on a
-  second stream) equals asf_predict + asf_sparse_ffn chained by hand on those
-  inputs, bit for bit, with oracle parity per layer.
+* The look-ahead form (layer l's set predicted from layer l-1's input, in
+  the same launches as layer l-1's FFN) equals asf_predict + asf_sparse_ffn
+  chained by hand on those inputs, bit for bit, with oracle parity per layer,
+  also over layers of mixed kind (gated / plain, fp16 / fp32).
 * The full 48-layer OPT-30B-shaped stack (7168x28672 fp16, predictors of
   512/1024/2048 hidden, ~40 GB resident) runs end to end; the oracle checks
   layers 0, 23 and 47 (their weights are read back from the device).
@@ -85,19 +86,14 @@ def test_small_stack_equals_chained_steps(orc, residual):
     assert torch.equal(inplace, ref)
 
 
-@pytest.mark.parametrize("residual", [False, True])
-def test_lookahead_stack_equals_chained_calls(orc, residual):
-    """Look-ahead reading: layer l's set is predicted from layer l-1's input
-    (layer 0's from its own).  The two-stream call equals asf_predict on
-    x_{l-1} then asf_sparse_ffn on x_l, chained by hand, bit for bit; each
-    layer's set and output agree with the oracle on those inputs."""
-    need_gpu()
-    d, f = 512, 2048
-    shapes = [wl.LayerShape(d, f, H, rho, "f16")
-              for H, rho in ((64, 0.03), (128, 0.08), (256, 0.15), (128, 0.10), (64, 0.05))]
-    layers, host = _device_layers(shapes, 760, keep=range(len(shapes)))
+def _lookahead_check(orc, shapes, seed, residual):
+    """The look-ahead call equals asf_predict on x_{l-1} then asf_sparse_ffn
+    on x_l, chained by hand, bit for bit; each layer's set and output agree
+    with the oracle on those inputs; in place and repeated calls agree."""
+    d, f = shapes[0].d, shapes[0].f
+    layers, host = _device_layers(shapes, seed, keep=range(len(shapes)))
     st = asf().Stack(layers, residual=residual)
-    x = wl.make_tokens(d, 3, 761)
+    x = wl.make_tokens(d, 3, seed + 1)
     for t in range(x.shape[0]):
         xt = to_dev(x[t:t + 1])
         y = st.decode_lookahead(xt)
@@ -114,11 +110,10 @@ def test_lookahead_stack_equals_chained_calls(orc, residual):
             _, s_orc, _ = orc.predict(L.p1, L.c1, L.p2, L.c2, xpred[None, :])
             check_set(ids, s_orc[0], 0.0, L.perm, "look-ahead layer %d token %d" % (l, t))
             yl = nxt.cpu().numpy()[0] - (xin if residual else 0.0)
-            y_orc = orc.ffn(L.w_up, L.w_down, xin, ids, b1=L.b1, b2=L.b2)
-            assert rel_l2(yl, y_orc[0]) <= TOL["f16"], (l, t)
+            y_orc = orc.ffn(L.w_up, L.w_down, xin, ids, b1=L.b1, b2=L.b2, W_gate=L.w_gate)
+            assert rel_l2(yl, y_orc[0]) <= TOL[shapes[l].wdtype], (l, t)
             prev, cur = cur, nxt
         assert torch.equal(y, cur), "look-ahead stack differs from the chained calls"
-    # in place (y == x), and a repeat gives the same bits
     xt = to_dev(x[:1])
     ref = st.decode_lookahead(xt)
     again = st.decode_lookahead(xt)
@@ -126,6 +121,33 @@ def test_lookahead_stack_equals_chained_calls(orc, residual):
     st.decode_lookahead(inplace, out=inplace)
     torch.cuda.synchronize()
     assert torch.equal(again, ref) and torch.equal(inplace, ref)
+
+
+@pytest.mark.parametrize("residual", [False, True])
+def test_lookahead_stack_equals_chained_calls(orc, residual):
+    """Look-ahead reading: layer l's set is predicted from layer l-1's input
+    (layer 0's from its own)."""
+    need_gpu()
+    d, f = 512, 2048
+    shapes = [wl.LayerShape(d, f, H, rho, "f16")
+              for H, rho in ((64, 0.03), (128, 0.08), (256, 0.15), (128, 0.10), (64, 0.05))]
+    _lookahead_check(orc, shapes, 760, residual)
+
+
+@pytest.mark.parametrize("residual", [False, True])
+def test_lookahead_mixed_stack(orc, residual):
+    """Layers of different kinds in one look-ahead stack: gated and plain,
+    fp16 and fp32 (a layer whose weight type differs from its predecessor's
+    gets its predictor layer 1 as a launch of its own), predictor rows of 1,
+    2 and 4 chunks per lane, a d_ffn that is not a multiple of 64."""
+    need_gpu()
+    d, f = 1024, 1500
+    shapes = [wl.LayerShape(d, f, 1024, 0.08, "f16", gated=True),
+              wl.LayerShape(d, f, 2048, 0.10, "f16"),
+              wl.LayerShape(d, f, 256, 0.06, "f32"),
+              wl.LayerShape(d, f, 512, 0.12, "f32", gated=True),
+              wl.LayerShape(d, f, 128, 0.05, "f16")]
+    _lookahead_check(orc, shapes, 790, residual)
 
 
 def test_stack_argument_errors():
