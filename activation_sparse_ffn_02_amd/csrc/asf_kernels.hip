@@ -373,6 +373,98 @@ __global__ __launch_bounds__(kThreads) void k_pred1(Pred1Args a) {
     pred1_block<WT>(a, blockIdx.x);
 }
 
+// Predictor layer 1 for 2..kPred1MaxB tokens (fp16 weights) in the geometry of
+// k_pred1: the weight chunks stay in registers while the tokens go by, the
+// x chunks of the next token loaded while the current one is summed.  Each
+// token's sum is formed exactly as k_pred1 forms it.  Also writes h as fp16
+// hi + lo halves (h16: [2][B][H]) for the batched scores and x as fp16 (x16)
+// for the batched FC1.
+constexpr int kPred1MaxB = 4;   // beyond, the matrix-core form is faster (one L2 round per token pair here)
+
+__global__ __launch_bounds__(kThreads) void k_pred1b(Pred1Args a, int B, _Float16 *__restrict__ h16,
+                                                     _Float16 *__restrict__ x16) {
+    constexpr int E = 8, CPL = kPred1Cpl;
+    __shared__ float red[kPred1MaxB][kWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wpr = a.wpr, H = a.H, d = a.d;
+    const int rpw = kWaves / wpr;
+    const int row = blockIdx.x * rpw + wave / wpr, part = wave % wpr;
+    const int C = d / E;
+    const bool live = row < H;
+    const int rowc = live ? row : H - 1;
+    const int rfin = blockIdx.x * rpw + (int)threadIdx.x / kPred1MaxB;
+    const float c1v = a.c1[rfin < H ? rfin : H - 1];
+    u32x4 w[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = part * 64 + lane + 64 * wpr * i;
+        w[i] = a.P1[(size_t)rowc * C + (c < C ? c : C - 1)];
+    }
+    // x chunks of token t (clamped to token B - 1)
+    auto load_tok = [&](int t, float (&xr)[CPL][E]) {
+        const int tt = t < B ? t : B - 1;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = part * 64 + lane + 64 * wpr * i;
+            load_f32<E>(a.x + (size_t)tt * d + (size_t)(c < C ? c : C - 1) * E, xr[i]);
+        }
+    };
+    auto tok_sum = [&](int t, const float (&xr)[CPL][E]) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = part * 64 + lane + 64 * wpr * i;
+            if (live && c < C) {
+                float wv[E];
+                unpack<1>(w[i], wv);
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc = fmaf(wv[e], xr[i][e], acc);
+            }
+        }
+        const float sum = wave_sum(acc);
+        if (lane == 0) red[t][wave] = sum;
+    };
+    float xa[CPL][E], xb[CPL][E];
+    load_tok(0, xa);
+    load_tok(1, xb);
+    // tokens alternate between the two register sets (2 <= B <= 4); the
+    // loads ahead are unconditional (clamped), so each wait covers one token
+#pragma unroll
+    for (int t = 0; t < kPred1MaxB; t += 2) {
+        if (t >= B) break;
+        tok_sum(t, xa);
+        load_tok(t + 2, xa);
+        if (t + 1 >= B) break;
+        tok_sum(t + 1, xb);
+        load_tok(t + 3, xb);
+    }
+    __syncthreads();
+    // thread t finishes row t / kPred1MaxB for token t % kPred1MaxB
+    {
+        const int rl = threadIdx.x / kPred1MaxB, t = threadIdx.x % kPred1MaxB;
+        const int r = blockIdx.x * rpw + rl;
+        if (rl < rpw && r < H && t < B) {
+            float sum = 0.0f;
+            for (int pp = 0; pp < wpr; ++pp) sum += red[t][rl * wpr + pp];
+            const float hv = fmaxf(sum + c1v, 0.0f);
+            const _Float16 hi = (_Float16)hv;
+            a.h[(size_t)t * H + r] = hv;
+            h16[(size_t)t * H + r] = hi;
+            h16[(size_t)(B + t) * H + r] = (_Float16)(hv - (float)hi);
+        }
+    }
+    // x -> fp16 for the batched FC1
+    const int n8 = B * d / 8;
+    for (int i = blockIdx.x * kThreads + threadIdx.x; i < n8; i += gridDim.x * kThreads) {
+        float v[8];
+        load_f32<8>(a.x + (size_t)8 * i, v);
+        f16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (_Float16)v[e];
+        *reinterpret_cast<f16x8 *>(x16 + (size_t)8 * i) = o;
+    }
+}
+
 // ---------------------------------------------------------------- predictor layer 2
 // Owner q, wave w scores the slots of bits i = 8w .. 8w+7 (slot q + nq*i);
 // lane l holds chunks l, l+64, ... of each row.  Loads are unconditional from
@@ -1590,6 +1682,11 @@ hipError_t launch_pred_l1(const LayerView &L, const float *x, int B, const Trace
         const Pred1Args a = pred1_args(L, x);
         if (L.wtype == ASF_F16) ASF_LAUNCH(ASF_K_PRED_L1, k_pred1<1>, grid, blk, a);
         else ASF_LAUNCH(ASF_K_PRED_L1, k_pred1<0>, grid, blk, a);
+        return hipGetLastError();
+    }
+    if (L.wtype == ASF_F16 && B <= kPred1MaxB) {
+        const dim3 grid(pred1_blocks(L)), blk(kThreads);
+        ASF_LAUNCH(ASF_K_PRED_L1, k_pred1b, grid, blk, pred1_args(L, x), B, L.h16, L.x16);
         return hipGetLastError();
     }
     if (L.wtype == ASF_F16) return launch_pred_mm(L, x, B, tr, s);

@@ -287,10 +287,13 @@ def _batched_check(orc, L, x, lay, label, check_dense=True, user_list=True):
           % (label, B, k, k / f, worst, amb))
 
 
-@pytest.mark.parametrize("B,gated", [(3, False), (16, False), (5, True), (32, True)])
+@pytest.mark.parametrize("B,gated", [(3, False), (16, False), (5, True), (32, True), (4, True),
+                                     (8, False)])
 def test_batched_matrix_core_path(orc, B, gated):
     """Scaled layers with ragged tiles (d not a multiple of 256, H not of 64,
-    f not of 64) through the batched kernels."""
+    f not of 64) through the batched kernels; B = 4 is the largest batch whose
+    predictor layer 1 runs as a vector kernel, B = 5 the smallest on the
+    matrix cores."""
     need_gpu()
     _, sh = wl.CONFIGS["llama7b_gated_relu" if gated else "opt13b_batched"]
     L = wl.make_layer(wl.scaled_shape(sh, 1152, 3000 + 7 * B, 200), 900 + B)
