@@ -155,6 +155,13 @@ asf_status asf_create_layer(const asf_layer_desc *desc, const asf_layer_weights 
     auto chk = [&](hipError_t r) {
         if (e == hipSuccess && r != hipSuccess) e = r;
     };
+    {
+        int dev = 0;
+        v.ncu = 0;
+        chk(hipGetDevice(&dev));
+        chk(hipDeviceGetAttribute(&v.ncu, hipDeviceAttributeMultiprocessorCount, dev));
+        if (v.ncu < 1) v.ncu = 1;
+    }
     // neuron table and its inverse
     if (neuron_table)
         chk(hipMemcpyAsync(v.perm, neuron_table, (size_t)f * 4, hipMemcpyDeviceToDevice, s));

@@ -368,6 +368,8 @@ struct Fc1MmParams {
     float *la;           // [rows][max_batch]
     int max_batch;
     int32_t *rows;       // number of list rows
+    int ncu;             // compute units
+    int per_cu;          // workgroups resident per CU at once (LDS, registers)
 };
 
 // x -> fp16 [B][d] (for FC1 calls that follow no predictor pass)
@@ -380,9 +382,15 @@ __global__ void k_to_f16(const float *__restrict__ x, int n, _Float16 *__restric
 // (row r is the (r - pre[q])-th set bit i of owner q, slot q + nq*i, for the
 // owner with pre[q] <= r < pre[q+1], pre the popcount prefix); mode 1 the
 // caller's ids in list order; mode 2 every slot.  Workgroup b takes rows
-// 32b .. 32b+31 as one tile streamed with the token tile of x (fp16) over
-// k = d in chunks of 256 k.  a = ReLU(up . x + b1) (gated: ReLU(gate . x +
+// Rb .. Rb+R-1 as one tile streamed with the token tile of x (fp16) over k = d
+// in chunks of 256 k.  R = 32 while the list needs at most one workgroup per
+// CU; a longer list is spread evenly over the workgroups resident at once
+// (R = its length over them, at least kFc1MinRows; the tile's other rows are
+// dead), since a CU holding two workgroups runs each ~30% slower and an
+// uneven split leaves the kernel waiting on the doubled CUs.  a = ReLU(up . x + b1) (gated: ReLU(gate . x +
 // b1) * (up . x)), written to la[r][t] and lslot[r].
+constexpr int kFc1MinRows = 16;
+
 template <bool GATED>
 __global__ __launch_bounds__(kThreads) void k_fc1_mm(Fc1MmParams p) {
     constexpr int CW = 32;
@@ -396,7 +404,14 @@ __global__ __launch_bounds__(kThreads) void k_fc1_mm(Fc1MmParams p) {
     __shared__ int rslot[kTile];
     __shared__ int nrows_lds;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r0 = kTile * blockIdx.x;
+    // rows per workgroup from the list length (the same in every workgroup)
+    auto tile_rows = [&](int n) {
+        if (n <= kTile * p.ncu) return kTile;
+        const int nw = p.per_cu * p.ncu;
+        const int r = (n + nw - 1) / nw;
+        return r < kFc1MinRows ? kFc1MinRows : (r > kTile ? kTile : r);
+    };
+    int R = kTile, r0 = 0;
     // ---- the list's length and this tile's slots
     if (p.mode == 0) {
         uint64_t *vb = reinterpret_cast<uint64_t *>(smem);
@@ -424,10 +439,12 @@ __global__ __launch_bounds__(kThreads) void k_fc1_mm(Fc1MmParams p) {
             nrows_lds = base + incl;
         }
         __syncthreads();
+        R = tile_rows(nrows_lds);
+        r0 = R * blockIdx.x;
         if (tid < kTile) {
             const int r = r0 + tid;
             int slot = -1;
-            if (r < nrows_lds) {
+            if (tid < R && r < nrows_lds) {
                 int lo = 0, hi = nq;                 // largest q with pre[q] <= r
                 while (hi - lo > 1) {
                     const int mid = (lo + hi) >> 1;
@@ -448,10 +465,12 @@ __global__ __launch_bounds__(kThreads) void k_fc1_mm(Fc1MmParams p) {
             nrows_lds = n;
         }
         __syncthreads();
+        R = tile_rows(nrows_lds);
+        r0 = R * blockIdx.x;
         if (tid < kTile) {
             const int r = r0 + tid;
             int slot = -1;
-            if (r < nrows_lds) {
+            if (tid < R && r < nrows_lds) {
                 if (p.mode == 2) {
                     slot = r;
                 } else {
@@ -538,7 +557,7 @@ __global__ __launch_bounds__(kThreads) void k_fc1_mm(Fc1MmParams p) {
     for (int j = 0; j < 2; ++j) {
         const int e = tid + kThreads * j;
         const int rr = e / kTile, t = e % kTile, r = r0 + rr;
-        if (r >= nrows || t >= p.B) continue;
+        if (rr >= R || r >= nrows || t >= p.B) continue;
         const int sl = rslot[rr];
         float a = 0.0f;
         if (sl >= 0) {
@@ -773,7 +792,12 @@ hipError_t launch_fc1_mm(const LayerView &L, const float *x, int B, int mode, co
     p.la = L.la;
     p.max_batch = L.max_batch;
     p.rows = L.rows;
-    const dim3 grid((L.f + kTile - 1) / kTile);     // the list has at most f rows
+    p.ncu = L.ncu;
+    p.per_cu = L.gated ? 1 : 2;
+    // enough workgroups for any list length (at most f rows): 32 rows each,
+    // or the spread (at most per_cu per CU); the rest return at once
+    const int g32 = (L.f + kTile - 1) / kTile;
+    const dim3 grid(g32 > p.per_cu * p.ncu ? g32 : p.per_cu * p.ncu);
     if (L.gated) ASF_LAUNCH(ASF_K_FC1, k_fc1_mm<true>, grid, dim3(kThreads), p);
     else ASF_LAUNCH(ASF_K_FC1, k_fc1_mm<false>, grid, dim3(kThreads), p);
     return hipGetLastError();

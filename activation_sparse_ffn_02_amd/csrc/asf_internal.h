@@ -56,6 +56,7 @@ struct LayerView {
     int words;     // 64-bit words of a slot-ordered mask: ceil(f / 64)
     int nq;        // owner workgroups (== words)
     int nmat;      // matrices per neuron bundle: 2 (up, down) or 3 (gate, up, down)
+    int ncu;       // compute units of the device the layer was created on
 
     // weights in the library layout
     void *p1;          // [H][d]            predictor layer 1 (as given)
