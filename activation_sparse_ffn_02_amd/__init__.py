@@ -247,6 +247,15 @@ class Layer:
         if rc != ASF_OK:
             raise AsfError(rc, "asf_decode_step")
 
+    def sparse_ffn_raw(self, x_ptr: int, B: int, active_ptr: int, n_active_ptr: int, y_ptr: int,
+                       stream_handle: int) -> None:
+        """sparse_ffn over a caller id list on raw device pointers and a raw
+        stream handle (no tensor checks), for launch-bound loops."""
+        rc = _lib.asf_sparse_ffn(self._h, x_ptr, B, active_ptr, n_active_ptr, None, y_ptr,
+                                 stream_handle)
+        if rc != ASF_OK:
+            raise AsfError(rc, "asf_sparse_ffn")
+
     def exact_ffn(self, x, residual=None, out=None, active=None, n_active=None, stream=None):
         """asf_exact_ffn: one token through the FFN over its true active set
         (every pre-activation computed, no predictor)."""

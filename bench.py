@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--trace-every", type=int, default=10,
                     help="record kernel events on every n-th timed step")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--ffn-rhos", type=float, nargs="*", default=[0.07, 0.10],
+                    help="mean activations of the sparse_ffn-alone measurement (none skips it)")
+    ap.add_argument("--ffn-sets", type=int, default=256)
     ap.add_argument("--stack-tokens", type=int, default=256,
                     help="tokens through the 48-layer stack (0 skips the stack)")
     ap.add_argument("--stack-warmup", type=int, default=8)
@@ -412,6 +415,58 @@ def bench_batched(args, asf, torch, np, wl, dev, stream):
             "by_batch": out}
 
 
+def bench_ffn_only(args, ring, Xd, Y, L, dense_ms, dense_bytes, torch, wl, dev, sh_):
+    """asf_sparse_ffn alone (FC1 + ReLU + FC2 over a caller's id list, no
+    predictor) on the benchmark ring, against the dense FFN of the same ring:
+    per-token sets drawn from the layer's firing law (its hotness order) at
+    each mean activation in --ffn-rhos."""
+    sh = L.shape
+    ws = 2 if sh.wdtype == "f16" else 4
+    nmat = 3 if sh.gated else 2
+    n = args.ffn_sets
+    out = []
+    for rho in args.ffn_rhos:
+        sets = wl.sampled_sets(L.perm, rho, n, seed=4000 + int(round(rho * 1000)))
+        ids = torch.zeros((n, sh.f), dtype=torch.int32)
+        cnt = torch.zeros(n, dtype=torch.int32)
+        for t, st in enumerate(sets):
+            ids[t, :len(st)] = torch.from_numpy(st)
+            cnt[t] = len(st)
+        ids, cnt = ids.to(dev), cnt.to(dev)
+        ap = [ids[t].data_ptr() for t in range(n)]
+        cp = [cnt[t:t + 1].data_ptr() for t in range(n)]
+        xs = [Xd[t % Xd.shape[0]].data_ptr() for t in range(n)]
+        ys = [Y[r].data_ptr() for r in range(len(ring))]
+        for i in range(20):
+            ring[i % len(ring)].sparse_ffn_raw(xs[i % n], 1, ap[i % n], cp[i % n],
+                                               ys[i % len(ring)], sh_)
+        torch.cuda.synchronize()
+        steps = max(args.dense_steps, n)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            ring[i % len(ring)].sparse_ffn_raw(xs[i % n], 1, ap[i % n], cp[i % n],
+                                               ys[i % len(ring)], sh_)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        k = float(sum(len(st) for st in sets)) / n
+        # the set's rows and down columns (+ b1, ids), x, b2, y
+        b = k * (nmat * sh.d * ws + 4 + 4) + sh.d * 4 * 3
+        r = {"rho": rho, "active_mean": k, "active_frac": k / sh.f, "calls": steps,
+             "ms_per_call": ms, "algorithmic_bytes_per_call": b,
+             "effective_gbps": b / (ms * 1e-3) / 1e9,
+             "effective_frac_of_peak": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+             "speedup_vs_dense": None if dense_ms is None else dense_ms / ms,
+             "byte_ceiling_vs_dense": dense_bytes / b}
+        out.append(r)
+        log(args, "sparse_ffn alone at rho %.2f: %.1f us per call, %.2fx dense"
+            % (rho, ms * 1e3, r["speedup_vs_dense"] or 0.0))
+    return {"workload": "asf_sparse_ffn over given per-token sets (firing law of the benchmark "
+                        "layer at each mean activation), batch 1, same ring as the decode step",
+            "sets_per_rho": n, "by_rho": out}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -570,6 +625,10 @@ def main():
         log(args, "exact-mask mode: %.1f us per step, true set %.1f%%" % (ex_ms * 1e3,
                                                                         100 * k_true / sh.f))
 
+    ffn_only = None
+    if args.dense_steps > 0 and args.ffn_rhos:
+        ffn_only = bench_ffn_only(args, ring, Xd, Y, L, dense_ms, dense_bytes, torch, wl, dev, sh_)
+
     tok_s = K / elapsed
     eff_gbs = step_bytes * K / elapsed / 1e9
     out = {
@@ -603,6 +662,7 @@ def main():
         "dense_gbps": None if dense_ms is None else dense_bytes / (dense_ms * 1e-3) / 1e9,
         "sparse_step_speedup_vs_dense": None if dense_ms is None else dense_ms / ms_per_step,
         "exact_mask": exact,
+        "sparse_ffn_only": ffn_only,
         "roofline": {"bound": "hbm", "kernel": dname, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(dname),

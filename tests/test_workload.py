@@ -113,3 +113,18 @@ def test_stack_generator_keeps_layer_inputs_calibrated(orc):
             ys.append(orc.ffn(L.w_up, L.w_down, xin[t:t + 1], ids, b1=L.b1, b2=L.b2)[0])
         x = np.asarray(ys)
     assert 0.75 < np.sqrt((x ** 2).mean()) < 1.2
+
+
+def test_sampled_sets_follow_the_law():
+    """Sets drawn at mean activation rho have mean size rho*f, and the hottest
+    slots of the table fire most often."""
+    f = 4096
+    perm = np.random.Generator(np.random.PCG64(5)).permutation(f).astype(np.int32)
+    sets = wl.sampled_sets(perm, 0.10, 400, seed=11)
+    sizes = np.array([len(s) for s in sets])
+    assert abs(sizes.mean() / f - 0.10) < 0.004
+    cnt = np.zeros(f)
+    for s in sets:
+        assert np.all(np.diff(s) > 0)
+        cnt[s] += 1
+    assert cnt[perm[:32]].mean() > 300 and cnt[perm[-1024:]].mean() < 20

@@ -82,6 +82,12 @@ def firing_probabilities(f: int, rho: float, rng: np.random.Generator,
     order = rng.permutation(f)                  # order[k] = id of rank k+1
     rank = np.empty(f, np.int64)
     rank[order] = np.arange(1, f + 1)
+    return law_by_rank(f, rho, s, cap)[rank - 1], rank
+
+
+def law_by_rank(f: int, rho: float, s: float = ZIPF_S, cap: float = P_CAP) -> np.ndarray:
+    """Firing probability of the neuron of hotness rank 1..f: min(cap, C r^-s),
+    C by bisection so that the mean is rho."""
     base = np.arange(1, f + 1, dtype=np.float64) ** (-s)
     lo, hi = 0.0, 1.0
     while np.minimum(cap, hi * base).mean() < rho:
@@ -92,8 +98,18 @@ def firing_probabilities(f: int, rho: float, rng: np.random.Generator,
             lo = mid
         else:
             hi = mid
-    p_by_rank = np.minimum(cap, hi * base)
-    return p_by_rank[rank - 1], rank
+    return np.minimum(cap, hi * base)
+
+
+def sampled_sets(perm: np.ndarray, rho: float, n: int, seed: int):
+    """n independent active sets (original ids, ascending) drawn from the
+    firing law at mean activation rho, with the hotness order of a layer's
+    neuron table (perm[slot] = id of hotness rank slot + 1)."""
+    f = perm.shape[0]
+    p = np.empty(f, np.float64)
+    p[perm] = law_by_rank(f, rho)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return [np.flatnonzero(rng.random(f) < p).astype(np.int32) for _ in range(n)]
 
 
 @dataclasses.dataclass
