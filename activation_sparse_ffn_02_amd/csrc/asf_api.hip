@@ -225,9 +225,10 @@ asf_status asf_sparse_ffn(const asf_layer *layer, const float *x, int32_t B,
     if (!aligned16(y) || (residual && !aligned16(residual))) return ASF_ERR_ALIGN;
     const LayerView &v = layer->v;
     hipStream_t s = (hipStream_t)stream;
-    if (!active && B == 1) {
-        // one token over the last set: the decode step's per-owner FC1 + FC2
-        if (launch_ffn1(v, x, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
+    if (B == 1) {
+        // one token: the decode step's per-owner FC1 + FC2 over the last set
+        // or the caller's list
+        if (launch_ffn1(v, x, active, n_active, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
         if (launch_fc2_sum(v, residual, y, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
         return ASF_OK;
     }

@@ -130,10 +130,12 @@ hipError_t launch_fc2(const LayerView &L, int B, bool listed, const float *resid
 // FC2 rows (part1) + b2 (+ resid)
 hipError_t launch_fc2_sum(const LayerView &L, const float *resid, float *y, const Trace *tr,
                           hipStream_t s);
-// one token over the set of the last prediction (the owner words): FC1 and
-// the owner FC2 rows, as the decode step does after its ballot (then
-// launch_fc2_sum)
-hipError_t launch_ffn1(const LayerView &L, const float *x, const Trace *tr, hipStream_t s);
+// one token over the set of the last prediction (the owner words), or over
+// a caller's list of original ids (ids, n_ids device pointers; ids null =
+// the last prediction): FC1 and the owner FC2 rows, as the decode step does
+// after its ballot (then launch_fc2_sum)
+hipError_t launch_ffn1(const LayerView &L, const float *x, const int32_t *ids,
+                       const int32_t *n_ids, const Trace *tr, hipStream_t s);
 // one-stream look-ahead stack: layer L's FFN over its set with predictor
 // layer 1 of layer N on the same input x, then layer N's scores with layer
 // L's owner-row sum (N null: layer L's kernels alone)

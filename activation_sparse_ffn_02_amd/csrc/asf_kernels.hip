@@ -40,6 +40,8 @@
 
 #include "asf_internal.h"
 
+#include <utility>
+
 namespace asf {
 namespace {
 
@@ -276,12 +278,19 @@ __device__ __forceinline__ void stage_load(const float *__restrict__ src, int n,
 // and places past n get copies of the last float4, never read), so the
 // staging loads stay where they were issued instead of sinking into a
 // guarded store behind a full wait.
+// (a pack expansion rather than a loop: a loop the compiler leaves rolled
+// indexes v at run time, which puts v in scratch memory)
+template <int N4, int NF, size_t... I>
+__device__ __forceinline__ void stage_store_i(float (&dst)[NF], const float4 (&v)[N4],
+                                              std::index_sequence<I...>) {
+    float4 *d4 = reinterpret_cast<float4 *>(dst);
+    ((d4[(int)threadIdx.x + kThreads * (int)I] = v[I]), ...);
+}
+
 template <int N4, int NF>
 __device__ __forceinline__ void stage_store(float (&dst)[NF], const float4 (&v)[N4]) {
     static_assert(NF >= N4 * 4 * kThreads, "LDS staging array too small");
-    float4 *d4 = reinterpret_cast<float4 *>(dst);
-#pragma unroll
-    for (int i = 0; i < N4; ++i) d4[(int)threadIdx.x + kThreads * i] = v[i];
+    stage_store_i(dst, v, std::make_index_sequence<N4>{});
 }
 
 // acc += chunk c of a weight row (in registers) . chunk c of an LDS vector
@@ -658,6 +667,10 @@ struct ScoreParams {
     // listed neurons of a * (down column), 16 outputs per slice
     int dn_off;       // chunk offset of the down column in a bundle
     float *part1;
+    // a caller's list of original ids (one token over a given set)
+    const int32_t *ids;
+    const int32_t *n_ids;
+    const int32_t *inv;
 };
 
 // Owner workgroup q: score its 64 slots for every token, store per-token and
@@ -824,13 +837,13 @@ __device__ __forceinline__ void owner_fc1_1(int q, uint64_t valid, SlotOf slot_o
 }
 
 // registers per FC1 row set (up, and gate when gated), in 16-byte chunks
-template <bool GATED, int CPL1, bool SPEC = false> struct Fc1Regs {
+template <bool GATED, int CPL1, bool SPEC = false, bool WIDE = false> struct Fc1Regs {
     static constexpr int chunks = CPL1 * (GATED ? 2 : 1);
     // at most 128 VGPRs (4 waves per SIMD) while the rows fit beside the P2
     // double buffer; more otherwise, and when the hottest rows are held
-    // through the scoring phase (used only when one workgroup per CU covers
-    // every owner)
-    static constexpr int waves_per_eu = (chunks <= 14 && !SPEC) ? 4 : 2;
+    // through the scoring phase or more down columns are requested ahead
+    // (WIDE; both used when one workgroup per CU covers every owner)
+    static constexpr int waves_per_eu = (chunks <= 14 && !SPEC && !WIDE) ? 4 : 2;
 };
 
 // Chunks t, t + 512, ... (thread t) of the down columns of the next N
@@ -875,7 +888,7 @@ __device__ __forceinline__ void fma_down(const u32x4 (&dv)[N][CPT], int n0, int 
 // FC1 of owner q's listed neurons (the bits of `valid`, slot q + nq*bit) and
 // the owner's FC2 row, one token, x in LDS.  With SPEC, waves below
 // kSpecRows already hold the rows (spu, spg) and bias of bit `wave`.
-template <int WT, bool GATED, int CPL1, bool SPEC>
+template <int WT, bool GATED, int CPL1, bool SPEC, bool WIDE = false>
 __device__ __forceinline__ void owner_ffn1(const ScoreParams &p, int q, int nq, uint64_t valid,
                                            const float *xs, float *a_lds,
                                            const u32x4 (&spu)[CPL1], const u32x4 (&spg)[CPL1],
@@ -890,7 +903,7 @@ __device__ __forceinline__ void owner_ffn1(const ScoreParams &p, int q, int nq, 
     // cut where the FC1 rows leave no registers under the 128-VGPR cap.
     constexpr int CPT = (CPL1 + 7) / 8;      // d-row chunks per thread
     constexpr int PF2 = 8 / CPT;
-    constexpr bool kWide = Fc1Regs<GATED, CPL1, SPEC>::waves_per_eu == 2;
+    constexpr bool kWide = Fc1Regs<GATED, CPL1, SPEC, WIDE>::waves_per_eu == 2;
     constexpr bool kTight = !kWide && CPT == 2;
     constexpr int PF = kTight ? (CPL1 >= 12 ? 0 : 2) : PF2;   // no spills
     constexpr int PFB = (kWide && Fc1Regs<GATED, CPL1>::chunks + 2 * PF * CPT <= 32) ? PF : 0;
@@ -1075,27 +1088,105 @@ __global__ __launch_bounds__(kThreads) __attribute__((
 // stack) and for asf_sparse_ffn of one token over the last prediction: the
 // same per-owner work as k_score1 after its ballot, so the results match
 // the decode step bit for bit.
-template <int WT, bool GATED, int CPL1>
+//
+// With LIST the set is a caller's list of original ids instead: every owner
+// reads the whole list (kListPer ids per thread per pass, all requested at
+// once, then their slots through the inverse table) and keeps the ids whose
+// slot it owns as its bits; out-of-range ids are skipped, a repeated id sets
+// its bit once.
+constexpr int kListPer = 4;
+
+// ids j0 + t + 512u (u < kListPer) of thread t (n > 0 ids in the list):
+// every request of a pass issued before its first wait; owner q's bits
+// ORed into *m
+__device__ __forceinline__ void list_pass(const ScoreParams &p, int n, int j0, int q, int nq,
+                                          unsigned long long *m) {
+    int id[kListPer], sl[kListPer];
+#pragma unroll
+    for (int u = 0; u < kListPer; ++u) {
+        const int e = j0 + (int)threadIdx.x + kThreads * u;
+        id[u] = p.ids[e < n ? e : n - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kListPer; ++u) {
+        const unsigned ic = (unsigned)id[u] < (unsigned)p.f ? (unsigned)id[u] : 0u;
+        sl[u] = p.inv[ic];
+    }
+#pragma unroll
+    for (int u = 0; u < kListPer; ++u) {
+        const int e = j0 + (int)threadIdx.x + kThreads * u;
+        if (e < n && (unsigned)id[u] < (unsigned)p.f && sl[u] % nq == q)
+            atomicOr(m, 1ull << (sl[u] / nq));
+    }
+}
+
+template <int WT, bool GATED, int CPL1, bool LIST = false>
 __device__ __forceinline__ void ffn1_block(const ScoreParams &p, int q, int nq) {
     __shared__ float xs[kMaxDLds];
     __shared__ float a_lds[kRowsPerWG];
+    __shared__ unsigned long long m_lds;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     float4 xv[4];
     stage_load<4>(p.x, p.d, xv);
-    const uint64_t valid = p.ubits[q];
-    stage_store<4>(xs, xv);
+    uint64_t valid = 0;
+    u32x4 spu[CPL1], spg[CPL1];
+#pragma unroll
+    for (int c = 0; c < CPL1; ++c) spu[c] = spg[c] = zero4();
+    float spec_bias = 0.0f;
+    if constexpr (LIST) {
+        int n = *p.n_ids;
+        n = n < 0 ? 0 : (n > p.f ? p.f : n);
+        // the first pass: ids requested beside x (an empty list reads the
+        // inverse table instead, a buffer that exists, and keeps nothing),
+        // x to LDS, then the slots
+        const int32_t *src = n > 0 ? p.ids : p.inv;
+        const int nn = n > 0 ? n : 1;
+        int id[kListPer], sl[kListPer];
+#pragma unroll
+        for (int u = 0; u < kListPer; ++u) {
+            const int e = (int)threadIdx.x + kThreads * u;
+            id[u] = src[e < nn ? e : nn - 1];
+        }
+        // the FC1 rows of the owner's two hottest slots, requested while the
+        // list is read (with a hot-first table they are in nearly every set)
+        {
+            const int spec_slot = q + nq * wave;
+            spec_bias = p.b1[spec_slot < p.f ? spec_slot : p.f - 1];
+            if (wave < kSpecRows && spec_slot < p.f)
+                load_fc1_rows<GATED, CPL1>(p.bundles, p.bstride, p.cd, spec_slot, lane, spu, spg);
+        }
+        if (threadIdx.x == 0) m_lds = 0ull;
+        stage_store<4>(xs, xv);
+#pragma unroll
+        for (int u = 0; u < kListPer; ++u) {
+            const unsigned ic = (unsigned)id[u] < (unsigned)p.f ? (unsigned)id[u] : 0u;
+            sl[u] = p.inv[ic];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kListPer; ++u) {
+            const int e = (int)threadIdx.x + kThreads * u;
+            if (e < n && (unsigned)id[u] < (unsigned)p.f && sl[u] % nq == q)
+                atomicOr(&m_lds, 1ull << (sl[u] / nq));
+        }
+        for (int j0 = kThreads * kListPer; j0 < n; j0 += kThreads * kListPer)
+            list_pass(p, n, j0, q, nq, &m_lds);
+        __syncthreads();
+        valid = m_lds;
+    } else {
+        valid = p.ubits[q];
+        stage_store<4>(xs, xv);
+    }
     if (threadIdx.x == 0) p.out.vbits[q] = valid;
     __syncthreads();
-    u32x4 none[CPL1];
-#pragma unroll
-    for (int c = 0; c < CPL1; ++c) none[c] = zero4();
-    owner_ffn1<WT, GATED, CPL1, false>(p, q, nq, valid, xs, a_lds, none, none, 0.0f, wave, lane);
+    owner_ffn1<WT, GATED, CPL1, LIST, LIST>(p, q, nq, valid, xs, a_lds, spu, spg, spec_bias, wave,
+                                            lane);
 }
 
-template <int WT, bool GATED, int CPL1>
+template <int WT, bool GATED, int CPL1, bool LIST>
 __global__ __launch_bounds__(kThreads) __attribute__((
-    amdgpu_waves_per_eu(Fc1Regs<GATED, CPL1>::waves_per_eu))) void k_ffn1(ScoreParams p) {
-    ffn1_block<WT, GATED, CPL1>(p, blockIdx.x, gridDim.x);
+    amdgpu_waves_per_eu(Fc1Regs<GATED, CPL1, LIST, LIST>::waves_per_eu))) void k_ffn1(ScoreParams p) {
+    ffn1_block<WT, GATED, CPL1, LIST>(p, blockIdx.x, gridDim.x);
 }
 
 // ---------------------------------------------------------------- exact mask, single token
@@ -1879,13 +1970,20 @@ hipError_t launch_fc2_sum(const LayerView &L, const float *resid, float *y, cons
     return hipGetLastError();
 }
 
-hipError_t launch_ffn1(const LayerView &L, const float *x, const Trace *tr, hipStream_t s) {
-    const ScoreParams p = score_params(L, x, 1);
+hipError_t launch_ffn1(const LayerView &L, const float *x, const int32_t *ids,
+                       const int32_t *n_ids, const Trace *tr, hipStream_t s) {
+    ScoreParams p = score_params(L, x, 1);
+    p.ids = ids;
+    p.n_ids = n_ids;
+    p.inv = L.inv;
+    const bool list = ids != nullptr;
     const dim3 grid(L.nq), blk(kThreads);
     const int cpl1 = fc1_cpl(L.cd);
-#define ASF_FF(WT, C1)                                                            \
-    if (L.gated) ASF_LAUNCH(ASF_K_FC1, (k_ffn1<WT, true, C1>), grid, blk, p);  \
-    else ASF_LAUNCH(ASF_K_FC1, (k_ffn1<WT, false, C1>), grid, blk, p);
+#define ASF_FFL(WT, G, C1)                                                        \
+    if (list) ASF_LAUNCH(ASF_K_FC1, (k_ffn1<WT, G, C1, true>), grid, blk, p);  \
+    else ASF_LAUNCH(ASF_K_FC1, (k_ffn1<WT, G, C1, false>), grid, blk, p);
+#define ASF_FF(WT, C1) \
+    if (L.gated) { ASF_FFL(WT, true, C1) } else { ASF_FFL(WT, false, C1) }
 #define ASF_FFW(WT)                  \
     switch (cpl1) {                  \
     case 1: ASF_FF(WT, 1) break;     \
@@ -1900,13 +1998,14 @@ hipError_t launch_ffn1(const LayerView &L, const float *x, const Trace *tr, hipS
     if (L.wtype == ASF_F16) { ASF_FFW(1) } else { ASF_FFW(0) }
 #undef ASF_FFW
 #undef ASF_FF
+#undef ASF_FFL
     return hipGetLastError();
 }
 
 hipError_t launch_ffn1_pred1(const LayerView &L, const LayerView *N, const float *x,
                              const Trace *tr, hipStream_t s) {
     if (!N || N->wtype != L.wtype) {
-        const hipError_t e = launch_ffn1(L, x, tr, s);
+        const hipError_t e = launch_ffn1(L, x, nullptr, nullptr, tr, s);
         if (e != hipSuccess || !N) return e;
         return launch_pred_l1(*N, x, 1, nullptr, s);
     }

@@ -43,7 +43,8 @@
  *   reported as ASF_ERR_HIP.  Device-side faults surface at the caller's next
  *   synchronisation.  No C++ exception crosses this ABI.  Neuron ids in a
  *   caller-supplied active list that are out of range are skipped; duplicate
- *   ids are the caller's error (they are counted twice).
+ *   ids are the caller's error (one token counts such a neuron once, a batch
+ *   as often as it is listed).
  */
 #ifndef ASF_H
 #define ASF_H
@@ -169,9 +170,11 @@ asf_status asf_predict(const asf_layer *layer, const float *x, int32_t B,
  *   residual  DEVICE float32 [B][d_model] or NULL (= 0)
  *   y         DEVICE float32 [B][d_model]; may alias residual
  * For B > 1 every token computes every neuron of the set (the union of the
- * batch's sets when the set comes from asf_predict).  One token over the last
- * set runs the decode step's own FC1 + FC2 kernels, so asf_predict followed
- * by this call gives asf_decode_step's y bit for bit. */
+ * batch's sets when the set comes from asf_predict).  One token runs the
+ * decode step's own FC1 + FC2 kernels (each owner workgroup takes the ids
+ * whose stored slot it owns), so asf_predict followed by this call, with
+ * active == NULL or with the predicted list, gives asf_decode_step's y bit
+ * for bit. */
 asf_status asf_sparse_ffn(const asf_layer *layer, const float *x, int32_t B,
                           const int32_t *active, const int32_t *n_active,
                           const float *residual, float *y, void *stream);

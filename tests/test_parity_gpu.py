@@ -335,3 +335,37 @@ def test_max_ffn_size(orc):
     check_set(ids, pre[0], 0.0, L.perm, "f=65536 exact")
     y_orc = orc.dense_ffn(L.w_up, L.w_down, x[:1], b1=L.b1, b2=L.b2)
     assert rel_l2(y.cpu().numpy()[0], y_orc[0]) <= TOL["f16"]
+
+
+@pytest.mark.parametrize("cfg,d,f,H", [("opt6.7b_ffn", 4096, 16384, 1024), ("opt6.7b_ffn", 512, 1000, 64),
+                                       ("llama7b_gated_relu", 1024, 3000, 256),
+                                       ("tiny_f32", 256, 1024, 64)])
+def test_one_token_list_is_the_decode_step(orc, cfg, d, f, H):
+    """One token over a caller's list runs the decode step's owner kernels:
+    the predicted list (in any order, with repeats and out-of-range ids
+    mixed in) gives decode_step's y bit for bit; a sampled set at 10%
+    matches the oracle."""
+    need_gpu()
+    _, sh = wl.CONFIGS[cfg]
+    L = wl.make_layer(wl.scaled_shape(sh, d, f, H), 300 + f)
+    lay = asf().layer_from_numpy(L)
+    x = wl.make_tokens(d, 3, 400 + f)
+    rng = np.random.default_rng(f)
+    for t in range(3):
+        xt = to_dev(x[t:t + 1])
+        active = torch.empty(f, dtype=torch.int32, device="cuda")
+        n = torch.empty(1, dtype=torch.int32, device="cuda")
+        y_step = lay.decode_step(xt, active=active, n_active=n)
+        torch.cuda.synchronize()
+        ids = active[:int(n.item())].cpu().numpy()
+        mixed = np.concatenate([rng.permutation(ids), ids[:5], np.array([-1, f, 1 << 30], np.int32)])
+        y_list = lay.sparse_ffn(xt, active=to_dev(mixed.astype(np.int32)),
+                                n_active=to_dev(np.array([mixed.size], np.int32)))
+        torch.cuda.synchronize()
+        assert torch.equal(y_list, y_step), "token %d: list path differs from decode_step" % t
+    sets = wl.sampled_sets(L.perm, 0.10, 2, seed=9)
+    for t, st in enumerate(sets):
+        y = lay.sparse_ffn(to_dev(x[t:t + 1]), active=to_dev(st),
+                           n_active=to_dev(np.array([st.size], np.int32)))
+        y_orc = orc.ffn(L.w_up, L.w_down, x[t], st, b1=L.b1, b2=L.b2, W_gate=L.w_gate)
+        assert rel_l2(y.cpu().numpy()[0], y_orc[0]) <= TOL[sh.wdtype]
