@@ -645,6 +645,48 @@ def main():
         log(args, "exact-mask mode: %.1f us per step, true set %.1f%%" % (ex_ms * 1e3,
                                                                         100 * k_true / sh.f))
 
+    # predictor quality on the same tokens: the predicted set against the
+    # true set (every pre-activation computed by asf_exact_ffn)
+    quality = None
+    if args.dense_steps > 0:
+        nqt = min(200, args.tokens)
+        act_p = torch.empty(sh.f, dtype=torch.int32, device=dev)
+        act_t = torch.empty(sh.f, dtype=torch.int32, device=dev)
+        n_p = torch.empty(1, dtype=torch.int32, device=dev)
+        n_t = torch.empty(1, dtype=torch.int32, device=dev)
+        hit = tot_p = tot_t = 0
+        for t in range(nqt):
+            ring[0].predict(Xd[t], active=act_p, n_active=n_p)
+            ring[0].exact_ffn(Xd[t], out=Y[0], active=act_t, n_active=n_t)
+            kp, kt_ = int(n_p.item()), int(n_t.item())
+            hit += int(torch.isin(act_p[:kp], act_t[:kt_]).sum().item())
+            tot_p += kp
+            tot_t += kt_
+        quality = {"tokens": nqt, "recall": hit / max(tot_t, 1), "precision": hit / max(tot_p, 1),
+                   "predicted_frac": tot_p / nqt / sh.f, "true_frac": tot_t / nqt / sh.f}
+        log(args, "predictor: recall %.3f precision %.3f" % (quality["recall"],
+                                                           quality["precision"]))
+
+    # a plain device-to-device copy of 1 GiB: this box's measured stream rate
+    stream = None
+    if args.dense_steps > 0:
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / 10
+        copy_gbs = 2 * src.numel() * 2 / (cms * 1e-3) / 1e9
+        stream = {"kind": "device-to-device copy of 1 GiB (read + write bytes)",
+                  "gbps": copy_gbs, "frac_of_peak": copy_gbs / HBM_PEAK_GBS}
+        del src, dst
+        torch.cuda.empty_cache()
+
     ffn_only = None
     if args.dense_steps > 0 and args.ffn_rhos:
         ffn_only = bench_ffn_only(args, ring, Xd, Y, L, dense_ms, dense_bytes, torch, wl, dev, sh_)
@@ -681,6 +723,9 @@ def main():
         "dense_ms_per_step": dense_ms,
         "dense_gbps": None if dense_ms is None else dense_bytes / (dense_ms * 1e-3) / 1e9,
         "sparse_step_speedup_vs_dense": None if dense_ms is None else dense_ms / ms_per_step,
+        "effective_frac_of_stream": None if stream is None else eff_gbs / stream["gbps"],
+        "stream_copy": stream,
+        "predictor_quality": quality,
         "exact_mask": exact,
         "sparse_ffn_only": ffn_only,
         "roofline": {"bound": "hbm", "kernel": dname, "achieved": achieved,
