@@ -668,7 +668,7 @@ def main():
                                                            quality["precision"]))
 
     # a plain device-to-device copy of 1 GiB: this box's measured stream rate
-    stream = None
+    stream_ref = None
     if args.dense_steps > 0:
         src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
         dst = torch.empty_like(src)
@@ -682,7 +682,7 @@ def main():
         torch.cuda.synchronize()
         cms = e0.elapsed_time(e1) / 10
         copy_gbs = 2 * src.numel() * 2 / (cms * 1e-3) / 1e9
-        stream = {"kind": "device-to-device copy of 1 GiB (read + write bytes)",
+        stream_ref = {"kind": "device-to-device copy of 1 GiB (read + write bytes)",
                   "gbps": copy_gbs, "frac_of_peak": copy_gbs / HBM_PEAK_GBS}
         del src, dst
         torch.cuda.empty_cache()
@@ -723,8 +723,8 @@ def main():
         "dense_ms_per_step": dense_ms,
         "dense_gbps": None if dense_ms is None else dense_bytes / (dense_ms * 1e-3) / 1e9,
         "sparse_step_speedup_vs_dense": None if dense_ms is None else dense_ms / ms_per_step,
-        "effective_frac_of_stream": None if stream is None else eff_gbs / stream["gbps"],
-        "stream_copy": stream,
+        "effective_frac_of_stream": None if stream_ref is None else eff_gbs / stream_ref["gbps"],
+        "stream_copy": stream_ref,
         "predictor_quality": quality,
         "exact_mask": exact,
         "sparse_ffn_only": ffn_only,
