@@ -383,8 +383,10 @@ __global__ void k_to_f16(const float *__restrict__ x, int n, _Float16 *__restric
 // owner with pre[q] <= r < pre[q+1], pre the popcount prefix); mode 1 the
 // caller's ids in list order; mode 2 every slot.  Workgroup b takes rows
 // Rb .. Rb+R-1 as one tile streamed with the token tile of x (fp16) over k = d
-// in chunks of 256 k.  R = 32 while the list needs at most one workgroup per
-// CU; a longer list is spread evenly over the workgroups resident at once
+// in chunks of 256 k.  While the list needs at most one 32-row workgroup
+// per CU it is spread over one workgroup per CU (R = its length over the
+// CUs, at least kFc1MinRows); a longer list is spread evenly over the
+// workgroups resident at once
 // (R = its length over them, at least kFc1MinRows; the tile's other rows are
 // dead), since a CU holding two workgroups runs each ~30% slower and an
 // uneven split leaves the kernel waiting on the doubled CUs.  a = ReLU(up . x + b1) (gated: ReLU(gate . x +
@@ -406,7 +408,11 @@ __global__ __launch_bounds__(kThreads) void k_fc1_mm(Fc1MmParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // rows per workgroup from the list length (the same in every workgroup)
     auto tile_rows = [&](int n) {
-        if (n <= kTile * p.ncu) return kTile;
+        if (n <= kTile * p.ncu) {
+            // one workgroup per CU at most: spread the list over every CU
+            const int r = (n + p.ncu - 1) / p.ncu;
+            return r < kFc1MinRows ? kFc1MinRows : r;
+        }
         const int nw = p.per_cu * p.ncu;
         const int r = (n + nw - 1) / nw;
         return r < kFc1MinRows ? kFc1MinRows : (r > kTile ? kTile : r);
