@@ -1520,6 +1520,9 @@ struct Fc2SumArgs {
     float *y;
 };
 
+// SQ: owner rows per thread (owners g, g + 128, ... below SQ * 128 >= nq),
+// so that no load repeats a row; the sums do not depend on it.
+template <int SQ = kSumQ>
 __device__ __forceinline__ void fc2_sum_block(const Fc2SumArgs &a, int s) {
     __shared__ float4 red[kThreads];
     const float *__restrict__ part = a.part;
@@ -1533,15 +1536,15 @@ __device__ __forceinline__ void fc2_sum_block(const Fc2SumArgs &a, int s) {
     const int o = tid & 15;
     const float bv = b2[16 * s + o];
     const float rv = resid ? resid[16 * s + o] : 0.0f;
-    float4 v[kSumQ];
+    float4 v[SQ];
 #pragma unroll
-    for (int k = 0; k < kSumQ; ++k) {
+    for (int k = 0; k < SQ; ++k) {
         const int q = g + (kThreads / 4) * k;
         v[k] = src[(size_t)(q < nq ? q : nq - 1) * 4 + c];
     }
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
-    for (int k = 0; k < kSumQ; ++k) {
+    for (int k = 0; k < SQ; ++k) {
         if (g + (kThreads / 4) * k < nq) {
             acc.x += v[k].x;
             acc.y += v[k].y;
@@ -1563,7 +1566,10 @@ __device__ __forceinline__ void fc2_sum_block(const Fc2SumArgs &a, int s) {
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_fc2_sum(Fc2SumArgs a) { fc2_sum_block(a, blockIdx.x); }
+template <int SQ>
+__global__ __launch_bounds__(kThreads) void k_fc2_sum(Fc2SumArgs a) {
+    fc2_sum_block<SQ>(a, blockIdx.x);
+}
 
 // ---------------------------------------------------------------- look-ahead stack on one stream
 // With layer l + 1's set predicted from layer l's input, each layer of the
@@ -1966,7 +1972,13 @@ hipError_t launch_fc2_sum(const LayerView &L, const float *resid, float *y, cons
                           hipStream_t s) {
     const dim3 grid(L.d / 16), blk(kThreads);
     const Fc2SumArgs a{L.part1, L.nq, L.b2, resid, y};
-    ASF_LAUNCH(ASF_K_FC2, k_fc2_sum, grid, blk, a);
+    const int sq = pow2_at_least((L.nq + kThreads / 4 - 1) / (kThreads / 4));
+    switch (sq) {
+    case 1: ASF_LAUNCH(ASF_K_FC2, k_fc2_sum<1>, grid, blk, a); break;
+    case 2: ASF_LAUNCH(ASF_K_FC2, k_fc2_sum<2>, grid, blk, a); break;
+    case 4: ASF_LAUNCH(ASF_K_FC2, k_fc2_sum<4>, grid, blk, a); break;
+    default: ASF_LAUNCH(ASF_K_FC2, k_fc2_sum<kSumQ>, grid, blk, a); break;
+    }
     return hipGetLastError();
 }
 
