@@ -927,7 +927,23 @@ __device__ __forceinline__ void owner_ffn1(const ScoreParams &p, int q, int nq, 
     }
     const uint64_t mr = SPEC ? (valid & ~((1ull << kSpecRows) - 1ull)) : valid;
     const int nr = __popcll(mr);
-    for (int r = (wave - off + kWaves) % kWaves; r < nr; r += kWaves) {
+    int r = (wave - off + kWaves) % kWaves;
+    if constexpr (kWide && Fc1Regs<GATED, CPL1>::chunks <= 8) {
+        // a wave with two rows requests both before using either
+        for (; r + kWaves < nr; r += 2 * kWaves) {
+            const int i0 = nth_set_bit(mr, r), i1 = nth_set_bit(mr, r + kWaves);
+            const int s0 = q + nq * i0, s1 = q + nq * i1;
+            const float bias0 = p.b1[s0], bias1 = p.b1[s1];
+            u32x4 wu0[CPL1], wg0[CPL1], wu1[CPL1], wg1[CPL1];
+            load_fc1_rows<GATED, CPL1>(p.bundles, p.bstride, p.cd, s0, lane, wu0, wg0);
+            load_fc1_rows<GATED, CPL1>(p.bundles, p.bstride, p.cd, s1, lane, wu1, wg1);
+            fc1_entry_1<WT, GATED, CPL1>(q, valid, i0, s0, wu0, wg0, p.cd, bias0, xs, p.out, a_lds,
+                                         lane);
+            fc1_entry_1<WT, GATED, CPL1>(q, valid, i1, s1, wu1, wg1, p.cd, bias1, xs, p.out, a_lds,
+                                         lane);
+        }
+    }
+    for (; r < nr; r += kWaves) {
         const int i = nth_set_bit(mr, r);
         const int slot = q + nq * i;
         const float bias = p.b1[slot];
