@@ -1606,11 +1606,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     else pred1_block<WT>(a, blockIdx.x - nq);
 }
 
-template <int WT, int CPL2>
+template <int WT, int CPL2, int SQ>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     Fc1Regs<false, 1>::waves_per_eu))) void k_score1_fc2sum(ScoreParams p, int nq, Fc2SumArgs a) {
     if ((int)blockIdx.x < nq) score1_block<WT, CPL2, false, false, 1, false>(p, blockIdx.x, nq);
-    else fc2_sum_block(a, blockIdx.x - nq);
+    else fc2_sum_block<SQ>(a, blockIdx.x - nq);
 }
 
 // ---------------------------------------------------------------- activation profiler
@@ -2068,14 +2068,23 @@ hipError_t launch_score1_fc2sum(const LayerView *N, const LayerView &L, const fl
     const Fc2SumArgs a{L.part1, L.nq, L.b2, resid, y};
     const dim3 grid(N->nq + L.d / 16), blk(kThreads);
     const int cpl2 = pow2_at_least((N->ch + 63) / 64);
-#define ASF_SF(WT)                                                                                  \
-    switch (cpl2) {                                                                                 \
-    case 1: ASF_LAUNCH(ASF_K_FC2, (k_score1_fc2sum<WT, 1>), grid, blk, p, N->nq, a); break;      \
-    case 2: ASF_LAUNCH(ASF_K_FC2, (k_score1_fc2sum<WT, 2>), grid, blk, p, N->nq, a); break;      \
-    default: ASF_LAUNCH(ASF_K_FC2, (k_score1_fc2sum<WT, 4>), grid, blk, p, N->nq, a); break;     \
+    const int sq = pow2_at_least((L.nq + kThreads / 4 - 1) / (kThreads / 4));
+#define ASF_SFQ(WT, C2)                                                                              \
+    switch (sq) {                                                                                    \
+    case 1: ASF_LAUNCH(ASF_K_FC2, (k_score1_fc2sum<WT, C2, 1>), grid, blk, p, N->nq, a); break;     \
+    case 2: ASF_LAUNCH(ASF_K_FC2, (k_score1_fc2sum<WT, C2, 2>), grid, blk, p, N->nq, a); break;     \
+    case 4: ASF_LAUNCH(ASF_K_FC2, (k_score1_fc2sum<WT, C2, 4>), grid, blk, p, N->nq, a); break;     \
+    default: ASF_LAUNCH(ASF_K_FC2, (k_score1_fc2sum<WT, C2, kSumQ>), grid, blk, p, N->nq, a); break; \
+    }
+#define ASF_SF(WT)                                  \
+    switch (cpl2) {                                 \
+    case 1: ASF_SFQ(WT, 1) break;                   \
+    case 2: ASF_SFQ(WT, 2) break;                   \
+    default: ASF_SFQ(WT, 4) break;                  \
     }
     if (N->wtype == ASF_F16) { ASF_SF(1) } else { ASF_SF(0) }
 #undef ASF_SF
+#undef ASF_SFQ
     return hipGetLastError();
 }
 
