@@ -369,3 +369,24 @@ def test_one_token_list_is_the_decode_step(orc, cfg, d, f, H):
                            n_active=to_dev(np.array([st.size], np.int32)))
         y_orc = orc.ffn(L.w_up, L.w_down, x[t], st, b1=L.b1, b2=L.b2, W_gate=L.w_gate)
         assert rel_l2(y.cpu().numpy()[0], y_orc[0]) <= TOL[sh.wdtype]
+
+
+def test_one_token_long_lists(orc):
+    """Caller lists longer than one pass of the list kernel (2048 ids per
+    pass): 40% of the neurons against the oracle, every neuron against the
+    dense comparator, both in shuffled order."""
+    need_gpu()
+    _, sh = wl.CONFIGS["opt6.7b_ffn"]
+    L = wl.make_layer(wl.scaled_shape(sh, 1024, 16384, 256), 555)
+    lay = asf().layer_from_numpy(L)
+    x = wl.make_tokens(1024, 2, 556)
+    rng = np.random.default_rng(557)
+    ids = rng.choice(16384, 6554, replace=False).astype(np.int32)
+    y = lay.sparse_ffn(to_dev(x[:1]), active=to_dev(ids), n_active=to_dev(np.array([ids.size], np.int32)))
+    y_orc = orc.ffn(L.w_up, L.w_down, x[0], ids, b1=L.b1, b2=L.b2)
+    assert rel_l2(y.cpu().numpy()[0], y_orc[0]) <= TOL["f16"]
+    allids = rng.permutation(16384).astype(np.int32)
+    yall = lay.sparse_ffn(to_dev(x[1:]), active=to_dev(allids),
+                          n_active=to_dev(np.array([allids.size], np.int32)))
+    yd = lay.dense_ffn_ref(to_dev(x[1:]))
+    assert rel_l2(yall.cpu().numpy(), yd.cpu().numpy()) <= 1e-5
