@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--ffn-rhos", type=float, nargs="*", default=[0.07, 0.10],
                     help="mean activations of the sparse_ffn-alone measurement (none skips it)")
     ap.add_argument("--ffn-sets", type=int, default=256)
+    ap.add_argument("--gated-steps", type=int, default=1000,
+                    help="decode steps of the gated Llama-7B-shaped layer (0 skips it)")
+    ap.add_argument("--gated-ring", type=int, default=12)
     ap.add_argument("--stack-tokens", type=int, default=256,
                     help="tokens through the 48-layer stack (0 skips the stack)")
     ap.add_argument("--stack-warmup", type=int, default=8)
@@ -331,6 +334,70 @@ def bench_layout(args, asf, torch, np, wl, dev, stream):
     log(args, "layout ablation (us per step): identity %.2f, profiled %.2f, generator %.2f; %.1f s"
         % (res["identity_us_per_step"], res["profiled_us_per_step"], res["generator_us_per_step"],
            time.perf_counter() - t0))
+    return res
+
+
+def bench_gated(args, asf, torch, np, wl, dev, stream):
+    """The Llama-7B-shaped gated ReLU layer (4096x11008, gate/up/down fp16,
+    predictor 4096->1024->11008, ~10% active): batch-1 decode steps over a
+    ring of layer copies, and the dense comparator on the same ring."""
+    name = "llama7b_gated_relu"
+    L = wl.config_layer(name)
+    sh = L.shape
+    X = torch.from_numpy(wl.config_tokens(name, args.tokens)).to(dev)
+
+    def up(a):
+        return None if a is None else torch.from_numpy(a).to(dev)
+    orig = dict(w_up=up(L.w_up), w_down=up(L.w_down), w_gate=up(L.w_gate), p1=up(L.p1),
+                p2=up(L.p2), b1=up(L.b1), b2=up(L.b2), c2=up(L.c2), neuron_table=up(L.perm))
+    ring = [asf.Layer(orig["w_up"], orig["w_down"], orig["p1"], orig["p2"],
+                      w_gate=orig["w_gate"], b1=orig["b1"], b2=orig["b2"], c2=orig["c2"],
+                      neuron_table=orig["neuron_table"]) for _ in range(args.gated_ring)]
+    torch.cuda.synchronize()
+    del orig
+    torch.cuda.empty_cache()
+    Y = torch.empty((len(ring), 1, sh.d), dtype=torch.float32, device=dev)
+    xs = [X[t].data_ptr() for t in range(X.shape[0])]
+    ys = [Y[r].data_ptr() for r in range(len(ring))]
+    sh_ = stream.cuda_stream
+    n = args.gated_steps
+    for i in range(50):
+        ring[i % len(ring)].decode_step_raw(xs[i % len(xs)], 1, ys[i % len(ring)], sh_)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        ring[i % len(ring)].decode_step_raw(xs[i % len(xs)], 1, ys[i % len(ring)], sh_)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    counts = torch.zeros(n, dtype=torch.int32, device=dev)
+    for i in range(n):
+        ring[i % len(ring)].predict(X[i % X.shape[0]], active=None, n_active=counts[i:i + 1],
+                                    want_list=False)
+    torch.cuda.synchronize()
+    k = float(counts.double().mean())
+    step_bytes, _, dense_bytes = bytes_model(sh, k)
+    nd = max(5, min(args.dense_steps, n))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ring[0].dense_ffn_ref(X[:1])
+    e0.record()
+    for i in range(nd):
+        ring[i % len(ring)].dense_ffn_ref(X[i % X.shape[0]], out=Y[i % len(ring)])
+    e1.record()
+    torch.cuda.synchronize()
+    dense_ms = e0.elapsed_time(e1) / nd
+    ms = el * 1e3 / n
+    for lay in ring:
+        lay.close()
+    res = {"workload": "Llama-7B-shaped gated ReLU FFN layer 4096x11008 fp16 (gate, up, down), "
+                       "predictor 4096->1024->11008, ~10% active, batch 1",
+           "ring_layers": len(ring), "steps": n, "tokens_per_s": n / el, "ms_per_step": ms,
+           "active_frac": k / sh.f, "algorithmic_bytes_per_step": step_bytes,
+           "effective_gbps": step_bytes / (ms * 1e-3) / 1e9,
+           "effective_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "dense_ms_per_step": dense_ms, "dense_gbps": dense_bytes / (dense_ms * 1e-3) / 1e9,
+           "speedup_vs_dense": dense_ms / ms, "byte_ceiling_vs_dense": dense_bytes / step_bytes}
+    log(args, "gated: %.1f us per step, %.1f%% active, %.2fx dense" % (ms * 1e3, 100 * k / sh.f,
+                                                                      dense_ms / ms))
     return res
 
 
@@ -740,6 +807,10 @@ def main():
     torch.cuda.empty_cache()
     if args.layout_steps > 0:
         out["layout"] = bench_layout(args, asf, torch, np, wl, dev, stream)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    if args.gated_steps > 0:
+        out["gated"] = bench_gated(args, asf, torch, np, wl, dev, stream)
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
     if args.stack_tokens > 0:
