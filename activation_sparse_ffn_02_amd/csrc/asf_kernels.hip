@@ -907,6 +907,25 @@ __device__ __forceinline__ void owner_ffn1(const ScoreParams &p, int q, int nq, 
     constexpr bool kTight = !kWide && CPT == 2;
     constexpr int PF = kTight ? (CPL1 >= 12 ? 0 : 2) : PF2;   // no spills
     constexpr int PFB = (kWide && Fc1Regs<GATED, CPL1>::chunks + 2 * PF * CPT <= 32) ? PF : 0;
+    // FC1 balanced by rank: with SPEC, bit b < kSpecRows (rows held) is
+    // wave b's; the other entries, ranked among themselves, go to waves
+    // off, off + 1, ... round the 8 waves
+    constexpr int off = SPEC ? kSpecRows : 0;
+    const uint64_t mr = SPEC ? (valid & ~((1ull << kSpecRows) - 1ull)) : valid;
+    const int nr = __popcll(mr);
+    int r = (wave - off + kWaves) % kWaves;
+    // with room for it, the wave's first FC1 row is requested ahead of the
+    // down columns (it is needed first); a wave without one requests the
+    // owner's first slot instead (held by wave 0 already) and drops it
+    constexpr bool kHoist = kWide && Fc1Regs<GATED, CPL1>::chunks <= 8;
+    u32x4 hu[kHoist ? CPL1 : 1], hg[kHoist ? CPL1 : 1];
+    const bool has_h = r < nr;
+    const int hbit = (kHoist && has_h) ? nth_set_bit(mr, r) : 0;
+    float hbias = 0.0f;
+    if constexpr (kHoist) {
+        hbias = p.b1[q + nq * hbit];
+        load_fc1_rows<GATED, CPL1>(p.bundles, p.bstride, p.cd, q + nq * hbit, lane, hu, hg);
+    }
     const u32x4 *dn = p.bundles + p.dn_off;
     u32x4 dv[PF > 0 ? PF : 1][CPT];
     u32x4 dvb[PFB > 0 ? PFB : 1][CPT];
@@ -914,10 +933,6 @@ __device__ __forceinline__ void owner_ffn1(const ScoreParams &p, int q, int nq, 
     if constexpr (PF > 0) rest = load_down<PF, CPT>(dv, valid, dn, p.bstride, q, nq, p.cd);
     if constexpr (PFB > 0)
         if (cnt > PF) rest = load_down<PFB, CPT>(dvb, rest, dn, p.bstride, q, nq, p.cd);
-    // FC1 balanced by rank: with SPEC, bit b < kSpecRows (rows held) is
-    // wave b's; the other entries, ranked among themselves, go to waves
-    // off, off + 1, ... round the 8 waves
-    constexpr int off = SPEC ? kSpecRows : 0;
     if constexpr (SPEC) {
         if (wave < kSpecRows && ((valid >> wave) & 1ull)) {
             const int slot = q + nq * wave;
@@ -925,11 +940,15 @@ __device__ __forceinline__ void owner_ffn1(const ScoreParams &p, int q, int nq, 
                                          p.out, a_lds, lane);
         }
     }
-    const uint64_t mr = SPEC ? (valid & ~((1ull << kSpecRows) - 1ull)) : valid;
-    const int nr = __popcll(mr);
-    int r = (wave - off + kWaves) % kWaves;
+    if constexpr (kHoist) {
+        if (has_h) {
+            fc1_entry_1<WT, GATED, CPL1>(q, valid, hbit, q + nq * hbit, hu, hg, p.cd, hbias, xs,
+                                         p.out, a_lds, lane);
+            r += kWaves;
+        }
+    }
     if constexpr (kWide && Fc1Regs<GATED, CPL1>::chunks <= 8) {
-        // a wave with two rows requests both before using either
+        // a wave with two more rows requests both before using either
         for (; r + kWaves < nr; r += 2 * kWaves) {
             const int i0 = nth_set_bit(mr, r), i1 = nth_set_bit(mr, r + kWaves);
             const int s0 = q + nq * i0, s1 = q + nq * i1;
