@@ -324,3 +324,61 @@ def test_count_and_active_list(orc):
     lst = orc.active_list(act[2], perm)
     assert lst.tolist() == [int(i) for i in perm if act[2, i]]
     assert orc.active_list(act[2]).tolist() == np.nonzero(act[2])[0].tolist()
+
+
+# --------------------------------------------------------------- true mask
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("dt", [np.float32, np.float16])
+def test_true_mask_pre_activations_vs_numpy_float64(orc, gated, dt):
+    """The true set rests on the FFN's own ReLU zero pattern ("Técnicas
+    dispersas…", section "Viabilidad de la sparsidad de activación"):
+    pre = W x + b1 with W the gate matrix when gated (the gated layer's set is
+    decided by ReLU(gate)), else the up matrix; act = pre > 0, strict."""
+    rng = np.random.default_rng(77 + 2 * gated + (dt == np.float16))
+    d, f, B = 48, 130, 4
+    Wu = (rng.standard_normal((f, d)) * 0.2).astype(dt)
+    Wg = (rng.standard_normal((f, d)) * 0.2).astype(dt) if gated else None
+    b1 = (rng.standard_normal(f) * 0.3).astype(np.float32)
+    x = rng.standard_normal((B, d)).astype(np.float32)
+    pre, act = orc.true_mask(Wu, x, b1=b1, W_gate=Wg)
+    W = (Wg if gated else Wu).astype(np.float64)
+    ref = x.astype(np.float64) @ W.T + b1.astype(np.float64)
+    np.testing.assert_allclose(pre, ref, rtol=1e-12, atol=1e-13)
+    assert np.array_equal(act, (pre > 0).astype(np.uint8))
+    # the set differs from the other matrix's (a swapped W would fail here)
+    if gated:
+        other = x.astype(np.float64) @ Wu.astype(np.float64).T + b1
+        assert not np.array_equal(act, (other > 0).astype(np.uint8))
+    # the gated FFN over the true set is the dense gated FFN bit for bit (the
+    # terms off the set are exact zeros and both sums run in ascending id)
+    Wd = (rng.standard_normal((d, f)) * 0.2).astype(dt)
+    b2 = (rng.standard_normal(d) * 0.1).astype(np.float32)
+    dense = orc.dense_ffn(Wu, Wd, x, b1=b1, b2=b2, W_gate=Wg)
+    for b in range(B):
+        T = np.nonzero(act[b])[0]
+        y = orc.ffn(Wu, Wd, x[b], T, b1=b1, b2=b2, W_gate=Wg)
+        assert np.array_equal(y[0], dense[b])
+
+
+def test_true_mask_bias_and_tie(orc):
+    """b1 is added before the comparison (not after the store), no bias means
+    zero, and a pre-activation of exactly 0 is inactive."""
+    d, f = 4, 6
+    W = np.zeros((f, d), np.float32)
+    W[0, 0] = 1.0          # z0 = x0
+    W[1, 1] = -1.0         # z1 = -x1
+    W[2, 2] = 0.5          # z2 = x2 / 2
+    x = np.array([[2.0, 3.0, -4.0, 1.0]], np.float32)
+    b1 = np.array([-2.0, 3.0, 2.5, 0.0, -1.0, 0.75], np.float32)
+    pre, act = orc.true_mask(W, x, b1=b1)
+    assert pre[0].tolist() == [0.0, 0.0, 0.5, 0.0, -1.0, 0.75]
+    assert act[0].tolist() == [0, 0, 1, 0, 0, 1]
+    pre0, act0 = orc.true_mask(W, x)
+    assert pre0[0].tolist() == [2.0, -3.0, -2.0, 0.0, 0.0, 0.0]
+    assert act0[0].tolist() == [1, 0, 0, 0, 0, 0]
+    # gated: the gate decides, up never does
+    Wg = np.zeros((f, d), np.float32)
+    Wg[3, 3] = 1.0
+    pre_g, act_g = orc.true_mask(W, x, W_gate=Wg)
+    assert pre_g[0].tolist() == [0.0, 0.0, 0.0, 1.0, 0.0, 0.0]
+    assert act_g[0].tolist() == [0, 0, 0, 1, 0, 0]
