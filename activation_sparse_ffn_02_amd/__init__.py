@@ -109,16 +109,41 @@ def _wtype(t: torch.Tensor) -> int:
     raise TypeError("weights must be float16 or float32, got %s" % t.dtype)
 
 
-def _dev_ptr(t: Optional[torch.Tensor], dtype=None, name: str = "") -> Optional[int]:
+def _arg(t: Optional[torch.Tensor], name: str, dtype=None, shape=None,
+         min_numel=None) -> Optional[int]:
+    """Check a tensor argument's dtype, shape (exact, or at least
+    ``min_numel`` elements) and contiguity, and return its data pointer
+    (None for None).  The C ABI takes bare pointers, so a short buffer would
+    be read or written out of bounds on the device: a mismatch raises
+    ValueError (TypeError for a wrong dtype) here instead.  Where the tensor
+    lives is checked by ``_on_device`` once every argument has passed."""
     if t is None:
         return None
-    if not t.is_cuda:
-        raise ValueError("%s must be a device tensor" % name)
-    if not t.is_contiguous():
-        raise ValueError("%s must be contiguous" % name)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
     if dtype is not None and t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError("%s must hold at least %d elements, got %d" % (name, min_numel, t.numel()))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
     return t.data_ptr()
+
+
+def _on_device(device, **tensors) -> None:
+    """Every given tensor (None skipped) is a GPU tensor on ``device`` (on
+    the same device as the others when ``device`` is None)."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("%s must be a device tensor" % name)
+        if device is None:
+            device = t.device
+        elif t.device != torch.device(device):
+            raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
 
 
 def _stream(stream) -> int:
@@ -141,18 +166,37 @@ def storage_bytes(d_model: int, d_ffn: int, pred_hidden: int, max_batch: int = 1
     return int(_lib.asf_layer_storage_bytes(ctypes.byref(desc)))
 
 
+def _tokens(x, d_model: int, max_b: int) -> torch.Tensor:
+    """x as [B][d_model] float32 (a 1-D x is one token), B in 1 .. max_b."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("x must be a torch.Tensor")
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    if x.dim() != 2 or x.shape[1] != d_model:
+        raise ValueError("x must be [B][%d], got %s" % (d_model, tuple(x.shape)))
+    if not 1 <= x.shape[0] <= max_b:
+        raise ValueError("batch %d outside 1 .. %d" % (x.shape[0], max_b))
+    _arg(x, "x", torch.float32)
+    return x
+
+
 class Layer:
     """One FFN layer resident in device storage owned by this object.
 
     Weights are given in their original nn.Linear layouts (device tensors):
     w_up/w_gate [f][d], w_down [d][f], p1 [H][d], p2 [f][H]; biases float32.
     ``neuron_table`` (int32 [f], slot -> original id, hot neurons first) sets
-    the stored order; None keeps the original order.
+    the stored order; None keeps the original order.  Every tensor argument
+    of every call is checked (dtype, shape, device) before the C call.
     """
 
     def __init__(self, w_up, w_down, p1, p2, *, w_gate=None, b1=None, b2=None, c1=None,
                  c2=None, neuron_table=None, max_batch: int = 1, threshold: float = 0.0,
                  stream=None, storage: Optional[torch.Tensor] = None):
+        if not isinstance(w_up, torch.Tensor) or w_up.dim() != 2:
+            raise ValueError("w_up must be a [d_ffn][d_model] tensor")
+        if not isinstance(p1, torch.Tensor) or p1.dim() != 2:
+            raise ValueError("p1 must be a [pred_hidden][d_model] tensor")
         f, d = w_up.shape
         H = p1.shape[0]
         wt = _wtype(w_up)
@@ -160,34 +204,34 @@ class Layer:
         self.d_model, self.d_ffn, self.pred_hidden, self.max_batch = d, f, H, max_batch
         self.gated = w_gate is not None
         self.device = w_up.device
+        w = LayerWeights(_arg(w_up, "w_up", tdt, (f, d)), _arg(w_gate, "w_gate", tdt, (f, d)),
+                         _arg(b1, "b1", torch.float32, (f,)), _arg(w_down, "w_down", tdt, (d, f)),
+                         _arg(b2, "b2", torch.float32, (d,)), _arg(p1, "p1", tdt, (H, d)),
+                         _arg(c1, "c1", torch.float32, (H,)), _arg(p2, "p2", tdt, (f, H)),
+                         _arg(c2, "c2", torch.float32, (f,)))
+        table = _arg(neuron_table, "neuron_table", torch.int32, (f,))
         self.desc = make_desc(d, f, H, max_batch, self.gated, wt, threshold)
         nbytes = int(_lib.asf_layer_storage_bytes(ctypes.byref(self.desc)))
         if nbytes == 0:
             raise AsfError(2, "asf_layer_storage_bytes")
+        _arg(storage, "storage", torch.uint8, min_numel=nbytes)
+        _on_device(None, w_up=w_up, w_gate=w_gate, b1=b1, w_down=w_down, b2=b2, p1=p1, c1=c1,
+                   p2=p2, c2=c2, neuron_table=neuron_table, storage=storage)
         if storage is None:
             storage = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         self.storage = storage
-        w = LayerWeights(_dev_ptr(w_up, tdt, "w_up"), _dev_ptr(w_gate, tdt, "w_gate"),
-                         _dev_ptr(b1, torch.float32, "b1"), _dev_ptr(w_down, tdt, "w_down"),
-                         _dev_ptr(b2, torch.float32, "b2"), _dev_ptr(p1, tdt, "p1"),
-                         _dev_ptr(c1, torch.float32, "c1"), _dev_ptr(p2, tdt, "p2"),
-                         _dev_ptr(c2, torch.float32, "c2"))
         handle = _vp()
         _check(_lib.asf_create_layer(ctypes.byref(self.desc), ctypes.byref(w),
-                                     _dev_ptr(neuron_table, torch.int32, "neuron_table"),
-                                     storage.data_ptr(), storage.numel(), _stream(stream),
+                                     table, storage.data_ptr(), storage.numel(), _stream(stream),
                                      ctypes.byref(handle)), "asf_create_layer")
         self._h = handle.value
 
     # ------------------------------------------------------------------ helpers
-    def _x(self, x: torch.Tensor) -> torch.Tensor:
-        if x.dim() == 1:
-            x = x.unsqueeze(0)
-        if x.shape[-1] != self.d_model:
-            raise ValueError("x must be [B][%d]" % self.d_model)
-        return x
+    def _vec(self, t, name, B):
+        """A [B][d_model] float32 operand (residual, out)."""
+        return _arg(t, name, torch.float32, (B, self.d_model))
 
-    def _out(self, out, B):
+    def _new_out(self, out, B):
         if out is None:
             out = torch.empty((B, self.d_model), dtype=torch.float32, device=self.device)
         return out
@@ -200,41 +244,60 @@ class Layer:
     def predict(self, x, active=None, n_active=None, token_masks=None, stream=None,
                 want_list: bool = True):
         """Returns (active ids [f] int32, n_active [1] int32); entries past
-        n_active are unspecified."""
-        x = self._x(x)
+        n_active are unspecified.  ``token_masks``: int64 [B][ceil(f/64)]."""
+        x = _tokens(x, self.d_model, self.max_batch)
         B = x.shape[0]
+        _arg(active, "active", torch.int32, min_numel=self.d_ffn)
+        _arg(n_active, "n_active", torch.int32, min_numel=1)
+        pm = _arg(token_masks, "token_masks", torch.int64, min_numel=B * ((self.d_ffn + 63) // 64))
+        _on_device(self.device, x=x, active=active, n_active=n_active, token_masks=token_masks)
         if want_list and active is None:
             active = torch.empty(self.d_ffn, dtype=torch.int32, device=self.device)
         if want_list and n_active is None:
             n_active = torch.empty(1, dtype=torch.int32, device=self.device)
-        _check(_lib.asf_predict(self._h, _dev_ptr(x, torch.float32, "x"), B,
-                                _dev_ptr(active, torch.int32, "active"),
-                                _dev_ptr(n_active, torch.int32, "n_active"),
-                                _dev_ptr(token_masks, torch.int64, "token_masks"), _stream(stream)),
+        pa, pn = _arg(active, "active"), _arg(n_active, "n_active")
+        _check(_lib.asf_predict(self._h, x.data_ptr(), B, pa, pn, pm, _stream(stream)),
                "asf_predict")
         return active, n_active
 
     def sparse_ffn(self, x, active=None, n_active=None, residual=None, out=None, stream=None):
-        x = self._x(x)
+        """FFN over a neuron set.  ``active``: a 1-D int32 list of at most
+        d_ffn original ids on the device, or None for the layer's last
+        prediction.  ``n_active``: a device int32 count, or None for all of
+        ``active``.  A device count is not read back here: it must not
+        exceed ``active.numel()`` (the library reads that many ids, at most
+        d_ffn)."""
+        x = _tokens(x, self.d_model, self.max_batch)
         B = x.shape[0]
-        out = self._out(out, B)
-        _check(_lib.asf_sparse_ffn(self._h, _dev_ptr(x, torch.float32, "x"), B,
-                                   _dev_ptr(active, torch.int32, "active"),
-                                   _dev_ptr(n_active, torch.int32, "n_active"),
-                                   _dev_ptr(residual, torch.float32, "residual"),
-                                   _dev_ptr(out, torch.float32, "out"), _stream(stream)),
+        if active is not None:
+            _arg(active, "active", torch.int32)
+            if active.dim() != 1 or active.numel() > self.d_ffn:
+                raise ValueError("active must be a 1-D list of at most %d ids" % self.d_ffn)
+        elif n_active is not None:
+            raise ValueError("n_active without active")
+        pr, po = self._vec(residual, "residual", B), self._vec(out, "out", B)
+        _arg(n_active, "n_active", torch.int32, min_numel=1)
+        _on_device(self.device, x=x, active=active, n_active=n_active, residual=residual, out=out)
+        out = self._new_out(out, B)
+        if active is not None and n_active is None:
+            n_active = torch.full((1,), active.numel(), dtype=torch.int32, device=self.device)
+        _check(_lib.asf_sparse_ffn(self._h, x.data_ptr(), B, _arg(active, "active"),
+                                   _arg(n_active, "n_active"), pr, out.data_ptr(),
+                                   _stream(stream)),
                "asf_sparse_ffn")
         return out
 
     def decode_step(self, x, residual=None, out=None, active=None, n_active=None, stream=None):
-        x = self._x(x)
+        x = _tokens(x, self.d_model, self.max_batch)
         B = x.shape[0]
-        out = self._out(out, B)
-        _check(_lib.asf_decode_step(self._h, _dev_ptr(x, torch.float32, "x"), B,
-                                    _dev_ptr(residual, torch.float32, "residual"),
-                                    _dev_ptr(out, torch.float32, "out"),
-                                    _dev_ptr(active, torch.int32, "active"),
-                                    _dev_ptr(n_active, torch.int32, "n_active"), _stream(stream)),
+        pr = self._vec(residual, "residual", B)
+        self._vec(out, "out", B)
+        pa = _arg(active, "active", torch.int32, min_numel=self.d_ffn)
+        pn = _arg(n_active, "n_active", torch.int32, min_numel=1)
+        _on_device(self.device, x=x, residual=residual, out=out, active=active, n_active=n_active)
+        out = self._new_out(out, B)
+        _check(_lib.asf_decode_step(self._h, x.data_ptr(), B, pr, out.data_ptr(), pa, pn,
+                                    _stream(stream)),
                "asf_decode_step")
         return out
 
@@ -259,14 +322,15 @@ class Layer:
     def exact_ffn(self, x, residual=None, out=None, active=None, n_active=None, stream=None):
         """asf_exact_ffn: one token through the FFN over its true active set
         (every pre-activation computed, no predictor)."""
-        x = self._x(x)
-        B = x.shape[0]
-        out = self._out(out, B)
-        _check(_lib.asf_exact_ffn(self._h, _dev_ptr(x, torch.float32, "x"), B,
-                                  _dev_ptr(residual, torch.float32, "residual"),
-                                  _dev_ptr(out, torch.float32, "out"),
-                                  _dev_ptr(active, torch.int32, "active"),
-                                  _dev_ptr(n_active, torch.int32, "n_active"), _stream(stream)),
+        x = _tokens(x, self.d_model, 1)
+        pr = self._vec(residual, "residual", 1)
+        self._vec(out, "out", 1)
+        pa = _arg(active, "active", torch.int32, min_numel=self.d_ffn)
+        pn = _arg(n_active, "n_active", torch.int32, min_numel=1)
+        _on_device(self.device, x=x, residual=residual, out=out, active=active, n_active=n_active)
+        out = self._new_out(out, 1)
+        _check(_lib.asf_exact_ffn(self._h, x.data_ptr(), 1, pr, out.data_ptr(), pa, pn,
+                                  _stream(stream)),
                "asf_exact_ffn")
         return out
 
@@ -280,22 +344,31 @@ class Layer:
         """asf_profile_activations: add each token's true active set (by
         original id) into `counts` (uint32 viewed as int32 [d_ffn]; zeros when
         not given); returns counts."""
-        x = self._x(x)
+        if not isinstance(x, torch.Tensor):
+            raise TypeError("x must be a torch.Tensor")
+        if x.dim() == 1:
+            x = x.unsqueeze(0)
+        if x.dim() != 2 or x.shape[1] != self.d_model:
+            raise ValueError("x must be [n][%d], got %s" % (self.d_model, tuple(x.shape)))
+        px = _arg(x, "x", torch.float32)
+        _arg(counts, "counts", torch.int32, (self.d_ffn,))
+        _on_device(self.device, x=x, counts=counts)
         if counts is None:
-            counts = torch.zeros(self.d_ffn, dtype=torch.int32, device=x.device)
-        _check(_lib.asf_profile_activations(self._h, _dev_ptr(x, torch.float32, "x"), x.shape[0],
-                                            _dev_ptr(counts, torch.int32, "counts"),
+            counts = torch.zeros(self.d_ffn, dtype=torch.int32, device=self.device)
+        _check(_lib.asf_profile_activations(self._h, px, x.shape[0], counts.data_ptr(),
                                             _stream(stream)),
                "asf_profile_activations")
         return counts
 
     def dense_ffn_ref(self, x, residual=None, out=None, stream=None):
-        x = self._x(x)
+        x = _tokens(x, self.d_model, self.max_batch)
         B = x.shape[0]
-        out = self._out(out, B)
-        _check(_lib.asf_dense_ffn_ref(self._h, _dev_ptr(x, torch.float32, "x"), B,
-                                      _dev_ptr(residual, torch.float32, "residual"),
-                                      _dev_ptr(out, torch.float32, "out"), _stream(stream)),
+        pr = self._vec(residual, "residual", B)
+        self._vec(out, "out", B)
+        _on_device(self.device, x=x, residual=residual, out=out)
+        out = self._new_out(out, B)
+        _check(_lib.asf_dense_ffn_ref(self._h, x.data_ptr(), B, pr, out.data_ptr(),
+                                      _stream(stream)),
                "asf_dense_ffn_ref")
         return out
 
@@ -320,7 +393,7 @@ class Layer:
 class Stack:
     """Layers run one after another in one call (asf_stack_decode):
     x_{l+1} = FFN_l(x_l), plus x_l when ``residual``.  Holds references to the
-    layers; every layer must have the same d_model."""
+    layers; every layer must have the same d_model and device."""
 
     def __init__(self, layers, residual: bool = False):
         self.layers = list(layers)
@@ -328,6 +401,10 @@ class Stack:
             raise ValueError("empty stack")
         self.d_model = self.layers[0].d_model
         self.device = self.layers[0].device
+        for l in self.layers:
+            if l.d_model != self.d_model or l.device != self.device:
+                raise ValueError("every layer of a stack needs the same d_model and device")
+        self.max_batch = min(l.max_batch for l in self.layers)
         self.residual = 1 if residual else 0
         self._arr = (_vp * len(self.layers))(*[l.handle for l in self.layers])
         self._work = {}
@@ -339,33 +416,34 @@ class Stack:
             self._work[B] = w
         return w
 
-    def decode(self, x, out=None, work=None, stream=None):
-        if x.dim() == 1:
-            x = x.unsqueeze(0)
+    def _args(self, x, out, work, max_b):
+        """x, out, work as [B][d_model] float32 on the stack's device."""
+        x = _tokens(x, self.d_model, max_b)
         B = x.shape[0]
+        shape = (B, self.d_model)
+        _arg(out, "out", torch.float32, shape)
+        _arg(work, "work", torch.float32, shape)
+        _on_device(self.device, x=x, out=out, work=work)
         if out is None:
-            out = torch.empty((B, self.d_model), dtype=torch.float32, device=self.device)
+            out = torch.empty(shape, dtype=torch.float32, device=self.device)
         if work is None:
             work = self._work_for(B)
-        _check(_lib.asf_stack_decode(self._arr, len(self.layers), _dev_ptr(x, torch.float32, "x"),
-                                     B, self.residual, _dev_ptr(out, torch.float32, "out"),
-                                     _dev_ptr(work, torch.float32, "work"), _stream(stream)),
+        return x, out, work
+
+    def decode(self, x, out=None, work=None, stream=None):
+        x, out, work = self._args(x, out, work, self.max_batch)
+        _check(_lib.asf_stack_decode(self._arr, len(self.layers), x.data_ptr(), x.shape[0],
+                                     self.residual, out.data_ptr(), work.data_ptr(),
+                                     _stream(stream)),
                "asf_stack_decode")
         return out
 
     def decode_lookahead(self, x, out=None, work=None, stream=None):
         """asf_stack_decode_lookahead: one token, layer l+1's set predicted
         from layer l's input, in the same launches as layer l's FFN."""
-        if x.dim() == 1:
-            x = x.unsqueeze(0)
-        if out is None:
-            out = torch.empty((1, self.d_model), dtype=torch.float32, device=self.device)
-        if work is None:
-            work = self._work_for(1)
-        _check(_lib.asf_stack_decode_lookahead(self._arr, len(self.layers),
-                                               _dev_ptr(x, torch.float32, "x"), self.residual,
-                                               _dev_ptr(out, torch.float32, "out"),
-                                               _dev_ptr(work, torch.float32, "work"),
+        x, out, work = self._args(x, out, work, 1)
+        _check(_lib.asf_stack_decode_lookahead(self._arr, len(self.layers), x.data_ptr(),
+                                               self.residual, out.data_ptr(), work.data_ptr(),
                                                _stream(stream)),
                "asf_stack_decode_lookahead")
         return out
@@ -389,10 +467,13 @@ class Stack:
 def hot_first_table(counts, stream=None):
     """asf_hot_first_table: int32 [d_ffn] table (slot -> original id), most
     frequently active first, ties by smaller id, from device counts."""
+    if not isinstance(counts, torch.Tensor) or counts.dim() != 1:
+        raise ValueError("counts must be a 1-D int32 device tensor")
     f = counts.numel()
+    pc = _arg(counts, "counts", torch.int32)
+    _on_device(None, counts=counts)
     table = torch.empty(f, dtype=torch.int32, device=counts.device)
-    _check(_lib.asf_hot_first_table(_dev_ptr(counts, torch.int32, "counts"), f,
-                                    _dev_ptr(table, torch.int32, "table"), _stream(stream)),
+    _check(_lib.asf_hot_first_table(pc, f, table.data_ptr(), _stream(stream)),
            "asf_hot_first_table")
     return table
 
