@@ -88,5 +88,11 @@ def test_exact_residual_repeat_and_batch_rejected():
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
     assert rel_l2(yr.cpu().numpy(), (y0 + r).cpu().numpy()) <= 1e-6
-    with pytest.raises(m.AsfError):
-        lay.exact_ffn(torch.cat([x, x]))
+    # two tokens: refused by the binding, and by the C ABI itself
+    x2 = torch.cat([x, x])
+    with pytest.raises(ValueError):
+        lay.exact_ffn(x2)
+    y2 = torch.empty_like(x2)
+    rc = m.library().asf_exact_ffn(lay.handle, x2.data_ptr(), 2, None, y2.data_ptr(), None,
+                                   None, None)
+    assert rc == 5   # ASF_ERR_UNSUPPORTED

@@ -245,6 +245,7 @@ def _batched_check(orc, L, x, lay, label, check_dense=True, user_list=True):
     for bit to predict + sparse_ffn; outputs against the oracle over the GPU's
     union; a caller id list in any order; the dense comparator."""
     B, f = x.shape[0], L.shape.f
+    tol = TOL[L.shape.wdtype]
     xd = to_dev(x)
     masks = torch.zeros((B, (f + 63) // 64), dtype=torch.int64, device="cuda")
     active, n = lay.predict(xd, token_masks=masks)
@@ -269,7 +270,7 @@ def _batched_check(orc, L, x, lay, label, check_dense=True, user_list=True):
     y_orc = orc.ffn(L.w_up, L.w_down, x, ids, b1=L.b1, b2=L.b2, W_gate=L.w_gate)
     yg = y1.cpu().numpy()
     worst = max(rel_l2(yg[t], y_orc[t]) for t in range(B))
-    assert worst <= TOL["f16"], "%s: rel-L2 %.3g" % (label, worst)
+    assert worst <= tol, "%s: rel-L2 %.3g" % (label, worst)
     if user_list:
         rng = np.random.default_rng(B)
         sub = rng.permutation(ids)[: max(1, k // 2)].astype(np.int32)
@@ -277,12 +278,12 @@ def _batched_check(orc, L, x, lay, label, check_dense=True, user_list=True):
         yl_orc = orc.ffn(L.w_up, L.w_down, x, sub, b1=L.b1, b2=L.b2, W_gate=L.w_gate)
         ylg = yl.cpu().numpy()
         for t in range(B):
-            assert rel_l2(ylg[t], yl_orc[t]) <= TOL["f16"]
+            assert rel_l2(ylg[t], yl_orc[t]) <= tol
     if check_dense:
         yd = lay.dense_ffn_ref(xd).cpu().numpy()
         yd_orc = orc.dense_ffn(L.w_up, L.w_down, x, b1=L.b1, b2=L.b2, W_gate=L.w_gate)
         for t in range(B):
-            assert rel_l2(yd[t], yd_orc[t]) <= TOL["f16"]
+            assert rel_l2(yd[t], yd_orc[t]) <= tol
     print("%s: B=%d union %d (%.3f), worst rel-L2 %.3g, ambiguous flips %d"
           % (label, B, k, k / f, worst, amb))
 
@@ -300,6 +301,20 @@ def test_batched_matrix_core_path(orc, B, gated):
     lay = asf().layer_from_numpy(L, max_batch=32)
     x = wl.make_tokens(1152, B, 950 + B)
     _batched_check(orc, L, x, lay, "mm %s" % ("gated" if gated else "plain"))
+
+
+@pytest.mark.parametrize("B", [2, 4, 5, 32])
+def test_batched_fp32_weights(orc, B):
+    """fp32 weights with B >= 2 run the vector kernels (predictor layer 1
+    over token chunks of 4, scores per token chunk, FC1 over the union, the
+    grouped FC2): per-token sets, the union, outputs over it, a caller list
+    and the dense comparator against the oracle, at a ragged d_ffn."""
+    need_gpu()
+    _, sh = wl.CONFIGS["tiny_f32"]
+    L = wl.make_layer(wl.scaled_shape(sh, 640, 2500 + 3 * B, 128), 1300 + B)
+    lay = asf().layer_from_numpy(L, max_batch=32)
+    x = wl.make_tokens(640, B, 1350 + B)
+    _batched_check(orc, L, x, lay, "fp32 B%d" % B)
 
 
 def test_batched_full_size(orc):

@@ -23,7 +23,7 @@ from gpu_util import TOL, asf, check_set, need_gpu, rel_l2, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _device_layers(shapes, seed0, keep=()):
+def _device_layers(shapes, seed0, keep=(), max_batch=1):
     """Create library layers from device-generated weights; keep host copies
     of the layers whose index is in `keep` (for the oracle)."""
     from workload.gpu import make_layer_device
@@ -32,7 +32,8 @@ def _device_layers(shapes, seed0, keep=()):
     for l, sh in enumerate(shapes):
         DL = make_layer_device(sh, seed0 + l, torch.device("cuda"))
         layers.append(m.Layer(DL.w_up, DL.w_down, DL.p1, DL.p2, w_gate=DL.w_gate, b1=DL.b1,
-                              b2=DL.b2, c1=DL.c1, c2=DL.c2, neuron_table=DL.perm))
+                              b2=DL.b2, c1=DL.c1, c2=DL.c2, neuron_table=DL.perm,
+                              max_batch=max_batch))
         if l in keep:
             host[l] = DL.to_numpy()
         del DL
@@ -84,6 +85,41 @@ def test_small_stack_equals_chained_steps(orc, residual):
     inplace = xt.clone()
     st.decode(inplace, out=inplace)
     assert torch.equal(inplace, ref)
+
+
+def test_small_stack_batched(orc):
+    """B = 4 tokens through the stack: the batched decode step per layer
+    (union of the tokens' sets), equal bit for bit to the chained batched
+    steps; per layer, the union against the oracle's scores on the layer's
+    actual input (a neuron surely in or out of every token's set is decided
+    the same way) and every token's output over the GPU's union."""
+    need_gpu()
+    d, f, B = 512, 2048, 4
+    shapes = [wl.LayerShape(d, f, H, rho, "f16")
+              for H, rho in ((64, 0.03), (128, 0.08), (256, 0.15), (128, 0.10))]
+    layers, host = _device_layers(shapes, 740, keep=range(len(shapes)), max_batch=B)
+    for residual in (False, True):
+        st = asf().Stack(layers, residual=residual)
+        xt = to_dev(wl.make_tokens(d, B, 741 + residual))
+        y = st.decode(xt)
+        cur = xt
+        for l, lay in enumerate(layers):
+            act = torch.empty(f, dtype=torch.int32, device="cuda")
+            n = torch.empty(1, dtype=torch.int32, device="cuda")
+            nxt = lay.decode_step(cur, residual=cur if residual else None, active=act,
+                                  n_active=n)
+            torch.cuda.synchronize()
+            ids = act[:int(n.item())].cpu().numpy()
+            xin = cur.cpu().numpy()
+            L = host[l]
+            _, s_orc, _ = orc.predict(L.p1, L.c1, L.p2, L.c2, xin)
+            check_set(ids, s_orc.max(axis=0), 0.0, L.perm, "B%d layer %d union" % (B, l))
+            y_orc = orc.ffn(L.w_up, L.w_down, xin, ids, b1=L.b1, b2=L.b2)
+            yl = nxt.cpu().numpy() - (xin if residual else 0.0)
+            for t in range(B):
+                assert rel_l2(yl[t], y_orc[t]) <= TOL["f16"], (residual, l, t)
+            cur = nxt
+        assert torch.equal(y, cur), "batched stack differs from the chained steps"
 
 
 def _lookahead_check(orc, shapes, seed, residual):
@@ -151,18 +187,32 @@ def test_lookahead_mixed_stack(orc, residual):
 
 
 def test_stack_argument_errors():
+    """The C ABI refuses a layer listed twice, a d_model mismatch, B above a
+    layer's max_batch and a work buffer overlapping x or y (the binding
+    refuses the shape errors before the call)."""
     need_gpu()
     m = asf()
+    lib = m.library()
     d, f = 256, 512
     layers, _ = _device_layers([wl.LayerShape(d, f, 64, 0.1, "f16")] * 2, 720)
     other, _ = _device_layers([wl.LayerShape(384, f, 64, 0.1, "f16")], 730)
     x = torch.zeros((1, d), device="cuda")
+    y = torch.zeros((2, 384), device="cuda")
+    w = torch.zeros((2, 384), device="cuda")
+
+    def arr(ls):
+        return (m._vp * len(ls))(*[l.handle for l in ls])
     with pytest.raises(m.AsfError):
         m.Stack([layers[0], layers[0]]).decode(x)               # a layer twice
-    with pytest.raises(m.AsfError):
-        m.Stack([layers[0], other[0]]).decode(x)                # d mismatch
-    with pytest.raises(m.AsfError):
-        m.Stack(layers).decode(torch.zeros((2, d), device="cuda"))   # B > max_batch
+    assert lib.asf_stack_decode(arr([layers[0], other[0]]), 2, x.data_ptr(), 1, 0, y.data_ptr(),
+                                w.data_ptr(), None) == 2        # d mismatch: ASF_ERR_SHAPE
+    with pytest.raises(ValueError):
+        m.Stack([layers[0], other[0]])
+    x2 = torch.zeros((2, d), device="cuda")
+    assert lib.asf_stack_decode(arr(layers), 2, x2.data_ptr(), 2, 0, y.data_ptr(),
+                                w.data_ptr(), None) == 2        # B > max_batch
+    with pytest.raises(ValueError):
+        m.Stack(layers).decode(x2)
     st = m.Stack(layers)
     buf = torch.zeros((2, d), device="cuda")
     with pytest.raises(m.AsfError):
@@ -174,7 +224,8 @@ def test_stack_argument_errors():
 
 
 def test_opt30b_stack_full_size(orc):
-    """48 layers of 7168x28672 fp16, 2 tokens; oracle on layers 0, 23, 47."""
+    """48 layers of 7168x28672 fp16, 2 tokens through asf_stack_decode and one
+    through the look-ahead form; oracle on layers 0, 23, 47."""
     need_gpu()
     from workload.gpu import stack_layer_device
     m = asf()
@@ -216,3 +267,33 @@ def test_opt30b_stack_full_size(orc):
         rms = float(y.pow(2).mean().sqrt())
         assert 0.5 < rms < 2.0, rms
         print("token %d: sampled-layer rel-L2 %s, output rms %.3f" % (t, errs, rms))
+    # the look-ahead form at this shape (d = 7168: FC1 rows of 14 chunks per
+    # lane beside the next layer's predictor layer 1; 448 owners): equal bit
+    # for bit to predict(x_{l-1}) + sparse_ffn(x_l) chained by hand; the
+    # sampled layers' sets against the oracle on x_{l-1}, outputs on x_l
+    xt = to_dev(x[:1])
+    y_la = st.decode_lookahead(xt)
+    prev, cur = xt, xt
+    errs = []
+    for l, lay in enumerate(layers):
+        if l in sampled:
+            act = torch.empty(f, dtype=torch.int32, device="cuda")
+            n = torch.empty(1, dtype=torch.int32, device="cuda")
+            lay.predict(prev, active=act, n_active=n)
+        else:
+            lay.predict(prev, want_list=False)
+        nxt = lay.sparse_ffn(cur)
+        if l in sampled:
+            torch.cuda.synchronize()
+            ids = act[:int(n.item())].cpu().numpy()
+            L = host[l]
+            _, s_orc, _ = orc.predict(L.p1, L.c1, L.p2, L.c2, prev.cpu().numpy())
+            check_set(ids, s_orc[0], 0.0, L.perm, "look-ahead layer %d" % l)
+            y_orc = orc.ffn(L.w_up, L.w_down, cur.cpu().numpy()[0], ids, b1=L.b1, b2=L.b2)
+            e = rel_l2(nxt.cpu().numpy()[0], y_orc[0])
+            assert e <= TOL["f16"], ("look-ahead", l, e)
+            errs.append(e)
+        prev, cur = cur, nxt
+    torch.cuda.synchronize()
+    assert torch.equal(y_la, cur), "look-ahead stack differs from the chained calls"
+    print("look-ahead: sampled-layer rel-L2 %s" % errs)
