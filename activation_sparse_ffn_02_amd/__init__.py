@@ -68,6 +68,8 @@ _lib.asf_hot_first_table.argtypes = [_vp, _i32, _vp, _vp]
 _lib.asf_hot_first_table.restype = ctypes.c_int
 _lib.asf_stack_decode.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _i32, _i32, _vp, _vp, _vp]
 _lib.asf_stack_decode.restype = ctypes.c_int
+_lib.asf_stack_decode_static.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _i32, _i32, _vp, _vp]
+_lib.asf_stack_decode_static.restype = ctypes.c_int
 _lib.asf_stack_decode_lookahead.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _i32, _vp, _vp, _vp]
 _lib.asf_stack_decode_lookahead.restype = ctypes.c_int
 _lib.asf_dense_ffn_ref.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp]
@@ -436,6 +438,22 @@ class Stack:
                                      self.residual, out.data_ptr(), work.data_ptr(),
                                      _stream(stream)),
                "asf_stack_decode")
+        return out
+
+    def decode_static(self, x, out, stream=None):
+        """asf_stack_decode_static: as decode, with the buffer between layers
+        in the library's static device array (the call allocates nothing;
+        ``out`` is required for the same reason).  Calls that overlap on one
+        GPU share that array and must be ordered by the caller."""
+        if out is None:
+            raise ValueError("decode_static needs out (it allocates nothing)")
+        x = _tokens(x, self.d_model, self.max_batch)
+        B = x.shape[0]
+        _arg(out, "out", torch.float32, (B, self.d_model))
+        _on_device(self.device, x=x, out=out)
+        _check(_lib.asf_stack_decode_static(self._arr, len(self.layers), x.data_ptr(), B,
+                                            self.residual, out.data_ptr(), _stream(stream)),
+               "asf_stack_decode_static")
         return out
 
     def decode_lookahead(self, x, out=None, work=None, stream=None):

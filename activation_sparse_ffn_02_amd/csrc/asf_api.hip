@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "asf_internal.h"
@@ -93,6 +94,32 @@ static hipError_t launch_fc2_step(const LayerView &v, int B, const float *resid,
                                   const Trace *tr, hipStream_t s) {
     if (B == 1) return launch_fc2_sum(v, resid, y, tr, s);
     return launch_fc2(v, B, false, resid, y, tr, s);
+}
+
+// Inter-layer buffer of asf_stack_decode_static: one [B][d_model] float32
+// block per GPU, the largest any layer allows (B <= 32, d_model * weight size
+// <= 16 KiB, so d_model <= 8192).  Device code never names it: its address on
+// each device comes from hipGetSymbolAddress, taken once per device with that
+// device current.
+constexpr size_t kStaticWorkFloats = (size_t)kMaxBatch * 8192;
+static __device__ __align__(256) float scratch[kStaticWorkFloats];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static float *g_scratch_ptr[kMaxDevices];   // per device, null until first use
+
+// The current device's copy of `scratch`, or null when its address cannot be
+// taken.
+static float *static_work() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = (float *)ptr;
+    }
+    return g_scratch_ptr[dev];
 }
 
 }  // namespace asf
@@ -344,6 +371,18 @@ asf_status asf_stack_decode(asf_layer *const *layers, int32_t n_layers, const fl
         in = out;
     }
     return ASF_OK;
+}
+
+asf_status asf_stack_decode_static(asf_layer *const *layers, int32_t n_layers, const float *x,
+                                   int32_t B, int32_t residual, float *y, void *stream) {
+    if (!layers || n_layers < 1 || !layers[0]) return ASF_ERR_ARG;
+    if (B < 1 || (size_t)B * (size_t)layers[0]->v.d > kStaticWorkFloats) return ASF_ERR_SHAPE;
+    float *work = nullptr;
+    if (n_layers > 1) {
+        work = static_work();
+        if (!work) return ASF_ERR_HIP;
+    }
+    return asf_stack_decode(layers, n_layers, x, B, residual, y, work, stream);
 }
 
 asf_status asf_stack_decode_lookahead(asf_layer *const *layers, int32_t n_layers,

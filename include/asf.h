@@ -208,6 +208,21 @@ asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
 asf_status asf_stack_decode(asf_layer *const *layers, int32_t n_layers, const float *x,
                             int32_t B, int32_t residual, float *y, float *work, void *stream);
 
+/* asf_stack_decode without a caller work buffer, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The [B][d_model] float32 buffer between
+ * layers is the library's own static device array of 32 * 8192 floats
+ * (1 MiB per GPU, held until the process ends), which covers every shape a
+ * layer accepts (B <= 32, d_model <= 8192); a larger B * d_model returns
+ * ASF_ERR_SHAPE.  The call allocates nothing.  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (other streams, other
+ * threads) race and must be ordered by the caller.  The first call on a
+ * device takes the array's address there (hipGetSymbolAddress); failure
+ * returns ASF_ERR_HIP.  Arguments and results otherwise as asf_stack_decode
+ * with work == NULL (y == x allowed). */
+asf_status asf_stack_decode_static(asf_layer *const *layers, int32_t n_layers, const float *x,
+                                   int32_t B, int32_t residual, float *y, void *stream);
+
 /* asf_stack_decode for one token with the look-ahead predictor (the
  * asynchronous reading of DejaVu, "LLM模型之PowerInfer1.0" appendix "DejaVu",
  * Eq. -2): layer l+1's set is predicted from layer l's INPUT, so its
