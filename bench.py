@@ -11,9 +11,15 @@ Steps rotate over a ring of identical layer copies at distinct addresses, so
 that the ~61 MB a step reads cannot be served from the 256 MB Infinity Cache
 (a layer ring standing in for the other layers of a model).
 
-Prints ONE JSON line: tokens/s (value), effective HBM GB/s on algorithmic
-bytes, the roofline of the dominant kernel (HIP events around it inside the
-timed region), the dense comparator, and the CPU oracle baseline.
+Prints ONE JSON line: tokens/s (value: exactly --steps steps after --warmup
+steps, bracketed by device synchronisations), effective HBM GB/s on
+algorithmic bytes, the median of five repeats of --repeat-steps steps (HIP
+events on the stream) and a cache-hot figure (one layer copy), the roofline
+of the dominant kernel (the median of --trace-samples kernel durations,
+timed by HIP events on the dispatch packets in a traced pass after the timed
+region, so that tracing never perturbs the timed steps), the dense
+comparator, the CPU oracle baseline and the per-token count of neurons
+inside the 1e-3 margin.
 """
 from __future__ import annotations
 
@@ -42,11 +48,15 @@ def parse():
     ap.add_argument("--ring", type=int, default=16, help="distinct layer copies")
     ap.add_argument("--tokens", type=int, default=1000)
     ap.add_argument("--dense-steps", type=int, default=200)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="oracle time on all host threads; the 1-thread, dense and stack-subset "
+                         "legs take about half, a third and a few seconds more")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--trace-every", type=int, default=50,
-                    help="record kernel events on every n-th timed step (a step launched "
-                         "with events costs ~13 us more, so 1 in 10 adds ~1.5 us per step)")
+    ap.add_argument("--trace-samples", type=int, default=48,
+                    help="steps traced with per-kernel HIP events, in a pass of their own "
+                         "after the timed region (one step in 8, from the 17th on)")
+    ap.add_argument("--repeat-steps", type=int, default=1000,
+                    help="steps per repeat of the median-of-5 and cache-hot measurements")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--ffn-rhos", type=float, nargs="*", default=[0.07, 0.10],
                     help="mean activations of the sparse_ffn-alone measurement (none skips it)")
@@ -174,25 +184,122 @@ class HipEvents:
         self.ev = []
 
 
-def cpu_baseline(args, L, x):
-    """The oracle as it stands, on the host cores, on a bounded sample of the
-    same workload: predict + FFN over the oracle's own set, token by token."""
+def cpu_info():
+    """Host CPU model and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    return model, ncpu
+
+
+def cpu_baseline(args, L, x, gpu_sets):
+    """The oracle as it stands, on the host cores, on bounded samples of the
+    same workload:
+      - predict + FFN over the oracle's own set, token by token, on every
+        thread OpenMP is given (the reported value) and on one thread;
+      - the dense FFN, token by token;
+      - the 48-layer OPT-30B-shaped stack's layers 0, 23 and 47 (weights
+        generated on the device and read back) x 16 tokens.
+    Beside the timing, the oracle's scores of the first tokens give the
+    per-token count of neurons inside the 1e-3 margin and how many of them
+    the GPU decided the other way (``gpu_sets``: the GPU's active ids of
+    those tokens)."""
+    import numpy as np
+
     import oracle
+    import workload as wl
+    model, ncpu = cpu_info()
     n_thr = oracle.num_threads()
-    t0 = time.perf_counter()
-    done = 0
-    while done < x.shape[0]:
-        xt = x[done:done + 1]
-        _, _, act = oracle.predict(L.p1, L.c1, L.p2, L.c2, xt)
+
+    def run(fn, seconds, n_max):
+        t0 = time.perf_counter()
+        done = 0
+        while done < n_max:
+            fn(done)
+            done += 1
+            if time.perf_counter() - t0 > seconds and done >= 2:
+                break
+        return done, time.perf_counter() - t0
+
+    scores = {}
+
+    def sparse_tok(t):
+        xt = x[t:t + 1]
+        _, s, act = oracle.predict(L.p1, L.c1, L.p2, L.c2, xt)
+        if t < len(gpu_sets):
+            scores[t] = s[0]
         ids = oracle.active_list(act[0], L.perm)
         oracle.ffn(L.w_up, L.w_down, xt, ids, b1=L.b1, b2=L.b2, W_gate=L.w_gate)
-        done += 1
-        if time.perf_counter() - t0 > args.cpu_seconds and done >= 3:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "tokens/s", "cores": int(n_thr), "kind": "oracle",
-            "sample": "%d decode tokens of the same layer and token stream (fp64 predictor "
-                      "+ FFN over the predicted set), %.1f s" % (done, dt)}
+
+    def dense_tok(t):
+        oracle.dense_ffn(L.w_up, L.w_down, x[t:t + 1], b1=L.b1, b2=L.b2, W_gate=L.w_gate)
+
+    done, dt = run(sparse_tok, args.cpu_seconds, x.shape[0])
+    oracle.set_num_threads(1)
+    try:
+        done1, dt1 = run(lambda t: sparse_tok(x.shape[0] - 1 - t), args.cpu_seconds / 2,
+                         x.shape[0])
+    finally:
+        oracle.set_num_threads(n_thr)
+    dn, ddt = run(dense_tok, args.cpu_seconds / 3, x.shape[0])
+    res = {"value": done / dt, "unit": "tokens/s", "cores": int(n_thr), "kind": "oracle",
+           "sample": "%d decode tokens of the same layer and token stream (fp64 predictor + "
+                     "FFN over the predicted set), %.1f s on %d threads" % (done, dt, n_thr),
+           "cpu_model": model, "host_cpus": ncpu,
+           "one_thread": {"tokens_per_s": done1 / dt1, "tokens": done1, "seconds": dt1},
+           "dense": {"tokens_per_s": dn / ddt, "tokens": dn, "seconds": ddt,
+                     "threads": int(n_thr)}}
+    if args.stack_tokens > 0:
+        import torch
+        from workload.gpu import stack_layer_device, stack_tokens
+        xs = stack_tokens(16)
+        t_all, n_all, ks = 0.0, 0, []
+        for l in (0, 23, 47):
+            SL = stack_layer_device(l, torch.device("cuda:0")).to_numpy()
+            torch.cuda.empty_cache()
+            t0 = time.perf_counter()
+            for t in range(xs.shape[0]):
+                _, _, act = oracle.predict(SL.p1, SL.c1, SL.p2, SL.c2, xs[t:t + 1])
+                ids = oracle.active_list(act[0], SL.perm)
+                oracle.ffn(SL.w_up, SL.w_down, xs[t:t + 1], ids, b1=SL.b1, b2=SL.b2)
+                ks.append(ids.size)
+            t_all += time.perf_counter() - t0
+            n_all += xs.shape[0]
+            del SL
+        res["stack_subset"] = {
+            "sample": "layers 0, 23, 47 of the 48-layer 7168x28672 stack x 16 tokens (each "
+                      "layer fed the stack's input tokens), predict + FFN over the set",
+            "layer_tokens": n_all, "seconds": t_all, "ms_per_layer_token": t_all * 1e3 / n_all,
+            "est_ms_per_token_48_layers": t_all * 1e3 / n_all * wl.STACK_LAYERS,
+            "active_mean": float(np.mean(ks))}
+    # margin statistics of the oracle's scores (not timed)
+    amb = None
+    if scores:
+        band, flips = [], []
+        for t, s in sorted(scores.items()):
+            inband = np.abs(s) <= 1e-3
+            g = np.zeros(s.shape[0], bool)
+            g[gpu_sets[t]] = True
+            diff = g != (s > 0)
+            band.append(int(inband.sum()))
+            flips.append(int(diff.sum()))
+            if np.any(diff & ~inband):
+                raise AssertionError("token %d: the GPU set differs from the oracle's beyond "
+                                     "the 1e-3 margin" % t)
+        amb = {"tokens": len(band), "in_margin_per_token": float(np.mean(band)),
+               "gpu_flips_per_token": float(np.mean(flips)), "max_in_margin": int(max(band)),
+               "rule": "|s - theta| <= 1e-3: either decision is correct"}
+    return res, amb
 
 
 def bench_stack(args, asf, torch, np, wl, dev, stream):
@@ -599,70 +706,110 @@ def main():
     stream = torch.cuda.current_stream()
     lib = asf.library()
 
-    # HIP events around each kernel of every timed step, recorded by the
-    # library on the stream the kernels run on.
-    used = [KERNELS.index(k) for k in ("pred_l1", "score_fc1", "fc2")]
-    NE = 2 * len(KERNELS)
-    traced_steps = list(range(0, K, max(1, args.trace_every)))
-    slot_of_step = {i: n for n, i in enumerate(traced_steps)}
-    hev = HipEvents(NE * len(traced_steps) + 2)
-    EvArr = ctypes.c_void_p * NE
-
-    def ev_slots(i):
-        slots = [None] * NE
-        for j in used:
-            slots[2 * j] = hev.ev[NE * i + 2 * j]
-            slots[2 * j + 1] = hev.ev[NE * i + 2 * j + 1]
-        return EvArr(*slots)
-
-    arrs = [ev_slots(n) for n in range(len(traced_steps))]
-
     sh_ = stream.cuda_stream
     xs = [Xd[t].data_ptr() for t in range(args.tokens)]
     ys = [Y[r].data_ptr() for r in range(args.ring)]
 
-    def step(i, traced):
-        lay = ring[i % args.ring]
-        if traced:
-            lay.set_trace(arrs[slot_of_step[i - W]], len(KERNELS))
-        lay.decode_step_raw(xs[i % args.tokens], 1, ys[i % args.ring], sh_)
-        if traced:
-            lay.set_trace(None)
+    def step(i, ring_n=args.ring):
+        ring[i % ring_n].decode_step_raw(xs[i % args.tokens], 1, ys[i % ring_n], sh_)
 
+    # the timed region: exactly K steps after W warm-up steps, no events
     for i in range(W):
-        step(i, False)
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    hev.record(NE * len(traced_steps), stream.cuda_stream)
     for i in range(W, W + K):
-        step(i, (i - W) in slot_of_step)
-    hev.record(NE * len(traced_steps) + 1, stream.cuda_stream)
+        step(i)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    gpu_span_ms = hev.ms(NE * len(traced_steps), NE * len(traced_steps) + 1)
-    elapsed = t1 - t0
+    elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / K
-    # active counts of the same steps, outside the timed region (the steps are
-    # deterministic, so these are the sets the timed steps used)
+
+    # repeats: 5 x R steps each bracketed by HIP events on the stream (the
+    # median of the five is the steady-state step time); then the same with
+    # one layer copy (its 61 MB stay in the 256 MB Infinity Cache: cache-hot)
+    R = max(1, args.repeat_steps)
+    hrep = HipEvents(20)
+
+    def repeats(ring_n, base):
+        per = []
+        for r in range(5):
+            hrep.record(base + 2 * r, sh_)
+            for i in range(R):
+                step(r * R + i, ring_n)
+            hrep.record(base + 2 * r + 1, sh_)
+        torch.cuda.synchronize()
+        return sorted(hrep.ms(base + 2 * r, base + 2 * r + 1) / R for r in range(5))
+
+    rep = repeats(args.ring, 0)
+    for i in range(50):
+        step(i, 1)
+    hot = repeats(1, 10)
+    hrep.close()
+
+    # per-kernel durations: a traced pass of its own (each traced step
+    # launches its kernels with HIP events on the dispatch packets, so the
+    # events time the kernels themselves on the stream they run on); one
+    # step in 8 from the 17th on, median per kernel
+    used = [KERNELS.index(k) for k in ("pred_l1", "score_fc1", "fc2")]
+    NE = 2 * len(KERNELS)
+    ns = max(1, args.trace_samples)
+    hev = HipEvents(NE * ns)
+    EvArr = ctypes.c_void_p * NE
+
+    def ev_slots(n):
+        slots = [None] * NE
+        for j in used:
+            slots[2 * j] = hev.ev[NE * n + 2 * j]
+            slots[2 * j + 1] = hev.ev[NE * n + 2 * j + 1]
+        return EvArr(*slots)
+
+    arrs = [ev_slots(n) for n in range(ns)]
+    for i in range(16 + 8 * ns):
+        traced = i >= 16 and (i - 16) % 8 == 0
+        lay = ring[i % args.ring]
+        if traced:
+            lay.set_trace(arrs[(i - 16) // 8], len(KERNELS))
+        step(i)
+        if traced:
+            lay.set_trace(None)
+    torch.cuda.synchronize()
+    kt = np.zeros((ns, len(KERNELS)))
+    for n in range(ns):
+        for j in used:
+            kt[n, j] = hev.ms(NE * n + 2 * j, NE * n + 2 * j + 1)
+    kmed = np.median(kt, axis=0)        # ms
+    # each traced step's span, first kernel's start to last kernel's stop:
+    # the kernels run one after another on one stream, so their durations
+    # must add up to at most that span (tracing itself makes a traced step
+    # slower than an untraced one)
+    j0, j1 = used[0], used[-1]
+    span = np.array([hev.ms(NE * n + 2 * j0, NE * n + 2 * j1 + 1) for n in range(ns)])
+    hev.close()
+
+    # active counts of the timed steps, outside the timed region (the steps
+    # are deterministic, so these are the sets the timed steps used)
     for i in range(W, W + K):
         ring[i % args.ring].predict(Xd[i % args.tokens], active=None, n_active=counts[i:i + 1],
                                     want_list=False)
     torch.cuda.synchronize()
     ks = counts[W:].cpu().numpy()
     k_mean = float(ks.mean())
-
-    # per-kernel durations from the events
-    kt = np.zeros((len(traced_steps), len(KERNELS)))
-    for n in range(len(traced_steps)):
-        for j in used:
-            kt[n, j] = hev.ms(NE * n + 2 * j, NE * n + 2 * j + 1)
-    hev.close()
-    kmean = kt.mean(axis=0)             # ms
     step_bytes, per_bytes, dense_bytes = bytes_model(sh, k_mean)
-    dom = int(np.argmax(kmean))
+    dom = int(np.argmax(kmed))
     dname = KERNELS[dom]
-    achieved = per_bytes[dname] / (kmean[dom] * 1e-3) / 1e9
-    gpu_kernel_ms = float(kt.sum(axis=1).mean())
+    achieved = per_bytes[dname] / (kmed[dom] * 1e-3) / 1e9
+    kernel_sum_ms = float(kmed[used].sum())
+    within = bool(np.all(kt[:, used].sum(axis=1) <= span + 1e-6))
+    if not within:
+        log(args, "warning: a traced step's kernel durations add up to more than its span")
+    # GPU sets of the first tokens, for the margin statistics of the CPU leg
+    n_amb = 0 if args.no_cpu else min(32, args.tokens)
+    gpu_sets = []
+    act_buf = torch.empty(sh.f, dtype=torch.int32, device=dev)
+    n_buf = torch.empty(1, dtype=torch.int32, device=dev)
+    for t in range(n_amb):
+        ring[0].predict(Xd[t], active=act_buf, n_active=n_buf)
+        gpu_sets.append(act_buf[:int(n_buf.item())].cpu().numpy())
 
     # dense comparator on the same ring (skipped with --dense-steps 0, e.g. for
     # counter runs that must see the sparse step's kernels only)
@@ -783,10 +930,18 @@ def main():
         "algorithmic_bytes_per_step": step_bytes,
         "active_mean": k_mean,
         "active_frac": k_mean / sh.f,
-        "kernel_ms_mean": {KERNELS[j]: float(kmean[j]) for j in used},
-        "gpu_kernel_ms_per_step": gpu_kernel_ms,
-        "traced_steps": len(traced_steps),
-        "gpu_span_ms_per_step": gpu_span_ms / K,
+        "repeats_ms_per_step": rep,
+        "median5_ms_per_step": rep[2],
+        "median5_tokens_per_s": 1.0 / (rep[2] * 1e-3),
+        "median5_effective_frac_of_peak": step_bytes / (rep[2] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "cache_hot": {"kind": "one layer copy, its bytes resident in the 256 MB Infinity Cache",
+                      "median5_ms_per_step": hot[2],
+                      "effective_gbps": step_bytes / (hot[2] * 1e-3) / 1e9},
+        "kernel_ms_median": {KERNELS[j]: float(kmed[j]) for j in used},
+        "kernel_ms_sum": kernel_sum_ms,
+        "traced_step_span_ms_median": float(np.median(span)),
+        "kernel_sum_within_traced_span": within,
+        "traced_steps": ns,
         "dense_ms_per_step": dense_ms,
         "dense_gbps": None if dense_ms is None else dense_bytes / (dense_ms * 1e-3) / 1e9,
         "sparse_step_speedup_vs_dense": None if dense_ms is None else dense_ms / ms_per_step,
@@ -798,10 +953,11 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dname, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(dname),
-                     "algorithmic_bytes": per_bytes[dname]},
+                     "algorithmic_bytes": per_bytes[dname],
+                     "duration_ms_median": float(kmed[dom]), "samples": ns},
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(args, L, X)
+        out["cpu_baseline"], out["ambiguous"] = cpu_baseline(args, L, X, gpu_sets)
     del ring, Xd, Y
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

@@ -25,7 +25,8 @@ def test_small_run_prints_one_json_line():
     if not torch.cuda.is_available():
         pytest.skip("needs a GPU")
     args = [sys.executable, BENCH, "--quiet", "--ring", "2", "--steps", "40", "--warmup", "5",
-            "--tokens", "16", "--dense-steps", "5", "--cpu-seconds", "0.5", "--trace-every", "10",
+            "--tokens", "16", "--dense-steps", "5", "--cpu-seconds", "0.5", "--trace-samples", "8",
+            "--repeat-steps", "20",
             "--stack-tokens", "0", "--layout-steps", "0", "--gated-steps", "0", "--batches",
             "--ffn-rhos", "0.1", "--ffn-sets", "8"]
     r = subprocess.run(args, capture_output=True, text=True, timeout=600, cwd=ROOT)
@@ -44,4 +45,9 @@ def test_small_run_prints_one_json_line():
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9 and rf["achieved"] > 0
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["sample"]
+    assert cb["one_thread"]["tokens_per_s"] > 0 and cb["dense"]["tokens_per_s"] > 0
+    assert cb["cpu_model"] and cb["host_cpus"] >= 1
+    assert d["traced_steps"] == 8 and rf["samples"] == 8 and d["kernel_sum_within_traced_span"]
+    assert len(d["repeats_ms_per_step"]) == 5 and d["cache_hot"]["median5_ms_per_step"] > 0
+    assert d["ambiguous"]["tokens"] > 0 and d["ambiguous"]["in_margin_per_token"] >= 0
     assert d["sparse_ffn_only"]["by_rho"][0]["ms_per_call"] > 0
