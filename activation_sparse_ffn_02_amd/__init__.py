@@ -74,6 +74,26 @@ _lib.asf_stack_decode_lookahead.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _i32
 _lib.asf_stack_decode_lookahead.restype = ctypes.c_int
 _lib.asf_dense_ffn_ref.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp]
 _lib.asf_dense_ffn_ref.restype = ctypes.c_int
+class HeadDesc(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("pred_hidden", ctypes.c_int32), ("max_batch", ctypes.c_int32),
+                ("wtype", ctypes.c_int32), ("threshold", ctypes.c_float)]
+
+
+class HeadWeights(ctypes.Structure):
+    _fields_ = [("q1", ctypes.c_void_p), ("c1", ctypes.c_void_p), ("q2", ctypes.c_void_p),
+                ("c2", ctypes.c_void_p)]
+
+
+_lib.asf_head_predictor_storage_bytes.argtypes = [ctypes.POINTER(HeadDesc)]
+_lib.asf_head_predictor_storage_bytes.restype = ctypes.c_size_t
+_lib.asf_create_head_predictor.argtypes = [ctypes.POINTER(HeadDesc), ctypes.POINTER(HeadWeights),
+                                           _vp, ctypes.c_size_t, _vp, ctypes.POINTER(_vp)]
+_lib.asf_create_head_predictor.restype = ctypes.c_int
+_lib.asf_destroy_head_predictor.argtypes = [_vp]
+_lib.asf_destroy_head_predictor.restype = None
+_lib.asf_predict_heads.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _vp]
+_lib.asf_predict_heads.restype = ctypes.c_int
 _lib.asf_layer_set_trace.argtypes = [_vp, ctypes.POINTER(ctypes.c_void_p), _i32]
 _lib.asf_layer_set_trace.restype = ctypes.c_int
 _lib.asf_status_string.argtypes = [ctypes.c_int]
@@ -480,6 +500,95 @@ class Stack:
                                    work_ptr, stream_handle)
         if rc != ASF_OK:
             raise AsfError(rc, "asf_stack_decode")
+
+
+class HeadPredictor:
+    """Attention-head predictor (asf_create_head_predictor): q1 [H][d],
+    q2 [heads][H] device tensors (float16 or float32), c1 [H] and c2 [heads]
+    float32 or None.  ``predict`` gives each token's selected heads."""
+
+    def __init__(self, q1, q2, *, c1=None, c2=None, max_batch: int = 1,
+                 threshold: float = 0.0, stream=None, storage: Optional[torch.Tensor] = None):
+        if not isinstance(q1, torch.Tensor) or q1.dim() != 2:
+            raise ValueError("q1 must be a [pred_hidden][d_model] tensor")
+        if not isinstance(q2, torch.Tensor) or q2.dim() != 2:
+            raise ValueError("q2 must be a [n_heads][pred_hidden] tensor")
+        H, d = q1.shape
+        nh = q2.shape[0]
+        wt = _wtype(q1)
+        self.d_model, self.n_heads, self.pred_hidden, self.max_batch = d, nh, H, max_batch
+        self.words = (nh + 63) // 64
+        self.device = q1.device
+        w = HeadWeights(_arg(q1, "q1", q1.dtype, (H, d)), _arg(c1, "c1", torch.float32, (H,)),
+                        _arg(q2, "q2", q1.dtype, (nh, H)), _arg(c2, "c2", torch.float32, (nh,)))
+        self.desc = HeadDesc(d, nh, H, int(max_batch), wt, float(threshold))
+        nbytes = int(_lib.asf_head_predictor_storage_bytes(ctypes.byref(self.desc)))
+        if nbytes == 0:
+            raise AsfError(2, "asf_head_predictor_storage_bytes")
+        _arg(storage, "storage", torch.uint8, min_numel=nbytes)
+        _on_device(None, q1=q1, c1=c1, q2=q2, c2=c2, storage=storage)
+        if storage is None:
+            storage = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        self.storage = storage
+        handle = _vp()
+        _check(_lib.asf_create_head_predictor(ctypes.byref(self.desc), ctypes.byref(w),
+                                              storage.data_ptr(), storage.numel(),
+                                              _stream(stream), ctypes.byref(handle)),
+               "asf_create_head_predictor")
+        self._h = handle.value
+
+    @property
+    def handle(self) -> int:
+        return self._h
+
+    def predict(self, x, masks=None, heads=None, counts=None, stream=None):
+        """Returns (masks int64 [B][ceil(heads/64)], heads int32 [B][n_heads]
+        (row b's first counts[b] entries are token b's heads, ascending),
+        counts int32 [B]); outputs not given are allocated."""
+        x = _tokens(x, self.d_model, self.max_batch)
+        B = x.shape[0]
+        _arg(masks, "masks", torch.int64, (B, self.words))
+        _arg(heads, "heads", torch.int32, (B, self.n_heads))
+        _arg(counts, "counts", torch.int32, (B,))
+        _on_device(self.device, x=x, masks=masks, heads=heads, counts=counts)
+        if masks is None:
+            masks = torch.zeros((B, self.words), dtype=torch.int64, device=self.device)
+        if heads is None:
+            heads = torch.full((B, self.n_heads), -1, dtype=torch.int32, device=self.device)
+        if counts is None:
+            counts = torch.zeros(B, dtype=torch.int32, device=self.device)
+        _check(_lib.asf_predict_heads(self._h, x.data_ptr(), B, masks.data_ptr(),
+                                      heads.data_ptr(), counts.data_ptr(), _stream(stream)),
+               "asf_predict_heads")
+        return masks, heads, counts
+
+    def predict_raw(self, x_ptr: int, B: int, masks_ptr, heads_ptr, counts_ptr,
+                    stream_handle: int) -> None:
+        """predict on raw device pointers (None skips an output)."""
+        rc = _lib.asf_predict_heads(self._h, x_ptr, B, masks_ptr, heads_ptr, counts_ptr,
+                                    stream_handle)
+        if rc != ASF_OK:
+            raise AsfError(rc, "asf_predict_heads")
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.asf_destroy_head_predictor(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def head_predictor_from_numpy(P, device="cuda", max_batch: int = 1, threshold: float = 0.0,
+                              stream=None) -> HeadPredictor:
+    """Upload a host-side head predictor (workload.HeadPredictor-like) and create it."""
+    def up(a):
+        return None if a is None else torch.from_numpy(a).to(device)
+    return HeadPredictor(up(P.q1), up(P.q2), c1=up(P.c1), c2=up(P.c2), max_batch=max_batch,
+                         threshold=threshold, stream=stream)
 
 
 def hot_first_table(counts, stream=None):

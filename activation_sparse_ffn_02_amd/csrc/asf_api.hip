@@ -88,6 +88,46 @@ size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v) {
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+static bool head_desc_ok(const asf_head_desc &d) {
+    if (d.d_model <= 0 || d.n_heads <= 0 || d.pred_hidden <= 0) return false;
+    if (d.n_heads > kMaxHeads || d.max_batch < 1 || d.max_batch > kMaxBatch) return false;
+    if (d.wtype != ASF_F32 && d.wtype != ASF_F16) return false;
+    const int ws = d.wtype == ASF_F16 ? 2 : 4;
+    if ((d.d_model * ws) % 16 != 0 || (d.pred_hidden * ws) % 16 != 0) return false;
+    return d.d_model * ws / 16 <= 1024 && d.pred_hidden * ws / 16 <= 256;
+}
+
+size_t carve_heads(const asf_head_desc &desc, uintptr_t base, HeadView *v) {
+    const int ws = desc.wtype == ASF_F16 ? 2 : 4;
+    const size_t d = desc.d_model, nh = desc.n_heads, H = desc.pred_hidden,
+                 Bm = desc.max_batch, words = (nh + 63) / 64;
+    uintptr_t p = align_up(base, 256);
+    auto take = [&](size_t bytes) {
+        uintptr_t q = p;
+        p = align_up(p + bytes, 256);
+        return q;
+    };
+    HeadView t;
+    t.d = (int)d;
+    t.nh = (int)nh;
+    t.H = (int)H;
+    t.max_batch = (int)Bm;
+    t.wtype = desc.wtype;
+    t.threshold = desc.threshold;
+    t.ws = ws;
+    t.cd = (int)(d * ws / 16);
+    t.ch = (int)(H * ws / 16);
+    t.words = (int)words;
+    t.q1 = (void *)take(H * d * ws);
+    t.c1 = (float *)take(H * 4);
+    t.q2 = (void *)take(nh * H * ws);
+    t.c2 = (float *)take(nh * 4);
+    t.h = (float *)take(Bm * H * 4);
+    t.wbits = (uint64_t *)take(Bm * words * 8);
+    if (v) *v = t;
+    return (size_t)(p - align_up(base, 256));
+}
+
 // FC2 after launch_score with FC1: a single token's owner rows are already
 // formed (launch_fc2_sum adds them); batches go through the owner lists
 static hipError_t launch_fc2_step(const LayerView &v, int B, const float *resid, float *y,
@@ -425,6 +465,55 @@ asf_status asf_dense_ffn_ref(const asf_layer *layer, const float *x, int32_t B,
     if (launch_fc1(v, x, B, 2, nullptr, nullptr, layer->tr(), s) != hipSuccess)
         return ASF_ERR_HIP;
     if (launch_fc2(v, B, false, residual, y, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
+    return ASF_OK;
+}
+
+size_t asf_head_predictor_storage_bytes(const asf_head_desc *desc) {
+    if (!desc || !head_desc_ok(*desc)) return 0;
+    return carve_heads(*desc, 0, nullptr) + 256;
+}
+
+asf_status asf_create_head_predictor(const asf_head_desc *desc, const asf_head_weights *w,
+                                     void *storage, size_t storage_bytes, void *stream,
+                                     asf_head_predictor **out) {
+    if (out) *out = nullptr;
+    if (!desc || !w || !storage || !out || !w->q1 || !w->q2) return ASF_ERR_ARG;
+    if (desc->wtype != ASF_F32 && desc->wtype != ASF_F16) return ASF_ERR_ARG;
+    if (!head_desc_ok(*desc)) return ASF_ERR_SHAPE;
+    if (!aligned16(w->q1) || !aligned16(w->q2) || !aligned16(storage)) return ASF_ERR_ALIGN;
+    if (storage_bytes < asf_head_predictor_storage_bytes(desc)) return ASF_ERR_STORAGE;
+    asf_head_predictor *P = new (std::nothrow) asf_head_predictor;
+    if (!P) return ASF_ERR_ARG;
+    carve_heads(*desc, (uintptr_t)storage, &P->v);
+    const HeadView &v = P->v;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    auto chk = [&](hipError_t r) {
+        if (e == hipSuccess && r != hipSuccess) e = r;
+    };
+    chk(hipMemcpyAsync(v.q1, w->q1, (size_t)v.H * v.d * v.ws, hipMemcpyDeviceToDevice, s));
+    chk(launch_gather_f32(w->c1, nullptr, v.H, v.c1, s));
+    chk(hipMemcpyAsync(v.q2, w->q2, (size_t)v.nh * v.H * v.ws, hipMemcpyDeviceToDevice, s));
+    chk(launch_gather_f32(w->c2, nullptr, v.nh, v.c2, s));
+    if (e != hipSuccess) {
+        delete P;
+        return ASF_ERR_HIP;
+    }
+    *out = P;
+    return ASF_OK;
+}
+
+void asf_destroy_head_predictor(asf_head_predictor *hp) { delete hp; }
+
+asf_status asf_predict_heads(const asf_head_predictor *hp, const float *x, int32_t B,
+                             uint64_t *head_masks, int32_t *heads, int32_t *n_sel,
+                             void *stream) {
+    if (!hp || !x || (!head_masks && !heads && !n_sel)) return ASF_ERR_ARG;
+    if (B < 1 || B > hp->v.max_batch) return ASF_ERR_SHAPE;
+    if (!aligned16(x)) return ASF_ERR_ALIGN;
+    if (launch_head_predict(hp->v, x, B, head_masks, heads, n_sel, (hipStream_t)stream) !=
+        hipSuccess)
+        return ASF_ERR_HIP;
     return ASF_OK;
 }
 

@@ -93,6 +93,24 @@ struct LayerView {
 
 size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v);
 
+// Device view of an attention-head predictor (two-layer X-H-heads MLP).
+struct HeadView {
+    int d, nh, H, max_batch, wtype;
+    float threshold;
+    int ws, cd, ch;
+    int words;         // 64-bit words of a head mask: ceil(nh / 64)
+    void *q1;          // [H][d]
+    float *c1;         // [H]
+    void *q2;          // [nh][H]
+    float *c2;         // [nh]
+    float *h;          // [max_batch][H]   scratch: hidden activations
+    uint64_t *wbits;   // [max_batch][words] scratch: head words
+};
+constexpr int kMaxHeads = 4096;   // head words per token fit one wave (64)
+
+size_t carve_heads(const asf_head_desc &desc, uintptr_t base, HeadView *v);
+
+
 // Optional HIP events recorded around each kernel (2 per asf_kernel_id).
 struct Trace {
     hipEvent_t ev[2 * ASF_K_COUNT];
@@ -162,11 +180,19 @@ hipError_t launch_fc1_mm(const LayerView &L, const float *x, int B, int mode, co
                          const int32_t *n_ids, bool x16, const Trace *tr, hipStream_t s);
 hipError_t launch_fc2_mm(const LayerView &L, int B, bool listed, const float *resid, float *y,
                          const Trace *tr, hipStream_t s);
+// attention-head predictor: layer 1 (the FFN predictor's kernels), layer 2 +
+// threshold into per-token head words, masks / ascending lists / counts
+hipError_t launch_head_predict(const HeadView &V, const float *x, int B, uint64_t *masks,
+                               int32_t *heads, int32_t *count, hipStream_t s);
 // slot-ordered outputs of the last prediction: token masks, ascending list
 hipError_t launch_list(const LayerView &L, int B, int32_t *active_ids, int32_t *n_active,
                        uint64_t *token_masks, const Trace *tr, hipStream_t s);
 
 }  // namespace asf
+
+struct asf_head_predictor {
+    asf::HeadView v;
+};
 
 struct asf_layer {
     asf::LayerView v;

@@ -1665,6 +1665,135 @@ __global__ __launch_bounds__(kRankTile) void k_rank_table(const uint32_t *__rest
     if (i < f) table[rank] = i;
 }
 
+// ---------------------------------------------------------------- attention-head predictor
+// Layer 2 of the attention-head predictor ("LLM模型之PowerInfer1.0", appendix
+// "DejaVu": the second two-layer MLP has one output per head of the
+// attention block, each a sigmoid select / skip decision; sigmoid(s) > 0.5
+// is s > 0, so the decision is taken on the logit against theta).
+// Workgroup (w, b) scores heads 64w .. 64w+63 of token b: wave v takes heads
+// 64w + 8v + j (j < 8), its rows of Q2 in registers (clamped past nh), h of
+// the token staged in LDS and held per lane as in the FFN scores; the 8 row
+// sums of a wave meet by rows8_sum, one ballot per wave, and the 64 bits are
+// head word w of the token.  With a single word per token the workgroup
+// also lists the selected heads (ascending) and their count.
+struct HeadArgs {
+    const u32x4 *q2;   // [nh][H] row-major
+    const float *c2;   // [nh]
+    const float *h;    // [B][H]
+    int H, nh, words;
+    float theta;
+    uint64_t *wbits;   // [B][words] (library scratch)
+    uint64_t *masks;   // [B][words] or null
+    int32_t *heads;    // [B][nh] or null
+    int32_t *count;    // [B] or null
+};
+
+template <int WT, int CPL2>
+__global__ __launch_bounds__(kThreads) void k_head_score(HeadArgs a) {
+    constexpr int E = Elt<WT>::E;
+    __shared__ float hs[kMaxHLds];
+    __shared__ uint32_t bits_lds[kWaves];
+    const int w = blockIdx.x, b = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int C2 = a.H / E;
+    float4 hv[1];
+    stage_load<1>(a.h + (size_t)b * a.H, a.H, hv);
+    u32x4 q[kL2Rows][CPL2];
+#pragma unroll
+    for (int j = 0; j < kL2Rows; ++j) {
+        const int r = w * kRowsPerWG + wave * kL2Rows + j;
+        const int rc = r < a.nh ? r : a.nh - 1;
+#pragma unroll
+        for (int i = 0; i < CPL2; ++i) {
+            const int c = lane + 64 * i;
+            q[j][i] = a.q2[(size_t)rc * C2 + (c < C2 ? c : C2 - 1)];
+        }
+    }
+    const int rr = (lane >> 3) & 7;
+    const int head_r = w * kRowsPerWG + wave * kL2Rows + rr;
+    const bool valid_r = head_r < a.nh;
+    const float bias_r = a.c2[valid_r ? head_r : a.nh - 1];
+    stage_store<1>(hs, hv);
+    __syncthreads();
+    float hr[CPL2][E];
+#pragma unroll
+    for (int i = 0; i < CPL2; ++i) {
+        const int c = lane + 64 * i;
+        const float4 *h4 = reinterpret_cast<const float4 *>(hs + (c < C2 ? c : 0) * E);
+#pragma unroll
+        for (int k = 0; k < E / 4; ++k) {
+            const float4 t = h4[k];
+            hr[i][4 * k + 0] = t.x;
+            hr[i][4 * k + 1] = t.y;
+            hr[i][4 * k + 2] = t.z;
+            hr[i][4 * k + 3] = t.w;
+        }
+    }
+    float acc[kL2Rows];
+#pragma unroll
+    for (int j = 0; j < kL2Rows; ++j) {
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPL2; ++i) {
+            const int c = lane + 64 * i;
+            if (c < C2) {
+                float wv[E];
+                unpack<WT>(q[j][i], wv);
+#pragma unroll
+                for (int e = 0; e < E; ++e) s = fmaf(wv[e], hr[i][e], s);
+            }
+        }
+        acc[j] = s;
+    }
+    const float sc = rows8_sum(acc, lane) + bias_r;
+    const uint64_t m = __ballot(valid_r && sc > a.theta);
+    if (lane == 0) {
+        uint32_t bb = 0;
+#pragma unroll
+        for (int j = 0; j < kL2Rows; ++j) bb |= (uint32_t)((m >> (8 * j)) & 1ull) << j;
+        bits_lds[wave] = bb;
+    }
+    __syncthreads();
+    uint64_t word = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) word |= (uint64_t)bits_lds[v] << (kL2Rows * v);
+    if (threadIdx.x == 0) {
+        a.wbits[(size_t)b * a.words + w] = word;
+        if (a.masks) a.masks[(size_t)b * a.words + w] = word;
+        if (a.words == 1 && a.count) a.count[b] = __popcll(word);
+    }
+    if (a.words == 1 && a.heads && threadIdx.x < 64 && ((word >> threadIdx.x) & 1ull))
+        a.heads[(size_t)b * a.nh + __popcll(word & ((1ull << threadIdx.x) - 1ull))] =
+            (int)threadIdx.x;
+}
+
+// Heads of token b (one 64-lane workgroup per token, words <= 64): lane t
+// takes head word t, its popcount is prefix-summed over the wave, and the
+// lane lists its word's heads at that offset in ascending order.
+__global__ __launch_bounds__(64) void k_head_list(const uint64_t *__restrict__ wbits, int words,
+                                                  int nh, int32_t *__restrict__ heads,
+                                                  int32_t *__restrict__ count) {
+    const int b = blockIdx.x, t = threadIdx.x;
+    const uint64_t m = t < words ? wbits[(size_t)b * words + t] : 0ull;
+    const int c = __popcll(m);
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (t >= o) incl += v;
+    }
+    if (heads) {
+        int off = incl - c;
+        uint64_t u = m;
+        while (u) {
+            const int j = __builtin_ctzll(u);
+            u &= u - 1ull;
+            heads[(size_t)b * nh + off++] = 64 * t + j;
+        }
+    }
+    if (count && t == 63) count[b] = incl;
+}
+
 // ---------------------------------------------------------------- list
 // Slot-ordered outputs from the owner bits: thread t builds slot word t
 // (slots 64t .. 64t+63; slot s is bit s / nq of owner s % nq), writes the
@@ -1780,22 +1909,27 @@ hipError_t launch_gather_f32(const float *src, const int32_t *perm, int n, float
     return hipGetLastError();
 }
 
-// waves per predictor layer-1 row and the resulting chunks per lane (batched form)
-static void l1_shape(const LayerView &L, int *wpr, int *cpl) {
-    int w = L.H >= 2048 ? 1 : pow2_at_least((2048 + L.H - 1) / L.H);
+// waves per predictor layer-1 row and the resulting chunks per lane (batched
+// form), for H rows of cd chunks
+static void l1_shape_of(int H, int cd, int *wpr, int *cpl) {
+    int w = H >= 2048 ? 1 : pow2_at_least((2048 + H - 1) / H);
     if (w > 8) w = 8;
-    while (w < 8 && (L.cd + 64 * w - 1) / (64 * w) > 8) w *= 2;
+    while (w < 8 && (cd + 64 * w - 1) / (64 * w) > 8) w *= 2;
     *wpr = w;
-    *cpl = pow2_at_least((L.cd + 64 * w - 1) / (64 * w));
+    *cpl = pow2_at_least((cd + 64 * w - 1) / (64 * w));
 }
+
+static void l1_shape(const LayerView &L, int *wpr, int *cpl) { l1_shape_of(L.H, L.cd, wpr, cpl); }
 
 // single-token form: waves per row = the smallest power of two (<= 8) for
 // which a lane takes at most kPred1Cpl chunks; rows per workgroup 8 / that
-static int pred1_wpr(const LayerView &L) {
+static int pred1_wpr_of(int cd) {
     int w = 1;
-    while (w < kWaves && (L.cd + 64 * w - 1) / (64 * w) > kPred1Cpl) w *= 2;
+    while (w < kWaves && (cd + 64 * w - 1) / (64 * w) > kPred1Cpl) w *= 2;
     return w;
 }
+
+static int pred1_wpr(const LayerView &L) { return pred1_wpr_of(L.cd); }
 
 static Pred1Args pred1_args(const LayerView &L, const float *x) {
     return Pred1Args{(const u32x4 *)L.p1, L.c1, x, L.d, L.H, pred1_wpr(L), L.h};
@@ -2173,6 +2307,59 @@ hipError_t launch_fc2(const LayerView &L, int B, bool listed, const float *resid
         if (B == 1) ASF_LAUNCH(ASF_K_FC2, (k_fc2<0, 1>), grid, blk, p);
         else ASF_LAUNCH(ASF_K_FC2, (k_fc2<0, 4>), grid, blk, p);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_head_predict(const HeadView &V, const float *x, int B, uint64_t *masks,
+                               int32_t *heads, int32_t *count, hipStream_t s) {
+    const Trace *tr = nullptr;
+    // layer 1: the FFN predictor's layer-1 kernels on the head predictor's rows
+    if (B == 1) {
+        const int wpr = pred1_wpr_of(V.cd), rpw = kWaves / wpr;
+        const Pred1Args a{(const u32x4 *)V.q1, V.c1, x, V.d, V.H, wpr, V.h};
+        const dim3 grid((V.H + rpw - 1) / rpw), blk(kThreads);
+        if (V.wtype == ASF_F16) ASF_LAUNCH(ASF_K_PRED_L1, k_pred1<1>, grid, blk, a);
+        else ASF_LAUNCH(ASF_K_PRED_L1, k_pred1<0>, grid, blk, a);
+    } else {
+        int wpr, cpl;
+        l1_shape_of(V.H, V.cd, &wpr, &cpl);
+        const int rpw = kWaves / wpr;
+        const dim3 grid((V.H + rpw - 1) / rpw), blk(kThreads);
+        const u32x4 *Q1 = (const u32x4 *)V.q1;
+#define ASF_HL1(WT, CPL)                                                                          \
+    ASF_LAUNCH(ASF_K_PRED_L1, (k_pred_l1<WT, CPL, 4>), grid, blk, Q1, V.c1, x, B, V.d, V.H, wpr, \
+               V.h);
+#define ASF_HL1W(WT)                  \
+    switch (cpl) {                    \
+    case 1: ASF_HL1(WT, 1) break;     \
+    case 2: ASF_HL1(WT, 2) break;     \
+    case 4: ASF_HL1(WT, 4) break;     \
+    default: ASF_HL1(WT, 8) break;    \
+    }
+        if (V.wtype == ASF_F16) { ASF_HL1W(1) } else { ASF_HL1W(0) }
+#undef ASF_HL1W
+#undef ASF_HL1
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // layer 2, threshold, masks (and lists of a single word per token)
+    const HeadArgs a{(const u32x4 *)V.q2, V.c2, V.h, V.H, V.nh, V.words, V.threshold,
+                     V.wbits, masks, heads, count};
+    const dim3 grid(V.words, B), blk(kThreads);
+    const int cpl2 = pow2_at_least((V.ch + 63) / 64);
+    if (V.wtype == ASF_F16) {
+        if (cpl2 == 1) hipLaunchKernelGGL((k_head_score<1, 1>), grid, blk, 0, s, a);
+        else if (cpl2 == 2) hipLaunchKernelGGL((k_head_score<1, 2>), grid, blk, 0, s, a);
+        else hipLaunchKernelGGL((k_head_score<1, 4>), grid, blk, 0, s, a);
+    } else {
+        if (cpl2 == 1) hipLaunchKernelGGL((k_head_score<0, 1>), grid, blk, 0, s, a);
+        else if (cpl2 == 2) hipLaunchKernelGGL((k_head_score<0, 2>), grid, blk, 0, s, a);
+        else hipLaunchKernelGGL((k_head_score<0, 4>), grid, blk, 0, s, a);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess || V.words == 1 || (!heads && !count)) return e;
+    hipLaunchKernelGGL(k_head_list, dim3(B), dim3(64), 0, s, (const uint64_t *)V.wbits, V.words,
+                       V.nh, heads, count);
     return hipGetLastError();
 }
 

@@ -287,6 +287,77 @@ asf_status asf_profile_activations(const asf_layer *layer, const float *x, int32
 asf_status asf_hot_first_table(const uint32_t *counts, int32_t d_ffn, int32_t *table,
                                void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Attention-head predictor ("LLM模型之PowerInfer1.0", appendix "DejaVu",
+ * the SP_A model of Eq. -1): per transformer layer a second two-layer MLP
+ * whose output layer has one unit per attention head, each a sigmoid
+ * select / skip decision, so only the selected heads need to run.  Here the
+ * decision is taken on the logit: head j is selected when
+ *   s_j = Q2[j] . ReLU(Q1 x + c1) + c2_j  >  threshold   (strict; 0 is the
+ *   sigmoid-0.5 decision).
+ * Run on layer l's input y_l it gives layer l's heads (Eq. -1); run on y_l
+ * with layer l+1's weights it is the look-ahead form of Eq. -2 (the same call
+ * on another input).  Attention itself and the KV cache are not part of
+ * this library.
+ * ------------------------------------------------------------------------- */
+typedef struct asf_head_predictor asf_head_predictor; /* opaque host handle */
+
+/* Shape of one head predictor:
+ *   d_model      input width d
+ *   n_heads      outputs, one per attention head (1 .. 4096)
+ *   pred_hidden  hidden size H
+ *   max_batch    largest B any call will use (1 .. 32)
+ *   wtype        asf_dtype of Q1 and Q2
+ *   threshold    logit threshold theta
+ * Alignment and limits: d_model * sizeof(weight) and pred_hidden *
+ * sizeof(weight) multiples of 16 bytes, at most 16 KiB and 4 KiB. */
+typedef struct {
+    int32_t d_model;
+    int32_t n_heads;
+    int32_t pred_hidden;
+    int32_t max_batch;
+    int32_t wtype;
+    float threshold;
+} asf_head_desc;
+
+/* DEVICE pointers, row-major: q1 [pred_hidden][d_model], c1 [pred_hidden]
+ * float32 or NULL (= 0), q2 [n_heads][pred_hidden], c2 [n_heads] float32 or
+ * NULL (= 0).  Matrices 16-byte aligned. */
+typedef struct {
+    const void *q1;
+    const float *c1;
+    const void *q2;
+    const float *c2;
+} asf_head_weights;
+
+/* Device storage bytes of a head predictor (weights + per-call scratch);
+ * 0 for an invalid desc. */
+size_t asf_head_predictor_storage_bytes(const asf_head_desc *desc);
+
+/* Copy the weights into caller storage (DEVICE, 256-byte aligned, at least
+ * asf_head_predictor_storage_bytes) on `stream` and return a handle in *out
+ * (NULL on error).  The originals may be freed once the copy has run. */
+asf_status asf_create_head_predictor(const asf_head_desc *desc, const asf_head_weights *w,
+                                     void *storage, size_t storage_bytes, void *stream,
+                                     asf_head_predictor **out);
+
+/* Free the host handle (never the caller's storage).  NULL is a no-op. */
+void asf_destroy_head_predictor(asf_head_predictor *hp);
+
+/* Selected heads of B tokens, each token on its own (no union):
+ *   x           DEVICE float32 [B][d_model]
+ *   head_masks  DEVICE uint64 [B][ceil(n_heads/64)] or NULL: bit (j % 64) of
+ *               word (j / 64) set when head j is selected
+ *   heads       DEVICE int32 [B][n_heads] or NULL: token b's selected heads
+ *               in ascending order at heads[b][0 .. n_sel[b]); the rest of
+ *               the row is left untouched
+ *   n_sel       DEVICE int32 [B] or NULL: the count per token
+ * At least one output must be given (ASF_ERR_ARG otherwise).  Two kernels
+ * (layer 1; layer 2 + threshold + masks), a third for the lists when
+ * n_heads > 64.  The handle's scratch serves one call at a time. */
+asf_status asf_predict_heads(const asf_head_predictor *hp, const float *x, int32_t B,
+                             uint64_t *head_masks, int32_t *heads, int32_t *n_sel, void *stream);
+
 /* Kernels behind the calls (ids for asf_layer_set_trace).
  *   asf_predict       PRED_L1, SCORE, then LIST when an output is requested
  *   asf_decode_step   PRED_L1, SCORE_FC1 (B == 1, fp16; else SCORE + FC1),

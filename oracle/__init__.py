@@ -137,6 +137,16 @@ def predict(P1, c1, P2, c2, x, theta: float = 0.0):
     return h, s, act
 
 
+def predict_heads(Q1, c1, Q2, c2, x, theta: float = 0.0):
+    """Attention-head predictor ("LLM模型之PowerInfer1.0", appendix "DejaVu",
+    SP_A of Eq. -1): the two-layer MLP of ``predict`` with one output per
+    head, head j selected when its logit s_j exceeds theta (the sigmoid-0.5
+    decision at theta = 0).  Each token keeps its own set.  Returns
+    (s [B][heads], selected [B][heads] uint8, per-token ascending lists)."""
+    _, s, act = predict(Q1, c1, Q2, c2, x, theta)
+    return s, act, [np.flatnonzero(act[b]).astype(np.int32) for b in range(act.shape[0])]
+
+
 def union(act):
     lib = _load()
     act = np.ascontiguousarray(act, dtype=np.uint8)

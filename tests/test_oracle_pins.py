@@ -382,3 +382,43 @@ def test_true_mask_bias_and_tie(orc):
     pre_g, act_g = orc.true_mask(W, x, W_gate=Wg)
     assert pre_g[0].tolist() == [0.0, 0.0, 0.0, 1.0, 0.0, 0.0]
     assert act_g[0].tolist() == [0, 0, 0, 1, 0, 0]
+
+
+# --------------------------------------------------------------- attention-head predictor
+def test_head_predictor_identity_closed_form(orc):
+    """The head predictor is the two-layer MLP with one output per head
+    ("LLM模型之PowerInfer1.0", appendix "DejaVu", SP_A): with Q1 = [I; -I],
+    Q2 = [I, -I] the head logits are x itself, so token b selects the heads
+    {j : x_bj > theta}, listed in ascending order, each token on its own."""
+    n = 40
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((3, n)).astype(np.float32)
+    x[2, 5] = 0.0
+    I = np.eye(n, dtype=np.float32)
+    for theta in (0.0, 0.5):
+        s, act, lists = orc.predict_heads(np.concatenate([I, -I]), None,
+                                          np.concatenate([I, -I], axis=1), None, x, theta=theta)
+        assert np.array_equal(s, x.astype(np.float64))
+        for b in range(3):
+            assert lists[b].tolist() == [j for j in range(n) if x[b, j] > theta]
+            assert np.array_equal(act[b], (x[b] > theta).astype(np.uint8))
+        assert 5 not in lists[2].tolist()      # a logit equal to theta = 0 is not selected
+
+
+def test_head_predictor_bruteforce(orc):
+    """d = 3, H = 4, 5 heads, dyadic weights (fp64-exact): every x in
+    {-1, 0, 1}^3 against a hand loop of relu(Q1 x + c1), Q2 h + c2, s > 0."""
+    rng = np.random.default_rng(9)
+    Q1 = (rng.integers(-4, 5, (4, 3)) / 4.0).astype(np.float32)
+    c1 = (rng.integers(-4, 5, 4) / 4.0).astype(np.float32)
+    Q2 = (rng.integers(-4, 5, (5, 4)) / 4.0).astype(np.float32)
+    c2 = (rng.integers(-4, 5, 5) / 8.0).astype(np.float32)
+    xs = np.array([[a, b, c] for a in (-1, 0, 1) for b in (-1, 0, 1) for c in (-1, 0, 1)],
+                  np.float32)
+    s, act, lists = orc.predict_heads(Q1, c1, Q2, c2, xs)
+    for t, xv in enumerate(xs):
+        h = [max(0.0, sum(float(Q1[k, j]) * float(xv[j]) for j in range(3)) + float(c1[k]))
+             for k in range(4)]
+        ref = [sum(float(Q2[i, k]) * h[k] for k in range(4)) + float(c2[i]) for i in range(5)]
+        assert s[t].tolist() == ref
+        assert lists[t].tolist() == [i for i in range(5) if ref[i] > 0.0]

@@ -128,3 +128,17 @@ def test_sampled_sets_follow_the_law():
         assert np.all(np.diff(s) > 0)
         cnt[s] += 1
     assert cnt[perm[:32]].mean() > 300 and cnt[perm[-1024:]].mean() < 20
+
+
+def test_head_predictor_workload():
+    """The head predictor generator selects about its configured fraction of
+    heads per token, head by head near its selection probability (the
+    recipe's moment matching of the logits)."""
+    import oracle
+    oracle.build()
+    for name in ("opt30b_heads", "heads256"):
+        P = wl.head_config(name)
+        x = wl.head_config_tokens(name, 96)
+        _, act, _ = oracle.predict_heads(P.q1, P.c1, P.q2, P.c2, x)
+        assert abs(act.mean() - P.shape.frac) < 0.03, (name, act.mean())
+        assert np.corrcoef(act.mean(axis=0), P.p)[0, 1] > 0.9

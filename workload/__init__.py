@@ -30,6 +30,19 @@ ChatGPT/Alpaca-style decode):
   first), i.e. the order an offline activation profile would give.
 * Tokens: x ~ N(0, 1)[d], float32.
 * Seeds: layer weights 1000 + 10*config + layer, tokens 2000 + config.
+
+Attention-head predictor (the pages' DejaVu appendix: a two-layer MLP with
+one sigmoid output per head; about 20% of the heads are needed per token):
+* Each head j gets a selection probability p_j from the same capped power
+  law over a seeded random head rank (mean ``frac``, cap 0.95).
+* Q1 ~ N(0, 1/d)[H][d], c1 = 0, so each hidden pre-activation is ~N(0, 1)
+  for x ~ N(0, I) and ReLU of it has mean 1/sqrt(2 pi) and variance
+  1/2 - 1/(2 pi).
+* Q2 ~ N(0, 1/H)[heads][H]; c2_j = -m_j + s_j Phi^-1(p_j) with m_j and s_j
+  the mean and standard deviation those moments give Q2[j] . h on the stored
+  (rounded) row, so P(select head j) is near p_j.
+* Shapes: the OPT-30B-shaped attention (d_model 7168, 56 heads) and the
+  pages' example of 256 heads (d_model 4096), hidden size 1024, fp16.
 """
 from __future__ import annotations
 
@@ -226,3 +239,55 @@ def random_layer(d: int, f: int, H: int, wdtype: str, gated: bool, seed: int,
     c2 = (rng.standard_normal(f, dtype=np.float32) * np.float32(0.5) - np.float32(0.5)).astype(np.float32)
     perm = rng.permutation(f).astype(np.int32)
     return Layer(sh, w_up, w_gate, b1, w_down, b2, p1, c1, p2, c2, perm, np.full(f, 0.5))
+
+
+# ---------------------------------------------------------------- attention-head predictor
+@dataclasses.dataclass(frozen=True)
+class HeadShape:
+    d: int            # d_model
+    heads: int        # outputs (attention heads)
+    H: int            # hidden size
+    frac: float       # mean selection probability
+    wdtype: str       # "f32" or "f16"
+
+
+HEAD_CONFIGS = {
+    "opt30b_heads": (5, HeadShape(7168, 56, 1024, 0.20, "f16")),
+    "heads256": (6, HeadShape(4096, 256, 1024, 0.20, "f16")),
+}
+
+
+@dataclasses.dataclass
+class HeadPredictor:
+    shape: HeadShape
+    q1: np.ndarray                   # [H][d]
+    c1: Optional[np.ndarray]         # [H] float32 or None (zero)
+    q2: np.ndarray                   # [heads][H]
+    c2: np.ndarray                   # [heads] float32
+    p: np.ndarray                    # [heads] selection probability
+
+
+def make_head_predictor(shape: HeadShape, seed: int) -> HeadPredictor:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    d, nh, H = shape.d, shape.heads, shape.H
+    wt = np.float16 if shape.wdtype == "f16" else np.float32
+    p, _ = firing_probabilities(nh, shape.frac, rng, s=ZIPF_S, cap=0.95)
+    q1 = (rng.standard_normal((H, d), dtype=np.float32) / np.float32(np.sqrt(d))).astype(wt)
+    q2 = (rng.standard_normal((nh, H), dtype=np.float32) / np.float32(np.sqrt(H))).astype(wt)
+    q2d = q2.astype(np.float64)
+    mean_h = 1.0 / np.sqrt(2.0 * np.pi)
+    var_h = 0.5 - 1.0 / (2.0 * np.pi)
+    m = mean_h * q2d.sum(axis=1)
+    sd = np.sqrt(var_h * (q2d ** 2).sum(axis=1))
+    c2 = (-m + sd * ndtri(p)).astype(np.float32)
+    return HeadPredictor(shape, np.ascontiguousarray(q1), None, np.ascontiguousarray(q2), c2, p)
+
+
+def head_config(name: str) -> HeadPredictor:
+    idx, sh = HEAD_CONFIGS[name]
+    return make_head_predictor(sh, layer_seed(idx))
+
+
+def head_config_tokens(name: str, n: int) -> np.ndarray:
+    idx, sh = HEAD_CONFIGS[name]
+    return make_tokens(sh.d, n, token_seed(idx))
