@@ -1795,67 +1795,93 @@ __global__ __launch_bounds__(64) void k_head_list(const uint64_t *__restrict__ w
 }
 
 // ---------------------------------------------------------------- list
-// Slot-ordered outputs from the owner bits: thread t builds slot word t
-// (slots 64t .. 64t+63; slot s is bit s / nq of owner s % nq), writes the
-// per-token masks, and the ascending list of union-active slots / ids.  The
-// owner words are staged in LDS first (nq <= 1024).
-__global__ __launch_bounds__(1024) void k_list(const uint64_t *__restrict__ ubits,
-                                               const uint64_t *__restrict__ wbits, int B, int f,
-                                               int nq, int words, const int32_t *__restrict__ perm,
-                                               uint64_t *__restrict__ token_masks,
-                                               int32_t *__restrict__ slots,
-                                               int32_t *__restrict__ count,
-                                               int32_t *__restrict__ active_ids,
-                                               int32_t *__restrict__ n_active) {
-    __shared__ uint64_t ob[kMaxFfn / 64];
-    __shared__ int wave_tot[16];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    auto build = [&]() {
-        uint64_t m = 0;
-        if (t < words) {
-            for (int j = 0; j < 64; ++j) {
-                const int s = t * 64 + j;
-                if (s < f && ((ob[s % nq] >> (s / nq)) & 1ull)) m |= 1ull << j;
-            }
-        }
-        return m;
-    };
-    if (token_masks) {
-        for (int b = 0; b < B; ++b) {
-            for (int i = t; i < nq; i += blockDim.x) ob[i] = wbits[(size_t)b * nq + i];
-            __syncthreads();
-            const uint64_t m = build();
-            if (t < words) token_masks[(size_t)b * words + t] = m;
-            __syncthreads();
-        }
-    }
-    for (int i = t; i < nq; i += blockDim.x) ob[i] = ubits[i];
-    __syncthreads();
-    uint64_t u = build();
-    const int c = __popcll(u);
-    int incl = c;
+// Slot-ordered outputs from the owner bits, one workgroup per 512 stored
+// slots (thread t: slot s0 + t; wave v: slot word s0/64 + v).  Slot s is
+// bit s / nq of owner word s % nq.  Every workgroup stages the nq union
+// owner words in LDS and counts the union slots below s0 itself (owner q
+// holds the slots q + nq*i, so those below s0 are its bits i < ceil((s0 -
+// q) / nq)); the table entry of each thread's slot is requested at the start,
+// so the ascending list of slots and original ids is written without a
+// dependent load.  Per-token masks: the token words of each slot are
+// requested together (up to 32 tokens), one ballot per slot word and token.
+constexpr int kListSlots = kThreads;
+
+__device__ __forceinline__ int block_sum_int(int v, int *red) {
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-    }
-    if (lane == 63) wave_tot[wave] = incl;
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
-    int base = 0;
-    for (int k = 0; k < wave; ++k) base += wave_tot[k];
-    int off = base + incl - c;
-    while (u) {
-        const int j = __ffsll((unsigned long long)u) - 1;
-        u &= u - 1;
-        const int s = t * 64 + j;
-        slots[off] = s;
-        if (active_ids) active_ids[off] = perm[s];
-        ++off;
+    int t = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) t += red[w];
+    __syncthreads();
+    return t;
+}
+
+__global__ __launch_bounds__(kThreads) void k_list(const uint64_t *__restrict__ ubits,
+                                                   const uint64_t *__restrict__ wbits, int B,
+                                                   int f, int nq, int words,
+                                                   const int32_t *__restrict__ perm,
+                                                   uint64_t *__restrict__ token_masks,
+                                                   int32_t *__restrict__ slots,
+                                                   int32_t *__restrict__ count,
+                                                   int32_t *__restrict__ active_ids,
+                                                   int32_t *__restrict__ n_active) {
+    __shared__ uint64_t ob[kMaxFfn / 64];
+    __shared__ int red[kWaves];
+    __shared__ int wave_cnt[kWaves];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int s0 = blockIdx.x * kListSlots;
+    const int s = s0 + t;
+    const bool in = s < f;
+    const int sc = in ? s : f - 1;
+    // requests first: the owner words (at most 2 per thread), this slot's
+    // table entry, the token words of this slot
+    uint64_t o0 = ubits[t < nq ? t : nq - 1];
+    uint64_t o1 = ubits[t + kThreads < nq ? t + kThreads : nq - 1];
+    const int32_t id = active_ids ? perm[sc] : 0;
+    uint64_t tw[kMaxBatch];
+    if (token_masks) {
+#pragma unroll
+        for (int b = 0; b < kMaxBatch; ++b)
+            tw[b] = wbits[(size_t)(b < B ? b : B - 1) * nq + sc % nq];
     }
-    if (t == (int)blockDim.x - 1) {
-        const int total = base + incl;
+    if (t < nq) ob[t] = o0;
+    if (t + kThreads < nq) ob[t + kThreads] = o1;
+    __syncthreads();
+    // union slots below s0, and in all, from the owner words
+    int before = 0, total = 0;
+    for (int q = t; q < nq; q += kThreads) {
+        const uint64_t m = ob[q];
+        total += __popcll(m);
+        const int k = s0 > q ? (s0 - q + nq - 1) / nq : 0;
+        before += __popcll(k >= 64 ? m : (m & ((1ull << k) - 1ull)));
+    }
+    before = block_sum_int(before, red);
+    total = block_sum_int(total, red);
+    const bool mine = in && ((ob[sc % nq] >> (sc / nq)) & 1ull);
+    const uint64_t bal = __ballot(mine);
+    if (lane == 0) wave_cnt[wave] = __popcll(bal);
+    __syncthreads();
+    int off = before + __popcll(bal & ((1ull << lane) - 1ull));
+    for (int v = 0; v < wave; ++v) off += wave_cnt[v];
+    if (mine) {
+        slots[off] = s;
+        if (active_ids) active_ids[off] = id;
+    }
+    if (blockIdx.x == 0 && t == 0) {
         *count = total;
         if (n_active) *n_active = total;
+    }
+    if (token_masks) {
+        const int w = s0 / 64 + wave;
+        const int sh = sc / nq;
+#pragma unroll
+        for (int b = 0; b < kMaxBatch; ++b) {
+            if (b >= B) break;
+            const uint64_t m = __ballot(in && ((tw[b] >> sh) & 1ull));
+            if (lane == 0 && w < words) token_masks[(size_t)b * words + w] = m;
+        }
     }
 }
 
@@ -2365,7 +2391,8 @@ hipError_t launch_head_predict(const HeadView &V, const float *x, int B, uint64_
 
 hipError_t launch_list(const LayerView &L, int B, int32_t *active_ids, int32_t *n_active,
                        uint64_t *token_masks, const Trace *tr, hipStream_t s) {
-    ASF_LAUNCH(ASF_K_LIST, k_list, dim3(1), dim3(1024), (const uint64_t *)L.ubits,
+    ASF_LAUNCH(ASF_K_LIST, k_list, dim3((L.f + kListSlots - 1) / kListSlots), dim3(kThreads),
+               (const uint64_t *)L.ubits,
                        (const uint64_t *)L.wbits, B, L.f, L.nq, L.words, (const int32_t *)L.perm,
                        token_masks, L.slots, L.count, active_ids, n_active);
     return hipGetLastError();
