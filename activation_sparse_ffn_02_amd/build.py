@@ -1,5 +1,7 @@
 """Build libasf.so (HIP, gfx950) in-tree with hipcc: each source compiled to an
-object in parallel, then linked."""
+object in parallel, then linked.  The same kernel objects with the host API
+compiled under ASF_DEBUG give libasf_debug.so, which checks the caller's
+device content (list ids, counts, the neuron table) before use."""
 from __future__ import annotations
 
 import os
@@ -11,6 +13,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libasf.so")
+LIB_DEBUG = os.path.join(HERE, "libasf_debug.so")
 SOURCES = ["asf_api.hip", "asf_kernels.hip", "asf_batched.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -22,19 +25,32 @@ FLAGS = [
 ]
 
 
+def _link(objs, out, verbose):
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed linking %s" % os.path.basename(out))
+    os.replace(tmp, out)
+
+
 def build(verbose: bool = False) -> str:
     inc = ["-I", os.path.join(HERE, "..", "include")]
     tmpdir = tempfile.mkdtemp(prefix="asf_build_")
     try:
-        objs, procs = [], []
-        for src in SOURCES:
-            obj = os.path.join(tmpdir, src.replace(".hip", ".o"))
-            cmd = [HIPCC] + FLAGS + inc + ["-c", os.path.join(CSRC, src), "-o", obj]
+        jobs = [(src, src.replace(".hip", ".o"), []) for src in SOURCES]
+        jobs.append(("asf_api.hip", "asf_api_debug.o", ["-DASF_DEBUG"]))
+        procs = []
+        for src, obj, extra in jobs:
+            cmd = [HIPCC] + FLAGS + extra + inc + ["-c", os.path.join(CSRC, src), "-o",
+                                                   os.path.join(tmpdir, obj)]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
                                           text=True))
-            objs.append(obj)
         failed = False
         for p in procs:
             out, _ = p.communicate()
@@ -43,15 +59,10 @@ def build(verbose: bool = False) -> str:
                 failed = True
         if failed:
             raise RuntimeError("hipcc failed compiling libasf.so")
-        tmp = LIB + ".tmp%d" % os.getpid()
-        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            sys.stderr.write(r.stdout + r.stderr)
-            raise RuntimeError("hipcc failed linking libasf.so")
-        os.replace(tmp, LIB)
+        objs = {obj: os.path.join(tmpdir, obj) for _, obj, _ in jobs}
+        kernels = [objs["asf_kernels.o"], objs["asf_batched.o"]]
+        _link([objs["asf_api.o"]] + kernels, LIB, verbose)
+        _link([objs["asf_api_debug.o"]] + kernels, LIB_DEBUG, verbose)
     finally:
         shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB

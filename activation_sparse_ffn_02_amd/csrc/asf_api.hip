@@ -82,11 +82,27 @@ size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v) {
     t.slots = (int32_t *)take(f * 4);
     t.count = (int32_t *)take(64);
     t.rows = (int32_t *)take(64);
+    t.dbg = (unsigned *)take(64);
     if (v) *v = t;
     return (size_t)(p - align_up(base, 256));
 }
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+#ifdef ASF_DEBUG
+// Debug builds: the caller's device content checked before use (ids in
+// range and distinct, count in 0 .. f); synchronises the stream.  The
+// layer's slot-ordered mask scratch (at least f bits) holds the bitmap.
+static asf_status debug_check_ids(const LayerView &v, const int32_t *ids, const int32_t *n_ids,
+                                  int n_fixed, hipStream_t s) {
+    unsigned flags = 0;
+    if (launch_check_ids(ids, n_ids, n_fixed, v.f, (uint32_t *)v.masks, v.dbg, s) != hipSuccess ||
+        hipMemcpyAsync(&flags, v.dbg, 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return ASF_ERR_HIP;
+    return flags ? ASF_ERR_ARG : ASF_OK;
+}
+#endif
 
 static bool head_desc_ok(const asf_head_desc &d) {
     if (d.d_model <= 0 || d.n_heads <= 0 || d.pred_hidden <= 0) return false;
@@ -168,7 +184,11 @@ using namespace asf;
 
 extern "C" {
 
-const char *asf_version(void) { return "asf 0.1 (gfx950)"; }
+#ifdef ASF_DEBUG
+const char *asf_version(void) { return "asf 0.2 (gfx950, debug checks)"; }
+#else
+const char *asf_version(void) { return "asf 0.2 (gfx950)"; }
+#endif
 
 const char *asf_status_string(asf_status s) {
     switch (s) {
@@ -256,6 +276,16 @@ asf_status asf_create_layer(const asf_layer_desc *desc, const asf_layer_weights 
         delete L;
         return ASF_ERR_HIP;
     }
+#ifdef ASF_DEBUG
+    if (neuron_table) {
+        // a permutation of 0 .. f-1: every entry in range, none repeated
+        const asf_status st = debug_check_ids(v, neuron_table, nullptr, f, s);
+        if (st != ASF_OK) {
+            delete L;
+            return st;
+        }
+    }
+#endif
     *out = L;
     return ASF_OK;
 }
@@ -292,6 +322,12 @@ asf_status asf_sparse_ffn(const asf_layer *layer, const float *x, int32_t B,
     if (!aligned16(y) || (residual && !aligned16(residual))) return ASF_ERR_ALIGN;
     const LayerView &v = layer->v;
     hipStream_t s = (hipStream_t)stream;
+#ifdef ASF_DEBUG
+    if (active) {
+        const asf_status dst = debug_check_ids(v, active, n_active, 0, s);
+        if (dst != ASF_OK) return dst;
+    }
+#endif
     if (B == 1) {
         // one token: the decode step's per-owner FC1 + FC2 over the last set
         // or the caller's list

@@ -89,6 +89,7 @@ struct LayerView {
     int32_t *slots;    // [f]                      ascending active slots
     int32_t *count;    // [1]                      their number
     int32_t *rows;     // [1]                      rows of the batched FC1 list
+    unsigned *dbg;     // [1]                      debug-build check flags
 };
 
 size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v);
@@ -184,6 +185,11 @@ hipError_t launch_fc2_mm(const LayerView &L, int B, bool listed, const float *re
 // threshold into per-token head words, masks / ascending lists / counts
 hipError_t launch_head_predict(const HeadView &V, const float *x, int B, uint64_t *masks,
                                int32_t *heads, int32_t *count, hipStream_t s);
+// debug builds: flags |= 1 (id out of range), 2 (id repeated), 4 (count
+// outside 0 .. f) for ids[0 .. *n_ids) (n_fixed when n_ids is null), with a
+// bitmap of f bits as scratch
+hipError_t launch_check_ids(const int32_t *ids, const int32_t *n_ids, int n_fixed, int f,
+                            uint32_t *bitmap, unsigned *flags, hipStream_t s);
 // slot-ordered outputs of the last prediction: token masks, ascending list
 hipError_t launch_list(const LayerView &L, int B, int32_t *active_ids, int32_t *n_active,
                        uint64_t *token_masks, const Trace *tr, hipStream_t s);

@@ -1885,6 +1885,35 @@ __global__ __launch_bounds__(kThreads) void k_list(const uint64_t *__restrict__ 
     }
 }
 
+// ---------------------------------------------------------------- debug-build checks
+// Caller content the release build does not validate, for builds with
+// ASF_DEBUG: flag bit 1 = an entry out of range, 2 = an entry that appears
+// twice (a bitmap of f bits, one atomicOr per entry), 4 = a count outside
+// 0 .. f.  The bitmap is cleared by k_zero_u32 first.
+__global__ void k_zero_u32(uint32_t *__restrict__ p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+__global__ void k_check_ids(const int32_t *__restrict__ ids, const int32_t *__restrict__ n_ids,
+                            int n_fixed, int f, uint32_t *__restrict__ bitmap,
+                            unsigned *__restrict__ flags) {
+    int n = n_ids ? *n_ids : n_fixed;
+    if (n < 0 || n > f) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(flags, 4u);
+        n = n < 0 ? 0 : f;
+    }
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < n; e += gridDim.x * blockDim.x) {
+        const int id = ids[e];
+        if ((unsigned)id >= (unsigned)f) {
+            atomicOr(flags, 1u);
+            continue;
+        }
+        const uint32_t bit = 1u << (id & 31);
+        if (atomicOr(bitmap + (id >> 5), bit) & bit) atomicOr(flags, 2u);
+    }
+}
+
 // Traced launches carry their start/stop events on the dispatch packet itself
 // (hipExtLaunchKernelGGL), so the events time exactly the kernel.
 inline hipEvent_t ev_start(const Trace *tr, int k) { return tr ? tr->ev[2 * k] : nullptr; }
@@ -2386,6 +2415,16 @@ hipError_t launch_head_predict(const HeadView &V, const float *x, int B, uint64_
     if (e != hipSuccess || V.words == 1 || (!heads && !count)) return e;
     hipLaunchKernelGGL(k_head_list, dim3(B), dim3(64), 0, s, (const uint64_t *)V.wbits, V.words,
                        V.nh, heads, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_check_ids(const int32_t *ids, const int32_t *n_ids, int n_fixed, int f,
+                            uint32_t *bitmap, unsigned *flags, hipStream_t s) {
+    const int words = (f + 31) / 32;
+    hipLaunchKernelGGL(k_zero_u32, dim3((words + 255) / 256), dim3(256), 0, s, bitmap, words);
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, s, (uint32_t *)flags, 1);
+    hipLaunchKernelGGL(k_check_ids, dim3((f + 255) / 256), dim3(256), 0, s, ids, n_ids, n_fixed, f,
+                       bitmap, flags);
     return hipGetLastError();
 }
 

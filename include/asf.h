@@ -45,6 +45,14 @@
  *   caller-supplied active list that are out of range are skipped; duplicate
  *   ids are the caller's error (one token counts such a neuron once, a batch
  *   as often as it is listed).
+ *
+ * Debug build
+ *   libasf_debug.so (the same kernels, the host API compiled with ASF_DEBUG)
+ *   checks the device content this build takes on trust, and synchronises
+ *   the stream to do so: asf_sparse_ffn returns ASF_ERR_ARG for a caller
+ *   list with an id out of range or listed twice, or a count outside
+ *   0 .. d_ffn; asf_create_layer for a neuron table that is not a
+ *   permutation of 0 .. d_ffn-1.  asf_version names the build.
  */
 #ifndef ASF_H
 #define ASF_H
