@@ -109,7 +109,8 @@ static bool head_desc_ok(const asf_head_desc &d) {
     if (d.n_heads > kMaxHeads || d.max_batch < 1 || d.max_batch > kMaxBatch) return false;
     if (d.wtype != ASF_F32 && d.wtype != ASF_F16) return false;
     const int ws = d.wtype == ASF_F16 ? 2 : 4;
-    if ((d.d_model * ws) % 16 != 0 || (d.pred_hidden * ws) % 16 != 0) return false;
+    // layer 1 runs on the FFN predictor's kernels: the same row alignment
+    if ((d.d_model * ws) % (16 * kSlices) != 0 || (d.pred_hidden * ws) % 16 != 0) return false;
     return d.d_model * ws / 16 <= 1024 && d.pred_hidden * ws / 16 <= 256;
 }
 
@@ -140,6 +141,9 @@ size_t carve_heads(const asf_head_desc &desc, uintptr_t base, HeadView *v) {
     t.c2 = (float *)take(nh * 4);
     t.h = (float *)take(Bm * H * 4);
     t.wbits = (uint64_t *)take(Bm * words * 8);
+    t.h16 = Bm > 1 ? (_Float16 *)take(2 * Bm * H * 2) : nullptr;
+    t.x16 = Bm > 1 ? (_Float16 *)take(Bm * d * 2) : nullptr;
+    t.pred_part = Bm > 1 ? (float *)take(((H + 31) / 32) * 8 * 1024 * 4) : nullptr;
     if (v) *v = t;
     return (size_t)(p - align_up(base, 256));
 }

@@ -106,6 +106,9 @@ struct HeadView {
     float *c2;         // [nh]
     float *h;          // [max_batch][H]   scratch: hidden activations
     uint64_t *wbits;   // [max_batch][words] scratch: head words
+    _Float16 *h16;     // [2][max_batch][H] scratch of the batched layer 1 (max_batch > 1)
+    _Float16 *x16;     // [max_batch][d]
+    float *pred_part;  // [ceil(H/32)][8][32*32]
 };
 constexpr int kMaxHeads = 4096;   // head words per token fit one wave (64)
 

@@ -2367,34 +2367,25 @@ hipError_t launch_fc2(const LayerView &L, int B, bool listed, const float *resid
 
 hipError_t launch_head_predict(const HeadView &V, const float *x, int B, uint64_t *masks,
                                int32_t *heads, int32_t *count, hipStream_t s) {
-    const Trace *tr = nullptr;
-    // layer 1: the FFN predictor's layer-1 kernels on the head predictor's rows
-    if (B == 1) {
-        const int wpr = pred1_wpr_of(V.cd), rpw = kWaves / wpr;
-        const Pred1Args a{(const u32x4 *)V.q1, V.c1, x, V.d, V.H, wpr, V.h};
-        const dim3 grid((V.H + rpw - 1) / rpw), blk(kThreads);
-        if (V.wtype == ASF_F16) ASF_LAUNCH(ASF_K_PRED_L1, k_pred1<1>, grid, blk, a);
-        else ASF_LAUNCH(ASF_K_PRED_L1, k_pred1<0>, grid, blk, a);
-    } else {
-        int wpr, cpl;
-        l1_shape_of(V.H, V.cd, &wpr, &cpl);
-        const int rpw = kWaves / wpr;
-        const dim3 grid((V.H + rpw - 1) / rpw), blk(kThreads);
-        const u32x4 *Q1 = (const u32x4 *)V.q1;
-#define ASF_HL1(WT, CPL)                                                                          \
-    ASF_LAUNCH(ASF_K_PRED_L1, (k_pred_l1<WT, CPL, 4>), grid, blk, Q1, V.c1, x, B, V.d, V.H, wpr, \
-               V.h);
-#define ASF_HL1W(WT)                  \
-    switch (cpl) {                    \
-    case 1: ASF_HL1(WT, 1) break;     \
-    case 2: ASF_HL1(WT, 2) break;     \
-    case 4: ASF_HL1(WT, 4) break;     \
-    default: ASF_HL1(WT, 8) break;    \
-    }
-        if (V.wtype == ASF_F16) { ASF_HL1W(1) } else { ASF_HL1W(0) }
-#undef ASF_HL1W
-#undef ASF_HL1
-    }
+    // layer 1 through the FFN predictor's launcher on a view of the head
+    // predictor's rows and scratch: one token as a GEMV, 2-4 fp16 tokens with
+    // the weights held while the tokens go by, more on the matrix cores
+    LayerView lv = {};
+    lv.d = V.d;
+    lv.H = V.H;
+    lv.f = V.nh;
+    lv.max_batch = V.max_batch;
+    lv.wtype = V.wtype;
+    lv.ws = V.ws;
+    lv.cd = V.cd;
+    lv.ch = V.ch;
+    lv.p1 = V.q1;
+    lv.c1 = V.c1;
+    lv.h = V.h;
+    lv.h16 = V.h16;
+    lv.x16 = V.x16;
+    lv.pred_part = V.pred_part;
+    if (launch_pred_l1(lv, x, B, nullptr, s) != hipSuccess) return hipGetLastError();
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // layer 2, threshold, masks (and lists of a single word per token)

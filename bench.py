@@ -74,6 +74,9 @@ def parse():
     ap.add_argument("--layout-steps", type=int, default=1000,
                     help="decode steps per neuron-table variant (0 skips the layout ablation)")
     ap.add_argument("--layout-ring", type=int, default=8)
+    ap.add_argument("--head-calls", type=int, default=1000,
+                    help="calls of the attention-head predictor per batch size (0 skips it)")
+    ap.add_argument("--head-ring", type=int, default=48)
     ap.add_argument("--layout-calib", type=int, default=512,
                     help="calibration tokens of the on-device activation profile")
     return ap.parse_args()
@@ -506,6 +509,59 @@ def bench_gated(args, asf, torch, np, wl, dev, stream):
     log(args, "gated: %.1f us per step, %.1f%% active, %.2fx dense" % (ms * 1e3, 100 * k / sh.f,
                                                                       dense_ms / ms))
     return res
+
+
+def bench_heads(args, asf, torch, np, wl, dev, stream):
+    """The attention-head predictor of the OPT-30B-shaped attention block
+    (d_model 7168, 56 heads, hidden 1024, fp16) over a ring of copies (one
+    per layer of the 48-layer stack): per-token head masks, lists and
+    counts, batch 1 and 32."""
+    name = "opt30b_heads"
+    P = wl.head_config(name)
+    sh = P.shape
+    X = torch.from_numpy(wl.head_config_tokens(name, 1024)).to(dev)
+    ring = [asf.head_predictor_from_numpy(P, device=dev, max_batch=32)
+            for _ in range(args.head_ring)]
+    torch.cuda.synchronize()
+    words = (sh.heads + 63) // 64
+    out = []
+    sh_ = stream.cuda_stream
+    for B in (1, 32):
+        n = args.head_calls
+        masks = torch.empty((len(ring), B, words), dtype=torch.int64, device=dev)
+        heads = torch.empty((len(ring), B, sh.heads), dtype=torch.int32, device=dev)
+        counts = torch.zeros((len(ring), B), dtype=torch.int32, device=dev)
+        xs = [X[(i * B) % (1024 - B):(i * B) % (1024 - B) + B].data_ptr() for i in range(n)]
+
+        def call(i):
+            r = i % len(ring)
+            ring[r].predict_raw(xs[i], B, masks[r].data_ptr(), heads[r].data_ptr(),
+                                counts[r].data_ptr(), sh_)
+        for i in range(min(50, n)):
+            call(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        ws = 2 if sh.wdtype == "f16" else 4
+        byts = (sh.H * sh.d + sh.heads * sh.H) * ws + 4 * (sh.H + sh.heads) + 4 * B * sh.d
+        out.append({"batch": B, "calls": n, "ms_per_call": ms,
+                    "tokens_per_s": B / (ms * 1e-3),
+                    "algorithmic_bytes_per_call": byts,
+                    "effective_gbps": byts / (ms * 1e-3) / 1e9,
+                    "effective_frac_of_peak": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "selected_frac": float(counts.double().mean()) / sh.heads})
+        log(args, "head predictor B=%d: %.2f us per call, %.1f%% of heads selected"
+            % (B, ms * 1e3, 100 * out[-1]["selected_frac"]))
+    for hp in ring:
+        hp.close()
+    return {"workload": "attention-head predictor of an OPT-30B-shaped layer: 7168 -> 1024 -> "
+                        "56 heads fp16, ~20%% of heads selected, ring of %d copies"
+                        % args.head_ring, "by_batch": out}
 
 
 def bench_batched(args, asf, torch, np, wl, dev, stream):
@@ -971,6 +1027,10 @@ def main():
         torch.cuda.empty_cache()
     if args.stack_tokens > 0:
         out["stack"] = bench_stack(args, asf, torch, np, wl, dev, stream)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    if args.head_calls > 0:
+        out["head_predictor"] = bench_heads(args, asf, torch, np, wl, dev, stream)
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
     if args.batches:

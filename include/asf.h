@@ -317,8 +317,9 @@ typedef struct asf_head_predictor asf_head_predictor; /* opaque host handle */
  *   max_batch    largest B any call will use (1 .. 32)
  *   wtype        asf_dtype of Q1 and Q2
  *   threshold    logit threshold theta
- * Alignment and limits: d_model * sizeof(weight) and pred_hidden *
- * sizeof(weight) multiples of 16 bytes, at most 16 KiB and 4 KiB. */
+ * Alignment and limits as asf_layer_desc: d_model * sizeof(weight) a
+ * multiple of 256 bytes, at most 16 KiB; pred_hidden * sizeof(weight) a
+ * multiple of 16 bytes, at most 4 KiB. */
 typedef struct {
     int32_t d_model;
     int32_t n_heads;

@@ -28,6 +28,7 @@ def test_small_run_prints_one_json_line():
             "--tokens", "16", "--dense-steps", "5", "--cpu-seconds", "0.5", "--trace-samples", "8",
             "--repeat-steps", "20",
             "--stack-tokens", "0", "--layout-steps", "0", "--gated-steps", "0", "--batches",
+            "--head-calls", "20", "--head-ring", "2",
             "--ffn-rhos", "0.1", "--ffn-sets", "8"]
     r = subprocess.run(args, capture_output=True, text=True, timeout=600, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
@@ -51,3 +52,4 @@ def test_small_run_prints_one_json_line():
     assert len(d["repeats_ms_per_step"]) == 5 and d["cache_hot"]["median5_ms_per_step"] > 0
     assert d["ambiguous"]["tokens"] > 0 and d["ambiguous"]["in_margin_per_token"] >= 0
     assert d["sparse_ffn_only"]["by_rho"][0]["ms_per_call"] > 0
+    assert [r["batch"] for r in d["head_predictor"]["by_batch"]] == [1, 32]
