@@ -377,9 +377,56 @@ __device__ __forceinline__ void pred1_block(const Pred1Args &a, int blk) {
     }
 }
 
+// The same rows with x staged in LDS once per workgroup: each thread's
+// global loads are its weight chunks and one share of x, instead of the x
+// chunks of every weight chunk it holds.  Sums as pred1_block.
+template <int WT>
+__device__ __forceinline__ void pred1_block_lds(const Pred1Args &a, int blk,
+                                                float (&xs)[kMaxDLds]) {
+    constexpr int CPL = kPred1Cpl;
+    __shared__ float red[kWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wpr = a.wpr, H = a.H;
+    const int rpw = kWaves / wpr;
+    const int row = blk * rpw + wave / wpr, part = wave % wpr;
+    const int C = a.d / Elt<WT>::E;
+    const bool live = row < H;
+    const int rowc = live ? row : H - 1;
+    const int rfin = blk * rpw + (int)threadIdx.x;
+    const float c1v = a.c1[rfin < H ? rfin : H - 1];
+    u32x4 w[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = part * 64 + lane + 64 * wpr * i;
+        w[i] = a.P1[(size_t)rowc * C + (c < C ? c : C - 1)];
+    }
+    float4 xv[4];
+    stage_load<4>(a.x, a.d, xv);
+    stage_store<4>(xs, xv);
+    __syncthreads();
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = part * 64 + lane + 64 * wpr * i;
+        if (live && c < C) acc = dot_chunk_lds<WT>(w[i], xs, c, acc);
+    }
+    const float sum = wave_sum(acc);
+    if (lane == 0) red[wave] = sum;
+    __syncthreads();
+    if ((int)threadIdx.x < rpw) {
+        const int r = blk * rpw + threadIdx.x;
+        if (r < H) {
+            float t = 0.0f;
+            for (int pp = 0; pp < wpr; ++pp) t += red[threadIdx.x * wpr + pp];
+            a.h[r] = fmaxf(t + c1v, 0.0f);
+        }
+    }
+}
+
 template <int WT>
 __global__ __launch_bounds__(kThreads) void k_pred1(Pred1Args a) {
-    pred1_block<WT>(a, blockIdx.x);
+    __shared__ float xs[kMaxDLds];
+    pred1_block_lds<WT>(a, blockIdx.x, xs);
 }
 
 // Predictor layer 1 for 2..kPred1MaxB tokens (fp16 weights) in the geometry of
