@@ -439,13 +439,17 @@ constexpr int kPred1MaxB = 4;   // beyond, the matrix-core form is faster (one L
 
 __global__ __launch_bounds__(kThreads) void k_pred1b(Pred1Args a, int B, _Float16 *__restrict__ h16,
                                                      _Float16 *__restrict__ x16) {
-    constexpr int E = 8, CPL = kPred1Cpl;
+    constexpr int CPL = kPred1Cpl;
     __shared__ float red[kPred1MaxB][kWaves];
+    // two tokens' x at a time, staged in LDS by the whole workgroup: each
+    // thread's global loads are its weight chunks and shares of x, not the x
+    // chunks of every weight chunk for every token
+    __shared__ float xs[2][kMaxDLds];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wpr = a.wpr, H = a.H, d = a.d;
     const int rpw = kWaves / wpr;
     const int row = blockIdx.x * rpw + wave / wpr, part = wave % wpr;
-    const int C = d / E;
+    const int C = d / 8;
     const bool live = row < H;
     const int rowc = live ? row : H - 1;
     const int rfin = blockIdx.x * rpw + (int)threadIdx.x / kPred1MaxB;
@@ -456,43 +460,33 @@ __global__ __launch_bounds__(kThreads) void k_pred1b(Pred1Args a, int B, _Float1
         const int c = part * 64 + lane + 64 * wpr * i;
         w[i] = a.P1[(size_t)rowc * C + (c < C ? c : C - 1)];
     }
-    // x chunks of token t (clamped to token B - 1)
-    auto load_tok = [&](int t, float (&xr)[CPL][E]) {
-        const int tt = t < B ? t : B - 1;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int c = part * 64 + lane + 64 * wpr * i;
-            load_f32<E>(a.x + (size_t)tt * d + (size_t)(c < C ? c : C - 1) * E, xr[i]);
-        }
+    // tokens t0, t0 + 1 (the second clamped to B - 1) into LDS
+    auto stage_pair = [&](int t0) {
+        float4 v0[4], v1[4];
+        const int t1 = t0 + 1 < B ? t0 + 1 : B - 1;
+        stage_load<4>(a.x + (size_t)t0 * d, d, v0);
+        stage_load<4>(a.x + (size_t)t1 * d, d, v1);
+        stage_store<4>(xs[0], v0);
+        stage_store<4>(xs[1], v1);
     };
-    auto tok_sum = [&](int t, const float (&xr)[CPL][E]) {
+    auto tok_sum = [&](int t, const float *xt) {
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = part * 64 + lane + 64 * wpr * i;
-            if (live && c < C) {
-                float wv[E];
-                unpack<1>(w[i], wv);
-#pragma unroll
-                for (int e = 0; e < E; ++e) acc = fmaf(wv[e], xr[i][e], acc);
-            }
+            if (live && c < C) acc = dot_chunk_lds<1>(w[i], xt, c, acc);
         }
         const float sum = wave_sum(acc);
         if (lane == 0) red[t][wave] = sum;
     };
-    float xa[CPL][E], xb[CPL][E];
-    load_tok(0, xa);
-    load_tok(1, xb);
-    // tokens alternate between the two register sets (2 <= B <= 4); the
-    // loads ahead are unconditional (clamped), so each wait covers one token
 #pragma unroll
     for (int t = 0; t < kPred1MaxB; t += 2) {
         if (t >= B) break;
-        tok_sum(t, xa);
-        load_tok(t + 2, xa);
-        if (t + 1 >= B) break;
-        tok_sum(t + 1, xb);
-        load_tok(t + 3, xb);
+        if (t > 0) __syncthreads();   // the previous pair is no longer read
+        stage_pair(t);
+        __syncthreads();
+        tok_sum(t, xs[0]);
+        if (t + 1 < B) tok_sum(t + 1, xs[1]);
     }
     __syncthreads();
     // thread t finishes row t / kPred1MaxB for token t % kPred1MaxB
