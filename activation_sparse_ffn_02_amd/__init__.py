@@ -94,6 +94,8 @@ _lib.asf_destroy_head_predictor.argtypes = [_vp]
 _lib.asf_destroy_head_predictor.restype = None
 _lib.asf_predict_heads.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _vp]
 _lib.asf_predict_heads.restype = ctypes.c_int
+_lib.asf_step_launches.argtypes = [_vp, _i32]
+_lib.asf_step_launches.restype = _i32
 _lib.asf_layer_set_trace.argtypes = [_vp, ctypes.POINTER(ctypes.c_void_p), _i32]
 _lib.asf_layer_set_trace.restype = ctypes.c_int
 _lib.asf_status_string.argtypes = [ctypes.c_int]
@@ -393,6 +395,10 @@ class Layer:
                                       _stream(stream)),
                "asf_dense_ffn_ref")
         return out
+
+    def step_launches(self, B: int = 1) -> int:
+        """Kernel launches of one decode step for B tokens (list left out)."""
+        return int(_lib.asf_step_launches(self._h, int(B)))
 
     def set_trace(self, events=None, n: int = 0):
         """Record HIP events (ctypes array of 2*n hipEvent_t) around each of

@@ -58,7 +58,10 @@ size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v) {
     t.nmat = nmat;
     t.p1 = (void *)take(H * d * ws);
     t.c1 = (float *)take(H * 4);
-    t.p2 = (void *)take(nq * kRowsPerWG * H * ws);   // owner-major rows, padded to nq*64
+    // owner-major rows (batched forms), padded to nq*64; k-major owner blocks
+    // (one token)
+    t.p2 = Bm > 1 ? (void *)take(nq * kRowsPerWG * H * ws) : nullptr;
+    t.p2k = (void *)take(nq * kRowsPerWG * H * ws);
     t.c2 = (float *)take(f * 4);
     t.bundles = (void *)take(f * nmat * d * ws);
     t.b1 = (float *)take(f * 4);
@@ -83,6 +86,10 @@ size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v) {
     t.count = (int32_t *)take(64);
     t.rows = (int32_t *)take(64);
     t.dbg = (unsigned *)take(64);
+    t.xstride = (int)H + 64;
+    t.xch = (uint64_t *)take((size_t)kXchCopies * t.xstride * 8);
+    t.epoch = (unsigned *)take(64);
+    t.fused = 0;
     if (v) *v = t;
     return (size_t)(p - align_up(base, 256));
 }
@@ -154,6 +161,22 @@ static hipError_t launch_fc2_step(const LayerView &v, int B, const float *resid,
                                   const Trace *tr, hipStream_t s) {
     if (B == 1) return launch_fc2_sum(v, resid, y, tr, s);
     return launch_fc2(v, B, false, resid, y, tr, s);
+}
+
+// One decode step of layer v (predict, FC1, FC2 into y): one token in one
+// launch when every owner can be resident at once (then the owner-row sum,
+// which also advances the exchange epoch), else predictor layer 1, the
+// scores with FC1, and FC2
+static hipError_t launch_step(const LayerView &v, const float *x, int B, const float *resid,
+                              float *y, const Trace *tr, hipStream_t s) {
+    hipError_t e;
+    if (B == 1 && v.fused) {
+        if ((e = launch_step1(v, x, tr, s)) != hipSuccess) return e;
+        return launch_fc2_sum(v, resid, y, tr, s, true);
+    }
+    if ((e = launch_pred_l1(v, x, B, tr, s)) != hipSuccess) return e;
+    if ((e = launch_score(v, x, B, true, tr, s)) != hipSuccess) return e;
+    return launch_fc2_step(v, B, resid, y, tr, s);
 }
 
 // Inter-layer buffer of asf_stack_decode_static: one [B][d_model] float32
@@ -262,8 +285,11 @@ asf_status asf_create_layer(const asf_layer_desc *desc, const asf_layer_weights 
     // predictor: layer 1 as given, layer 2 rows and bias in slot order
     chk(hipMemcpyAsync(v.p1, w->p1, (size_t)H * d * ws, hipMemcpyDeviceToDevice, s));
     chk(launch_gather_f32(w->c1, nullptr, H, v.c1, s));
-    chk(hipMemsetAsync(v.p2, 0, (size_t)v.nq * kRowsPerWG * H * ws, s));
-    chk(launch_perm_rows(w->p2, v.ch, v.perm, f, v.p2, v.ch, 0, v.nq, s));
+    if (v.p2) {
+        chk(hipMemsetAsync(v.p2, 0, (size_t)v.nq * kRowsPerWG * H * ws, s));
+        chk(launch_perm_rows(w->p2, v.ch, v.perm, f, v.p2, v.ch, 0, v.nq, s));
+    }
+    chk(launch_p2_kmajor(w->p2, H, f, v.nq, ws, v.perm, v.p2k, s));
     chk(launch_gather_f32(w->c2, v.perm, f, v.c2, s));
     // neuron bundles: [gate,] up row, down column (W_down transposed), slot order
     const size_t bstride_chunks = (size_t)v.nmat * v.cd;
@@ -276,6 +302,12 @@ asf_status asf_create_layer(const asf_layer_desc *desc, const asf_layer_weights 
     chk(launch_gather_f32(w->b1, v.perm, f, v.b1, s));
     chk(launch_gather_f32(w->b2, nullptr, d, v.b2, s));
     chk(hipMemsetAsync(v.arrive, 0, kArrive * 4, s));
+    // the one-launch step: exchange words tagged 0, epoch 1; used when every
+    // owner can be resident at once
+    chk(hipMemsetAsync(v.xch, 0, (size_t)kXchCopies * v.xstride * 8, s));
+    chk(hipMemsetAsync(v.dbg, 0, 64, s));
+    chk(hipMemsetD32Async((hipDeviceptr_t)v.epoch, 1, 1, s));
+    v.fused = step1_fits(v) ? 1 : 0;
     if (e != hipSuccess) {
         delete L;
         return ASF_ERR_HIP;
@@ -346,6 +378,11 @@ asf_status asf_sparse_ffn(const asf_layer *layer, const float *x, int32_t B,
     return ASF_OK;
 }
 
+int32_t asf_step_launches(const asf_layer *layer, int32_t B) {
+    if (!layer || B < 1 || B > layer->v.max_batch) return 0;
+    return (B == 1 && layer->v.fused) ? 2 : 3;
+}
+
 asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
                            const float *residual, float *y, int32_t *active, int32_t *n_active,
                            void *stream) {
@@ -355,9 +392,7 @@ asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
     if (!aligned16(y) || (residual && !aligned16(residual))) return ASF_ERR_ALIGN;
     const LayerView &v = layer->v;
     hipStream_t s = (hipStream_t)stream;
-    if (launch_pred_l1(v, x, B, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
-    if (launch_score(v, x, B, true, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
-    if (launch_fc2_step(v, B, residual, y, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
+    if (launch_step(v, x, B, residual, y, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
     if ((active || n_active) &&
         launch_list(v, B, active, n_active, nullptr, layer->tr(), s) != hipSuccess)
         return ASF_ERR_HIP;
@@ -444,9 +479,7 @@ asf_status asf_stack_decode(asf_layer *const *layers, int32_t n_layers, const fl
         const LayerView &v = layers[l]->v;
         const asf::Trace *tr = layers[l]->tr();
         float *out = ((n_layers - 1 - l) % 2 == 0) ? y : work;
-        if (launch_pred_l1(v, in, B, tr, s) != hipSuccess) return ASF_ERR_HIP;
-        if (launch_score(v, in, B, true, tr, s) != hipSuccess) return ASF_ERR_HIP;
-        if (launch_fc2_step(v, B, residual ? in : nullptr, out, tr, s) != hipSuccess)
+        if (launch_step(v, in, B, residual ? in : nullptr, out, tr, s) != hipSuccess)
             return ASF_ERR_HIP;
         in = out;
     }

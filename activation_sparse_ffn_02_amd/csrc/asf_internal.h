@@ -17,6 +17,7 @@ constexpr int kGroups = 16;       // FC2: neuron groups (partials per output)
 constexpr int kMaxBatch = 32;
 constexpr int kMaxFfn = 65536;    // the list kernel handles up to 1024 mask words
 constexpr int kArrive = 64;       // arrival counters (FC2 slices, predictor row tiles)
+constexpr int kXchCopies = 16;    // copies of h exchanged between the owners (one-launch step)
 
 // Position of the r-th set bit of m (r < popcount(m)), by halving.
 __device__ __forceinline__ int nth_set_bit(uint64_t m, int r) {
@@ -57,12 +58,17 @@ struct LayerView {
     int nq;        // owner workgroups (== words)
     int nmat;      // matrices per neuron bundle: 2 (up, down) or 3 (gate, up, down)
     int ncu;       // compute units of the device the layer was created on
+    int fused;     // one-token steps run in one launch (every owner resident at once)
 
     // weights in the library layout
     void *p1;          // [H][d]            predictor layer 1 (as given)
     float *c1;         // [H]
     void *p2;          // [nq*64][H]        predictor layer 2, owner-major: slot q + nq*i
-                       //                   at row q*64 + i (rows past f are zero)
+                       //                   at row q*64 + i (rows past f are zero); the
+                       //                   batched forms' layout, null when max_batch == 1
+    void *p2k;         // [H][nq][64]       the same entries k-major (entry k of slot
+                       //                   q + nq*i at (k, q, i)): the one-token form reads
+                       //                   the runs of the nonzero h_k
     float *c2;         // [f]               slot order
     void *bundles;     // [f][nmat][d]      per slot: (gate,) up row, down column
     float *b1;         // [f]               slot order (gate bias when gated)
@@ -89,7 +95,11 @@ struct LayerView {
     int32_t *slots;    // [f]                      ascending active slots
     int32_t *count;    // [1]                      their number
     int32_t *rows;     // [1]                      rows of the batched FC1 list
-    unsigned *dbg;     // [1]                      debug-build check flags
+    unsigned *dbg;     // [1]                      debug-build check flags; bit 8: a wait of
+                       //                          the one-launch step's h exchange gave up
+    uint64_t *xch;     // [kXchCopies][xstride]    h words of the one-launch step
+    int xstride;       //                          (epoch << 32 | h bits), H + 64 per copy
+    unsigned *epoch;   // [1]                      the step's epoch, advanced by its sum
 };
 
 size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v);
@@ -129,6 +139,9 @@ hipError_t launch_transpose_perm(const void *wdown, int d, int f, int ws, const 
                                  void *bundles, size_t bundle_stride_elems,
                                  size_t dst_off_elems, hipStream_t s);
 hipError_t launch_invert(const int32_t *perm, int f, int32_t *inv, hipStream_t s);
+// P2 [f][H] (original ids) into the k-major layout [H][nq][64]
+hipError_t launch_p2_kmajor(const void *p2, int H, int f, int nq, int ws, const int32_t *perm,
+                            void *dst, hipStream_t s);
 hipError_t launch_gather_f32(const float *src, const int32_t *perm, int n, float *dst,
                              hipStream_t s);
 
@@ -148,10 +161,16 @@ hipError_t launch_fc1(const LayerView &L, const float *x, int B, int mode, const
 // entries' slots come from the list (caller ids) rather than the owner bits
 hipError_t launch_fc2(const LayerView &L, int B, bool listed, const float *resid, float *y,
                       const Trace *tr, hipStream_t s);
-// single token, after launch_score with FC1: y = sum over owners of their
-// FC2 rows (part1) + b2 (+ resid)
+// single token, after launch_score with FC1 (or launch_step1): y = sum over
+// owners of their FC2 rows (part1) + b2 (+ resid); after launch_step1,
+// advance_epoch moves the exchange epoch on for the next step
 hipError_t launch_fc2_sum(const LayerView &L, const float *resid, float *y, const Trace *tr,
-                          hipStream_t s);
+                          hipStream_t s, bool advance_epoch = false);
+// one-token decode step (predict + FC1 + owner FC2 rows) in one launch:
+// predictor layer 1 computed by the owners, h exchanged between them through
+// memory; needs every owner resident at once (step1_fits, set at create)
+bool step1_fits(const LayerView &L);
+hipError_t launch_step1(const LayerView &L, const float *x, const Trace *tr, hipStream_t s);
 // one token over the set of the last prediction (the owner words), or over
 // a caller's list of original ids (ids, n_ids device pointers; ids null =
 // the last prediction): FC1 and the owner FC2 rows, as the decode step does

@@ -46,6 +46,7 @@ namespace asf {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = kThreads / 64;
@@ -121,6 +122,32 @@ __device__ __forceinline__ float rows8_sum(const float (&v)[8], int lane) {
 
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
+// Buffer loads (gfx9 raw buffer instructions): the resource bounds the
+// access to [base, base + bytes); a 16-byte load at an offset past the bound
+// returns zeros without a memory access.  Loads that a wave may or may not
+// need are issued unconditionally this way, so the count of loads in flight
+// does not depend on data and the compiler's waits stay exact.  The base and
+// bound must be wave-uniform (they go to scalar registers).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kBufWord3 = 0x00020000;   // descriptor word 3: 32-bit data format
+
+__device__ __forceinline__ rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kBufWord3);
+}
+
+__device__ __forceinline__ u32x4 buf_load(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+}
+
+// a wave-uniform 64-bit value (e.g. an owner word read from LDS) moved to
+// scalar registers
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // ---------------------------------------------------------------- layout
 // dst row of slot r: r, or with owner_major = nq > 0 the row q*64 + i of
 // slot r = q + nq*i (each owner's 64 rows contiguous)
@@ -158,6 +185,29 @@ __global__ __launch_bounds__(256) void k_transpose_perm(const T *__restrict__ wd
             if ((unsigned)s >= (unsigned)f) s = i;
             bundles[(size_t)s * bstride + doff + m] = tile[tx][r];
         }
+    }
+}
+
+// One-token layout of predictor layer 2, k-major: row k holds, for every
+// owner q, the 64-entry segment of hidden unit k: (k, q, i) = entry k of
+// the P2 row of slot q + nq*i (original id perm[slot]); zero past f.  One
+// workgroup per (owner, 64 hidden units), through LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void k_p2_kmajor(const T *__restrict__ p2, int H, int f, int nq,
+                                                   const int32_t *__restrict__ perm,
+                                                   T *__restrict__ dst) {
+    __shared__ T tile[kRowsPerWG][65];
+    const int q = blockIdx.x, k0 = blockIdx.y * 64;
+    for (int e = threadIdx.x; e < kRowsPerWG * 64; e += 256) {
+        const int i = e / 64, kk = e % 64;
+        const int slot = q + nq * i, k = k0 + kk;
+        tile[i][kk] = (slot < f && k < H) ? p2[(size_t)perm[slot] * H + k] : (T)0;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < kRowsPerWG * 64; e += 256) {
+        const int kk = e / kRowsPerWG, i = e % kRowsPerWG;
+        const int k = k0 + kk;
+        if (k < H) dst[((size_t)k * nq + q) * kRowsPerWG + i] = tile[i][kk];
     }
 }
 
@@ -655,6 +705,26 @@ __device__ __forceinline__ void load_fc1_rows(const u32x4 *__restrict__ bundles,
     }
 }
 
+// The same rows through a buffer bounded to the bundle of `slot` (wave-
+// uniform); with present false nothing is read and the rows are zero.
+template <bool GATED, int CPL>
+__device__ __forceinline__ void load_fc1_rows_buf(const u32x4 *__restrict__ bundles,
+                                                  size_t bstride, int C, int slot, bool present,
+                                                  int lane, u32x4 (&wu)[CPL], u32x4 (&wg)[CPL]) {
+    slot = __builtin_amdgcn_readfirstlane(slot);
+    const uint32_t bytes = present ? (uint32_t)(16 * bstride) : 0u;
+    const rsrc_t rs = buf_rsrc(bundles + (size_t)slot * bstride, bytes);
+    constexpr int UP = GATED ? 1 : 0;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = lane + 64 * i;
+        // chunks past the row read past the bound
+        wu[i] = buf_load(rs, c < C ? 16u * (UP * C + c) : bytes);
+        if constexpr (GATED) wg[i] = buf_load(rs, c < C ? 16u * c : bytes);
+        else wg[i] = zero4();
+    }
+}
+
 // FC1 of owner q over its valid entries (bit i of `valid`, slot slot_of(i)):
 // wave w takes entries i = w, w+8, ...; the entry of rank r (r-th set bit)
 // is listed at lslot[q][r], la[q][r][0..B).  When spec is set, wave w's
@@ -690,6 +760,7 @@ __device__ __forceinline__ void owner_fc1(int q, uint64_t valid, SlotOf slot_of,
 
 struct ScoreParams {
     const u32x4 *p2;
+    const void *p2k;  // [nq][H][64] one-token layout of P2 (k-major per owner)
     const float *c2;
     const float *h;
     int B, H, f;
@@ -712,6 +783,16 @@ struct ScoreParams {
     const int32_t *ids;
     const int32_t *n_ids;
     const int32_t *inv;
+    // one-token step in one launch: predictor layer 1 rows of each owner and
+    // the exchange of h between the owners
+    const void *p1;       // [H][d]
+    const float *c1;      // [H]
+    int l1_rows;          // rows of h per owner
+    int l1_wpr;           // waves per row
+    uint64_t *xch;        // [kXchCopies][xstride]: (epoch << 32) | h bits
+    int xstride;
+    const unsigned *epoch;
+    unsigned *flags;      // bit kFlagXchTimeout: an exchange wait gave up
 };
 
 // Owner workgroup q: score its 64 slots for every token, store per-token and
@@ -888,22 +969,22 @@ template <bool GATED, int CPL1, bool SPEC = false, bool WIDE = false> struct Fc1
 };
 
 // Chunks t, t + 512, ... (thread t) of the down columns of the next N
-// entries of `m` (ascending bits, slot q + nq*bit; past the last entry the
-// owner's slot q); returns m without those entries.
+// entries of `m` (ascending bits, slot q + nq*bit); returns m without those
+// entries.  Buffer loads bounded to the column: entries past the last one
+// (and chunks past the row) read zeros without touching memory.
 template <int N, int CPT>
 __device__ __forceinline__ uint64_t load_down(u32x4 (&dv)[N][CPT], uint64_t m,
                                               const u32x4 *__restrict__ dn, size_t bstride, int q,
                                               int nq, int cd) {
+    m = uniform64(m);
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-        const int i = m ? __builtin_ctzll(m) : 0;
+        const bool present = m != 0ull;
+        const int i = present ? __builtin_ctzll(m) : 0;
         m &= m - 1ull;
-        const u32x4 *bp = dn + (size_t)(q + nq * i) * bstride;
+        const rsrc_t rs = buf_rsrc(dn + (size_t)(q + nq * i) * bstride, present ? 16u * cd : 0u);
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            const int c = threadIdx.x + kThreads * j;
-            dv[n][j] = bp[c < cd ? c : cd - 1];
-        }
+        for (int j = 0; j < CPT; ++j) dv[n][j] = buf_load(rs, 16u * (threadIdx.x + kThreads * j));
     }
     return m;
 }
@@ -930,18 +1011,19 @@ __device__ __forceinline__ void fma_down(const u32x4 (&dv)[N][CPT], int n0, int 
 // the owner's FC2 row, one token, x in LDS.  With SPEC, waves below
 // kSpecRows already hold the rows (spu, spg) and bias of bit `wave`.
 template <int WT, bool GATED, int CPL1, bool SPEC, bool WIDE = false>
-__device__ __forceinline__ void owner_ffn1(const ScoreParams &p, int q, int nq, uint64_t valid,
+__device__ __forceinline__ void owner_ffn1(const ScoreParams &p, int q, int nq, uint64_t valid_in,
                                            const float *xs, float *a_lds,
                                            const u32x4 (&spu)[CPL1], const u32x4 (&spg)[CPL1],
                                            float spec_bias, int wave, int lane) {
     constexpr int E = Elt<WT>::E;
+    const uint64_t valid = uniform64(valid_in);
     const int cnt = __popcll(valid);
     // FC2 of this owner's listed neurons: thread t takes chunks t, t + 512
     // of the down columns.  The chunks of the first PF entries (rank
-    // order) are loaded now, beside the FC1 rows, and with a 256-VGPR
-    // budget those of the next PFB too when the owner lists more; the
-    // rest in batches of PF2 once the FC1 rows are no longer held.  PF is
-    // cut where the FC1 rows leave no registers under the 128-VGPR cap.
+    // order) are requested now, after the FC1 rows, and with a 256-VGPR
+    // budget those of the next PFB too; the rest in batches of PF2 once the
+    // FC1 rows are no longer held.  PF is cut where the FC1 rows leave no
+    // registers under the 128-VGPR cap.
     constexpr int CPT = (CPL1 + 7) / 8;      // d-row chunks per thread
     constexpr int PF2 = 8 / CPT;
     constexpr bool kWide = Fc1Regs<GATED, CPL1, SPEC, WIDE>::waves_per_eu == 2;
@@ -955,25 +1037,31 @@ __device__ __forceinline__ void owner_ffn1(const ScoreParams &p, int q, int nq, 
     const uint64_t mr = SPEC ? (valid & ~((1ull << kSpecRows) - 1ull)) : valid;
     const int nr = __popcll(mr);
     int r = (wave - off + kWaves) % kWaves;
-    // with room for it, the wave's first FC1 row is requested ahead of the
-    // down columns (it is needed first); a wave without one requests the
-    // owner's first slot instead (held by wave 0 already) and drops it
-    constexpr bool kHoist = kWide && Fc1Regs<GATED, CPL1>::chunks <= 8;
-    u32x4 hu[kHoist ? CPL1 : 1], hg[kHoist ? CPL1 : 1];
-    const bool has_h = r < nr;
-    const int hbit = (kHoist && has_h) ? nth_set_bit(mr, r) : 0;
-    float hbias = 0.0f;
-    if constexpr (kHoist) {
-        hbias = p.b1[q + nq * hbit];
-        load_fc1_rows<GATED, CPL1>(p.bundles, p.bstride, p.cd, q + nq * hbit, lane, hu, hg);
+    // with room for them, every FC1 row of the wave (two for up to 16
+    // listed neurons when a neuron's rows take 8 chunks per lane, else one)
+    // is requested before the down columns, in one round trip; a row the
+    // wave does not have reads nothing
+    constexpr int kCh = Fc1Regs<GATED, CPL1>::chunks;
+    constexpr int HR = !kWide ? 0
+                       : kCh <= 8 ? 2
+                       : ((SPEC ? kCh : 0) + kCh + (PF + PFB) * CPT <= 48 ? 1 : 0);
+    u32x4 hu[HR > 0 ? HR : 1][CPL1], hg[HR > 0 ? HR : 1][CPL1];
+    float hbias[HR > 0 ? HR : 1];
+    int hbit[HR > 0 ? HR : 1];
+#pragma unroll
+    for (int k = 0; k < HR; ++k) {
+        const bool has = r + kWaves * k < nr;
+        hbit[k] = has ? nth_set_bit(mr, r + kWaves * k) : 0;
+        const int slot = q + nq * hbit[k];
+        hbias[k] = p.b1[slot < p.f ? slot : p.f - 1];
+        load_fc1_rows_buf<GATED, CPL1>(p.bundles, p.bstride, p.cd, slot, has, lane, hu[k], hg[k]);
     }
     const u32x4 *dn = p.bundles + p.dn_off;
     u32x4 dv[PF > 0 ? PF : 1][CPT];
     u32x4 dvb[PFB > 0 ? PFB : 1][CPT];
     uint64_t rest = valid;
     if constexpr (PF > 0) rest = load_down<PF, CPT>(dv, valid, dn, p.bstride, q, nq, p.cd);
-    if constexpr (PFB > 0)
-        if (cnt > PF) rest = load_down<PFB, CPT>(dvb, rest, dn, p.bstride, q, nq, p.cd);
+    if constexpr (PFB > 0) rest = load_down<PFB, CPT>(dvb, rest, dn, p.bstride, q, nq, p.cd);
     if constexpr (SPEC) {
         if (wave < kSpecRows && ((valid >> wave) & 1ull)) {
             const int slot = q + nq * wave;
@@ -981,29 +1069,13 @@ __device__ __forceinline__ void owner_ffn1(const ScoreParams &p, int q, int nq, 
                                          p.out, a_lds, lane);
         }
     }
-    if constexpr (kHoist) {
-        if (has_h) {
-            fc1_entry_1<WT, GATED, CPL1>(q, valid, hbit, q + nq * hbit, hu, hg, p.cd, hbias, xs,
-                                         p.out, a_lds, lane);
-            r += kWaves;
-        }
+#pragma unroll
+    for (int k = 0; k < HR; ++k) {
+        if (r + kWaves * k < nr)
+            fc1_entry_1<WT, GATED, CPL1>(q, valid, hbit[k], q + nq * hbit[k], hu[k], hg[k], p.cd,
+                                         hbias[k], xs, p.out, a_lds, lane);
     }
-    if constexpr (kWide && Fc1Regs<GATED, CPL1>::chunks <= 8) {
-        // a wave with two more rows requests both before using either
-        for (; r + kWaves < nr; r += 2 * kWaves) {
-            const int i0 = nth_set_bit(mr, r), i1 = nth_set_bit(mr, r + kWaves);
-            const int s0 = q + nq * i0, s1 = q + nq * i1;
-            const float bias0 = p.b1[s0], bias1 = p.b1[s1];
-            u32x4 wu0[CPL1], wg0[CPL1], wu1[CPL1], wg1[CPL1];
-            load_fc1_rows<GATED, CPL1>(p.bundles, p.bstride, p.cd, s0, lane, wu0, wg0);
-            load_fc1_rows<GATED, CPL1>(p.bundles, p.bstride, p.cd, s1, lane, wu1, wg1);
-            fc1_entry_1<WT, GATED, CPL1>(q, valid, i0, s0, wu0, wg0, p.cd, bias0, xs, p.out, a_lds,
-                                         lane);
-            fc1_entry_1<WT, GATED, CPL1>(q, valid, i1, s1, wu1, wg1, p.cd, bias1, xs, p.out, a_lds,
-                                         lane);
-        }
-    }
-    for (; r < nr; r += kWaves) {
+    for (r += kWaves * HR; r < nr; r += kWaves) {
         const int i = nth_set_bit(mr, r);
         const int slot = q + nq * i;
         const float bias = p.b1[slot];
@@ -1019,8 +1091,7 @@ __device__ __forceinline__ void owner_ffn1(const ScoreParams &p, int q, int nq, 
 #pragma unroll
         for (int e = 0; e < E; ++e) acc2[j][e] = 0.0f;
     if constexpr (PF > 0) fma_down<WT, PF, CPT>(dv, 0, cnt, a_lds, acc2);
-    if constexpr (PFB > 0)
-        if (cnt > PF) fma_down<WT, PFB, CPT>(dvb, PF, cnt, a_lds, acc2);
+    if constexpr (PFB > 0) fma_down<WT, PFB, CPT>(dvb, PF, cnt, a_lds, acc2);
     for (int n0 = PF + PFB; n0 < cnt; n0 += PF2) {
         u32x4 dv2[PF2][CPT];
         rest = load_down<PF2, CPT>(dv2, rest, dn, p.bstride, q, nq, p.cd);
@@ -1033,9 +1104,11 @@ __device__ __forceinline__ void owner_ffn1(const ScoreParams &p, int q, int nq, 
             const int o = c * E;
             float4 *dst = reinterpret_cast<float4 *>(p.part1 + ((size_t)(o >> 4) * nq + q) * 16 + (o & 15));
 #pragma unroll
-            for (int k = 0; k < E / 4; ++k)
-                dst[k] = make_float4(acc2[j][4 * k], acc2[j][4 * k + 1], acc2[j][4 * k + 2],
-                                     acc2[j][4 * k + 3]);
+            for (int k = 0; k < E / 4; ++k) {
+                const f32x4 v = {acc2[j][4 * k], acc2[j][4 * k + 1], acc2[j][4 * k + 2],
+                                 acc2[j][4 * k + 3]};
+                __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(dst + k));
+            }
         }
     }
 }
@@ -1045,107 +1118,300 @@ __device__ __forceinline__ void owner_ffn1(const ScoreParams &p, int q, int nq, 
 // listed neurons' a times their down columns, added in rank order), which
 // k_fc2_sum adds over owners.  The down columns sit right after the up rows
 // in each bundle, so every listed neuron costs one contiguous bundle read.
+//
+// Predictor layer 2 skips the hidden units that ReLU set to zero: they add
+// nothing to any score, so only the P2 entries of the nonzero units are read
+// (the pages' principle, computing only what a nonzero activation needs,
+// applied to the predictor's own ReLU layer; with a ReLU hidden layer about
+// half the units are zero for each token).  P2 is stored k-major (p2k,
+// [H][nq][64]): hidden unit k is one contiguous run holding every owner's
+// 64-entry segment (128 bytes in fp16), so a zero unit is skipped as a
+// whole run and the units that are read are read in full by the owners
+// together.  The nonzero units are listed in LDS in ascending order; lane l
+// of a wave takes chunk l % CPS of segment l / CPS of each load, every
+// segment of a round requested before the first is used, units past the
+// list read out of the buffer's range (zeros, no memory traffic).  Sums per
+// slot: lane order over the wave's segments, a halving exchange over the
+// lanes of one chunk position, then the waves in order, then c2.
+//
 // With at most 128 VGPRs (4 waves per SIMD) two workgroups fit on a CU, so
 // up to 512 owners (f <= 32768) run in one round.
-template <int WT, int CPL2, bool FC1, bool GATED, int CPL1, bool SPEC>
-__device__ __forceinline__ void score1_block(const ScoreParams &p, int q, int nq) {
-    constexpr int E = Elt<WT>::E;
-    constexpr int RG = kL2Rows / CPL2;      // rows per group
-    constexpr int NG = CPL2;                // groups per wave
-    __shared__ float hs[kMaxHLds];
-    __shared__ float xs[FC1 ? kMaxDLds : 4];
-    __shared__ uint32_t bits_lds[kWaves];
-    __shared__ uint64_t u_lds;
-    __shared__ float a_lds[FC1 ? kRowsPerWG : 1];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int C2 = p.H / E;
-    // staging loads first: their waits then leave the weight loads in flight
-    float4 hv[1];
-    stage_load<1>(p.h, p.H, hv);
-    float4 xv[FC1 ? 4 : 1];
-    if constexpr (FC1) stage_load<4>(p.x, p.d, xv);
-    u32x4 wb[2][RG][CPL2];
-    auto load_group = [&](int g, u32x4 (&dst)[RG][CPL2]) {
+constexpr int kSegRound = 16;   // segment loads per wave per round
+
+template <int WT, class After>
+__device__ __forceinline__ void score1_p2(const ScoreParams &p, int q, int nq, int n,
+                                          const int2 *seg,
+                                          float (&part)[kWaves][kRowsPerWG], int wave, int lane,
+                                          After after_first_round) {
+    constexpr int E = Elt<WT>::E;           // slots per 16-byte chunk
+    constexpr int CPS = kRowsPerWG / E;     // chunks per segment: 8 (fp16) or 16 (fp32)
+    constexpr int SPI = 64 / CPS;           // segments per wave load: 8 or 4
+    constexpr int STEP = kSegRound * kWaves * SPI;
+    const uint32_t seg_bytes = kRowsPerWG * (WT ? 2u : 4u);
+    const uint32_t all_bytes = (uint32_t)p.H * (uint32_t)nq * seg_bytes;
+    const rsrc_t rs = buf_rsrc(p.p2k, all_bytes);
+    const uint32_t own = (uint32_t)q * seg_bytes + 16u * (lane % CPS);
+    const int sl = lane / CPS, ch = lane % CPS;
+    float acc[E];
 #pragma unroll
-        for (int j = 0; j < RG; ++j) {
-            const int row = q * kRowsPerWG + wave * kL2Rows + g * RG + j;   // owner-major
+    for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+    u32x4 w[kSegRound];
+    float hg[kSegRound];
+    auto issue = [&](int g0) {
 #pragma unroll
-            for (int i = 0; i < CPL2; ++i) {
-                const int c = lane + 64 * i;
-                dst[j][i] = p.p2[(size_t)row * C2 + (c < C2 ? c : C2 - 1)];
-            }
+        for (int j = 0; j < kSegRound; ++j) {
+            const int g = g0 + (j * kWaves + wave) * SPI + sl;
+            const int2 e = seg[g < n ? g : 0];
+            hg[j] = g < n ? __int_as_float(e.y) : 0.0f;
+            w[j] = buf_load(rs, g < n ? (uint32_t)e.x + own : all_bytes);
         }
     };
-    load_group(0, wb[0]);
-    if constexpr (NG > 1) load_group(1, wb[1]);
-    u32x4 spu[FC1 ? CPL1 : 1], spg[FC1 ? CPL1 : 1];
-    float spec_bias = 0.0f;
-    if constexpr (SPEC) {
-        const int spec_slot = q + nq * wave;
-        spec_bias = p.b1[spec_slot < p.f ? spec_slot : p.f - 1];
-        if (wave < kSpecRows && spec_slot < p.f)
-            load_fc1_rows<GATED, CPL1>(p.bundles, p.bstride, p.cd, spec_slot, lane, spu, spg);
+    auto consume = [&]() {
+#pragma unroll
+        for (int j = 0; j < kSegRound; ++j) {
+            float wv[E];
+            unpack<WT>(w[j], wv);
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] = fmaf(hg[j], wv[e], acc[e]);
+        }
+    };
+    issue(0);
+    // the owner's hottest FC1 rows follow the first round of segments
+    __builtin_amdgcn_sched_barrier(0);
+    after_first_round();
+    __builtin_amdgcn_sched_barrier(0);
+    consume();
+    for (int g0 = STEP; g0 < n; g0 += STEP) {
+        issue(g0);
+        consume();
     }
-    stage_store<1>(hs, hv);
-    if constexpr (FC1) stage_store<4>(xs, xv);
-    __syncthreads();
-    // every row of the wave uses the same chunks of h: keep them in registers
-    float hr[CPL2][E];
+    // halving exchange over lane bits 5, 4 (, 3): the lanes of one chunk
+    // position hold the same E slots; each step keeps half of them and adds
+    // the partner's other half, so every lane ends with one slot
+    float v[E];
 #pragma unroll
-    for (int i = 0; i < CPL2; ++i) {
-        const int c = lane + 64 * i;
-        const float4 *h4 = reinterpret_cast<const float4 *>(hs + (c < C2 ? c : 0) * E);
+    for (int e = 0; e < E; ++e) v[e] = acc[e];
+    int off = 0;
 #pragma unroll
-        for (int k = 0; k < E / 4; ++k) {
-            const float4 t = h4[k];
-            hr[i][4 * k + 0] = t.x;
-            hr[i][4 * k + 1] = t.y;
-            hr[i][4 * k + 2] = t.z;
-            hr[i][4 * k + 3] = t.w;
+    for (int half = E / 2, b = 32; half >= 1; half /= 2, b /= 2) {
+        const bool hi = lane & b;
+#pragma unroll
+        for (int k = 0; k < half; ++k) {
+            const float keep = hi ? v[half + k] : v[k], send = hi ? v[k] : v[half + k];
+            v[k] = keep + __shfl_xor(send, b, 64);
+        }
+        off += hi ? half : 0;
+    }
+    part[wave][ch * E + off] = v[0];
+}
+
+// The one-launch step (FUSED): owner q first computes rows q*R .. q*R+R-1 of
+// h = ReLU(P1 x + c1) in k_pred1's geometry (x staged in LDS, WPR waves per
+// row, at most two passes of 8 / WPR rows, every P1 chunk requested up front),
+// publishes them to kXchCopies copies of the exchange buffer as 64-bit words
+// (epoch << 32 | h bits, device-scope stores) and reads all H words of copy
+// q % kXchCopies back (device-scope loads) until every word carries this
+// call's epoch.  Nothing else is in flight meanwhile: P2 is requested only
+// once h is known (its nonzero units decide which P2 runs are read).  Every
+// owner must be resident at once (the launcher checks the occupancy); each
+// wait is bounded (kSpinMax reads), after which the word is taken as it is
+// and kFlagXchTimeout is raised.  The epoch advances once per step, in the
+// owner-row sum that follows the launch.
+constexpr int kSpinMax = 1 << 16;
+constexpr unsigned kFlagXchTimeout = 8u;
+
+// this owner's P1 chunks: pass ps, row q*R + ps*rpw + wave/wpr (rows past
+// R or H read nothing)
+template <int CPL>
+__device__ __forceinline__ void step1_load_p1(const ScoreParams &p, int q, int wave, int lane,
+                                              u32x4 (&w)[2][CPL]) {
+    const int H = p.H, R = p.l1_rows, wpr = p.l1_wpr, rpw = kWaves / wpr;
+    const int C = p.cd, part = wave % wpr;
+    const uint32_t row_bytes = 16u * (uint32_t)C;
+    const uint32_t p1_bytes = (uint32_t)H * row_bytes;
+    const rsrc_t rs = buf_rsrc(p.p1, p1_bytes);
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+        const int r = ps * rpw + wave / wpr, row = q * R + r;
+        const bool live = r < R && row < H;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = part * 64 + lane + 64 * wpr * i;
+            w[ps][i] = buf_load(rs, (live && c < C) ? (uint32_t)row * row_bytes + 16u * c : p1_bytes);
         }
     }
-    float acc[kL2Rows];
+}
+
+template <int WT>
+__device__ __forceinline__ void step1_h(const ScoreParams &p, int q, const u32x4 (&w)[2][kPred1Cpl],
+                                        const float *xs, float *hs, float (&red)[2][kWaves],
+                                        unsigned ep, float c1v, int wave, int lane) {
+    constexpr int CPL = kPred1Cpl;
+    const int H = p.H, R = p.l1_rows, wpr = p.l1_wpr, rpw = kWaves / wpr;
+    const int C = p.cd, part = wave % wpr;
 #pragma unroll
-    for (int j = 0; j < kL2Rows; ++j) acc[j] = 0.0f;
+    for (int ps = 0; ps < 2; ++ps) {
+        float acc = 0.0f;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-#pragma unroll
-        for (int j = 0; j < RG; ++j)
-#pragma unroll
-            for (int i = 0; i < CPL2; ++i) {
-                const int c = lane + 64 * i;
-                if (c < C2) {
-                    float wv[E];
-                    unpack<WT>(wb[g & 1][j][i], wv);
-                    float a = acc[g * RG + j];
-#pragma unroll
-                    for (int e = 0; e < E; ++e) a = fmaf(wv[e], hr[i][e], a);
-                    acc[g * RG + j] = a;
-                }
-            }
-        if (g + 2 < NG) load_group(g + 2, wb[g & 1]);
-    }
-    // lane L ends with row (L >> 3) & 7 of this wave
-    const int r = (lane >> 3) & 7;
-    const int slot_r = q + nq * (wave * kL2Rows + r);
-    const bool valid_r = slot_r < p.f;
-    const float sc = rows8_sum(acc, lane) + p.c2[valid_r ? slot_r : p.f - 1];
-    const uint64_t m = __ballot(valid_r && sc > p.theta);
-    if (lane == 0) {
-        uint32_t b = 0;
-#pragma unroll
-        for (int j = 0; j < kL2Rows; ++j) b |= (uint32_t)((m >> (8 * j)) & 1ull) << j;
-        bits_lds[wave] = b;
+        for (int i = 0; i < CPL; ++i) {
+            const int c = part * 64 + lane + 64 * wpr * i;
+            if (c < C) acc = dot_chunk_lds<WT>(w[ps][i], xs, c, acc);
+        }
+        const float sum = wave_sum(acc);
+        if (lane == 0) red[ps][wave] = sum;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        uint64_t u = 0;
+    // publish: thread t < R * kXchCopies stores row t % R to copy t / R
+    if ((int)threadIdx.x < R * kXchCopies) {
+        const int r = (int)threadIdx.x % R, cp = (int)threadIdx.x / R, row = q * R + r;
+        if (row < H) {
+            const int ps = r / rpw, rl = r % rpw;
+            float t = 0.0f;
+            for (int pp = 0; pp < wpr; ++pp) t += red[ps][rl * wpr + pp];
+            const float hv = fmaxf(t + c1v, 0.0f);
+            const uint64_t word = ((uint64_t)ep << 32) | __float_as_uint(hv);
+            __hip_atomic_store(p.xch + (size_t)cp * p.xstride + row, word, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    // read h back: thread t takes units t, t + 512, ...
+    constexpr int NU = kMaxHLds / kThreads;
+    uint64_t *src = p.xch + (size_t)(q % kXchCopies) * p.xstride;
+    uint64_t v[NU];
+    bool wait[NU];
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) u |= (uint64_t)bits_lds[w] << (kL2Rows * w);
-        p.wbits[q] = u;
-        p.ubits[q] = u;
-        if (FC1) p.out.vbits[q] = u;
-        u_lds = u;
+    for (int u = 0; u < NU; ++u) {
+        wait[u] = (int)threadIdx.x + kThreads * u < H;
+        v[u] = 0;
+    }
+    for (int it = 0; it < kSpinMax; ++it) {
+        bool any = false;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            if (wait[u]) {
+                v[u] = __hip_atomic_load(src + threadIdx.x + kThreads * u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+                wait[u] = (unsigned)(v[u] >> 32) != ep;
+                any |= wait[u];
+            }
+        }
+        if (!any) break;
+    }
+    bool late = false;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int k = (int)threadIdx.x + kThreads * u;
+        if (k < H) hs[k] = __uint_as_float((uint32_t)v[u]);
+        late |= wait[u];
+    }
+    if (late) atomicOr(p.flags, kFlagXchTimeout);
+}
+
+template <int WT, bool FC1, bool GATED, int CPL1, bool SPEC, bool FUSED = false>
+__device__ __forceinline__ void score1_block(const ScoreParams &p, int q, int nq) {
+    __shared__ float hs[kMaxHLds];
+    __shared__ int2 seg[kMaxHLds];          // nonzero units: (byte offset of the segment, h)
+    __shared__ int cnt_lds[kMaxHLds / kThreads][kWaves];
+    __shared__ float part[kWaves][kRowsPerWG];
+    __shared__ float xs[FC1 ? kMaxDLds : 4];
+    __shared__ uint64_t u_lds;
+    __shared__ float a_lds[FC1 ? kRowsPerWG : 1];
+    constexpr int NU = kMaxHLds / kThreads;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int H = p.H;
+    const int slot_l = q + nq * lane;
+    float c2v;
+    if constexpr (FUSED) {
+        // x staged (predictor layer 1 and FC1), this owner's rows of h, the
+        // exchange; the score bias of bit lane
+        __shared__ float red[2][kWaves];
+        // the epoch first, through a vector load (a scalar load would be
+        // waited for with the kernel arguments, before any other request);
+        // it is needed only at the publication
+        const unsigned ep = __hip_atomic_load(p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        u32x4 w1[2][kPred1Cpl];
+        step1_load_p1<kPred1Cpl>(p, q, wave, lane, w1);
+        // the layer-1 bias of the row this thread publishes
+        const int c1_row = q * p.l1_rows + (int)threadIdx.x % p.l1_rows;
+        const float c1v = p.c1[c1_row < H ? c1_row : H - 1];
+        __builtin_amdgcn_sched_barrier(0);
+        float4 xv[4];
+        stage_load<4>(p.x, p.d, xv);
+        c2v = p.c2[slot_l < p.f ? slot_l : p.f - 1];
+        stage_store<4>(xs, xv);
+        __syncthreads();
+        step1_h<WT>(p, q, w1, xs, hs, red, ep, c1v, wave, lane);
+    } else {
+        // staging: h first (the segments depend on it), the score bias of
+        // bit lane, x for FC1
+        float4 hv[1];
+        stage_load<1>(p.h, H, hv);
+        c2v = p.c2[slot_l < p.f ? slot_l : p.f - 1];
+        float4 xv[FC1 ? 4 : 1];
+        if constexpr (FC1) stage_load<4>(p.x, p.d, xv);
+        stage_store<1>(hs, hv);
+        if constexpr (FC1) stage_store<4>(xs, xv);
+    }
+    __syncthreads();
+    // nonzero hidden units k = t + 512u, listed u-major, then by wave and
+    // lane: ascending k
+    uint64_t bal[NU];
+    bool nz[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int k = (int)threadIdx.x + kThreads * u;
+        nz[u] = k < H && hs[k < H ? k : 0] != 0.0f;
+        bal[u] = __ballot(nz[u]);
+        if (lane == 0) cnt_lds[u][wave] = __popcll(bal[u]);
+    }
+    __syncthreads();
+    int base[NU], n = 0;
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            if (w == wave) base[u] = n;
+            n += cnt_lds[u][w];
+        }
+    // byte offset of unit k's run
+    const uint32_t run_bytes = (uint32_t)nq * kRowsPerWG * (WT ? 2u : 4u);
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int k = (int)threadIdx.x + kThreads * u;
+        if (nz[u])
+            seg[base[u] + __popcll(bal[u] & below)] =
+                make_int2((int)((uint32_t)k * run_bytes), __float_as_int(hs[k]));
+    }
+    __syncthreads();
+    // the FC1 rows of the owner's kSpecRows hottest slots (bit wave, slot
+    // q + nq*wave), requested behind the first round of P2 segments; waves
+    // without one read nothing
+    u32x4 spu[FC1 ? CPL1 : 1], spg[FC1 ? CPL1 : 1];
+    float spec_bias = 0.0f;
+    auto spec_rows = [&]() {
+        if constexpr (SPEC) {
+            const int spec_slot = q + nq * wave;
+            const bool has = wave < kSpecRows && spec_slot < p.f;
+            spec_bias = p.b1[spec_slot < p.f ? spec_slot : p.f - 1];
+            load_fc1_rows_buf<GATED, CPL1>(p.bundles, p.bstride, p.cd, spec_slot, has, lane, spu,
+                                           spg);
+        }
+    };
+    score1_p2<WT>(p, q, nq, n, seg, part, wave, lane, spec_rows);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        float s = part[0][lane];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) s += part[w][lane];
+        s += c2v;
+        const uint64_t m = __ballot(slot_l < p.f && s > p.theta);
+        if (threadIdx.x == 0) {
+            p.wbits[q] = m;
+            p.ubits[q] = m;
+            if (FC1) p.out.vbits[q] = m;
+            u_lds = m;
+        }
     }
     __syncthreads();
     if constexpr (FC1)
@@ -1153,10 +1419,18 @@ __device__ __forceinline__ void score1_block(const ScoreParams &p, int q, int nq
                                           lane);
 }
 
-template <int WT, int CPL2, bool FC1, bool GATED, int CPL1, bool SPEC>
+template <int WT, bool FC1, bool GATED, int CPL1, bool SPEC>
 __global__ __launch_bounds__(kThreads) __attribute__((
     amdgpu_waves_per_eu(Fc1Regs<GATED, CPL1, SPEC>::waves_per_eu))) void k_score1(ScoreParams p) {
-    score1_block<WT, CPL2, FC1, GATED, CPL1, SPEC>(p, blockIdx.x, gridDim.x);
+    score1_block<WT, FC1, GATED, CPL1, SPEC>(p, blockIdx.x, gridDim.x);
+}
+
+// the one-token step in one launch: predictor layer 1 in the owners, h
+// exchanged between them, then k_score1's body with FC1
+template <int WT, bool GATED, int CPL1, bool SPEC>
+__global__ __launch_bounds__(kThreads) __attribute__((
+    amdgpu_waves_per_eu(Fc1Regs<GATED, CPL1, SPEC>::waves_per_eu))) void k_step1(ScoreParams p) {
+    score1_block<WT, true, GATED, CPL1, SPEC, true>(p, blockIdx.x, gridDim.x);
 }
 
 // FC1 + FC2 rows of one token over the set of the layer's last prediction
@@ -1374,9 +1648,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((
             const int o = c * E;
             float4 *dst = reinterpret_cast<float4 *>(p.part1 + ((size_t)(o >> 4) * nq + q) * 16 + (o & 15));
 #pragma unroll
-            for (int k = 0; k < E / 4; ++k)
-                dst[k] = make_float4(acc2[j][4 * k], acc2[j][4 * k + 1], acc2[j][4 * k + 2],
-                                     acc2[j][4 * k + 3]);
+            for (int k = 0; k < E / 4; ++k) {
+                const f32x4 v = {acc2[j][4 * k], acc2[j][4 * k + 1], acc2[j][4 * k + 2],
+                                 acc2[j][4 * k + 3]};
+                __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(dst + k));
+            }
         }
     }
 }
@@ -1594,6 +1870,7 @@ struct Fc2SumArgs {
     const float *b2;
     const float *resid;
     float *y;
+    unsigned *epoch;   // advanced by one after a one-launch step (null otherwise)
 };
 
 // SQ: owner rows per thread (owners g, g + 128, ... below SQ * 128 >= nq),
@@ -1644,6 +1921,9 @@ __device__ __forceinline__ void fc2_sum_block(const Fc2SumArgs &a, int s) {
 
 template <int SQ>
 __global__ __launch_bounds__(kThreads) void k_fc2_sum(Fc2SumArgs a) {
+    // every owner of the step has finished with the exchange: the next
+    // step's words carry the next epoch
+    if (a.epoch && blockIdx.x == 0 && threadIdx.x == 0) *a.epoch += 1u;
     fc2_sum_block<SQ>(a, blockIdx.x);
 }
 
@@ -1666,10 +1946,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     else pred1_block<WT>(a, blockIdx.x - nq);
 }
 
-template <int WT, int CPL2, int SQ>
+template <int WT, int SQ>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     Fc1Regs<false, 1>::waves_per_eu))) void k_score1_fc2sum(ScoreParams p, int nq, Fc2SumArgs a) {
-    if ((int)blockIdx.x < nq) score1_block<WT, CPL2, false, false, 1, false>(p, blockIdx.x, nq);
+    if ((int)blockIdx.x < nq) score1_block<WT, false, false, 1, false>(p, blockIdx.x, nq);
     else fc2_sum_block<SQ>(a, blockIdx.x - nq);
 }
 
@@ -1992,6 +2272,18 @@ hipError_t launch_transpose_perm(const void *wd, int d, int f, int ws, const int
     return hipGetLastError();
 }
 
+hipError_t launch_p2_kmajor(const void *p2, int H, int f, int nq, int ws, const int32_t *perm,
+                            void *dst, hipStream_t s) {
+    const dim3 grid(nq, (H + 63) / 64);
+    if (ws == 2)
+        hipLaunchKernelGGL(k_p2_kmajor<uint16_t>, grid, dim3(256), 0, s, (const uint16_t *)p2, H,
+                           f, nq, perm, (uint16_t *)dst);
+    else
+        hipLaunchKernelGGL(k_p2_kmajor<uint32_t>, grid, dim3(256), 0, s, (const uint32_t *)p2, H,
+                           f, nq, perm, (uint32_t *)dst);
+    return hipGetLastError();
+}
+
 hipError_t launch_invert(const int32_t *perm, int f, int32_t *inv, hipStream_t s) {
     const int blocks = (f + 255) / 256;
     hipLaunchKernelGGL(k_fill_identity, dim3(blocks), dim3(256), 0, s, inv, f);
@@ -2090,6 +2382,7 @@ static Fc1Out fc1_out(const LayerView &L) { return Fc1Out{L.vbits, L.lslot, L.la
 static ScoreParams score_params(const LayerView &L, const float *x, int B) {
     ScoreParams p = {};
     p.p2 = (const u32x4 *)L.p2;
+    p.p2k = L.p2k;
     p.c2 = L.c2;
     p.h = L.h;
     p.B = B;
@@ -2122,34 +2415,27 @@ hipError_t launch_score(const LayerView &L, const float *x, int B, bool fc1, con
         // 8 chunks per lane of up and gate rows) and one workgroup per CU
         // covers every owner
         const bool spec = L.nq <= 256;
-#define ASF_S1F(WT, C2, G, C1)                                                                 \
-    if (spec && C1 * (G ? 2 : 1) <= 8)                                                         \
-        ASF_LAUNCH(k, (k_score1<WT, C2, true, G, C1, (C1 * (G ? 2 : 1) <= 8)>), grid, blk, p); \
-    else ASF_LAUNCH(k, (k_score1<WT, C2, true, G, C1, false>), grid, blk, p);
-#define ASF_S1G(WT, C2, C1) \
-    if (L.gated) { ASF_S1F(WT, C2, true, C1) } else { ASF_S1F(WT, C2, false, C1) }
-#define ASF_S1C(WT, C2)                  \
-    if (!fc1) {                          \
-        ASF_LAUNCH(k, (k_score1<WT, C2, false, false, 1, false>), grid, blk, p); \
-    } else switch (cpl1) {               \
-    case 1: ASF_S1G(WT, C2, 1) break;    \
-    case 2: ASF_S1G(WT, C2, 2) break;    \
-    case 4: ASF_S1G(WT, C2, 4) break;    \
-    case 8: ASF_S1G(WT, C2, 8) break;    \
-    case 10: ASF_S1G(WT, C2, 10) break;  \
-    case 12: ASF_S1G(WT, C2, 12) break;  \
-    case 14: ASF_S1G(WT, C2, 14) break;  \
-    default: ASF_S1G(WT, C2, 16) break;  \
-    }
-#define ASF_S1W(WT)                  \
-    switch (cpl2) {                  \
-    case 1: ASF_S1C(WT, 1) break;    \
-    case 2: ASF_S1C(WT, 2) break;    \
-    default: ASF_S1C(WT, 4) break;   \
+#define ASF_S1F(WT, G, C1)                                                                 \
+    if (spec && C1 * (G ? 2 : 1) <= 8)                                                     \
+        ASF_LAUNCH(k, (k_score1<WT, true, G, C1, (C1 * (G ? 2 : 1) <= 8)>), grid, blk, p); \
+    else ASF_LAUNCH(k, (k_score1<WT, true, G, C1, false>), grid, blk, p);
+#define ASF_S1G(WT, C1) \
+    if (L.gated) { ASF_S1F(WT, true, C1) } else { ASF_S1F(WT, false, C1) }
+#define ASF_S1W(WT)                                                         \
+    if (!fc1) {                                                             \
+        ASF_LAUNCH(k, (k_score1<WT, false, false, 1, false>), grid, blk, p); \
+    } else switch (cpl1) {                                                  \
+    case 1: ASF_S1G(WT, 1) break;                                           \
+    case 2: ASF_S1G(WT, 2) break;                                           \
+    case 4: ASF_S1G(WT, 4) break;                                           \
+    case 8: ASF_S1G(WT, 8) break;                                           \
+    case 10: ASF_S1G(WT, 10) break;                                         \
+    case 12: ASF_S1G(WT, 12) break;                                         \
+    case 14: ASF_S1G(WT, 14) break;                                         \
+    default: ASF_S1G(WT, 16) break;                                         \
     }
         if (L.wtype == ASF_F16) { ASF_S1W(1) } else { ASF_S1W(0) }
 #undef ASF_S1W
-#undef ASF_S1C
 #undef ASF_S1G
 #undef ASF_S1F
         return hipGetLastError();
@@ -2173,6 +2459,70 @@ hipError_t launch_score(const LayerView &L, const float *x, int B, bool fc1, con
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !fc1) return e;
     return launch_fc1(L, x, B, 0, nullptr, nullptr, tr, s);
+}
+
+// parameters of the one-launch step: the owner kernels' plus predictor layer
+// 1 (rows per owner, waves per row) and the exchange
+static ScoreParams step1_params(const LayerView &L, const float *x) {
+    ScoreParams p = score_params(L, x, 1);
+    p.p1 = L.p1;
+    p.c1 = L.c1;
+    p.l1_rows = (L.H + L.nq - 1) / L.nq;
+    p.l1_wpr = pred1_wpr(L);
+    p.xch = L.xch;
+    p.xstride = L.xstride;
+    p.epoch = L.epoch;
+    p.flags = L.dbg;
+    return p;
+}
+
+// the k_step1 instantiation for layer L (fn) and whether it applies at all
+template <int WT, bool G, int C1>
+static const void *step1_fn_g(bool spec) {
+    if constexpr (C1 * (G ? 2 : 1) <= 8)
+        if (spec) return (const void *)k_step1<WT, G, C1, true>;
+    return (const void *)k_step1<WT, G, C1, false>;
+}
+
+template <int WT, bool G>
+static const void *step1_fn_c(int cpl1, bool spec) {
+    switch (cpl1) {
+    case 1: return step1_fn_g<WT, G, 1>(spec);
+    case 2: return step1_fn_g<WT, G, 2>(spec);
+    case 4: return step1_fn_g<WT, G, 4>(spec);
+    case 8: return step1_fn_g<WT, G, 8>(spec);
+    default: return nullptr;
+    }
+}
+
+static const void *step1_fn(const LayerView &L) {
+    const int cpl1 = fc1_cpl(L.cd);
+    const bool spec = L.nq <= 256 && cpl1 * (L.gated ? 2 : 1) <= 8;
+    if (L.wtype == ASF_F16)
+        return L.gated ? step1_fn_c<1, true>(cpl1, spec) : step1_fn_c<1, false>(cpl1, spec);
+    return L.gated ? step1_fn_c<0, true>(cpl1, spec) : step1_fn_c<0, false>(cpl1, spec);
+}
+
+bool step1_fits(const LayerView &L) {
+    // predictor layer 1 in at most two passes of 8 / WPR rows per owner
+    const int rows = (L.H + L.nq - 1) / L.nq, rpw = kWaves / pred1_wpr(L);
+    if (rows > 2 * rpw || L.H > kMaxHLds || L.cd > kThreads * 4) return false;
+    const void *fn = step1_fn(L);
+    if (!fn) return false;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess)
+        return false;
+    return per_cu >= 1 && (long long)per_cu * L.ncu >= L.nq;
+}
+
+hipError_t launch_step1(const LayerView &L, const float *x, const Trace *tr, hipStream_t s) {
+    const ScoreParams p = step1_params(L, x);
+    const void *fn = step1_fn(L);
+    if (!fn) return hipErrorInvalidValue;
+    const dim3 grid(L.nq), blk(kThreads);
+    void *args[] = {(void *)&p};
+    return hipExtLaunchKernel(fn, grid, blk, args, 0, s, ev_start(tr, ASF_K_SCORE_FC1),
+                              ev_stop(tr, ASF_K_SCORE_FC1), 0);
 }
 
 hipError_t launch_fc1(const LayerView &L, const float *x, int B, int mode, const int32_t *ids,
@@ -2234,9 +2584,9 @@ hipError_t launch_fc1(const LayerView &L, const float *x, int B, int mode, const
 }
 
 hipError_t launch_fc2_sum(const LayerView &L, const float *resid, float *y, const Trace *tr,
-                          hipStream_t s) {
+                          hipStream_t s, bool advance_epoch) {
     const dim3 grid(L.d / 16), blk(kThreads);
-    const Fc2SumArgs a{L.part1, L.nq, L.b2, resid, y};
+    const Fc2SumArgs a{L.part1, L.nq, L.b2, resid, y, advance_epoch ? L.epoch : nullptr};
     const int sq = pow2_at_least((L.nq + kThreads / 4 - 1) / (kThreads / 4));
     switch (sq) {
     case 1: ASF_LAUNCH(ASF_K_FC2, k_fc2_sum<1>, grid, blk, a); break;
@@ -2314,26 +2664,18 @@ hipError_t launch_score1_fc2sum(const LayerView *N, const LayerView &L, const fl
                                 float *y, const Trace *tr, hipStream_t s) {
     if (!N) return launch_fc2_sum(L, resid, y, tr, s);
     const ScoreParams p = score_params(*N, nullptr, 1);
-    const Fc2SumArgs a{L.part1, L.nq, L.b2, resid, y};
+    const Fc2SumArgs a{L.part1, L.nq, L.b2, resid, y, nullptr};
     const dim3 grid(N->nq + L.d / 16), blk(kThreads);
-    const int cpl2 = pow2_at_least((N->ch + 63) / 64);
     const int sq = pow2_at_least((L.nq + kThreads / 4 - 1) / (kThreads / 4));
-#define ASF_SFQ(WT, C2)                                                                              \
-    switch (sq) {                                                                                    \
-    case 1: ASF_LAUNCH(ASF_K_FC2, (k_score1_fc2sum<WT, C2, 1>), grid, blk, p, N->nq, a); break;     \
-    case 2: ASF_LAUNCH(ASF_K_FC2, (k_score1_fc2sum<WT, C2, 2>), grid, blk, p, N->nq, a); break;     \
-    case 4: ASF_LAUNCH(ASF_K_FC2, (k_score1_fc2sum<WT, C2, 4>), grid, blk, p, N->nq, a); break;     \
-    default: ASF_LAUNCH(ASF_K_FC2, (k_score1_fc2sum<WT, C2, kSumQ>), grid, blk, p, N->nq, a); break; \
-    }
-#define ASF_SF(WT)                                  \
-    switch (cpl2) {                                 \
-    case 1: ASF_SFQ(WT, 1) break;                   \
-    case 2: ASF_SFQ(WT, 2) break;                   \
-    default: ASF_SFQ(WT, 4) break;                  \
+#define ASF_SF(WT)                                                                              \
+    switch (sq) {                                                                               \
+    case 1: ASF_LAUNCH(ASF_K_FC2, (k_score1_fc2sum<WT, 1>), grid, blk, p, N->nq, a); break;     \
+    case 2: ASF_LAUNCH(ASF_K_FC2, (k_score1_fc2sum<WT, 2>), grid, blk, p, N->nq, a); break;     \
+    case 4: ASF_LAUNCH(ASF_K_FC2, (k_score1_fc2sum<WT, 4>), grid, blk, p, N->nq, a); break;     \
+    default: ASF_LAUNCH(ASF_K_FC2, (k_score1_fc2sum<WT, kSumQ>), grid, blk, p, N->nq, a); break; \
     }
     if (N->wtype == ASF_F16) { ASF_SF(1) } else { ASF_SF(0) }
 #undef ASF_SF
-#undef ASF_SFQ
     return hipGetLastError();
 }
 

@@ -89,32 +89,46 @@ def log(args, *a):
         print(*a, file=sys.stderr, flush=True)
 
 
-def bytes_model(sh, k_mean):
+def bytes_model(sh, k_mean, nz=None, one_launch=False):
     """Algorithmic bytes (each distinct byte the method must read or write,
-    counted once) of one decode step and of each kernel."""
+    counted once) of one decode step and of each kernel.  nz: hidden units of
+    the predictor that are nonzero (mean per token); predictor layer 2 reads
+    the P2 entries of those units only (one token), all H of them when nz is
+    None (batches).  one_launch: predictor layer 1 runs in the score/FC1
+    kernel (its bytes are that kernel's)."""
     d, f, H = sh.d, sh.f, sh.H
     ws = 2 if sh.wdtype == "f16" else 4
     nmat = 3 if sh.gated else 2
     words = (f + 63) // 64
+    nz = H if nz is None else nz
+    l1 = H * d * ws + H * 4 + d * 4            # P1, c1, x
+    l2 = nz * f * ws + f * 4                   # P2 entries of the nonzero units, c2
+    rows = k_mean * (nmat * d * ws + 4)        # bundles (gate,) up, down + b1
     # single-token decode step: the score/FC1 kernel also reads the listed
     # down columns (FC2 into per-owner rows); the FC2 kernel adds the owner
     # rows (implementation traffic, not counted) with b2 into y
     per = {
-        "pred_l1": H * d * ws + H * 4 + d * 4 + H * 4,
-        "score": f * H * ws + f * 4 + H * 4 + words * 8,
-        "score_fc1": (f * H * ws + f * 4 + H * 4 + words * 8 + k_mean * (d * ws + 4) + d * 4
-                      + k_mean * d * ws),
-        "fc1": k_mean * (d * ws + 4) + d * 4,
+        "pred_l1": l1 + H * 4,
+        "score": l2 + H * 4 + words * 8,
+        "score_fc1": (l1 if one_launch else H * 4 + d * 4) + l2 + words * 8 + rows,
+        "fc1": k_mean * ((nmat - 1) * d * ws + 4) + d * 4,
         "fc2": d * 4 * 2,
         "list": words * 8 + k_mean * 4,
     }
-    if sh.gated:
-        per["score_fc1"] += k_mean * d * ws
-        per["fc1"] += k_mean * d * ws
-    step = (H * d * ws + H * 4 + f * H * ws + f * 4 + d * 4
-            + k_mean * (nmat * d * ws + 4) + d * 4 + d * 4)
+    step = l1 + l2 + rows + d * 4 + d * 4
     dense = f * (nmat * d * ws + 4) + d * 4 * 3
     return step, per, dense
+
+
+def hidden_nonzero(torch, p1, c1, X):
+    """Mean count per token of the predictor's hidden units with
+    ReLU(P1 x + c1) != 0 (fp32 on the device; the one-token predictor layer
+    2 reads the P2 entries of these units only)."""
+    w = p1.float().t().contiguous()
+    h = torch.matmul(X.float(), w)
+    if c1 is not None:
+        h = h + c1.float()
+    return float((torch.relu(h) != 0).sum(dim=1).double().mean())
 
 
 PROFILE = os.path.join(ROOT, "profiles", "decode_step_opt6.7b_4096x16384_fp16.md")
@@ -312,12 +326,13 @@ def bench_stack(args, asf, torch, np, wl, dev, stream):
     B = 1 tokens through all layers per asf_stack_decode call."""
     from workload.gpu import stack_layer_device, stack_tokens
     t0 = time.perf_counter()
-    layers, shapes = [], []
+    layers, shapes, p1s = [], [], []
     for l in range(wl.STACK_LAYERS):
         DL = stack_layer_device(l, dev)
         layers.append(asf.Layer(DL.w_up, DL.w_down, DL.p1, DL.p2, b1=DL.b1, b2=DL.b2, c2=DL.c2,
                                 neuron_table=DL.perm))
         shapes.append(DL.shape)
+        p1s.append(DL.p1)
         del DL
         torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -351,14 +366,19 @@ def bench_stack(args, asf, torch, np, wl, dev, stream):
     elapsed_la = time.perf_counter() - t0
     # per-layer active counts of the same tokens (outside the timed region)
     counts = torch.zeros((n, len(layers)), dtype=torch.int32, device=dev)
+    nzs = np.zeros(len(layers))
     for t in range(n):
         cur = X[t:t + 1]
         for l, lay in enumerate(layers):
             lay.predict(cur, n_active=counts[t, l:l + 1], want_list=False)
+            if t < 16:
+                nzs[l] += hidden_nonzero(torch, p1s[l], None, cur) / min(n, 16)
             cur = lay.decode_step(cur)
     torch.cuda.synchronize()
+    del p1s
     k = counts.double().mean(dim=0).cpu().numpy()
-    tok_bytes = sum(bytes_model(shapes[l], float(k[l]))[0] for l in range(len(layers)))
+    tok_bytes = sum(bytes_model(shapes[l], float(k[l]), float(nzs[l]))[0]
+                    for l in range(len(layers)))
     dense_bytes = sum(bytes_model(shapes[l], 0.0)[2] for l in range(len(layers)))
     # dense comparator: every layer's dense FFN, chained, a few tokens
     nd = args.stack_dense_tokens
@@ -466,6 +486,7 @@ def bench_gated(args, asf, torch, np, wl, dev, stream):
                       w_gate=orig["w_gate"], b1=orig["b1"], b2=orig["b2"], c2=orig["c2"],
                       neuron_table=orig["neuron_table"]) for _ in range(args.gated_ring)]
     torch.cuda.synchronize()
+    nz = hidden_nonzero(torch, orig["p1"], None, X)
     del orig
     torch.cuda.empty_cache()
     Y = torch.empty((len(ring), 1, sh.d), dtype=torch.float32, device=dev)
@@ -487,7 +508,7 @@ def bench_gated(args, asf, torch, np, wl, dev, stream):
                                     want_list=False)
     torch.cuda.synchronize()
     k = float(counts.double().mean())
-    step_bytes, _, dense_bytes = bytes_model(sh, k)
+    step_bytes, _, dense_bytes = bytes_model(sh, k, nz)
     nd = max(5, min(args.dense_steps, n))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ring[0].dense_ffn_ref(X[:1])
@@ -503,7 +524,8 @@ def bench_gated(args, asf, torch, np, wl, dev, stream):
     res = {"workload": "Llama-7B-shaped gated ReLU FFN layer 4096x11008 fp16 (gate, up, down), "
                        "predictor 4096->1024->11008, ~10% active, batch 1",
            "ring_layers": len(ring), "steps": n, "tokens_per_s": n / el, "ms_per_step": ms,
-           "active_frac": k / sh.f, "algorithmic_bytes_per_step": step_bytes,
+           "active_frac": k / sh.f, "pred_hidden_nonzero_mean": nz,
+           "algorithmic_bytes_per_step": step_bytes,
            "effective_gbps": step_bytes / (ms * 1e-3) / 1e9,
            "effective_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
            "dense_ms_per_step": dense_ms, "dense_gbps": dense_bytes / (dense_ms * 1e-3) / 1e9,
@@ -586,6 +608,7 @@ def bench_batched(args, asf, torch, np, wl, dev, stream):
                       c2=orig["c2"], neuron_table=orig["neuron_table"], max_batch=32)
             for _ in range(args.batched_ring)]
     torch.cuda.synchronize()
+    nz1 = hidden_nonzero(torch, orig["p1"], None, X)
     del orig
     sh_ = stream.cuda_stream
     out = []
@@ -609,7 +632,7 @@ def bench_batched(args, asf, torch, np, wl, dev, stream):
             ring[0].predict(X[i * B:(i + 1) * B], n_active=counts[i:i + 1], want_list=False)
         torch.cuda.synchronize()
         k = float(counts.double().mean())
-        step_bytes, _, dense_bytes = bytes_model(sh, k)
+        step_bytes, _, dense_bytes = bytes_model(sh, k, nz1 if B == 1 else None)
         ms = el * 1e3 / steps
         rec = {
             "batch": B, "steps": steps, "tokens_per_s": B * steps / el, "ms_per_step": ms,
@@ -759,6 +782,7 @@ def main():
                               w_gate=orig["w_gate"], b1=orig["b1"], b2=orig["b2"],
                               c1=orig["c1"], c2=orig["c2"], neuron_table=orig["neuron_table"]))
     torch.cuda.synchronize()
+    nz_mean = hidden_nonzero(torch, orig["p1"], orig["c1"], torch.from_numpy(X).to(dev))
     del orig
     torch.cuda.empty_cache()
     ring_bytes = sum(l.storage.numel() for l in ring)
@@ -815,7 +839,9 @@ def main():
     # launches its kernels with HIP events on the dispatch packets, so the
     # events time the kernels themselves on the stream they run on); one
     # step in 8 from the 17th on, median per kernel
-    used = [KERNELS.index(k) for k in ("pred_l1", "score_fc1", "fc2")]
+    one_launch = ring[0].step_launches(1) == 2
+    used = [KERNELS.index(k) for k in
+            (("score_fc1", "fc2") if one_launch else ("pred_l1", "score_fc1", "fc2"))]
     NE = 2 * len(KERNELS)
     ns = max(1, args.trace_samples)
     hev = HipEvents(NE * ns)
@@ -859,7 +885,7 @@ def main():
     torch.cuda.synchronize()
     ks = counts[W:].cpu().numpy()
     k_mean = float(ks.mean())
-    step_bytes, per_bytes, dense_bytes = bytes_model(sh, k_mean)
+    step_bytes, per_bytes, dense_bytes = bytes_model(sh, k_mean, nz_mean, one_launch)
     dom = int(np.argmax(kmed))
     dname = KERNELS[dom]
     achieved = per_bytes[dname] / (kmed[dom] * 1e-3) / 1e9
@@ -995,6 +1021,8 @@ def main():
         "algorithmic_bytes_per_step": step_bytes,
         "active_mean": k_mean,
         "active_frac": k_mean / sh.f,
+        "pred_hidden_nonzero_mean": nz_mean,
+        "step_launches": 2 if one_launch else 3,
         "repeats_ms_per_step": rep,
         "median5_ms_per_step": rep[2],
         "median5_tokens_per_s": 1.0 / (rep[2] * 1e-3),

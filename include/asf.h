@@ -370,7 +370,9 @@ asf_status asf_predict_heads(const asf_head_predictor *hp, const float *x, int32
 /* Kernels behind the calls (ids for asf_layer_set_trace).
  *   asf_predict       PRED_L1, SCORE, then LIST when an output is requested
  *   asf_decode_step   PRED_L1, SCORE_FC1 (B == 1, fp16; else SCORE + FC1),
- *                     FC2, then LIST when an output is requested
+ *                     FC2, then LIST when an output is requested; one token
+ *                     on a layer whose owners fit the device at once: SCORE_FC1
+ *                     (with predictor layer 1), FC2 (asf_step_launches)
  *   asf_sparse_ffn    FC1, FC2
  *   asf_dense_ffn_ref FC1 (every neuron), FC2
  *   asf_exact_ffn     FC1 (pre-activations, true set, owner FC2 rows), FC2
@@ -396,6 +398,16 @@ typedef enum {
  * tracing off.  The handles are borrowed: the caller creates and destroys
  * them. */
 asf_status asf_layer_set_trace(asf_layer *layer, void *const *events, int32_t n);
+
+/* Launches of one asf_decode_step of `layer` for B tokens, the list kernel
+ * left out: 2 when a one-token step runs predict, FC1 and the owner FC2 rows
+ * in one launch (SCORE_FC1: the owners compute predictor layer 1 and exchange
+ * h through device memory, which needs every owner workgroup resident at
+ * once; the layer checks this at creation) followed by the owner-row sum
+ * (FC2), else 3 (PRED_L1, SCORE_FC1 or SCORE + FC1, FC2).  A caller tracing
+ * kernels learns from it which ids a step uses.  0 for a null layer or B
+ * outside 1 .. max_batch. */
+int32_t asf_step_launches(const asf_layer *layer, int32_t B);
 
 /* Human-readable name of a status code (static string). */
 const char *asf_status_string(asf_status s);
