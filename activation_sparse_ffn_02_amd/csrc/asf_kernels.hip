@@ -1251,6 +1251,7 @@ __device__ __forceinline__ void step1_h(const ScoreParams &p, int q, const u32x4
     const int C = p.cd, part = wave % wpr;
 #pragma unroll
     for (int ps = 0; ps < 2; ++ps) {
+        if (ps > 0 && R <= rpw) break;   // one pass covers the owner's rows
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
