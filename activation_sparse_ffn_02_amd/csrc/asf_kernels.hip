@@ -1218,6 +1218,7 @@ __device__ __forceinline__ void score1_p2(const ScoreParams &p, int q, int nq, i
 // and kFlagXchTimeout is raised.  The epoch advances once per step, in the
 // owner-row sum that follows the launch.
 constexpr int kSpinMax = 1 << 16;
+constexpr int kXchPause = 16;   // s_sleep units (64 clocks) before the first exchange read
 constexpr unsigned kFlagXchTimeout = 8u;
 
 // this owner's P1 chunks: pass ps, row q*R + ps*rpw + wave/wpr (rows past
@@ -1285,6 +1286,9 @@ __device__ __forceinline__ void step1_h(const ScoreParams &p, int q, const u32x4
         wait[u] = (int)threadIdx.x + kThreads * u < H;
         v[u] = 0;
     }
+    // the other owners publish within a few hundred ns of this one: a short
+    // pause lets the first read find nearly all of them
+    __builtin_amdgcn_s_sleep(kXchPause);
     for (int it = 0; it < kSpinMax; ++it) {
         bool any = false;
 #pragma unroll
