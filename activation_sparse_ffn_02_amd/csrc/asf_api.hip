@@ -166,17 +166,25 @@ static hipError_t launch_fc2_step(const LayerView &v, int B, const float *resid,
 // One decode step of layer v (predict, FC1, FC2 into y): one token in one
 // launch when every owner can be resident at once (then the owner-row sum,
 // which also advances the exchange epoch), else predictor layer 1, the
-// scores with FC1, and FC2
+// scores with FC1, and FC2.  With active / n_active, the list of the step's
+// set too: for one token in the owner-row sum's grid, else by the list
+// kernel.
 static hipError_t launch_step(const LayerView &v, const float *x, int B, const float *resid,
-                              float *y, const Trace *tr, hipStream_t s) {
+                              float *y, int32_t *active, int32_t *n_active, const Trace *tr,
+                              hipStream_t s) {
     hipError_t e;
+    const bool list = active || n_active;
     if (B == 1 && v.fused) {
         if ((e = launch_step1(v, x, tr, s)) != hipSuccess) return e;
+        if (list) return launch_fc2_sum_list(v, resid, y, active, n_active, tr, s, true);
         return launch_fc2_sum(v, resid, y, tr, s, true);
     }
     if ((e = launch_pred_l1(v, x, B, tr, s)) != hipSuccess) return e;
     if ((e = launch_score(v, x, B, true, tr, s)) != hipSuccess) return e;
-    return launch_fc2_step(v, B, resid, y, tr, s);
+    if (B == 1 && list) return launch_fc2_sum_list(v, resid, y, active, n_active, tr, s, false);
+    if ((e = launch_fc2_step(v, B, resid, y, tr, s)) != hipSuccess) return e;
+    if (list) return launch_list(v, B, active, n_active, nullptr, tr, s);
+    return hipSuccess;
 }
 
 // Inter-layer buffer of asf_stack_decode_static: one [B][d_model] float32
@@ -392,9 +400,7 @@ asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
     if (!aligned16(y) || (residual && !aligned16(residual))) return ASF_ERR_ALIGN;
     const LayerView &v = layer->v;
     hipStream_t s = (hipStream_t)stream;
-    if (launch_step(v, x, B, residual, y, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
-    if ((active || n_active) &&
-        launch_list(v, B, active, n_active, nullptr, layer->tr(), s) != hipSuccess)
+    if (launch_step(v, x, B, residual, y, active, n_active, layer->tr(), s) != hipSuccess)
         return ASF_ERR_HIP;
     return ASF_OK;
 }
@@ -479,7 +485,8 @@ asf_status asf_stack_decode(asf_layer *const *layers, int32_t n_layers, const fl
         const LayerView &v = layers[l]->v;
         const asf::Trace *tr = layers[l]->tr();
         float *out = ((n_layers - 1 - l) % 2 == 0) ? y : work;
-        if (launch_step(v, in, B, residual ? in : nullptr, out, tr, s) != hipSuccess)
+        if (launch_step(v, in, B, residual ? in : nullptr, out, nullptr, nullptr, tr, s) !=
+            hipSuccess)
             return ASF_ERR_HIP;
         in = out;
     }

@@ -215,6 +215,10 @@ hipError_t launch_check_ids(const int32_t *ids, const int32_t *n_ids, int n_fixe
 // slot-ordered outputs of the last prediction: token masks, ascending list
 hipError_t launch_list(const LayerView &L, int B, int32_t *active_ids, int32_t *n_active,
                        uint64_t *token_masks, const Trace *tr, hipStream_t s);
+// launch_fc2_sum and, in the same grid, the one-token list (ids, count)
+hipError_t launch_fc2_sum_list(const LayerView &L, const float *resid, float *y,
+                               int32_t *active_ids, int32_t *n_active, const Trace *tr,
+                               hipStream_t s, bool advance_epoch);
 
 }  // namespace asf
 

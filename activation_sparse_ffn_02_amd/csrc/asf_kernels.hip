@@ -2132,50 +2132,64 @@ __global__ __launch_bounds__(64) void k_head_list(const uint64_t *__restrict__ w
 // requested together (up to 32 tokens), one ballot per slot word and token.
 constexpr int kListSlots = kThreads;
 
-__device__ __forceinline__ int block_sum_int(int v, int *red) {
+// the workgroup sums of two ints (every thread gets both): butterflies over
+// the wave, then the wave partials in wave order; one barrier
+__device__ __forceinline__ int2 block_sum_int2(int a, int b, int2 *red) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    for (int o = 32; o > 0; o >>= 1) {
+        a += __shfl_xor(a, o, 64);
+        b += __shfl_xor(b, o, 64);
+    }
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_int2(a, b);
     __syncthreads();
-    int t = 0;
+    int2 t = make_int2(0, 0);
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) t += red[w];
-    __syncthreads();
+    for (int w = 0; w < kWaves; ++w) {
+        t.x += red[w].x;
+        t.y += red[w].y;
+    }
     return t;
 }
 
-__global__ __launch_bounds__(kThreads) void k_list(const uint64_t *__restrict__ ubits,
-                                                   const uint64_t *__restrict__ wbits, int B,
-                                                   int f, int nq, int words,
-                                                   const int32_t *__restrict__ perm,
-                                                   uint64_t *__restrict__ token_masks,
-                                                   int32_t *__restrict__ slots,
-                                                   int32_t *__restrict__ count,
-                                                   int32_t *__restrict__ active_ids,
-                                                   int32_t *__restrict__ n_active) {
+struct ListArgs {
+    const uint64_t *ubits;
+    const uint64_t *wbits;
+    int B, f, nq, words;
+    const int32_t *perm;
+    uint64_t *token_masks;
+    int32_t *slots;
+    int32_t *count;
+    int32_t *active_ids;
+    int32_t *n_active;
+};
+
+template <bool MASKS>
+__device__ __forceinline__ void list_block(const ListArgs &a, int blk) {
     __shared__ uint64_t ob[kMaxFfn / 64];
-    __shared__ int red[kWaves];
+    __shared__ int2 red[kWaves];
     __shared__ int wave_cnt[kWaves];
+    const int B = a.B, f = a.f, nq = a.nq, words = a.words;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int s0 = blockIdx.x * kListSlots;
+    const int s0 = blk * kListSlots;
     const int s = s0 + t;
     const bool in = s < f;
     const int sc = in ? s : f - 1;
     // requests first: the owner words (at most 2 per thread), this slot's
     // table entry, the token words of this slot
-    uint64_t o0 = ubits[t < nq ? t : nq - 1];
-    uint64_t o1 = ubits[t + kThreads < nq ? t + kThreads : nq - 1];
-    const int32_t id = active_ids ? perm[sc] : 0;
-    uint64_t tw[kMaxBatch];
-    if (token_masks) {
+    uint64_t o0 = a.ubits[t < nq ? t : nq - 1];
+    uint64_t o1 = a.ubits[t + kThreads < nq ? t + kThreads : nq - 1];
+    const int32_t id = a.active_ids ? a.perm[sc] : 0;
+    uint64_t tw[MASKS ? kMaxBatch : 1];
+    if constexpr (MASKS) {
 #pragma unroll
         for (int b = 0; b < kMaxBatch; ++b)
-            tw[b] = wbits[(size_t)(b < B ? b : B - 1) * nq + sc % nq];
+            tw[b] = a.wbits[(size_t)(b < B ? b : B - 1) * nq + sc % nq];
     }
     if (t < nq) ob[t] = o0;
     if (t + kThreads < nq) ob[t + kThreads] = o1;
     __syncthreads();
-    // union slots below s0, and in all, from the owner words
+    // union slots below s0, and in all, from the owner words; this thread's
+    // slot bit
     int before = 0, total = 0;
     for (int q = t; q < nq; q += kThreads) {
         const uint64_t m = ob[q];
@@ -2183,31 +2197,47 @@ __global__ __launch_bounds__(kThreads) void k_list(const uint64_t *__restrict__ 
         const int k = s0 > q ? (s0 - q + nq - 1) / nq : 0;
         before += __popcll(k >= 64 ? m : (m & ((1ull << k) - 1ull)));
     }
-    before = block_sum_int(before, red);
-    total = block_sum_int(total, red);
     const bool mine = in && ((ob[sc % nq] >> (sc / nq)) & 1ull);
     const uint64_t bal = __ballot(mine);
     if (lane == 0) wave_cnt[wave] = __popcll(bal);
-    __syncthreads();
-    int off = before + __popcll(bal & ((1ull << lane) - 1ull));
+    const int2 bt = block_sum_int2(before, total, red);
+    int off = bt.x + __popcll(bal & ((1ull << lane) - 1ull));
     for (int v = 0; v < wave; ++v) off += wave_cnt[v];
     if (mine) {
-        slots[off] = s;
-        if (active_ids) active_ids[off] = id;
+        a.slots[off] = s;
+        if (a.active_ids) a.active_ids[off] = id;
     }
-    if (blockIdx.x == 0 && t == 0) {
-        *count = total;
-        if (n_active) *n_active = total;
+    if (blk == 0 && t == 0) {
+        *a.count = bt.y;
+        if (a.n_active) *a.n_active = bt.y;
     }
-    if (token_masks) {
+    if constexpr (MASKS) {
         const int w = s0 / 64 + wave;
         const int sh = sc / nq;
 #pragma unroll
         for (int b = 0; b < kMaxBatch; ++b) {
             if (b >= B) break;
             const uint64_t m = __ballot(in && ((tw[b] >> sh) & 1ull));
-            if (lane == 0 && w < words) token_masks[(size_t)b * words + w] = m;
+            if (lane == 0 && w < words) a.token_masks[(size_t)b * words + w] = m;
         }
+    }
+}
+
+template <bool MASKS>
+__global__ __launch_bounds__(kThreads) void k_list(ListArgs a) {
+    list_block<MASKS>(a, blockIdx.x);
+}
+
+// the owner-row sum of a one-token step (workgroups below nsum) and the
+// step's slot-ordered list (the others) in one grid: the list needs only
+// the owner words, which the step's launch has finished writing
+template <int SQ>
+__global__ __launch_bounds__(kThreads) void k_fc2_sum_list(Fc2SumArgs a, int nsum, ListArgs l) {
+    if ((int)blockIdx.x < nsum) {
+        if (a.epoch && blockIdx.x == 0 && threadIdx.x == 0) *a.epoch += 1u;
+        fc2_sum_block<SQ>(a, blockIdx.x);
+    } else {
+        list_block<false>(l, blockIdx.x - nsum);
     }
 }
 
@@ -2807,12 +2837,35 @@ hipError_t launch_check_ids(const int32_t *ids, const int32_t *n_ids, int n_fixe
     return hipGetLastError();
 }
 
+static ListArgs list_args(const LayerView &L, int B, int32_t *active_ids, int32_t *n_active,
+                          uint64_t *token_masks) {
+    return ListArgs{(const uint64_t *)L.ubits, (const uint64_t *)L.wbits, B, L.f, L.nq, L.words,
+                    (const int32_t *)L.perm, token_masks, L.slots, L.count, active_ids, n_active};
+}
+
 hipError_t launch_list(const LayerView &L, int B, int32_t *active_ids, int32_t *n_active,
                        uint64_t *token_masks, const Trace *tr, hipStream_t s) {
-    ASF_LAUNCH(ASF_K_LIST, k_list, dim3((L.f + kListSlots - 1) / kListSlots), dim3(kThreads),
-               (const uint64_t *)L.ubits,
-                       (const uint64_t *)L.wbits, B, L.f, L.nq, L.words, (const int32_t *)L.perm,
-                       token_masks, L.slots, L.count, active_ids, n_active);
+    const dim3 grid((L.f + kListSlots - 1) / kListSlots), blk(kThreads);
+    const ListArgs a = list_args(L, B, active_ids, n_active, token_masks);
+    if (token_masks) ASF_LAUNCH(ASF_K_LIST, k_list<true>, grid, blk, a);
+    else ASF_LAUNCH(ASF_K_LIST, k_list<false>, grid, blk, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fc2_sum_list(const LayerView &L, const float *resid, float *y,
+                               int32_t *active_ids, int32_t *n_active, const Trace *tr,
+                               hipStream_t s, bool advance_epoch) {
+    const int nsum = L.d / 16, nlist = (L.f + kListSlots - 1) / kListSlots;
+    const dim3 grid(nsum + nlist), blk(kThreads);
+    const Fc2SumArgs a{L.part1, L.nq, L.b2, resid, y, advance_epoch ? L.epoch : nullptr};
+    const ListArgs l = list_args(L, 1, active_ids, n_active, nullptr);
+    const int sq = pow2_at_least((L.nq + kThreads / 4 - 1) / (kThreads / 4));
+    switch (sq) {
+    case 1: ASF_LAUNCH(ASF_K_FC2, k_fc2_sum_list<1>, grid, blk, a, nsum, l); break;
+    case 2: ASF_LAUNCH(ASF_K_FC2, k_fc2_sum_list<2>, grid, blk, a, nsum, l); break;
+    case 4: ASF_LAUNCH(ASF_K_FC2, k_fc2_sum_list<4>, grid, blk, a, nsum, l); break;
+    default: ASF_LAUNCH(ASF_K_FC2, k_fc2_sum_list<kSumQ>, grid, blk, a, nsum, l); break;
+    }
     return hipGetLastError();
 }
 

@@ -369,8 +369,9 @@ asf_status asf_predict_heads(const asf_head_predictor *hp, const float *x, int32
 
 /* Kernels behind the calls (ids for asf_layer_set_trace).
  *   asf_predict       PRED_L1, SCORE, then LIST when an output is requested
- *   asf_decode_step   PRED_L1, SCORE_FC1 (B == 1, fp16; else SCORE + FC1),
- *                     FC2, then LIST when an output is requested; one token
+ *   asf_decode_step   PRED_L1, SCORE_FC1 (B == 1; else SCORE + FC1), FC2,
+ *                     then LIST when an output is requested (for one token
+ *                     the list runs in FC2's grid, timed as FC2); one token
  *                     on a layer whose owners fit the device at once: SCORE_FC1
  *                     (with predictor layer 1), FC2 (asf_step_launches)
  *   asf_sparse_ffn    FC1, FC2
@@ -399,8 +400,8 @@ typedef enum {
  * them. */
 asf_status asf_layer_set_trace(asf_layer *layer, void *const *events, int32_t n);
 
-/* Launches of one asf_decode_step of `layer` for B tokens, the list kernel
- * left out: 2 when a one-token step runs predict, FC1 and the owner FC2 rows
+/* Launches of one asf_decode_step of `layer` for B tokens, a list kernel of
+ * a batch left out: 2 when a one-token step runs predict, FC1 and the owner FC2 rows
  * in one launch (SCORE_FC1: the owners compute predictor layer 1 and exchange
  * h through device memory, which needs every owner workgroup resident at
  * once; the layer checks this at creation) followed by the owner-row sum
