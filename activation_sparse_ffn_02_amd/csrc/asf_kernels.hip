@@ -2526,7 +2526,10 @@ static const void *step1_fn_c(int cpl1, bool spec) {
     case 2: return step1_fn_g<WT, G, 2>(spec);
     case 4: return step1_fn_g<WT, G, 4>(spec);
     case 8: return step1_fn_g<WT, G, 8>(spec);
-    default: return nullptr;
+    case 10: return step1_fn_g<WT, G, 10>(spec);
+    case 12: return step1_fn_g<WT, G, 12>(spec);
+    case 14: return step1_fn_g<WT, G, 14>(spec);
+    default: return step1_fn_g<WT, G, 16>(spec);
     }
 }
 
