@@ -70,12 +70,16 @@ size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v) {
     t.inv = (int32_t *)take(f * 4);
     t.h = (float *)take(Bm * H * 4);
     t.h16 = Bm > 1 ? (_Float16 *)take(2 * Bm * H * 2) : nullptr;
-    t.x16 = Bm > 1 ? (_Float16 *)take(Bm * d * 2) : nullptr;
+    t.x16 = Bm > 1 ? (_Float16 *)take(2 * Bm * (size_t)x16_pitch((int)d) * 2) : nullptr;
     t.wbits = (uint64_t *)take(Bm * nq * 8);
     t.ubits = (uint64_t *)take(nq * 8);
     t.vbits = (uint64_t *)take(nq * 8);
     t.lslot = (int32_t *)take(nq * kRowsPerWG * 4);
     t.la = (float *)take(nq * kRowsPerWG * Bm * 4);
+    t.la16 = Bm > 1 ? (_Float16 *)take(2 * Bm * nq * kRowsPerWG * 2) : nullptr;
+    t.fc1_part = Bm > 1 ? (float *)take((size_t)fc1_slices((int)d) * (nmat - 1) * Bm * nq *
+                                        kRowsPerWG * 4)
+                        : nullptr;
     t.partial = (float *)take((size_t)kGroups * Bm * d * 4);
     t.part1 = (float *)take(nq * d * 4);
     t.arrive = (unsigned *)take(kArrive * 4);
@@ -149,7 +153,7 @@ size_t carve_heads(const asf_head_desc &desc, uintptr_t base, HeadView *v) {
     t.h = (float *)take(Bm * H * 4);
     t.wbits = (uint64_t *)take(Bm * words * 8);
     t.h16 = Bm > 1 ? (_Float16 *)take(2 * Bm * H * 2) : nullptr;
-    t.x16 = Bm > 1 ? (_Float16 *)take(Bm * d * 2) : nullptr;
+    t.x16 = Bm > 1 ? (_Float16 *)take(2 * Bm * (size_t)x16_pitch((int)d) * 2) : nullptr;
     t.pred_part = Bm > 1 ? (float *)take(((H + 31) / 32) * 8 * 1024 * 4) : nullptr;
     if (v) *v = t;
     return (size_t)(p - align_up(base, 256));
@@ -310,6 +314,9 @@ asf_status asf_create_layer(const asf_layer_desc *desc, const asf_layer_weights 
     chk(launch_gather_f32(w->b1, v.perm, f, v.b1, s));
     chk(launch_gather_f32(w->b2, nullptr, d, v.b2, s));
     chk(hipMemsetAsync(v.arrive, 0, kArrive * 4, s));
+    // the batched FC1 reads x16's row padding (zero) against absent weights
+    if (v.x16)
+        chk(hipMemsetAsync(v.x16, 0, 2 * (size_t)v.max_batch * x16_pitch(v.d) * 2, s));
     // the one-launch step: exchange words tagged 0, epoch 1; used when every
     // owner can be resident at once
     chk(hipMemsetAsync(v.xch, 0, (size_t)kXchCopies * v.xstride * 8, s));

@@ -140,13 +140,14 @@ __global__ __launch_bounds__(kThreads) void k_pred_mm(const u32x4 *__restrict__ 
 
 // Element e of row tile mt (row 32mt + e/32, token e%32): the KS partial
 // tiles in ks order, then c1, then ReLU -> h and its fp16 hi/lo halves.  The
-// grid also converts x to fp16 for the FC1 of the step.
+// grid also converts x to fp16 hi + lo for the FC1 of the step.
 __global__ __launch_bounds__(kThreads) void k_pred_fin(const float *__restrict__ part,
                                                        const float *__restrict__ c1,
                                                        const float *__restrict__ x, int B, int d,
                                                        int H, int KS, float *__restrict__ h,
                                                        _Float16 *__restrict__ h16,
-                                                       _Float16 *__restrict__ x16) {
+                                                       _Float16 *__restrict__ x16, int dp,
+                                                       int Bm) {
     const int gid = blockIdx.x * kThreads + threadIdx.x;
     const int mt = gid / (kTile * kTile), e = gid % (kTile * kTile);
     const int r = kTile * mt + e / kTile, t = e % kTile;
@@ -167,11 +168,7 @@ __global__ __launch_bounds__(kThreads) void k_pred_fin(const float *__restrict__
         h16[(size_t)(B + t) * H + r] = (_Float16)(hv - (float)hi);
     }
     const int n8 = B * d / 8;
-    for (int i = gid; i < n8; i += gridDim.x * kThreads) {
-        h8 hv, unused;
-        frag_f32<false>(x + (size_t)8 * i, true, hv, unused);
-        *reinterpret_cast<h8 *>(x16 + (size_t)8 * i) = hv;
-    }
+    for (int i = gid; i < n8; i += gridDim.x * kThreads) x16_chunk(x, d, dp, Bm, x16, i);
 }
 
 // ---------------------------------------------------------------- operand tiles through LDS
@@ -351,78 +348,252 @@ __global__ __launch_bounds__(kThreads) void k_score_mm(const u32x4 *__restrict__
     }
 }
 
+// ---------------------------------------------------------------- buffer loads
+// Raw buffer loads: the resource bounds the access to [base, base + bytes);
+// a 16-byte load at an offset past the bound returns zeros without a memory
+// access, so loads of absent rows or tokens are issued like any other (the
+// count in flight does not depend on data and the compiler's waits stay
+// exact).  Base and bound must be wave-uniform.  Every weight array fits 32-bit
+// offsets (at most 65536 bundles of 3 x 16 KiB).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kBufWord3 = 0x00020000;     // descriptor word 3: 32-bit data format
+constexpr uint32_t kOob = 0xFFFFFFF0u;    // an offset past every bound
+
+__device__ __forceinline__ rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kBufWord3);
+}
+// weights: streamed once (non-temporal)
+__device__ __forceinline__ u32x4 ld_stream(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+}
+// operands every workgroup reads (x, activations): cached
+__device__ __forceinline__ u32x4 ld_shared(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
 // ---------------------------------------------------------------- FC1
 struct Fc1MmParams {
-    const u32x4 *bundles;
-    size_t bstride;      // chunks per bundle
-    int cd;              // chunks per d row
+    const void *bundles;
+    uint32_t bundle_bytes;   // bytes per bundle
+    uint32_t all_bytes;      // f bundles
+    int cd;                  // chunks per d row
     const float *b1;
-    const _Float16 *x16; // x as fp16 [B][d]
-    int B, d, f, nq;
-    int mode;            // 0 union of the last prediction, 1 caller ids, 2 all
+    const _Float16 *x16;     // [2][Bm][dp] x as fp16 hi, lo (padding zero); FC1 reads hi
+    int dp, Bm;
+    int B, f, nq;
+    int mode;                // 0 union of the last prediction, 1 caller ids, 2 all
     const uint64_t *ubits;
     const int32_t *ids;
     const int32_t *n_ids;
     const int32_t *inv;
-    int32_t *lslot;      // [rows] slot of list row r (-1: a skipped caller id)
-    float *la;           // [rows][max_batch]
-    int max_batch;
-    int32_t *rows;       // number of list rows
-    int ncu;             // compute units
-    int per_cu;          // workgroups resident per CU at once (LDS, registers)
+    int32_t *lslot;          // [rows] slot of list row r (-1: a skipped caller id)
+    _Float16 *la16;          // [2][Bm][LR] activations hi, lo, token-major
+    int LR;
+    int32_t *rows;           // number of list rows
+    float *part;             // [ks][NM][Bm][LR] partial sums per k slice
+    int ks;                  // k slices
 };
 
-// x -> fp16 [B][d] (for FC1 calls that follow no predictor pass)
-__global__ void k_to_f16(const float *__restrict__ x, int n, _Float16 *__restrict__ x16) {
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
-        x16[i] = (_Float16)x[i];
+// x -> fp16 hi + lo (for FC1 calls that follow no predictor pass)
+__global__ void k_to_f16(const float *__restrict__ x, int B, int d, int dp, int Bm,
+                         _Float16 *__restrict__ x16) {
+    const int n8 = B * d / 8;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += gridDim.x * blockDim.x)
+        x16_chunk(x, d, dp, Bm, x16, i);
 }
 
 // The FC1 list: mode 0 the union of the last prediction, owner by owner
 // (row r is the (r - pre[q])-th set bit i of owner q, slot q + nq*i, for the
 // owner with pre[q] <= r < pre[q+1], pre the popcount prefix); mode 1 the
-// caller's ids in list order; mode 2 every slot.  Workgroup b takes rows
-// Rb .. Rb+R-1 as one tile streamed with the token tile of x (fp16) over k = d
-// in chunks of 256 k.  While the list needs at most one 32-row workgroup
-// per CU it is spread over one workgroup per CU (R = its length over the
-// CUs, at least kFc1MinRows); a longer list is spread evenly over the
-// workgroups resident at once
-// (R = its length over them, at least kFc1MinRows; the tile's other rows are
-// dead), since a CU holding two workgroups runs each ~30% slower and an
-// uneven split leaves the kernel waiting on the doubled CUs.  a = ReLU(up . x + b1) (gated: ReLU(gate . x +
-// b1) * (up . x)), written to la[r][t] and lslot[r].
-constexpr int kFc1MinRows = 16;
+// caller's ids in list order; mode 2 every slot.
+//
+// Workgroup (g, ks) takes the list rows of group g (the list spread evenly
+// over GR groups) over the k slice ks (1024 k; KS slices cover d): its slice
+// of x (32 tokens x 1024 k as fp16, 64 KiB) is read once into LDS, so the
+// weight stream carries no x traffic, and the KS partial sums of a row are
+// added by k_fc1_fin.  The rows go in passes of NRT row tiles (32 rows);
+// a stage is one row tile x one 1 KiB piece (512 k) of one matrix: each
+// piece of a row is one buffer load of one wave, so every request reads a
+// row contiguously (the gather pattern that streams fastest; absent rows and
+// pieces past d read nothing), kFc1Pre stages ahead, also across passes.
+// The stage goes through LDS (16-byte chunks XOR-swizzled by row) to be read
+// as MFMA fragments; wave w takes chunks 8w .. 8w+7 of the piece, its lane
+// (row or token t, half h) the k groups of chunks 8w+4h .. 8w+4h+3 on both
+// sides.  At the end of a pass each row tile's eight wave tiles are added in
+// wave order into the partial sums.
+constexpr int kPieceK = 512;                   // k per row piece (1 KiB of fp16)
+constexpr int kPieceC = kPieceK / 8;           // 16-byte chunks per piece (64)
+constexpr int kSliceP = 2;                     // pieces per k slice
+constexpr int kSliceC = kSliceP * kPieceC;     // chunks per token row of the x slice (128)
+constexpr int kStageCh = kTile * kPieceC;      // chunks per stage buffer (32 KiB)
+constexpr int kFc1Pre = 4;                     // stages in flight
+constexpr int kFc1MaxRows = 2048;              // rows per workgroup (the grid guarantees it)
+constexpr int kMaxKSlices = 8;                 // d <= 8192
+
+template <bool GATED, int NRT_> struct Fc1Geo {
+    static constexpr int NM = GATED ? 2 : 1;               // matrices per row: [gate,] up
+    static constexpr int NRT = NRT_;                       // row tiles per pass
+    static constexpr int SPP = NRT * kSliceP * NM;         // stages per pass
+    static_assert(SPP % kFc1Pre == 0 && kFc1Pre % 2 == 0, "ring slots repeat every pass");
+};
+
+// wave tile -> LDS, element (row, col) at row*32 + (col ^ row), so that both
+// the rows of a column (the epilogue's reads) and the columns of a row (the
+// writes) fall on distinct banks
+__device__ __forceinline__ void tile_to_lds_x(float *dst, const f32x16 &acc, int lane) {
+    const int col = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int row = acc_row(i, lane);
+        dst[row * kTile + (col ^ row)] = acc[i];
+    }
+}
+
+// The weight stream of workgroup slice ks over its nr rows (slots in rslot,
+// x slice in xs), in passes of NRT row tiles.
+template <bool GATED, int NRT>
+__device__ __forceinline__ void fc1_stream(const Fc1MmParams &p, const u32x4 *xs, u32x4 *stg,
+                                           const int *rslot, int ks, int r0, int nr) {
+    using G1 = Fc1Geo<GATED, NRT>;
+    constexpr int NM = G1::NM, SPP = G1::SPP;
+    constexpr int TT = kTile * kTile;
+    static_assert((NRT * NM) % 2 == 0 && 2 * kW * TT * 4 <= 2 * kStageCh * 16,
+                  "the epilogue reduces two tiles per round in the stage buffers");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // ---- the weight stream
+    const int npass = (nr + kTile * NRT - 1) / (kTile * NRT);
+    const uint32_t rowb = 16u * (uint32_t)p.cd;                // bytes of a weight row
+    const int tk = lane & 31, hh = lane >> 5;
+    // stage j of pass ps: row tile j / (2 NM), piece (j / NM) % 2, matrix j % NM;
+    // wave w loads rows w, w+8, w+16, w+24 of the tile
+    auto issue = [&](int ps, int j, u32x4 (&w)[4]) {
+        const int i = j / (kSliceP * NM), pc = (j / NM) % kSliceP, m = j % NM;
+        const uint32_t koff = 1024u * (uint32_t)(kSliceP * ks + pc);
+        const uint32_t moff = (GATED && m == 1) ? rowb : 0u;   // [gate,] up
+        // the four slots read together (clamped index, unconditional)
+        int sv[4];
+#pragma unroll
+        for (int l = 0; l < 4; ++l) {
+            const int rr = kTile * (NRT * ps + i) + wave + kW * l;
+            sv[l] = rslot[rr < kFc1MaxRows ? rr : kFc1MaxRows - 1];
+        }
+#pragma unroll
+        for (int l = 0; l < 4; ++l) {
+            const int rr = kTile * (NRT * ps + i) + wave + kW * l;
+            const int sl = __builtin_amdgcn_readfirstlane(rr < nr ? sv[l] : -1);
+            const bool ok = sl >= 0 && koff < rowb;
+            const char *base = static_cast<const char *>(p.bundles) +
+                               (ok ? (size_t)sl * p.bundle_bytes + moff + koff : 0);
+            w[l] = ld_stream(buf_rsrc(base, ok ? rowb - koff : 0u), 16u * lane);
+        }
+    };
+    u32x4 ring[kFc1Pre][4];
+#pragma unroll
+    for (int u = 0; u < kFc1Pre; ++u) issue(0, u, ring[u]);
+    f32x16 acc[NRT * NM];
+    float *red = reinterpret_cast<float *>(stg);
+    auto pass = [&](int ps) {
+#pragma unroll
+        for (int a = 0; a < NRT * NM; ++a) acc[a] = zero16();
+        // slice 0 adds b1 to the (gate or up) sum of a present row: the b1 of
+        // this thread's epilogue rows, requested before the pass's stages
+        // (every slice loads, from a clamped index, and keeps zero)
+        float bias[NRT * NM / 2][4];
+#pragma unroll
+        for (int a0 = 0; a0 < NRT * NM; a0 += 2)
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const int e = tid + kThreads * h;
+                const int a = a0 + e / TT, i = a / NM, rr = e % kTile;
+                const int row = kTile * (NRT * ps + i) + rr;
+                const int sl = rslot[row < nr ? row : 0];
+                const bool use = ks == 0 && row < nr && sl >= 0;
+                const float b = p.b1[use ? sl : 0];
+                bias[a0 / 2][h] = use ? b : 0.0f;
+            }
+#pragma unroll
+        for (int j = 0; j < SPP; ++j) {
+            const int u = j % kFc1Pre, b = j & 1;
+            const int i = j / (kSliceP * NM), pc = (j / NM) % kSliceP, m = j % NM;
+            u32x4 *bufp = stg + b * kStageCh;
+#pragma unroll
+            for (int l = 0; l < 4; ++l) {
+                const int row = wave + kW * l;
+                bufp[row * kPieceC + (lane ^ (row & 15))] = ring[u][l];
+            }
+            if (j + kFc1Pre < SPP) issue(ps, j + kFc1Pre, ring[u]);
+            else issue(ps + 1, j + kFc1Pre - SPP, ring[u]);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int c = 8 * wave + 4 * hh + kk;
+                const h8 a = __builtin_bit_cast(h8, bufp[tk * kPieceC + (c ^ (tk & 15))]);
+                const int cx = kPieceC * pc + c;
+                const h8 bx = __builtin_bit_cast(h8, xs[tk * kSliceC + (cx ^ (tk & 15))]);
+                acc[i * NM + m] = mfma(a, bx, acc[i * NM + m]);
+            }
+        }
+        // pass end: each row tile's wave tiles summed in wave order into the
+        // partial sums of this slice (two tiles per round), rows fastest
+        // (coalesced stores)
+#pragma unroll
+        for (int a0 = 0; a0 < NRT * NM; a0 += 2) {
+            __syncthreads();
+            tile_to_lds_x(red + wave * TT, acc[a0], lane);
+            tile_to_lds_x(red + (kW + wave) * TT, acc[a0 + 1], lane);
+            __syncthreads();
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const int e = tid + kThreads * h;
+                const int a = a0 + e / TT, i = a / NM, m = a % NM;
+                const int t = (e % TT) / kTile, rr = e % kTile;
+                const int row = kTile * (NRT * ps + i) + rr;
+                float sum = 0.0f;
+#pragma unroll
+                for (int w = 0; w < kW; ++w)
+                    sum += red[((e / TT) * kW + w) * TT + rr * kTile + (t ^ rr)];
+                if (m == 0) sum += bias[a0 / 2][h];
+                if (t < p.B && row < nr)
+                    p.part[((size_t)(ks * NM + m) * p.Bm + t) * p.LR + r0 + row] = sum;
+            }
+        }
+        __syncthreads();
+    };
+    // the first pass is peeled: the loop is then entered from a copy of its
+    // own body (partial stores included), so the wait at its head stays
+    // fine-grained
+    pass(0);
+    for (int ps = 1; ps < npass; ++ps) pass(ps);
+}
 
 template <bool GATED>
 __global__ __launch_bounds__(kThreads) void k_fc1_mm(Fc1MmParams p) {
-    constexpr int CW = 32;
-    constexpr int EL = Geo<CW>::ELEMS;
-    constexpr int NT = GATED ? 3 : 2;                // staged tiles: [gate,] up, x
-    constexpr int PRE = kPre;                        // chunks in flight per thread
-    __shared__ u32x4 smem[2 * NT * EL];              // chunks; before: owner words; after: wave tiles
-    __shared__ float gsum[GATED ? kTile * kTile : 1];
+    __shared__ u32x4 xs[kTile * kSliceC];            // x slice [token][chunk], swizzled
+    __shared__ u32x4 stg[2 * kStageCh];              // stage buffers; before: owner words; pass ends: wave tiles
     __shared__ int pre[kMaxFfn / 64 + 1];
+    __shared__ int rslot[kFc1MaxRows];
     __shared__ int wave_tot[kW];
-    __shared__ int rslot[kTile];
     __shared__ int nrows_lds;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // rows per workgroup from the list length (the same in every workgroup)
-    auto tile_rows = [&](int n) {
-        if (n <= kTile * p.ncu) {
-            // one workgroup per CU at most: spread the list over every CU
-            const int r = (n + p.ncu - 1) / p.ncu;
-            return r < kFc1MinRows ? kFc1MinRows : r;
-        }
-        const int nw = p.per_cu * p.ncu;
-        const int r = (n + nw - 1) / nw;
-        return r < kFc1MinRows ? kFc1MinRows : (r > kTile ? kTile : r);
-    };
-    int R = kTile, r0 = 0;
-    // ---- the list's length and this tile's slots
+    const int KS = p.ks, ks = blockIdx.x % KS, g = blockIdx.x / KS, GR = gridDim.x / KS;
+    // ---- this slice of x, requested first (tokens past B read zeros; a slice
+    // past d reads x of the next token or zeros: finite, against zero weights)
+    const int xt = tid >> 4, xc = tid & 15;
+    u32x4 xv[kSliceC / 16];
+    {
+        const rsrc_t xh = buf_rsrc(p.x16, (uint32_t)p.B * p.dp * 2);
+        const uint32_t xo = (uint32_t)(xt * p.dp + kSliceP * kPieceK * ks) * 2;
+#pragma unroll
+        for (int j = 0; j < kSliceC / 16; ++j) xv[j] = ld_shared(xh, xo + 16u * (xc + 16 * j));
+    }
+    // ---- the list's length
+    const uint64_t *vb = reinterpret_cast<const uint64_t *>(stg);
     if (p.mode == 0) {
-        uint64_t *vb = reinterpret_cast<uint64_t *>(smem);
+        uint64_t *vw = reinterpret_cast<uint64_t *>(stg);
         const int nq = p.nq;
-        for (int q = tid; q < nq; q += kThreads) vb[q] = p.ubits[q];
+        for (int q = tid; q < nq; q += kThreads) vw[q] = p.ubits[q];
         __syncthreads();
         const int q0 = 2 * tid, q1 = 2 * tid + 1;
         const int c0 = q0 < nq ? __popcll(vb[q0]) : 0, c1 = q1 < nq ? __popcll(vb[q1]) : 0;
@@ -444,247 +615,260 @@ __global__ __launch_bounds__(kThreads) void k_fc1_mm(Fc1MmParams p) {
             pre[nq] = base + incl;
             nrows_lds = base + incl;
         }
-        __syncthreads();
-        R = tile_rows(nrows_lds);
-        r0 = R * blockIdx.x;
-        if (tid < kTile) {
-            const int r = r0 + tid;
-            int slot = -1;
-            if (tid < R && r < nrows_lds) {
-                int lo = 0, hi = nq;                 // largest q with pre[q] <= r
-                while (hi - lo > 1) {
-                    const int mid = (lo + hi) >> 1;
-                    if (pre[mid] <= r) lo = mid;
-                    else hi = mid;
-                }
-                slot = lo + nq * nth_set_bit(vb[lo], r - pre[lo]);
-            }
-            rslot[tid] = slot;
+    } else if (tid == 0) {
+        int n = p.f;
+        if (p.mode == 1) {
+            n = *p.n_ids;
+            n = n < 0 ? 0 : (n > p.f ? p.f : n);
         }
-    } else {
-        if (tid == 0) {
-            int n = p.f;
-            if (p.mode == 1) {
-                n = *p.n_ids;
-                n = n < 0 ? 0 : (n > p.f ? p.f : n);
-            }
-            nrows_lds = n;
-        }
-        __syncthreads();
-        R = tile_rows(nrows_lds);
-        r0 = R * blockIdx.x;
-        if (tid < kTile) {
-            const int r = r0 + tid;
-            int slot = -1;
-            if (tid < R && r < nrows_lds) {
-                if (p.mode == 2) {
-                    slot = r;
-                } else {
-                    const int id = p.ids[r];
-                    slot = (unsigned)id < (unsigned)p.f ? p.inv[id] : -1;
-                    if ((unsigned)slot >= (unsigned)p.f) slot = -1;
-                }
-            }
-            rslot[tid] = slot;
-        }
+        nrows_lds = n;
     }
     __syncthreads();
     const int nrows = nrows_lds;
-    // (the list length is stored after the tile: a global store in flight
-    // would make the compiler wait for every load of the ring)
+    const int R = (nrows + GR - 1) / GR;
+    const int r0 = R * g;
     if (r0 >= nrows) {
         if (blockIdx.x == 0 && tid == 0) *p.rows = nrows;
         return;
     }
-    // ---- the tile over k = d
-    const int C = p.cd;
-    const int nch = (C + CW - 1) / CW;
-    const int lrow = tid / 16, lc = tid % 16;
-    const int myslot = rslot[lrow];
-    const bool live = myslot >= 0;
-    constexpr int UP = GATED ? 1 : 0;
-    const u32x4 *bp = p.bundles + (size_t)(live ? myslot : 0) * p.bstride;
-    const u32x4 *rpu = bp + (size_t)UP * C, *rpg = bp;
-    const bool tokr = lrow < p.B;
-    const u32x4 *xr = reinterpret_cast<const u32x4 *>(p.x16 + (size_t)(tokr ? lrow : 0) * p.d);
-    // chunks past nch load zeros (chunk indices past C are clamped and
-    // zeroed), so the loop body stays free of branches and the ring registers
-    // carry over without copies that would wait
-    u32x4 ra[PRE][NT][Geo<CW>::LPT];
-    auto load = [&](int ch, u32x4 (&v)[NT][Geo<CW>::LPT]) {
-        ld_chunk<CW>(rpu, C, ch, lc, v[0]);
-        ld_chunk<CW>(xr, C, ch, lc, v[1]);
-        if constexpr (GATED) ld_chunk<CW>(rpg, C, ch, lc, v[NT - 1]);
-    };
-#pragma unroll
-    for (int u = 0; u < PRE; ++u) load(u, ra[u]);
-    f32x16 accu = zero16(), accg = zero16();
-    auto pass = [&](int ch0) {
-#pragma unroll
-        for (int u = 0; u < PRE; ++u) {
-            const int ch = ch0 + u;
-            u32x4 *bufp = smem + (u & 1) * NT * EL;
-            st_chunk<CW>(bufp, lrow, lc, live, C, ch, ra[u][0]);
-            st_chunk<CW>(bufp + EL, lrow, lc, tokr, C, ch, ra[u][1]);
-            if constexpr (GATED) st_chunk<CW>(bufp + (NT - 1) * EL, lrow, lc, live, C, ch, ra[u][NT - 1]);
-            load(ch + PRE, ra[u]);
-            __syncthreads();
-#pragma unroll
-            for (int k = 0; k < Geo<CW>::SPW; ++k) {
-                const int st = Geo<CW>::SPW * wave + k;
-                const h8 bx = frag<CW>(bufp + EL, st, lane);
-                accu = mfma(frag<CW>(bufp, st, lane), bx, accu);
-                if constexpr (GATED) accg = mfma(frag<CW>(bufp + (NT - 1) * EL, st, lane), bx, accg);
+    const int nr = R < nrows - r0 ? R : nrows - r0;
+    // ---- this workgroup's slots; x slice to LDS
+    for (int i = tid; i < nr; i += kThreads) {
+        const int r = r0 + i;
+        int slot;
+        if (p.mode == 0) {
+            int lo = 0, hi = p.nq;                   // largest q with pre[q] <= r
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (pre[mid] <= r) lo = mid;
+                else hi = mid;
             }
+            slot = lo + p.nq * nth_set_bit(vb[lo], r - pre[lo]);
+        } else if (p.mode == 2) {
+            slot = r;
+        } else {
+            const int id = p.ids[r];
+            slot = (unsigned)id < (unsigned)p.f ? p.inv[id] : -1;
+            if ((unsigned)slot >= (unsigned)p.f) slot = -1;
         }
-    };
-    // the first pass is peeled (nch >= 1): the loop is then entered from a
-    // copy of its own body, with the ring's loads in the loop's order, so the
-    // wait at the loop head can stay fine-grained (entered from the prologue
-    // it would have to wait for every load in flight, on every pass)
-    pass(0);
-    for (int ch0 = PRE; ch0 < nch; ch0 += PRE) pass(ch0);
-    // ---- epilogue
-    float *red = reinterpret_cast<float *>(smem);
-    float v[2];
-    if constexpr (GATED) {
-        __syncthreads();
-        tile_to_lds(red + wave * kTile * kTile, accg, lane);
-        __syncthreads();
-        tile_sum(red, v);
+        rslot[i] = slot;
+        if (ks == 0) p.lslot[r] = slot;
+    }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) gsum[tid + kThreads * j] = v[j];
+    for (int j = 0; j < kSliceC / 16; ++j) {
+        const int c = xc + 16 * j;
+        xs[xt * kSliceC + (c ^ (xt & 15))] = xv[j];
     }
     __syncthreads();
-    tile_to_lds(red + wave * kTile * kTile, accu, lane);
-    __syncthreads();
-    tile_sum(red, v);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int e = tid + kThreads * j;
-        const int rr = e / kTile, t = e % kTile, r = r0 + rr;
-        if (rr >= R || r >= nrows || t >= p.B) continue;
-        const int sl = rslot[rr];
-        float a = 0.0f;
-        if (sl >= 0) {
-            if constexpr (GATED) a = fmaxf(gsum[e] + p.b1[sl], 0.0f) * v[j];
-            else a = fmaxf(v[j] + p.b1[sl], 0.0f);
-        }
-        p.la[(size_t)r * p.max_batch + t] = a;
-        if (t == 0) p.lslot[r] = sl;
+    // ---- the weight stream, passes sized to the rows (wave-uniform)
+    if constexpr (GATED) {
+        if (nr <= kTile) fc1_stream<true, 1>(p, xs, stg, rslot, ks, r0, nr);
+        else if (nr <= 2 * kTile) fc1_stream<true, 2>(p, xs, stg, rslot, ks, r0, nr);
+        else fc1_stream<true, 3>(p, xs, stg, rslot, ks, r0, nr);
+    } else {
+        if (nr <= 2 * kTile) fc1_stream<false, 2>(p, xs, stg, rslot, ks, r0, nr);
+        else if (nr <= 4 * kTile) fc1_stream<false, 4>(p, xs, stg, rslot, ks, r0, nr);
+        else fc1_stream<false, 6>(p, xs, stg, rslot, ks, r0, nr);
     }
     if (blockIdx.x == 0 && tid == 0) *p.rows = nrows;
 }
 
+// The KS partial sums of each list row and token added in slice order (slice
+// 0 carries b1), then the activation: a = ReLU(up . x + b1) (gated:
+// ReLU(gate . x + b1) * (up . x)), written as fp16 hi + lo to la16
+// (token-major).  A row whose caller id was skipped has zero sums.  Thread:
+// token t, rows 8c .. 8c+7, its loads issued beside the list length; rows
+// past the list (up to the next multiple of 8, which FC2 reads in 8-row
+// chunks) get zeros.
+template <bool GATED>
+__global__ __launch_bounds__(256) void k_fc1_fin(Fc1MmParams p) {
+    constexpr int NM = GATED ? 2 : 1;
+    const int c8 = p.LR / 8;
+    const int gid = blockIdx.x * 256 + threadIdx.x;
+    if (gid >= p.B * c8) return;
+    const int t = gid / c8, r = 8 * (gid % c8);
+    const int KS = p.ks;
+    const int n = *p.rows;
+    // every slice's loads in flight (unrolled to the largest count, clamped)
+    float4 v[kMaxKSlices][NM][2];
+#pragma unroll
+    for (int s = 0; s < kMaxKSlices; ++s)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            const float *q = p.part + ((size_t)((s < KS ? s : 0) * NM + m) * p.Bm + t) * p.LR + r;
+            v[s][m][0] = *reinterpret_cast<const float4 *>(q);
+            v[s][m][1] = *reinterpret_cast<const float4 *>(q + 4);
+        }
+    if (r >= n) return;
+    float sum[NM][8];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum[m][e] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kMaxKSlices; ++s) {
+        if (s < KS) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                const float f[8] = {v[s][m][0].x, v[s][m][0].y, v[s][m][0].z, v[s][m][0].w,
+                                    v[s][m][1].x, v[s][m][1].y, v[s][m][1].z, v[s][m][1].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sum[m][e] += f[e];
+            }
+        }
+    }
+    h8 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float a = 0.0f;
+        if (r + e < n) {
+            if constexpr (GATED) a = fmaxf(sum[0][e], 0.0f) * sum[1][e];
+            else a = fmaxf(sum[0][e], 0.0f);
+        }
+        hi[e] = (_Float16)a;
+        lo[e] = (_Float16)(a - (float)hi[e]);
+    }
+    *reinterpret_cast<h8 *>(p.la16 + (size_t)t * p.LR + r) = hi;
+    *reinterpret_cast<h8 *>(p.la16 + (size_t)(p.Bm + t) * p.LR + r) = lo;
+}
+
 // ---------------------------------------------------------------- FC2
 struct Fc2MmParams {
-    const u32x4 *bundles;
-    size_t bstride;      // chunks per bundle
-    int dn_off;          // chunk offset of the down column in a bundle
-    int cd;              // chunks per down column
+    const void *bundles;
+    uint32_t bundle_bytes;   // bytes per bundle
+    uint32_t all_bytes;      // f bundles
+    uint32_t dn_off;         // byte offset of the down column in a bundle
+    int cd;                  // chunks per down column
     const int32_t *lslot;
-    const float *la;
+    const _Float16 *la16;    // [2][Bm][LR]
+    int LR, Bm;
     const int32_t *rows;
-    int max_batch;
     int d, B;
-    const float *b2;
-    const float *resid;
-    float *y;
-    float *partial;      // [groups][B][d]
-    int groups;          // list-row ranges (<= kGroups)
+    float *partial;          // [groups][B][d]
+    int groups;              // list-row ranges (<= kGroups)
 };
 
-constexpr int kFc2N = 64;                   // neurons per step (4 MFMA k-steps)
+constexpr int kFc2N = 64;                   // list rows per step (4 MFMA k-steps)
 constexpr int kWPitch = kSliceOut + 8;      // halfs per staged down row
 constexpr int kAPitch = kFc2N + 8;          // halfs per staged token row of a
-constexpr int kFc2Pre = 4;                  // steps in flight per thread
+constexpr int kFc2Pre = 4;                  // steps in flight
 constexpr int kFc2Rows = 8192;              // list rows per group (f <= 65536, >= 8 groups)
 
-// Workgroup (slice s, group g): outputs 256s .. 256s+255 over list rows
-// [g*R/G, (g+1)*R/G).  Per step of 64 rows each thread loads four 16-byte
-// chunks of down segments (row tid/32 + 16j, chunk tid%32) and four a values
-// (row tid/32 + 16j, token tid%32), kFc2Pre steps ahead; the step is staged
-// in LDS (double buffered) and wave w multiplies tokens x its 32 outputs x
-// 64 rows, reading each lane's 8 rows of one output column transposed.
-// Group tiles go to `partial`; k_fc2_fin adds the G in group order, then b2,
-// then the residual.
+// 16-byte chunk of staged down row r holding outputs 8c .. 8c+7: rows 32
+// apart sit 4 chunks apart, so the two half-waves of a fragment read (rows
+// r and r + 32, the same 32 outputs) use different banks
+__device__ __forceinline__ int wl_chunk(int r, int c) { return c ^ (((r >> 5) & 1) << 2); }
+
+// Workgroup (slice s, group g): outputs 256s .. 256s+255 over the list rows
+// of steps [S*g/G, S*(g+1)/G) (S steps of 64 rows).  Per step each thread
+// loads four 16-byte chunks of down columns (rows tid/32 + 16j, chunk tid%32
+// of the slice: two rows x 512 contiguous bytes per wave load; absent rows
+// and chunks read nothing) and one chunk of a (hi or lo half, token, 8 rows),
+// four steps ahead; the step goes through LDS (double buffered) and wave w
+// multiplies tokens x its 32 outputs x 64 rows, a as hi + lo (two MFMAs per
+// k-step), the down fragments read transposed.  Rows are paired with the
+// same permutation on both sides: lane half h takes rows 32h + 8j .. 32h+8j+7
+// at k-step j.  Group tiles go to `partial`; k_fc2_fin adds the G in group
+// order, then b2, then the residual.
 __global__ __launch_bounds__(kThreads) void k_fc2_mm(Fc2MmParams p) {
     __shared__ __attribute__((aligned(16))) _Float16 wl[2][kFc2N * kWPitch];
-    __shared__ __attribute__((aligned(16))) _Float16 al[2][kTile * kAPitch];
+    __shared__ __attribute__((aligned(16))) _Float16 al[2][2 * kTile * kAPitch];
     __shared__ int rslot[kFc2Rows];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = p.groups;
     const int nslice = gridDim.x / G;
     const int s = blockIdx.x % nslice, g = blockIdx.x / nslice;
     const int R = *p.rows;
-    const int rb = (int)((long long)R * g / G), re = (int)((long long)R * (g + 1) / G);
-    const int nst = (re - rb + kFc2N - 1) / kFc2N;
+    const int S = (R + kFc2N - 1) / kFc2N;
+    const int sb = (int)((long long)S * g / G), se = (int)((long long)S * (g + 1) / G);
+    const int rb = kFc2N * sb;
+    const int re = kFc2N * se < R ? kFc2N * se : R;
+    const int nst = se - sb;
     for (int i = tid; i < re - rb; i += kThreads) rslot[i] = p.lslot[rb + i];
     __syncthreads();
-    const int ln = tid / kTile, lc = tid % kTile;
-    const int chunk = s * (kSliceOut / 8) + lc;
+    // down chunk of this thread
+    const int ln = tid >> 5, lc = tid & 31;
+    const int chunk = 32 * s + lc;
     const bool cin = chunk < p.cd;
-    const u32x4 *dbase = p.bundles + p.dn_off + (cin ? chunk : 0);
-    const bool tok_a = lc < p.B;
-    u32x4 rv[kFc2Pre][4];
-    float ra[kFc2Pre][4];
-    // the group's list slots are staged in LDS, so a step's down-segment
-    // loads do not wait on a load of their slot
-    // loads from clamped addresses; the values are zeroed only when staged,
-    // a ring period later, so that no instruction touches them before then
-    auto row_ok = [&](int st, int j) {                   // branch free (bitwise and)
-        const int rl = st * kFc2N + ln + 16 * j;              // row within the group
-        const bool in = (st < nst) & (rb + rl < re);
-        return in & (rslot[in ? rl : 0] >= 0);
-    };
-    auto load_step = [&](int st, u32x4 (&v)[4], float (&a)[4]) {
+    const uint32_t coff = p.dn_off + 16u * (uint32_t)chunk;
+    const rsrc_t wr = buf_rsrc(p.bundles, p.all_bytes);
+    // a chunk of this thread: half hl (waves 0-3 hi, 4-7 lo), token ta, rows 8ca ..
+    const int hl = __builtin_amdgcn_readfirstlane(tid >> 8);   // wave-uniform
+    const int ta = (tid >> 3) & 31, ca = tid & 7;
+    const rsrc_t ar = buf_rsrc(p.la16 + (size_t)hl * p.Bm * p.LR, (uint32_t)p.B * p.LR * 2);
+    const uint32_t ao = (uint32_t)(ta * p.LR + rb + 8 * ca) * 2;   // tokens past B read zeros
+    u32x4 rv[kFc2Pre][4], ra[kFc2Pre];
+    // the group's slots are staged in LDS, so a step's down loads do not wait
+    // on a load of their slot
+    auto load_step = [&](int st, u32x4 (&v)[4], u32x4 &a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int rl = st * kFc2N + ln + 16 * j;
+            const int rl = kFc2N * st + ln + 16 * j;
             const bool in = (st < nst) & (rb + rl < re);
             const int sl = rslot[in ? rl : 0];
-            v[j] = dbase[(size_t)(sl >= 0 ? sl : 0) * p.bstride];
-            a[j] = p.la[(size_t)(in ? rb + rl : rb) * p.max_batch + (tok_a ? lc : 0)];
+            v[j] = ld_stream(wr, (in & (sl >= 0) & cin) ? (uint32_t)sl * p.bundle_bytes + coff : kOob);
         }
+        const bool ain = (st < nst) & (rb + kFc2N * st + 8 * ca < R);
+        a = ld_shared(ar, ain ? ao + 2u * kFc2N * st : kOob);
     };
-    auto stage = [&](int st, int buf, const u32x4 (&v)[4], const float (&a)[4]) {
+    auto stage = [&](int st, int buf, const u32x4 (&v)[4], const u32x4 &a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const bool ok = row_ok(st, j);
-            *reinterpret_cast<u32x4 *>(&wl[buf][(ln + 16 * j) * kWPitch + 8 * lc]) = sel4(ok & cin, v[j]);
-            al[buf][lc * kAPitch + ln + 16 * j] = (_Float16)((ok & tok_a) ? a[j] : 0.0f);
+            const int r = ln + 16 * j;
+            *reinterpret_cast<u32x4 *>(&wl[buf][r * kWPitch + 8 * wl_chunk(r, lc)]) = v[j];
         }
+        // (a chunk across the list's end holds zeros past it: FC1 clears them)
+        *reinterpret_cast<u32x4 *>(&al[buf][(hl * kTile + ta) * kAPitch + 8 * ca]) = a;
     };
-    const int gk = lane >> 5, col = lane & 31;
-    const int jw = kTile * wave + col;
+    const int tk = lane & 31, hh = lane >> 5;
+    const int jw = kTile * wave + tk;                     // output column within the slice
     f32x16 acc = zero16();
     if (nst > 0) {
 #pragma unroll
         for (int u = 0; u < kFc2Pre; ++u) load_step(u, rv[u], ra[u]);
         // steps past nst stage zeros: the loop body stays free of branches, so
         // the ring registers carry over without copies that would wait
-        auto pass = [&](int st0) {
+        // step st from ring slot u (LDS buffer u % 2); NEXT: request step st + kFc2Pre
+        auto step = [&](int st, int u, bool next) {
+            const int buf = u & 1;
+            stage(st, buf, rv[u], ra[u]);
+            if (next) load_step(st + kFc2Pre, rv[u], ra[u]);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < kFc2Pre; ++u) {
-                const int st = st0 + u;
-                const int buf = u & 1;
-                stage(st, buf, rv[u], ra[u]);
-                load_step(st + kFc2Pre, rv[u], ra[u]);
-                __syncthreads();
+            for (int j = 0; j < kFc2N / 16; ++j) {
+                const int k0 = 32 * hh + 8 * j;
+                const h8 ahi = *reinterpret_cast<const h8 *>(&al[buf][tk * kAPitch + k0]);
+                const h8 alo = *reinterpret_cast<const h8 *>(&al[buf][(kTile + tk) * kAPitch + k0]);
+                h8 bv;
 #pragma unroll
-                for (int k = 0; k < kFc2N / 16; ++k) {
-                    const h8 av = *reinterpret_cast<const h8 *>(&al[buf][col * kAPitch + 16 * k + 8 * gk]);
-                    h8 bv;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) bv[j] = wl[buf][(16 * k + 8 * gk + j) * kWPitch + jw];
-                    acc = mfma(av, bv, acc);
+                for (int e = 0; e < 8; ++e) {
+                    const int r = k0 + e;
+                    bv[e] = wl[buf][r * kWPitch + 8 * wl_chunk(r, jw >> 3) + (jw & 7)];
                 }
+                acc = mfma(ahi, bv, acc);
+                acc = mfma(alo, bv, acc);
             }
         };
-        // first pass peeled: the loop is entered from a copy of its body, so
-        // the wait at its head need not cover every load in flight
-        pass(0);
-        for (int st0 = kFc2Pre; st0 < nst; st0 += kFc2Pre) pass(st0);
+        // whole passes of kFc2Pre steps (the first peeled: the loop is entered
+        // from a copy of its body, so the wait at its head need not cover every
+        // load in flight), then the group's last 0-3 steps without requests
+        int st0 = 0;
+        if (nst >= kFc2Pre) {
+#pragma unroll
+            for (int u = 0; u < kFc2Pre; ++u) step(u, u, true);
+            for (st0 = kFc2Pre; st0 + kFc2Pre <= nst; st0 += kFc2Pre) {
+#pragma unroll
+                for (int u = 0; u < kFc2Pre; ++u) step(st0 + u, u, true);
+            }
+        }
+        static_assert(kFc2Pre == 4, "the tail below covers 0-3 steps");
+        switch (nst - st0) {
+        case 3: step(st0, 0, false); step(st0 + 1, 1, false); step(st0 + 2, 2, false); break;
+        case 2: step(st0, 0, false); step(st0 + 1, 1, false); break;
+        case 1: step(st0, 0, false); break;
+        default: break;
+        }
     }
     // group tile -> partial (k_fc2_fin adds the groups)
 #pragma unroll
@@ -761,7 +945,7 @@ hipError_t launch_pred_mm(const LayerView &L, const float *x, int B, const Trace
     const int nfin = mt * (kTile * kTile) / kThreads;
     hipExtLaunchKernelGGL(k_pred_fin, dim3(nfin), dim3(kThreads), 0, s, nullptr,
                           ev_stop(tr, ASF_K_PRED_L1), 0u, (const float *)L.pred_part, L.c1, x, B,
-                          L.d, L.H, ks, L.h, L.h16, L.x16);
+                          L.d, L.H, ks, L.h, L.h16, L.x16, x16_pitch(L.d), L.max_batch);
     return hipGetLastError();
 }
 
@@ -771,22 +955,27 @@ hipError_t launch_score_mm(const LayerView &L, int B, const Trace *tr, hipStream
     return hipGetLastError();
 }
 
+int fc1_slices(int d) { return (x16_pitch(d) + kSliceP * kPieceK - 1) / (kSliceP * kPieceK); }
+
 hipError_t launch_fc1_mm(const LayerView &L, const float *x, int B, int mode, const int32_t *ids,
                          const int32_t *n_ids, bool x16, const Trace *tr, hipStream_t s) {
+    const int dp = x16_pitch(L.d);
     if (!x16) {
-        // x as fp16 first (the predictor writes this copy in a decode step)
-        const int n = B * L.d;
-        hipLaunchKernelGGL(k_to_f16, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024),
-                           dim3(256), 0, s, x, n, L.x16);
+        // x as fp16 hi + lo first (the predictor writes this copy in a decode step)
+        const int n8 = B * L.d / 8;
+        hipLaunchKernelGGL(k_to_f16, dim3((n8 + 255) / 256 < 1024 ? (n8 + 255) / 256 : 1024),
+                           dim3(256), 0, s, x, B, L.d, dp, L.max_batch, L.x16);
     }
     Fc1MmParams p;
-    p.bundles = (const u32x4 *)L.bundles;
-    p.bstride = (size_t)L.nmat * L.cd;
+    p.bundles = L.bundles;
+    p.bundle_bytes = (uint32_t)(L.nmat * L.cd * 16);
+    p.all_bytes = (uint32_t)((size_t)L.f * p.bundle_bytes);
     p.cd = L.cd;
     p.b1 = L.b1;
     p.x16 = L.x16;
+    p.dp = dp;
+    p.Bm = L.max_batch;
     p.B = B;
-    p.d = L.d;
     p.f = L.f;
     p.nq = L.nq;
     p.mode = mode;
@@ -795,17 +984,31 @@ hipError_t launch_fc1_mm(const LayerView &L, const float *x, int B, int mode, co
     p.n_ids = n_ids;
     p.inv = L.inv;
     p.lslot = L.lslot;
-    p.la = L.la;
-    p.max_batch = L.max_batch;
+    p.la16 = L.la16;
+    p.LR = L.nq * kRowsPerWG;
     p.rows = L.rows;
-    p.ncu = L.ncu;
-    p.per_cu = L.gated ? 1 : 2;
-    // enough workgroups for any list length (at most f rows): 32 rows each,
-    // or the spread (at most per_cu per CU); the rest return at once
-    const int g32 = (L.f + kTile - 1) / kTile;
-    const dim3 grid(g32 > p.per_cu * p.ncu ? g32 : p.per_cu * p.ncu);
-    if (L.gated) ASF_LAUNCH(ASF_K_FC1, k_fc1_mm<true>, grid, dim3(kThreads), p);
-    else ASF_LAUNCH(ASF_K_FC1, k_fc1_mm<false>, grid, dim3(kThreads), p);
+    p.part = L.fc1_part;
+    p.ks = fc1_slices(L.d);
+    // KS slices x GR row groups: about one workgroup per CU (each holds
+    // ~140 KiB of LDS), and enough groups that none takes more than
+    // kFc1MaxRows rows
+    const int gmin = (L.f + kFc1MaxRows - 1) / kFc1MaxRows;
+    int GR = L.ncu / p.ks;
+    GR = GR > gmin ? GR : gmin;
+    // the traced interval spans both kernels
+    if (L.gated)
+        hipExtLaunchKernelGGL(k_fc1_mm<true>, dim3(GR * p.ks), dim3(kThreads), 0, s,
+                              ev_start(tr, ASF_K_FC1), nullptr, 0u, p);
+    else
+        hipExtLaunchKernelGGL(k_fc1_mm<false>, dim3(GR * p.ks), dim3(kThreads), 0, s,
+                              ev_start(tr, ASF_K_FC1), nullptr, 0u, p);
+    const int nfin = (B * (p.LR / 8) + 255) / 256;
+    if (L.gated)
+        hipExtLaunchKernelGGL(k_fc1_fin<true>, dim3(nfin), dim3(256), 0, s, nullptr,
+                              ev_stop(tr, ASF_K_FC1), 0u, p);
+    else
+        hipExtLaunchKernelGGL(k_fc1_fin<false>, dim3(nfin), dim3(256), 0, s, nullptr,
+                              ev_stop(tr, ASF_K_FC1), 0u, p);
     return hipGetLastError();
 }
 
@@ -813,22 +1016,22 @@ hipError_t launch_fc2_mm(const LayerView &L, int B, bool listed, const float *re
                          const Trace *tr, hipStream_t s) {
     (void)listed;   // the batched list always carries its slots
     Fc2MmParams p;
-    p.bundles = (const u32x4 *)L.bundles;
-    p.bstride = (size_t)L.nmat * L.cd;
-    p.dn_off = (L.nmat - 1) * L.cd;
+    p.bundles = L.bundles;
+    p.bundle_bytes = (uint32_t)(L.nmat * L.cd * 16);
+    p.all_bytes = (uint32_t)((size_t)L.f * p.bundle_bytes);
+    p.dn_off = (uint32_t)((L.nmat - 1) * L.cd * 16);
     p.cd = L.cd;
     p.lslot = L.lslot;
-    p.la = L.la;
+    p.la16 = L.la16;
+    p.LR = L.nq * kRowsPerWG;
+    p.Bm = L.max_batch;
     p.rows = L.rows;
-    p.max_batch = L.max_batch;
     p.d = L.d;
     p.B = B;
-    p.b2 = L.b2;
-    p.resid = resid;
-    p.y = y;
     p.partial = L.partial;
     // one workgroup per CU covers the grid: groups = 256 / slices, at most 16
-    const int nslice = (L.d + kSliceOut - 1) / kSliceOut;
+    // (at least 8: d <= 8192 gives at most 32 slices)
+    const int nslice = (L.cd + 31) / 32;
     int G = 256 / nslice;
     G = G < 1 ? 1 : (G > kGroups ? kGroups : G);
     p.groups = G;

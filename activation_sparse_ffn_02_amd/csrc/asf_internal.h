@@ -19,6 +19,32 @@ constexpr int kMaxFfn = 65536;    // the list kernel handles up to 1024 mask wor
 constexpr int kArrive = 64;       // arrival counters (FC2 slices, predictor row tiles)
 constexpr int kXchCopies = 16;    // copies of h exchanged between the owners (one-launch step)
 
+// k slices of the batched FC1 (1024 k each)
+int fc1_slices(int d);
+
+// Row pitch (halfs) of the batched form's fp16 copy of x: d rounded up to the
+// 512 k that its FC1 takes per stage (the padding stays zero).
+inline int x16_pitch(int d) { return (d + 511) / 512 * 512; }
+
+// Chunk i (8 values) of x [B][d] written to x16 as fp16 hi (rows 0 .. Bm-1)
+// and lo = the fp16 rounding of what hi left out (rows Bm .. 2Bm-1), pitch dp.
+__device__ __forceinline__ void x16_chunk(const float *__restrict__ x, int d, int dp, int Bm,
+                                          _Float16 *__restrict__ x16, int i) {
+    typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+    const int c8 = d / 8, t = i / c8, k = 8 * (i % c8);
+    const float4 u = *reinterpret_cast<const float4 *>(x + (size_t)t * d + k);
+    const float4 v = *reinterpret_cast<const float4 *>(x + (size_t)t * d + k + 4);
+    const float f[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+    h8v hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        hi[e] = (_Float16)f[e];
+        lo[e] = (_Float16)(f[e] - (float)hi[e]);
+    }
+    *reinterpret_cast<h8v *>(x16 + (size_t)t * dp + k) = hi;
+    *reinterpret_cast<h8v *>(x16 + (size_t)(Bm + t) * dp + k) = lo;
+}
+
 // Position of the r-th set bit of m (r < popcount(m)), by halving.
 __device__ __forceinline__ int nth_set_bit(uint64_t m, int r) {
     int pos = 0;
@@ -79,14 +105,18 @@ struct LayerView {
     // per-call scratch
     float *h;          // [max_batch][H]           predictor hidden activations
     _Float16 *h16;     // [2][max_batch][H]        h as fp16 hi, lo (batched form)
-    _Float16 *x16;     // [max_batch][d]           x as fp16 (batched form)
+    _Float16 *x16;     // [2][max_batch][dp]       x as fp16 hi, lo (batched form;
+                       //                          dp = x16_pitch(d), padding zero)
     uint64_t *wbits;   // [max_batch][nq]          per-token owner bits
     uint64_t *ubits;   // [nq]                     union over the batch
     uint64_t *vbits;   // [nq]                     entries listed by each owner
     int32_t *lslot;    // [nq][64]                 their slots (ascending bit); batched
                        //                          form: [rows] in list order
-    float *la;         // [nq][64][max_batch]      their FC1 activations; batched
-                       //                          form: [rows][max_batch]
+    float *la;         // [nq][64][max_batch]      their FC1 activations
+    _Float16 *la16;    // [2][max_batch][nq*64]    batched form: the list rows' FC1
+                       //                          activations as fp16 hi, lo, token-major
+    float *fc1_part;   // [ks][nmat-1][max_batch][nq*64] batched FC1 partial sums per
+                       //                          k slice (ks = fc1_slices(d))
     float *partial;    // [kGroups][max_batch][d]  FC2 partial sums
     float *part1;      // [d/16][nq][16]           single-token FC2 rows per owner
     unsigned *arrive;  // [kArrive]                FC2 arrivals per slice
@@ -117,7 +147,7 @@ struct HeadView {
     float *h;          // [max_batch][H]   scratch: hidden activations
     uint64_t *wbits;   // [max_batch][words] scratch: head words
     _Float16 *h16;     // [2][max_batch][H] scratch of the batched layer 1 (max_batch > 1)
-    _Float16 *x16;     // [max_batch][d]
+    _Float16 *x16;     // [2][max_batch][x16_pitch(d)]
     float *pred_part;  // [ceil(H/32)][8][32*32]
 };
 constexpr int kMaxHeads = 4096;   // head words per token fit one wave (64)

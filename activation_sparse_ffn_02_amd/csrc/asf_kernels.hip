@@ -483,12 +483,12 @@ __global__ __launch_bounds__(kThreads) void k_pred1(Pred1Args a) {
 // k_pred1: the weight chunks stay in registers while the tokens go by, the
 // x chunks of the next token loaded while the current one is summed.  Each
 // token's sum is formed exactly as k_pred1 forms it.  Also writes h as fp16
-// hi + lo halves (h16: [2][B][H]) for the batched scores and x as fp16 (x16)
-// for the batched FC1.
+// hi + lo halves (h16: [2][B][H]) for the batched scores and x as fp16 hi +
+// lo (x16, pitch dp, lo rows after Bm hi rows) for the batched FC1.
 constexpr int kPred1MaxB = 4;   // beyond, the matrix-core form is faster (one L2 round per token pair here)
 
 __global__ __launch_bounds__(kThreads) void k_pred1b(Pred1Args a, int B, _Float16 *__restrict__ h16,
-                                                     _Float16 *__restrict__ x16) {
+                                                     _Float16 *__restrict__ x16, int dp, int Bm) {
     constexpr int CPL = kPred1Cpl;
     __shared__ float red[kPred1MaxB][kWaves];
     // two tokens' x at a time, staged in LDS by the whole workgroup: each
@@ -553,16 +553,10 @@ __global__ __launch_bounds__(kThreads) void k_pred1b(Pred1Args a, int B, _Float1
             h16[(size_t)(B + t) * H + r] = (_Float16)(hv - (float)hi);
         }
     }
-    // x -> fp16 for the batched FC1
+    // x -> fp16 hi + lo for the batched FC1
     const int n8 = B * d / 8;
-    for (int i = blockIdx.x * kThreads + threadIdx.x; i < n8; i += gridDim.x * kThreads) {
-        float v[8];
-        load_f32<8>(a.x + (size_t)8 * i, v);
-        f16x8 o;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (_Float16)v[e];
-        *reinterpret_cast<f16x8 *>(x16 + (size_t)8 * i) = o;
-    }
+    for (int i = blockIdx.x * kThreads + threadIdx.x; i < n8; i += gridDim.x * kThreads)
+        x16_chunk(a.x, d, dp, Bm, x16, i);
 }
 
 // ---------------------------------------------------------------- predictor layer 2
@@ -2375,7 +2369,8 @@ hipError_t launch_pred_l1(const LayerView &L, const float *x, int B, const Trace
     }
     if (L.wtype == ASF_F16 && B <= kPred1MaxB) {
         const dim3 grid(pred1_blocks(L)), blk(kThreads);
-        ASF_LAUNCH(ASF_K_PRED_L1, k_pred1b, grid, blk, pred1_args(L, x), B, L.h16, L.x16);
+        ASF_LAUNCH(ASF_K_PRED_L1, k_pred1b, grid, blk, pred1_args(L, x), B, L.h16, L.x16,
+                   x16_pitch(L.d), L.max_batch);
         return hipGetLastError();
     }
     if (L.wtype == ASF_F16) return launch_pred_mm(L, x, B, tr, s);
