@@ -84,7 +84,7 @@ size_t carve(const asf_layer_desc &desc, uintptr_t base, LayerView *v) {
     t.part1 = (float *)take(nq * d * 4);
     t.arrive = (unsigned *)take(kArrive * 4);
     // batched predictor partial tiles (row tiles x up to 8 k-splits x 32x32)
-    t.pred_part = Bm > 1 ? (float *)take(((H + 31) / 32) * 8 * 1024 * 4) : nullptr;
+    t.pred_part = Bm > 1 ? (float *)take((size_t)pred_slices((int)d) * Bm * H * 4) : nullptr;
     t.masks = (uint64_t *)take(Bm * words * 8);
     t.slots = (int32_t *)take(f * 4);
     t.count = (int32_t *)take(64);
@@ -154,7 +154,7 @@ size_t carve_heads(const asf_head_desc &desc, uintptr_t base, HeadView *v) {
     t.wbits = (uint64_t *)take(Bm * words * 8);
     t.h16 = Bm > 1 ? (_Float16 *)take(2 * Bm * H * 2) : nullptr;
     t.x16 = Bm > 1 ? (_Float16 *)take(2 * Bm * (size_t)x16_pitch((int)d) * 2) : nullptr;
-    t.pred_part = Bm > 1 ? (float *)take(((H + 31) / 32) * 8 * 1024 * 4) : nullptr;
+    t.pred_part = Bm > 1 ? (float *)take((size_t)pred_slices((int)d) * Bm * H * 4) : nullptr;
     if (v) *v = t;
     return (size_t)(p - align_up(base, 256));
 }
@@ -572,6 +572,14 @@ asf_status asf_create_head_predictor(const asf_head_desc *desc, const asf_head_w
     asf_head_predictor *P = new (std::nothrow) asf_head_predictor;
     if (!P) return ASF_ERR_ARG;
     carve_heads(*desc, (uintptr_t)storage, &P->v);
+    {
+        int dev = 0;
+        P->v.ncu = 1;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&P->v.ncu, hipDeviceAttributeMultiprocessorCount, dev) !=
+                hipSuccess || P->v.ncu < 1)
+            P->v.ncu = 1;
+    }
     const HeadView &v = P->v;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipSuccess;

@@ -7,21 +7,24 @@
 // l % 32 with the 8 consecutive k of group l / 32, and accumulator element
 // i of lane l holds D[8(i/4) + 4(l/32) + i%4][l % 32].
 //
-//   predictor layer 1   rows of P1 x tokens, k = d, split over workgroups;
-//                       a second kernel adds the partials (many workgroups:
-//                       a last-arriver reduction costs an L2 write-back and
-//                       an atomic round trip per workgroup, then a serial sum)
+//   predictor layer 1   the FC1 stream below over the rows of P1, x as fp16
+//                       hi + lo in LDS (k slices of 512 k); a second kernel
+//                       adds the slices' partials, c1, ReLU
 //   predictor layer 2   per owner: its 64 slot rows x tokens, k = H; then
 //                       threshold and one ballot per token
-//   FC1                 per owner: its union rows (compacted) x tokens
+//   FC1                 the union list spread over row groups x k slices
+//                       (1024 k, x slice in LDS), whole-row 1 KiB gathers;
+//                       a second kernel adds the slices' partials, then the
+//                       activation
 //   FC2                 tokens x outputs, k = the group's listed neurons;
 //                       down segments go through LDS to be read transposed;
 //                       a second kernel adds the groups' partials
 //
 // The predictor feeds x and h to the MFMA as fp16 hi + lo halves (two
 // instructions per step), so its sums keep fp32 accuracy and the active
-// sets stay those of an fp32 GEMV; FC1 and FC2 take x and a rounded to fp16
-// once (their error stays orders of magnitude inside the output tolerance).
+// sets stay those of an fp32 GEMV; FC2 takes the activations as hi + lo
+// too; FC1 takes x rounded to fp16 once (an error orders of magnitude inside
+// the output tolerance, for half the LDS and operand traffic).
 // Every sum runs in a fixed order, so results are reproducible bit for bit.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -38,9 +41,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kW = kThreads / 64;   // waves per workgroup
 constexpr int kTile = 32;           // rows / tokens / outputs of one MFMA tile
-constexpr int kSteps = 8;           // 16-k steps whose loads are in flight per wave
 constexpr int kSliceOut = kTile * kW;  // FC2 outputs per workgroup (256)
-constexpr int kMaxSplit = 8;        // predictor layer 1: k split over at most 8 workgroups
 
 __device__ __forceinline__ f32x16 mfma(const h8 a, const h8 b, const f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -65,110 +66,11 @@ __device__ __forceinline__ int acc_row(int i, int lane) {
     return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
 }
 
-// 8 consecutive fp32 values at p (16-byte aligned, always a valid address) as
-// fp16; with HILO also the fp16 rounding of what the first rounding left
-// out.  live == false gives zeros.
-template <bool HILO>
-__device__ __forceinline__ void frag_f32(const float *p, bool live, h8 &hi, h8 &lo) {
-    const float4 *q = reinterpret_cast<const float4 *>(p);
-    const float4 u = q[0], v = q[1];
-    const float f[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const float t = live ? f[j] : 0.0f;
-        const _Float16 a = (_Float16)t;
-        hi[j] = a;
-        if constexpr (HILO) lo[j] = (_Float16)(t - (float)a);
-    }
-}
-
 // Wave tiles -> LDS; returns nothing, caller synchronises.
 __device__ __forceinline__ void tile_to_lds(float *dst, const f32x16 &acc, int lane) {
     const int col = lane & 31;
 #pragma unroll
     for (int i = 0; i < 16; ++i) dst[acc_row(i, lane) * kTile + col] = acc[i];
-}
-
-// ---------------------------------------------------------------- predictor layer 1
-// Workgroup (mt, ks): rows 32mt .. 32mt+31 of P1 over k in [ks*KW, (ks+1)*KW),
-// KW = d / KS; wave w takes the w-th eighth of that range.  Wave tiles are
-// added in wave order into the workgroup's partial tile; k_pred_fin adds the
-// KS partial tiles of a row tile in ks order, then c1, then ReLU.
-__global__ __launch_bounds__(kThreads) void k_pred_mm(const u32x4 *__restrict__ P1,
-                                                      const float *__restrict__ x, int B, int d,
-                                                      int H, int KS, float *__restrict__ part) {
-    __shared__ float red[kW][kTile * kTile];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int mt = blockIdx.x / KS, ks = blockIdx.x % KS;
-    const int KWw = d / KS / kW;                  // k per wave, a multiple of 16
-    const int k_beg = ks * (d / KS) + wave * KWw, k_end = k_beg + KWw;
-    const int g = lane >> 5, col = lane & 31;
-    const int row = kTile * mt + col;
-    const u32x4 *arow = P1 + (size_t)(row < H ? row : H - 1) * (d / 8);
-    const bool tok = col < B;
-    const float *xrow = x + (size_t)(tok ? col : 0) * d;
-    f32x16 acc = zero16();
-    for (int k0 = k_beg; k0 < k_end; k0 += 16 * kSteps) {
-        u32x4 a[kSteps];
-        h8 bh[kSteps], bl[kSteps];
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            const int kk = (k0 + 16 * s < k_end ? k0 + 16 * s : k_end - 16) + 8 * g;
-            a[s] = arow[kk / 8];
-            frag_f32<true>(xrow + kk, tok, bh[s], bl[s]);
-        }
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            if (k0 + 16 * s < k_end) {
-                const h8 av = __builtin_bit_cast(h8, a[s]);
-                acc = mfma(av, bh[s], acc);
-                acc = mfma(av, bl[s], acc);
-            }
-        }
-    }
-    tile_to_lds(red[wave], acc, lane);
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int e = tid + kThreads * j;
-        float sum = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kW; ++w) sum += red[w][e];
-        part[((size_t)mt * KS + ks) * (kTile * kTile) + e] = sum;
-    }
-}
-
-// Element e of row tile mt (row 32mt + e/32, token e%32): the KS partial
-// tiles in ks order, then c1, then ReLU -> h and its fp16 hi/lo halves.  The
-// grid also converts x to fp16 hi + lo for the FC1 of the step.
-__global__ __launch_bounds__(kThreads) void k_pred_fin(const float *__restrict__ part,
-                                                       const float *__restrict__ c1,
-                                                       const float *__restrict__ x, int B, int d,
-                                                       int H, int KS, float *__restrict__ h,
-                                                       _Float16 *__restrict__ h16,
-                                                       _Float16 *__restrict__ x16, int dp,
-                                                       int Bm) {
-    const int gid = blockIdx.x * kThreads + threadIdx.x;
-    const int mt = gid / (kTile * kTile), e = gid % (kTile * kTile);
-    const int r = kTile * mt + e / kTile, t = e % kTile;
-    if (r < H && t < B) {
-        // all KS loads in flight (unrolled to the largest split, clamped)
-        const float *pp = part + (size_t)mt * KS * (kTile * kTile) + e;
-        float pv[kMaxSplit];
-#pragma unroll
-        for (int ks = 0; ks < kMaxSplit; ++ks) pv[ks] = pp[(size_t)(ks < KS ? ks : 0) * (kTile * kTile)];
-        float sum = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < kMaxSplit; ++ks)
-            if (ks < KS) sum += pv[ks];
-        const float hv = fmaxf(sum + c1[r], 0.0f);
-        const _Float16 hi = (_Float16)hv;
-        h[(size_t)t * H + r] = hv;
-        h16[(size_t)t * H + r] = hi;
-        h16[(size_t)(B + t) * H + r] = (_Float16)(hv - (float)hi);
-    }
-    const int n8 = B * d / 8;
-    for (int i = gid; i < n8; i += gridDim.x * kThreads) x16_chunk(x, d, dp, Bm, x16, i);
 }
 
 // ---------------------------------------------------------------- operand tiles through LDS
@@ -393,6 +295,7 @@ struct Fc1MmParams {
     int32_t *rows;           // number of list rows
     float *part;             // [ks][NM][Bm][LR] partial sums per k slice
     int ks;                  // k slices
+    int add_b1;              // slice 0 adds b1 (b1 is read, and stays valid, either way)
 };
 
 // x -> fp16 hi + lo (for FC1 calls that follow no predictor pass)
@@ -430,12 +333,19 @@ constexpr int kStageCh = kTile * kPieceC;      // chunks per stage buffer (32 Ki
 constexpr int kFc1Pre = 4;                     // stages in flight
 constexpr int kFc1MaxRows = 2048;              // rows per workgroup (the grid guarantees it)
 constexpr int kMaxKSlices = 8;                 // d <= 8192
+constexpr int kMaxPredSlices = 16;             // predictor slices of 512 k, d <= 8192
 
-template <bool GATED, int NRT_> struct Fc1Geo {
+// HILO: x as fp16 hi + lo (two MFMAs per k-step) in slices of one piece (the
+// LDS holds hi and lo of 512 k), as the batched predictor layer 1 takes it
+template <bool GATED, int NRT_, bool HILO = false> struct Fc1Geo {
     static constexpr int NM = GATED ? 2 : 1;               // matrices per row: [gate,] up
     static constexpr int NRT = NRT_;                       // row tiles per pass
-    static constexpr int SPP = NRT * kSliceP * NM;         // stages per pass
-    static_assert(SPP % kFc1Pre == 0 && kFc1Pre % 2 == 0, "ring slots repeat every pass");
+    static constexpr int SP = HILO ? 1 : kSliceP;          // pieces per k slice
+    static constexpr int XC = SP * kPieceC;                // chunks per token row of a half of xs
+    static constexpr int SPP = NRT * SP * NM;              // stages per pass
+    static constexpr int PRE = SPP < kFc1Pre ? SPP : kFc1Pre;  // stages in flight
+    static_assert(SPP % PRE == 0 && PRE % 2 == 0, "ring slots repeat every pass");
+    static_assert(XC * (HILO ? 2 : 1) == kSliceC, "the x slice fills its LDS");
 };
 
 // wave tile -> LDS, element (row, col) at row*32 + (col ^ row), so that both
@@ -452,11 +362,11 @@ __device__ __forceinline__ void tile_to_lds_x(float *dst, const f32x16 &acc, int
 
 // The weight stream of workgroup slice ks over its nr rows (slots in rslot,
 // x slice in xs), in passes of NRT row tiles.
-template <bool GATED, int NRT>
+template <bool GATED, int NRT, bool HILO = false>
 __device__ __forceinline__ void fc1_stream(const Fc1MmParams &p, const u32x4 *xs, u32x4 *stg,
                                            const int *rslot, int ks, int r0, int nr) {
-    using G1 = Fc1Geo<GATED, NRT>;
-    constexpr int NM = G1::NM, SPP = G1::SPP;
+    using G1 = Fc1Geo<GATED, NRT, HILO>;
+    constexpr int NM = G1::NM, SPP = G1::SPP, SP = G1::SP, XC = G1::XC, PRE = G1::PRE;
     constexpr int TT = kTile * kTile;
     static_assert((NRT * NM) % 2 == 0 && 2 * kW * TT * 4 <= 2 * kStageCh * 16,
                   "the epilogue reduces two tiles per round in the stage buffers");
@@ -468,8 +378,8 @@ __device__ __forceinline__ void fc1_stream(const Fc1MmParams &p, const u32x4 *xs
     // stage j of pass ps: row tile j / (2 NM), piece (j / NM) % 2, matrix j % NM;
     // wave w loads rows w, w+8, w+16, w+24 of the tile
     auto issue = [&](int ps, int j, u32x4 (&w)[4]) {
-        const int i = j / (kSliceP * NM), pc = (j / NM) % kSliceP, m = j % NM;
-        const uint32_t koff = 1024u * (uint32_t)(kSliceP * ks + pc);
+        const int i = j / (SP * NM), pc = (j / NM) % SP, m = j % NM;
+        const uint32_t koff = 1024u * (uint32_t)(SP * ks + pc);
         const uint32_t moff = (GATED && m == 1) ? rowb : 0u;   // [gate,] up
         // the four slots read together (clamped index, unconditional)
         int sv[4];
@@ -488,9 +398,9 @@ __device__ __forceinline__ void fc1_stream(const Fc1MmParams &p, const u32x4 *xs
             w[l] = ld_stream(buf_rsrc(base, ok ? rowb - koff : 0u), 16u * lane);
         }
     };
-    u32x4 ring[kFc1Pre][4];
+    u32x4 ring[PRE][4];
 #pragma unroll
-    for (int u = 0; u < kFc1Pre; ++u) issue(0, u, ring[u]);
+    for (int u = 0; u < PRE; ++u) issue(0, u, ring[u]);
     f32x16 acc[NRT * NM];
     float *red = reinterpret_cast<float *>(stg);
     auto pass = [&](int ps) {
@@ -508,22 +418,22 @@ __device__ __forceinline__ void fc1_stream(const Fc1MmParams &p, const u32x4 *xs
                 const int a = a0 + e / TT, i = a / NM, rr = e % kTile;
                 const int row = kTile * (NRT * ps + i) + rr;
                 const int sl = rslot[row < nr ? row : 0];
-                const bool use = ks == 0 && row < nr && sl >= 0;
+                const bool use = p.add_b1 && ks == 0 && row < nr && sl >= 0;
                 const float b = p.b1[use ? sl : 0];
                 bias[a0 / 2][h] = use ? b : 0.0f;
             }
 #pragma unroll
         for (int j = 0; j < SPP; ++j) {
-            const int u = j % kFc1Pre, b = j & 1;
-            const int i = j / (kSliceP * NM), pc = (j / NM) % kSliceP, m = j % NM;
+            const int u = j % PRE, b = j & 1;
+            const int i = j / (SP * NM), pc = (j / NM) % SP, m = j % NM;
             u32x4 *bufp = stg + b * kStageCh;
 #pragma unroll
             for (int l = 0; l < 4; ++l) {
                 const int row = wave + kW * l;
                 bufp[row * kPieceC + (lane ^ (row & 15))] = ring[u][l];
             }
-            if (j + kFc1Pre < SPP) issue(ps, j + kFc1Pre, ring[u]);
-            else issue(ps + 1, j + kFc1Pre - SPP, ring[u]);
+            if (j + PRE < SPP) issue(ps, j + PRE, ring[u]);
+            else issue(ps + 1, j + PRE - SPP, ring[u]);
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -531,8 +441,12 @@ __device__ __forceinline__ void fc1_stream(const Fc1MmParams &p, const u32x4 *xs
                 const int c = 8 * wave + 4 * hh + kk;
                 const h8 a = __builtin_bit_cast(h8, bufp[tk * kPieceC + (c ^ (tk & 15))]);
                 const int cx = kPieceC * pc + c;
-                const h8 bx = __builtin_bit_cast(h8, xs[tk * kSliceC + (cx ^ (tk & 15))]);
+                const h8 bx = __builtin_bit_cast(h8, xs[tk * XC + (cx ^ (tk & 15))]);
                 acc[i * NM + m] = mfma(a, bx, acc[i * NM + m]);
+                if constexpr (HILO) {
+                    const h8 bl = __builtin_bit_cast(h8, xs[(kTile + tk) * XC + (cx ^ (tk & 15))]);
+                    acc[i * NM + m] = mfma(a, bl, acc[i * NM + m]);
+                }
             }
         }
         // pass end: each row tile's wave tiles summed in wave order into the
@@ -732,6 +646,89 @@ __global__ __launch_bounds__(256) void k_fc1_fin(Fc1MmParams p) {
     *reinterpret_cast<h8 *>(p.la16 + (size_t)(p.Bm + t) * p.LR + r) = lo;
 }
 
+// ---------------------------------------------------------------- predictor layer 1 (stream form)
+// Batched predictor layer 1 on the FC1 stream: workgroup (g, ks) takes the
+// P1 rows of group g over k slice ks (512 k), x read once as fp32 and kept
+// in LDS as fp16 hi + lo (two MFMAs per k-step, so the sums keep fp32
+// accuracy and the active sets stay those of an fp32 GEMV); the KS partial
+// sums of each row and token go to k_pred_sum.
+__global__ __launch_bounds__(kThreads) void k_pred_rows(Fc1MmParams p, const float *__restrict__ x,
+                                                        int d) {
+    __shared__ u32x4 xs[kTile * kSliceC];            // [hi rows 0-31 | lo rows 32-63][64 chunks]
+    __shared__ u32x4 stg[2 * kStageCh];
+    __shared__ int rslot[kFc1MaxRows];
+    const int tid = threadIdx.x;
+    const int KS = p.ks, ks = blockIdx.x % KS, g = blockIdx.x / KS, GR = gridDim.x / KS;
+    // x slice: token xt, chunks xc + 16j (8 k each); tokens past B read zeros,
+    // k past d reads x of the next token (against zero weights) or zeros
+    const int xt = tid >> 4, xc = tid & 15;
+    {
+        const rsrc_t xr = buf_rsrc(x, (uint32_t)p.B * d * 4);
+        u32x4 v[kPieceC / 16][2];
+#pragma unroll
+        for (int j = 0; j < kPieceC / 16; ++j) {
+            const uint32_t o = (uint32_t)(xt * d + kPieceK * ks + 8 * (xc + 16 * j)) * 4;
+            v[j][0] = ld_shared(xr, o);
+            v[j][1] = ld_shared(xr, o + 16);
+        }
+#pragma unroll
+        for (int j = 0; j < kPieceC / 16; ++j) {
+            const int c = xc + 16 * j;
+            const float4 u0 = __builtin_bit_cast(float4, v[j][0]);
+            const float4 u1 = __builtin_bit_cast(float4, v[j][1]);
+            const float fv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+            h8 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                hi[e] = (_Float16)fv[e];
+                lo[e] = (_Float16)(fv[e] - (float)hi[e]);
+            }
+            xs[xt * kPieceC + (c ^ (xt & 15))] = __builtin_bit_cast(u32x4, hi);
+            xs[(kTile + xt) * kPieceC + (c ^ (xt & 15))] = __builtin_bit_cast(u32x4, lo);
+        }
+    }
+    const int H = p.f;
+    const int R = (H + GR - 1) / GR;
+    const int r0 = R * g;
+    const int nr = r0 < H ? (R < H - r0 ? R : H - r0) : 0;
+    for (int i = tid; i < nr; i += kThreads) rslot[i] = r0 + i;
+    __syncthreads();
+    if (nr <= 0) return;
+    if (nr <= 2 * kTile) fc1_stream<false, 2, true>(p, xs, stg, rslot, ks, r0, nr);
+    else fc1_stream<false, 4, true>(p, xs, stg, rslot, ks, r0, nr);
+}
+
+// Element (t, r): the KS partial sums of row r for token t in slice order,
+// then c1, then ReLU -> h and its fp16 hi/lo halves.  The grid also converts
+// x to fp16 hi + lo for the FC1 of the step.
+__global__ __launch_bounds__(kThreads) void k_pred_sum(const float *__restrict__ part, int KS,
+                                                       int Bm, const float *__restrict__ c1,
+                                                       const float *__restrict__ x, int B, int d,
+                                                       int H, float *__restrict__ h,
+                                                       _Float16 *__restrict__ h16,
+                                                       _Float16 *__restrict__ x16, int dp) {
+    const int gid = blockIdx.x * kThreads + threadIdx.x;
+    if (gid < B * H) {
+        const int t = gid / H, r = gid % H;
+        // every slice's load in flight (unrolled to the largest count, clamped)
+        float pv[kMaxPredSlices];
+#pragma unroll
+        for (int s = 0; s < kMaxPredSlices; ++s)
+            pv[s] = part[((size_t)(s < KS ? s : 0) * Bm + t) * H + r];
+        float sum = 0.0f;
+#pragma unroll
+        for (int s = 0; s < kMaxPredSlices; ++s)
+            if (s < KS) sum += pv[s];
+        const float hv = fmaxf(sum + c1[r], 0.0f);
+        const _Float16 hi = (_Float16)hv;
+        h[(size_t)t * H + r] = hv;
+        h16[(size_t)t * H + r] = hi;
+        h16[(size_t)(B + t) * H + r] = (_Float16)(hv - (float)hi);
+    }
+    const int n8 = B * d / 8;
+    for (int i = gid; i < n8; i += gridDim.x * kThreads) x16_chunk(x, d, dp, Bm, x16, i);
+}
+
 // ---------------------------------------------------------------- FC2
 struct Fc2MmParams {
     const void *bundles;
@@ -926,26 +923,35 @@ inline hipEvent_t ev_stop(const Trace *tr, int k) { return tr ? tr->ev[2 * k + 1
 
 }  // namespace
 
-// split of the predictor's k over workgroups: the largest power of two <=
-// kMaxSplit with d a multiple of 128 * KS (every wave then takes a multiple
-// of 16 k)
-int pred_mm_splits(int d) {
-    int ks = kMaxSplit;
-    while (ks > 1 && d % (128 * ks) != 0) ks >>= 1;
-    return ks;
-}
+int pred_slices(int d) { return (x16_pitch(d) + kPieceK - 1) / kPieceK; }
 
 hipError_t launch_pred_mm(const LayerView &L, const float *x, int B, const Trace *tr,
                           hipStream_t s) {
-    const int mt = (L.H + kTile - 1) / kTile, ks = pred_mm_splits(L.d);
+    Fc1MmParams p = {};
+    p.bundles = L.p1;
+    p.bundle_bytes = (uint32_t)(L.cd * 16);          // P1 rows, d fp16 each
+    p.cd = L.cd;
+    p.b1 = L.c1;                                     // read, not added (k_pred_sum adds c1)
+    p.add_b1 = 0;
+    p.B = B;
+    p.f = L.H;
+    p.Bm = L.max_batch;
+    p.LR = L.H;
+    p.part = L.pred_part;
+    p.ks = pred_slices(L.d);
+    const int ncu = L.ncu > 0 ? L.ncu : 1;
+    int GR = ncu / p.ks;
+    const int gmin = (L.H + kFc1MaxRows - 1) / kFc1MaxRows;
+    GR = GR > gmin ? GR : gmin;
+    GR = GR < 1 ? 1 : GR;
     // the traced interval spans both kernels
-    hipExtLaunchKernelGGL(k_pred_mm, dim3(mt * ks), dim3(kThreads), 0, s,
-                          ev_start(tr, ASF_K_PRED_L1), nullptr, 0u, (const u32x4 *)L.p1, x, B,
-                          L.d, L.H, ks, L.pred_part);
-    const int nfin = mt * (kTile * kTile) / kThreads;
-    hipExtLaunchKernelGGL(k_pred_fin, dim3(nfin), dim3(kThreads), 0, s, nullptr,
-                          ev_stop(tr, ASF_K_PRED_L1), 0u, (const float *)L.pred_part, L.c1, x, B,
-                          L.d, L.H, ks, L.h, L.h16, L.x16, x16_pitch(L.d), L.max_batch);
+    hipExtLaunchKernelGGL(k_pred_rows, dim3(GR * p.ks), dim3(kThreads), 0, s,
+                          ev_start(tr, ASF_K_PRED_L1), nullptr, 0u, p, x, L.d);
+    const int n = B * L.H > B * L.d / 8 ? B * L.H : B * L.d / 8;
+    hipExtLaunchKernelGGL(k_pred_sum, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
+                          nullptr, ev_stop(tr, ASF_K_PRED_L1), 0u, (const float *)L.pred_part,
+                          p.ks, L.max_batch, L.c1, x, B, L.d, L.H, L.h, L.h16, L.x16,
+                          x16_pitch(L.d));
     return hipGetLastError();
 }
 
@@ -989,6 +995,7 @@ hipError_t launch_fc1_mm(const LayerView &L, const float *x, int B, int mode, co
     p.rows = L.rows;
     p.part = L.fc1_part;
     p.ks = fc1_slices(L.d);
+    p.add_b1 = 1;
     // KS slices x GR row groups: about one workgroup per CU (each holds
     // ~140 KiB of LDS), and enough groups that none takes more than
     // kFc1MaxRows rows

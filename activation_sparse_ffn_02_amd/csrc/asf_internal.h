@@ -120,7 +120,7 @@ struct LayerView {
     float *partial;    // [kGroups][max_batch][d]  FC2 partial sums
     float *part1;      // [d/16][nq][16]           single-token FC2 rows per owner
     unsigned *arrive;  // [kArrive]                FC2 arrivals per slice
-    float *pred_part;  // [ceil(H/32)][8][32*32]   batched predictor partial tiles
+    float *pred_part;  // [pred_slices(d)][max_batch][H] batched predictor partial sums
     uint64_t *masks;   // [max_batch][words]       slot-ordered token masks
     int32_t *slots;    // [f]                      ascending active slots
     int32_t *count;    // [1]                      their number
@@ -148,7 +148,8 @@ struct HeadView {
     uint64_t *wbits;   // [max_batch][words] scratch: head words
     _Float16 *h16;     // [2][max_batch][H] scratch of the batched layer 1 (max_batch > 1)
     _Float16 *x16;     // [2][max_batch][x16_pitch(d)]
-    float *pred_part;  // [ceil(H/32)][8][32*32]
+    float *pred_part;  // [pred_slices(d)][max_batch][H]
+    int ncu;           // compute units of the device it was created on
 };
 constexpr int kMaxHeads = 4096;   // head words per token fit one wave (64)
 
@@ -224,7 +225,7 @@ hipError_t launch_exact1(const LayerView &L, const float *x, bool mask_only, con
 hipError_t launch_count_bits(const LayerView &L, uint32_t *counts, hipStream_t s);
 hipError_t launch_rank_table(const uint32_t *counts, int f, int32_t *table, hipStream_t s);
 // batched forms on the matrix cores (B >= 2, fp16 weights)
-int pred_mm_splits(int d);
+int pred_slices(int d);   // k slices (512 k) of the batched predictor layer 1
 hipError_t launch_pred_mm(const LayerView &L, const float *x, int B, const Trace *tr,
                           hipStream_t s);
 hipError_t launch_score_mm(const LayerView &L, int B, const Trace *tr, hipStream_t s);

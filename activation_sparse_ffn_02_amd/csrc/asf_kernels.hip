@@ -2801,6 +2801,7 @@ hipError_t launch_head_predict(const HeadView &V, const float *x, int B, uint64_
     lv.h16 = V.h16;
     lv.x16 = V.x16;
     lv.pred_part = V.pred_part;
+    lv.ncu = V.ncu;
     if (launch_pred_l1(lv, x, B, nullptr, s) != hipSuccess) return hipGetLastError();
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
