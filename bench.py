@@ -675,6 +675,9 @@ def bench_batched(args, asf, torch, np, wl, dev, stream):
         lay.close()
     return {"workload": "OPT-13B-shaped FFN layer 5120x20480 fp16, predictor 5120->1024->20480, "
                         "~5% active per token, batch union", "ring_layers": len(ring),
+            "operand_precision": "fp16 weights, fp32 accumulation; predictor x and h and the FC2 "
+                                 "activations enter the matrix cores as fp16 hi + lo (products "
+                                 "exact in fp32); FC1 takes x rounded to fp16 once",
             "by_batch": out}
 
 

@@ -133,6 +133,48 @@ def test_empty_set_and_residual_alias(orc):
     assert rel_l2(rd.cpu().numpy(), y_orc) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("B,gated", [(6, False), (32, False), (5, True)])
+def test_batched_caller_lists(orc, B, gated):
+    """Batches over a caller's list on the matrix-core kernels (k-sliced FC1,
+    hi + lo FC2), at a d whose last k slice is partly past the row: out-of-
+    range ids skipped, a repeated id computed once per listing, an empty list
+    giving b2 + residual exactly, and every id in a shuffled order matching
+    the dense comparator's slot order to summation rounding."""
+    need_gpu()
+    d, f = 1408, 1000
+    L = wl.random_layer(d, f, 64, "f16", gated, 40 + B)
+    lay = asf().layer_from_numpy(L, max_batch=32)
+    rng = np.random.default_rng(B)
+    x = rng.standard_normal((B, d)).astype(np.float32)
+    r = rng.standard_normal((B, d)).astype(np.float32)
+    ids = rng.choice(f, 230, replace=False).astype(np.int32)
+    lst = np.concatenate([ids[:100], np.array([-3, f, 1 << 30], np.int32), ids[100:],
+                          ids[:5]]).astype(np.int32)
+    y = lay.sparse_ffn(to_dev(x), active=to_dev(lst),
+                       n_active=to_dev(np.array([lst.size], np.int32)), residual=to_dev(r))
+    # the five repeated ids count twice: the oracle over the list as given
+    # (valid entries, repeats kept)
+    valid = lst[(lst >= 0) & (lst < f)]
+    y_orc = np.zeros((B, d))
+    for once in (valid[:230], valid[230:]):
+        y_orc += orc.ffn(L.w_up, L.w_down, x, once, b1=L.b1, b2=None, W_gate=L.w_gate)
+    y_orc += L.b2.astype(np.float64) + r
+    yg = y.cpu().numpy()
+    for t in range(B):
+        assert rel_l2(yg[t], y_orc[t]) <= TOL["f16"], t
+    # an empty list: b2 + residual, exactly
+    y0 = lay.sparse_ffn(to_dev(x), active=to_dev(np.zeros(4, np.int32)),
+                        n_active=to_dev(np.array([0], np.int32)), residual=to_dev(r))
+    assert np.array_equal(y0.cpu().numpy(), (np.float32(0.0) + L.b2) + r)
+    # every neuron, shuffled, against the dense comparator
+    allids = to_dev(rng.permutation(f).astype(np.int32))
+    ya = lay.sparse_ffn(to_dev(x), active=allids, n_active=to_dev(np.array([f], np.int32)))
+    yd = lay.dense_ffn_ref(to_dev(x))
+    torch.cuda.synchronize()
+    for t in range(B):
+        assert rel_l2(ya.cpu().numpy()[t], yd.cpu().numpy()[t]) <= 1e-5, t
+
+
 def test_true_mask_sparse_equals_dense_on_gpu(orc):
     """With the true mask as the set, the sparse FFN equals the dense one."""
     need_gpu()
