@@ -395,7 +395,12 @@ asf_status asf_sparse_ffn(const asf_layer *layer, const float *x, int32_t B,
 
 int32_t asf_step_launches(const asf_layer *layer, int32_t B) {
     if (!layer || B < 1 || B > layer->v.max_batch) return 0;
-    return (B == 1 && layer->v.fused) ? 2 : 3;
+    const LayerView &v = layer->v;
+    if (B == 1) return v.fused ? 2 : 3;
+    if (v.wtype != ASF_F16) return 4;
+    // predictor layer 1 (with its slice sum from kPred1MaxB + 1 tokens on),
+    // scores, FC1 and its slice sum, FC2 and its group sum
+    return (B <= kPred1MaxB ? 1 : 2) + 1 + 2 + 2;
 }
 
 asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,

@@ -15,6 +15,7 @@ constexpr int kRowsPerWG = 64;    // neuron slots owned by one scoring workgroup
 constexpr int kSlices = 16;       // FC2: output slices
 constexpr int kGroups = 16;       // FC2: neuron groups (partials per output)
 constexpr int kMaxBatch = 32;
+constexpr int kPred1MaxB = 4;    // fp16 predictor layer 1 as a GEMV up to this batch, beyond on the matrix cores
 constexpr int kMaxFfn = 65536;    // the list kernel handles up to 1024 mask words
 constexpr int kArrive = 64;       // arrival counters (FC2 slices, predictor row tiles)
 constexpr int kXchCopies = 16;    // copies of h exchanged between the owners (one-launch step)

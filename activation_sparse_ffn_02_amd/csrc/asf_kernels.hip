@@ -485,7 +485,6 @@ __global__ __launch_bounds__(kThreads) void k_pred1(Pred1Args a) {
 // token's sum is formed exactly as k_pred1 forms it.  Also writes h as fp16
 // hi + lo halves (h16: [2][B][H]) for the batched scores and x as fp16 hi +
 // lo (x16, pitch dp, lo rows after Bm hi rows) for the batched FC1.
-constexpr int kPred1MaxB = 4;   // beyond, the matrix-core form is faster (one L2 round per token pair here)
 
 __global__ __launch_bounds__(kThreads) void k_pred1b(Pred1Args a, int B, _Float16 *__restrict__ h16,
                                                      _Float16 *__restrict__ x16, int dp, int Bm) {

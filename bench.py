@@ -64,6 +64,10 @@ def parse():
     ap.add_argument("--gated-steps", type=int, default=1000,
                     help="decode steps of the gated Llama-7B-shaped layer (0 skips it)")
     ap.add_argument("--gated-ring", type=int, default=12)
+    ap.add_argument("--shards", type=int, nargs="*", default=[2, 4, 8],
+                    help="neuron-shard counts G of the per-GPU shard measurement (none skips it)")
+    ap.add_argument("--shard-steps", type=int, default=1000)
+    ap.add_argument("--shard-ring", type=int, default=16)
     ap.add_argument("--stack-tokens", type=int, default=256,
                     help="tokens through the 48-layer stack (0 skips the stack)")
     ap.add_argument("--stack-warmup", type=int, default=8)
@@ -533,6 +537,85 @@ def bench_gated(args, asf, torch, np, wl, dev, stream):
     log(args, "gated: %.1f us per step, %.1f%% active, %.2fx dense" % (ms * 1e3, 100 * k / sh.f,
                                                                       dense_ms / ms))
     return res
+
+
+def shard_slices(L, G):
+    """Shard 0 of layer L sharded by neurons over G GPUs: every G-th neuron by
+    hotness rank (so each shard's expected active count is the same), in rank
+    order, with its up rows, down columns, b1, P2 rows and c2; P1 (and c1)
+    replicated; b2 added by shard 0."""
+    ids = L.perm[0::G]
+    return dict(w_up=L.w_up[ids], w_down=L.w_down[:, ids], p1=L.p1, p2=L.p2[ids],
+                b1=L.b1[ids], b2=L.b2, c2=L.c2[ids])
+
+
+def bench_shards(args, asf, torch, np, wl, dev, stream, L, X):
+    """One GPU's share of a layer sharded by neurons over G GPUs (shard_slices):
+    batch-1 decode steps of the OPT-6.7B-shaped layer's shard, and batch-32
+    steps of the OPT-13B-shaped layer's shard, each over a ring of shard
+    copies.  The all-reduce of the partial y that joins the shards is not part
+    of it."""
+    sh_ = stream.cuda_stream
+    L13 = wl.config_layer("opt13b_batched")
+    X13 = wl.config_tokens("opt13b_batched", 1000)
+    out = []
+    for G in args.shards:
+        for B, lay, toks in ((1, L, X), (32, L13, X13)):
+            sh = lay.shape
+            if G < 1 or sh.f % (64 * G):
+                continue
+            Xd = torch.from_numpy(toks).to(dev)
+            w = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev)
+                 for k, v in shard_slices(lay, G).items()}
+            nring = args.shard_ring if B == 1 else max(4, args.shard_ring // 2)
+            ring = [asf.Layer(w["w_up"], w["w_down"], w["p1"], w["p2"], b1=w["b1"], b2=w["b2"],
+                              c2=w["c2"], max_batch=B) for _ in range(nring)]
+            torch.cuda.synchronize()
+            nz = hidden_nonzero(torch, w["p1"], None, Xd) if B == 1 else None
+            del w
+            torch.cuda.empty_cache()
+            nst = Xd.shape[0] // B
+            Y = torch.empty((nring, B, sh.d), dtype=torch.float32, device=dev)
+            xs = [Xd[i * B:(i + 1) * B].data_ptr() for i in range(nst)]
+            ys = [Y[r].data_ptr() for r in range(nring)]
+            n = args.shard_steps if B == 1 else max(10, args.shard_steps // 10)
+            for i in range(min(100, n)):
+                ring[i % nring].decode_step_raw(xs[i % nst], B, ys[i % nring], sh_)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(n):
+                ring[i % nring].decode_step_raw(xs[i % nst], B, ys[i % nring], sh_)
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+            counts = torch.zeros(n, dtype=torch.int32, device=dev)
+            for i in range(n):
+                ring[i % nring].predict(Xd[(i % nst) * B:(i % nst + 1) * B], active=None,
+                                        n_active=counts[i:i + 1], want_list=False)
+            torch.cuda.synchronize()
+            k = float(counts.double().mean())
+            fs = sh.f // G
+            step_bytes, _, _ = bytes_model(wl.scaled_shape(sh, sh.d, fs, sh.H), k, nz)
+            ms = el * 1e3 / n
+            rec = {"layer": "OPT-6.7B-shaped 4096x16384" if B == 1 else
+                            "OPT-13B-shaped 5120x20480",
+                   "batch": B, "gpus": G, "d_ffn_per_gpu": fs, "launches": ring[0].step_launches(B),
+                   "ring_layers": nring, "steps": n, "us_per_step": ms * 1e3,
+                   "active_per_step": k, "active_frac": k / fs,
+                   "algorithmic_bytes_per_step": step_bytes,
+                   "effective_gbps": step_bytes / (ms * 1e-3) / 1e9,
+                   "effective_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            out.append(rec)
+            log(args, "shard 1/%d, B=%d: %.1f us per step, %.0f active" % (G, B, ms * 1e3, k))
+            for lay_ in ring:
+                lay_.close()
+            del ring, Y, Xd
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+    return {"workload": "one GPU's shard of a layer sharded by neurons over G GPUs (every G-th "
+                        "neuron by hotness rank, P1 replicated, fp16): the OPT-6.7B-shaped "
+                        "layer at batch 1 and the OPT-13B-shaped layer at batch 32; the "
+                        "all-reduce of y is not included",
+            "by_gpus": out}
 
 
 def bench_heads(args, asf, torch, np, wl, dev, stream):
@@ -1057,6 +1140,10 @@ def main():
     del ring, Xd, Y
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+    if args.shards:
+        out["shards"] = bench_shards(args, asf, torch, np, wl, dev, stream, L, X)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     if args.layout_steps > 0:
         out["layout"] = bench_layout(args, asf, torch, np, wl, dev, stream)
         torch.cuda.synchronize()

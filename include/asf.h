@@ -189,9 +189,11 @@ asf_status asf_sparse_ffn(const asf_layer *layer, const float *x, int32_t B,
 
 /* One decode step of one layer: asf_predict followed by asf_sparse_ffn over
  * the predicted union set, with no host round trip in between.  The optional
- * outputs are those of asf_predict.  One token: three kernels (predictor
- * layer 1; layer 2 + threshold + FC1 + each owner's FC2 into one row; the
- * sum of the owner rows).  The results are bit-identical to asf_predict
+ * outputs are those of asf_predict.  One token: two kernels when every
+ * owner workgroup can be resident at once (predictor layers 1 and 2,
+ * threshold, FC1 and each owner's FC2 into one row; the sum of the owner
+ * rows), else three (predictor layer 1 as a kernel of its own); both forms
+ * give the same bits (asf_step_launches tells which runs).  The results are bit-identical to asf_predict
  * followed by asf_sparse_ffn with active == NULL, and repeated calls give
  * identical bits. */
 asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
@@ -400,14 +402,18 @@ typedef enum {
  * them. */
 asf_status asf_layer_set_trace(asf_layer *layer, void *const *events, int32_t n);
 
-/* Launches of one asf_decode_step of `layer` for B tokens, a list kernel of
- * a batch left out: 2 when a one-token step runs predict, FC1 and the owner FC2 rows
- * in one launch (SCORE_FC1: the owners compute predictor layer 1 and exchange
- * h through device memory, which needs every owner workgroup resident at
- * once; the layer checks this at creation) followed by the owner-row sum
- * (FC2), else 3 (PRED_L1, SCORE_FC1 or SCORE + FC1, FC2).  A caller tracing
- * kernels learns from it which ids a step uses.  0 for a null layer or B
- * outside 1 .. max_batch. */
+/* Kernel launches of one asf_decode_step of `layer` for B tokens, a list
+ * kernel of a batch left out.  One token: 2 when the step runs predict, FC1
+ * and the owner FC2 rows in one launch (SCORE_FC1: the owners compute
+ * predictor layer 1 and exchange h through device memory, which needs every
+ * owner workgroup resident at once; the layer checks this at creation)
+ * followed by the owner-row sum (FC2), else 3 (PRED_L1, SCORE_FC1, FC2).
+ * B >= 2 traces four phases, PRED_L1, SCORE, FC1 and FC2: with fp32 weights
+ * one launch each (4); with fp16 weights FC1 and FC2 are two launches each
+ * (the stream kernel and its sum of k-slice or group partials) and so is
+ * predictor layer 1 from 5 tokens on (6 or 7), a phase's events spanning
+ * its launches.  A caller tracing kernels learns from it which ids a step
+ * uses.  0 for a null layer or B outside 1 .. max_batch. */
 int32_t asf_step_launches(const asf_layer *layer, int32_t B);
 
 /* Human-readable name of a status code (static string). */
