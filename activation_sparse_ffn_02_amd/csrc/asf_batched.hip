@@ -54,13 +54,6 @@ __device__ __forceinline__ f32x16 zero16() {
     return z;
 }
 
-__device__ __forceinline__ h8 zero_h8() {
-    h8 z;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = (_Float16)0.0f;
-    return z;
-}
-
 // row of accumulator element i in lane `lane` (its column is lane % 32)
 __device__ __forceinline__ int acc_row(int i, int lane) {
     return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
@@ -78,7 +71,7 @@ __device__ __forceinline__ void tile_to_lds(float *dst, const f32x16 &acc, int l
 // chunks of CW 16-byte chunks (8*CW k) per row: the weight tile (32 rows)
 // and the token tile (32 token rows of fp16).  Thread t loads chunk t%16
 // (and t%16 + 16) of row t/16, so a wave instruction covers 4 rows x 256
-// contiguous bytes.  Loads run kPre chunks ahead into registers, always
+// contiguous bytes.  Loads run a few chunks ahead into registers, always
 // from clamped addresses and zeroed afterwards (a load under a lane
 // condition makes the compiler wait for every outstanding load before the
 // next LDS store, which would cancel the prefetch).  A chunk is stored to one
@@ -86,11 +79,8 @@ __device__ __forceinline__ void tile_to_lds(float *dst, const f32x16 &acc, int l
 // fragment read (32 rows at one chunk) hits distinct banks.  Wave w
 // multiplies its CW/16 of the CW/2 MFMA steps of every chunk: a k split over
 // the waves, whose 8 partial tiles are added in wave order at the end.
-constexpr int kPre = 4;                      // chunks in flight per thread
-
 template <int CW> struct Geo {
     static constexpr int LPT = CW / 16;      // loads per thread per tile chunk
-    static constexpr int SPW = CW / 16;      // MFMA steps per wave per chunk
     static constexpr int ELEMS = kTile * CW; // 16-byte elements per tile chunk
 };
 
