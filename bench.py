@@ -411,6 +411,9 @@ def bench_stack(args, asf, torch, np, wl, dev, stream):
         "lookahead_tokens_per_s": n / elapsed_la,
         "lookahead_ms_per_token": elapsed_la * 1e3 / n,
         "active_frac_by_layer": [round(float(k[l]) / shapes[l].f, 4) for l in range(len(layers))],
+        "pred_hidden_by_layer": [shapes[l].H for l in range(len(layers))],
+        "pred_hidden_nonzero_by_layer": [round(float(nzs[l]), 1) for l in range(len(layers))],
+        "launches_by_layer": [lay.step_launches(1) for lay in layers],
         "dense_ms_per_token": dense_ms,
         "dense_gbps": None if dense_ms is None else dense_bytes / (dense_ms * 1e-3) / 1e9,
         "speedup_vs_dense": None if dense_ms is None else dense_ms / ms_tok,
