@@ -193,9 +193,9 @@ asf_status asf_sparse_ffn(const asf_layer *layer, const float *x, int32_t B,
  * owner workgroup can be resident at once (predictor layers 1 and 2,
  * threshold, FC1 and each owner's FC2 into one row; the sum of the owner
  * rows), else three (predictor layer 1 as a kernel of its own); both forms
- * give the same bits (asf_step_launches tells which runs).  The results are bit-identical to asf_predict
- * followed by asf_sparse_ffn with active == NULL, and repeated calls give
- * identical bits. */
+ * give the same bits (asf_step_launches tells which runs).  The results are
+ * bit-identical to asf_predict followed by asf_sparse_ffn with active ==
+ * NULL, and repeated calls give identical bits. */
 asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
                            const float *residual, float *y, int32_t *active,
                            int32_t *n_active, void *stream);
@@ -375,7 +375,9 @@ asf_status asf_predict_heads(const asf_head_predictor *hp, const float *x, int32
  *                     then LIST when an output is requested (for one token
  *                     the list runs in FC2's grid, timed as FC2); one token
  *                     on a layer whose owners fit the device at once: SCORE_FC1
- *                     (with predictor layer 1), FC2 (asf_step_launches)
+ *                     (with predictor layer 1), FC2 (asf_step_launches);
+ *                     B >= 2 with fp16 weights: a phase can be two launches,
+ *                     its events spanning both
  *   asf_sparse_ffn    FC1, FC2
  *   asf_dense_ffn_ref FC1 (every neuron), FC2
  *   asf_exact_ffn     FC1 (pre-activations, true set, owner FC2 rows), FC2
