@@ -83,12 +83,31 @@ __device__ __forceinline__ void load_f32(const float *p, float *v) {
     }
 }
 
-// Butterfly sum over the 64 lanes of a wave.  Each step adds a pair in both
-// lanes of the pair, so every lane ends with the same bits.
+// v of a neighbouring lane through a DPP source modifier (CTRL: the DPP
+// control, all rows and banks enabled; every source lane lies inside the
+// same 16-lane row, so no lane reads outside the wave)
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float lane_f(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// Sum over the 64 lanes of a wave (every lane active), the same bits in
+// every lane: inside each 16-lane row, DPP adds of lane pairs (quad_perm
+// 1,0,3,2), quads (2,3,0,1), half-rows (row_half_mirror) and rows
+// (row_mirror) leave the row's sum in each of its lanes; the four row sums,
+// read from lanes 0, 16, 32 and 48, are added as (r0 + r1) + (r2 + r3).
+// Four dependent ALU steps and four lane reads instead of six cross-lane
+// shuffles through the LDS crossbar.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
+    v += dpp_f<0x140>(v);
+    return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
 // Sums eight per-lane values v[0..7] (one per row) over the 64 lanes of a
