@@ -1049,14 +1049,14 @@ __device__ __forceinline__ void owner_ffn1(const ScoreParams &p, int q, int nq, 
     const uint64_t mr = SPEC ? (valid & ~((1ull << kSpecRows) - 1ull)) : valid;
     const int nr = __popcll(mr);
     int r = (wave - off + kWaves) % kWaves;
-    // with room for them, every FC1 row of the wave (two for up to 16
-    // listed neurons when a neuron's rows take 8 chunks per lane, else one)
-    // is requested before the down columns, in one round trip; a row the
-    // wave does not have reads nothing
+    // with room for them, every FC1 row set of the wave (two for up to 16
+    // listed neurons when two sets and the down columns in flight fit 48
+    // chunks per lane, else one) is requested before the down columns, in
+    // one round trip; a row the wave does not have reads nothing
     constexpr int kCh = Fc1Regs<GATED, CPL1>::chunks;
-    constexpr int HR = !kWide ? 0
-                       : kCh <= 8 ? 2
-                       : ((SPEC ? kCh : 0) + kCh + (PF + PFB) * CPT <= 48 ? 1 : 0);
+    constexpr int kHeld = (SPEC ? kCh : 0) + (PF + PFB) * CPT;
+    constexpr int HR = !kWide ? 0 : kCh <= 8 || kHeld + 2 * kCh <= 48 ? 2
+                                  : kHeld + kCh <= 48 ? 1 : 0;
     u32x4 hu[HR > 0 ? HR : 1][CPL1], hg[HR > 0 ? HR : 1][CPL1];
     float hbias[HR > 0 ? HR : 1];
     int hbit[HR > 0 ? HR : 1];
@@ -2144,14 +2144,25 @@ __global__ __launch_bounds__(64) void k_head_list(const uint64_t *__restrict__ w
 // requested together (up to 32 tokens), one ballot per slot word and token.
 constexpr int kListSlots = kThreads;
 
-// the workgroup sums of two ints (every thread gets both): butterflies over
-// the wave, then the wave partials in wave order; one barrier
+// integer wave sum (every lane active), the DPP pattern of wave_sum
+template <int CTRL> __device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+    v += dpp_i<0xB1>(v);
+    v += dpp_i<0x4E>(v);
+    v += dpp_i<0x141>(v);
+    v += dpp_i<0x140>(v);
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
+// the workgroup sums of two ints (every thread gets both): wave sums, then
+// the wave partials in wave order; one barrier
 __device__ __forceinline__ int2 block_sum_int2(int a, int b, int2 *red) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        a += __shfl_xor(a, o, 64);
-        b += __shfl_xor(b, o, 64);
-    }
+    a = wave_sum_int(a);
+    b = wave_sum_int(b);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_int2(a, b);
     __syncthreads();
     int2 t = make_int2(0, 0);
@@ -2406,7 +2417,7 @@ hipError_t launch_pred_l1(const LayerView &L, const float *x, int B, const Trace
     case 4: ASF_L1(WT, 4) break;      \
     default: ASF_L1(WT, 8) break;     \
     }
-    if (L.wtype == ASF_F16) { ASF_L1W(1) } else { ASF_L1W(0) }
+    ASF_L1W(0)   // fp32 weights (fp16 batches went to the forms above)
 #undef ASF_L1W
 #undef ASF_L1
     return hipGetLastError();
@@ -2501,7 +2512,7 @@ hipError_t launch_score(const LayerView &L, const float *x, int B, bool fc1, con
     case 2: ASF_S(WT, 2) break;     \
     default: ASF_S(WT, 4) break;    \
     }
-    if (L.wtype == ASF_F16) { ASF_SW(1) } else { ASF_SW(0) }
+    ASF_SW(0)   // fp32 weights (fp16 batches went to the matrix cores above)
 #undef ASF_SW
 #undef ASF_S
     hipError_t e = hipGetLastError();
@@ -2628,7 +2639,7 @@ hipError_t launch_fc1(const LayerView &L, const float *x, int B, int mode, const
     case 8: ASF_F(WT, 8) break;      \
     default: ASF_F(WT, 16) break;    \
     }
-    if (L.wtype == ASF_F16) { ASF_FW(1) } else { ASF_FW(0) }
+    ASF_FW(0)   // fp32 weights (fp16 batches went to the matrix cores above)
 #undef ASF_FW
 #undef ASF_F
     return hipGetLastError();
@@ -2790,8 +2801,7 @@ hipError_t launch_fc2(const LayerView &L, int B, bool listed, const float *resid
     if (B > 1 && L.wtype == ASF_F16) return launch_fc2_mm(L, B, listed, resid, y, tr, s);
     const dim3 grid(kSlices * kGroups), blk(kThreads);
     if (L.wtype == ASF_F16) {
-        if (B == 1) ASF_LAUNCH(ASF_K_FC2, (k_fc2<1, 1>), grid, blk, p);
-        else ASF_LAUNCH(ASF_K_FC2, (k_fc2<1, 4>), grid, blk, p);
+        ASF_LAUNCH(ASF_K_FC2, (k_fc2<1, 1>), grid, blk, p);   // one token (batches: above)
     } else {
         if (B == 1) ASF_LAUNCH(ASF_K_FC2, (k_fc2<0, 1>), grid, blk, p);
         else ASF_LAUNCH(ASF_K_FC2, (k_fc2<0, 4>), grid, blk, p);
