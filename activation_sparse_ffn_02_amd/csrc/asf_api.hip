@@ -399,8 +399,9 @@ int32_t asf_step_launches(const asf_layer *layer, int32_t B) {
     if (B == 1) return v.fused ? 2 : 3;
     if (v.wtype != ASF_F16) return 4;
     // predictor layer 1 (with its slice sum from kPred1MaxB + 1 tokens on),
-    // scores, FC1 and its slice sum, FC2 and its group sum
-    return (B <= kPred1MaxB ? 1 : 2) + 1 + 2 + 2;
+    // scores, FC1 (and its slice sum unless FC2 forms it), FC2 and its group
+    // sum
+    return (B <= kPred1MaxB ? 1 : 2) + 1 + (fc2_fuses_fin(v, B, false) ? 1 : 2) + 2;
 }
 
 asf_status asf_decode_step(const asf_layer *layer, const float *x, int32_t B,
@@ -556,7 +557,8 @@ asf_status asf_dense_ffn_ref(const asf_layer *layer, const float *x, int32_t B,
     hipStream_t s = (hipStream_t)stream;
     if (launch_fc1(v, x, B, 2, nullptr, nullptr, layer->tr(), s) != hipSuccess)
         return ASF_ERR_HIP;
-    if (launch_fc2(v, B, false, residual, y, layer->tr(), s) != hipSuccess) return ASF_ERR_HIP;
+    if (launch_fc2(v, B, false, residual, y, layer->tr(), s, true) != hipSuccess)
+        return ASF_ERR_HIP;
     return ASF_OK;
 }
 

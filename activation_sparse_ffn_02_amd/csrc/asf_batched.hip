@@ -38,6 +38,8 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
 constexpr int kW = kThreads / 64;   // waves per workgroup
 constexpr int kTile = 32;           // rows / tokens / outputs of one MFMA tile
@@ -733,6 +735,8 @@ struct Fc2MmParams {
     int d, B;
     float *partial;          // [groups][B][d]
     int groups;              // list-row ranges (<= kGroups)
+    const float *part;       // FUSED: FC1's k-slice partials [ks][1][Bm][LR]
+    int ks;                  // FUSED: k slices (<= kFc2FuseKS)
 };
 
 constexpr int kFc2N = 64;                   // list rows per step (4 MFMA k-steps)
@@ -740,6 +744,7 @@ constexpr int kWPitch = kSliceOut + 8;      // halfs per staged down row
 constexpr int kAPitch = kFc2N + 8;          // halfs per staged token row of a
 constexpr int kFc2Pre = 4;                  // steps in flight
 constexpr int kFc2Rows = 8192;              // list rows per group (f <= 65536, >= 8 groups)
+constexpr int kFc2FuseKS = 5;               // FUSED: at most this many FC1 k slices (d <= 5120)
 
 // 16-byte chunk of staged down row r holding outputs 8c .. 8c+7: rows 32
 // apart sit 4 chunks apart, so the two half-waves of a fragment read (rows
@@ -757,6 +762,14 @@ __device__ __forceinline__ int wl_chunk(int r, int c) { return c ^ (((r >> 5) & 
 // same permutation on both sides: lane half h takes rows 32h + 8j .. 32h+8j+7
 // at k-step j.  Group tiles go to `partial`; k_fc2_fin adds the G in group
 // order, then b2, then the residual.
+//
+// FUSED (plain layers of at most kFc2FuseKS FC1 k slices, small batches): a
+// is formed here from FC1's k-slice partials instead of read from la16, so
+// FC1 needs no finishing kernel: thread t takes token t / 16 and rows
+// 4 (t % 16) .. +3 of the step, sums its KS partials in slice order, applies
+// the ReLU (rows past the list are zero) and splits the result into fp16 hi
+// + lo, exactly as k_fc1_fin does.
+template <bool FUSED>
 __global__ __launch_bounds__(kThreads) void k_fc2_mm(Fc2MmParams p) {
     __shared__ __attribute__((aligned(16))) _Float16 wl[2][kFc2N * kWPitch];
     __shared__ __attribute__((aligned(16))) _Float16 al[2][2 * kTile * kAPitch];
@@ -784,42 +797,80 @@ __global__ __launch_bounds__(kThreads) void k_fc2_mm(Fc2MmParams p) {
     const int ta = (tid >> 3) & 31, ca = tid & 7;
     const rsrc_t ar = buf_rsrc(p.la16 + (size_t)hl * p.Bm * p.LR, (uint32_t)p.B * p.LR * 2);
     const uint32_t ao = (uint32_t)(ta * p.LR + rb + 8 * ca) * 2;   // tokens past B read zeros
-    u32x4 rv[kFc2Pre][4], ra[kFc2Pre];
+    // FUSED: partials of token ft, rows 4fc .. 4fc+3 of the step, slice k at
+    // po + k * pstride (tokens past B read zeros)
+    const int ft = tid >> 4, fc = tid & 15;
+    const rsrc_t pr = buf_rsrc(p.part, FUSED ? (uint32_t)(p.ks * p.Bm * p.LR * 4) : 0u);
+    const uint32_t pstride = (uint32_t)(p.Bm * p.LR * 4);
+    const uint32_t po = (uint32_t)(ft * p.LR + rb + 4 * fc) * 4;
+    u32x4 rv[kFc2Pre][4], ra[FUSED ? 1 : kFc2Pre], rp[FUSED ? kFc2Pre : 1][kFc2FuseKS];
     // the group's slots are staged in LDS, so a step's down loads do not wait
     // on a load of their slot
-    auto load_step = [&](int st, u32x4 (&v)[4], u32x4 &a) {
+    auto load_step = [&](int st, int u) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int rl = kFc2N * st + ln + 16 * j;
             const bool in = (st < nst) & (rb + rl < re);
             const int sl = rslot[in ? rl : 0];
-            v[j] = ld_stream(wr, (in & (sl >= 0) & cin) ? (uint32_t)sl * p.bundle_bytes + coff : kOob);
+            rv[u][j] = ld_stream(wr, (in & (sl >= 0) & cin) ? (uint32_t)sl * p.bundle_bytes + coff
+                                                            : kOob);
         }
-        const bool ain = (st < nst) & (rb + kFc2N * st + 8 * ca < R);
-        a = ld_shared(ar, ain ? ao + 2u * kFc2N * st : kOob);
+        if constexpr (FUSED) {
+            const bool pin = (st < nst) & (ft < p.B);
+#pragma unroll
+            for (int k = 0; k < kFc2FuseKS; ++k)
+                rp[u][k] = ld_shared(pr, (pin & (k < p.ks)) ? po + k * pstride + 4u * kFc2N * st
+                                                            : kOob);
+        } else {
+            const bool ain = (st < nst) & (rb + kFc2N * st + 8 * ca < R);
+            ra[u] = ld_shared(ar, ain ? ao + 2u * kFc2N * st : kOob);
+        }
     };
-    auto stage = [&](int st, int buf, const u32x4 (&v)[4], const u32x4 &a) {
+    auto stage = [&](int st, int buf, int u) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = ln + 16 * j;
-            *reinterpret_cast<u32x4 *>(&wl[buf][r * kWPitch + 8 * wl_chunk(r, lc)]) = v[j];
+            *reinterpret_cast<u32x4 *>(&wl[buf][r * kWPitch + 8 * wl_chunk(r, lc)]) = rv[u][j];
         }
-        // (a chunk across the list's end holds zeros past it: FC1 clears them)
-        *reinterpret_cast<u32x4 *>(&al[buf][(hl * kTile + ta) * kAPitch + 8 * ca]) = a;
+        if constexpr (FUSED) {
+            // slice sums in slice order, ReLU, zero past the list, hi + lo
+            f32x4v pv[kFc2FuseKS];
+#pragma unroll
+            for (int k = 0; k < kFc2FuseKS; ++k) pv[k] = __builtin_bit_cast(f32x4v, rp[u][k]);
+            h4 hv, lv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float sum = 0.0f;
+#pragma unroll
+                for (int k = 0; k < kFc2FuseKS; ++k)
+                    if (k < p.ks) sum += pv[k][e];
+                const bool live = rb + kFc2N * st + 4 * fc + e < R;
+                const float a = live ? fmaxf(sum, 0.0f) : 0.0f;
+                hv[e] = (_Float16)a;
+                lv[e] = (_Float16)(a - (float)hv[e]);
+            }
+            *reinterpret_cast<uint2 *>(&al[buf][ft * kAPitch + 4 * fc]) =
+                __builtin_bit_cast(uint2, hv);
+            *reinterpret_cast<uint2 *>(&al[buf][(kTile + ft) * kAPitch + 4 * fc]) =
+                __builtin_bit_cast(uint2, lv);
+        } else {
+            // (a chunk across the list's end holds zeros past it: FC1 clears them)
+            *reinterpret_cast<u32x4 *>(&al[buf][(hl * kTile + ta) * kAPitch + 8 * ca]) = ra[u];
+        }
     };
     const int tk = lane & 31, hh = lane >> 5;
     const int jw = kTile * wave + tk;                     // output column within the slice
     f32x16 acc = zero16();
     if (nst > 0) {
 #pragma unroll
-        for (int u = 0; u < kFc2Pre; ++u) load_step(u, rv[u], ra[u]);
+        for (int u = 0; u < kFc2Pre; ++u) load_step(u, u);
         // steps past nst stage zeros: the loop body stays free of branches, so
         // the ring registers carry over without copies that would wait
         // step st from ring slot u (LDS buffer u % 2); NEXT: request step st + kFc2Pre
         auto step = [&](int st, int u, bool next) {
             const int buf = u & 1;
-            stage(st, buf, rv[u], ra[u]);
-            if (next) load_step(st + kFc2Pre, rv[u], ra[u]);
+            stage(st, buf, u);
+            if (next) load_step(st + kFc2Pre, u);
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -953,6 +1004,17 @@ hipError_t launch_score_mm(const LayerView &L, int B, const Trace *tr, hipStream
 
 int fc1_slices(int d) { return (x16_pitch(d) + kSliceP * kPieceK - 1) / (kSliceP * kPieceK); }
 
+// FC2 forms FC1's activations itself (no FC1 finishing kernel) for plain
+// layers of at most kFc2FuseKS k slices, batches up to kFc2FuseB tokens and a
+// neuron set (not every neuron): its workgroups then re-read few partials.
+// Measured on the OPT-13B-shaped layer: B = 4 46.8 -> 45.3 us per step; at
+// B = 16 / 32, and for all 20480 rows, the partial reads cost more than the
+// finishing kernel saves.
+constexpr int kFc2FuseB = 4;
+bool fc2_fuses_fin(const LayerView &L, int B, bool all_rows) {
+    return !all_rows && !L.gated && fc1_slices(L.d) <= kFc2FuseKS && B <= kFc2FuseB;
+}
+
 hipError_t launch_fc1_mm(const LayerView &L, const float *x, int B, int mode, const int32_t *ids,
                          const int32_t *n_ids, bool x16, const Trace *tr, hipStream_t s) {
     const int dp = x16_pitch(L.d);
@@ -992,13 +1054,17 @@ hipError_t launch_fc1_mm(const LayerView &L, const float *x, int B, int mode, co
     const int gmin = (L.f + kFc1MaxRows - 1) / kFc1MaxRows;
     int GR = L.ncu / p.ks;
     GR = GR > gmin ? GR : gmin;
-    // the traced interval spans both kernels
+    // the traced interval spans both kernels (FC2 finishes FC1 itself when
+    // fc2_fuses_fin: one kernel)
+    const bool fused = fc2_fuses_fin(L, B, mode == 2);
     if (L.gated)
         hipExtLaunchKernelGGL(k_fc1_mm<true>, dim3(GR * p.ks), dim3(kThreads), 0, s,
                               ev_start(tr, ASF_K_FC1), nullptr, 0u, p);
     else
         hipExtLaunchKernelGGL(k_fc1_mm<false>, dim3(GR * p.ks), dim3(kThreads), 0, s,
-                              ev_start(tr, ASF_K_FC1), nullptr, 0u, p);
+                              ev_start(tr, ASF_K_FC1), fused ? ev_stop(tr, ASF_K_FC1) : nullptr,
+                              0u, p);
+    if (fused) return hipGetLastError();
     const int nfin = (B * (p.LR / 8) + 255) / 256;
     if (L.gated)
         hipExtLaunchKernelGGL(k_fc1_fin<true>, dim3(nfin), dim3(256), 0, s, nullptr,
@@ -1009,9 +1075,8 @@ hipError_t launch_fc1_mm(const LayerView &L, const float *x, int B, int mode, co
     return hipGetLastError();
 }
 
-hipError_t launch_fc2_mm(const LayerView &L, int B, bool listed, const float *resid, float *y,
+hipError_t launch_fc2_mm(const LayerView &L, int B, bool all_rows, const float *resid, float *y,
                          const Trace *tr, hipStream_t s) {
-    (void)listed;   // the batched list always carries its slots
     Fc2MmParams p;
     p.bundles = L.bundles;
     p.bundle_bytes = (uint32_t)(L.nmat * L.cd * 16);
@@ -1026,6 +1091,8 @@ hipError_t launch_fc2_mm(const LayerView &L, int B, bool listed, const float *re
     p.d = L.d;
     p.B = B;
     p.partial = L.partial;
+    p.part = L.fc1_part;
+    p.ks = fc1_slices(L.d);
     // one workgroup per CU covers the grid: groups = 256 / slices, at most 16
     // (at least 8: d <= 8192 gives at most 32 slices)
     const int nslice = (L.cd + 31) / 32;
@@ -1033,8 +1100,12 @@ hipError_t launch_fc2_mm(const LayerView &L, int B, bool listed, const float *re
     G = G < 1 ? 1 : (G > kGroups ? kGroups : G);
     p.groups = G;
     // the traced interval spans both kernels
-    hipExtLaunchKernelGGL(k_fc2_mm, dim3(nslice * G), dim3(kThreads), 0, s,
-                          ev_start(tr, ASF_K_FC2), nullptr, 0u, p);
+    if (fc2_fuses_fin(L, B, all_rows))
+        hipExtLaunchKernelGGL(k_fc2_mm<true>, dim3(nslice * G), dim3(kThreads), 0, s,
+                              ev_start(tr, ASF_K_FC2), nullptr, 0u, p);
+    else
+        hipExtLaunchKernelGGL(k_fc2_mm<false>, dim3(nslice * G), dim3(kThreads), 0, s,
+                              ev_start(tr, ASF_K_FC2), nullptr, 0u, p);
     const int n4 = B * (L.d / 4);
     hipExtLaunchKernelGGL(k_fc2_fin, dim3((n4 + 255) / 256), dim3(256), 0, s, nullptr,
                           ev_stop(tr, ASF_K_FC2), 0u, (const float *)L.partial, G, B, L.d, L.b2,

@@ -22,6 +22,10 @@ constexpr int kXchCopies = 16;    // copies of h exchanged between the owners (o
 
 // k slices of the batched FC1 (1024 k each)
 int fc1_slices(int d);
+struct LayerView;
+// the batched FC2 forms FC1's activations itself (no FC1 finishing kernel);
+// all_rows: FC1 ran over every neuron (the dense comparator)
+bool fc2_fuses_fin(const LayerView &L, int B, bool all_rows);
 
 // Row pitch (halfs) of the batched form's fp16 copy of x: d rounded up to the
 // 512 k that its FC1 takes per stage (the padding stays zero).
@@ -190,9 +194,10 @@ hipError_t launch_score(const LayerView &L, const float *x, int B, bool fc1, con
 hipError_t launch_fc1(const LayerView &L, const float *x, int B, int mode, const int32_t *ids,
                       const int32_t *n_ids, const Trace *tr, hipStream_t s);
 // FC2 over the owners' lists + per-slice reduction into y; listed: the
-// entries' slots come from the list (caller ids) rather than the owner bits
+// entries' slots come from the list (caller ids) rather than the owner bits;
+// all_rows: FC1 ran over every neuron (mode 2)
 hipError_t launch_fc2(const LayerView &L, int B, bool listed, const float *resid, float *y,
-                      const Trace *tr, hipStream_t s);
+                      const Trace *tr, hipStream_t s, bool all_rows = false);
 // single token, after launch_score with FC1 (or launch_step1): y = sum over
 // owners of their FC2 rows (part1) + b2 (+ resid); after launch_step1,
 // advance_epoch moves the exchange epoch on for the next step
@@ -233,7 +238,7 @@ hipError_t launch_score_mm(const LayerView &L, int B, const Trace *tr, hipStream
 // x16: take x as fp16 from L.x16 (written by launch_pred_mm for the same x)
 hipError_t launch_fc1_mm(const LayerView &L, const float *x, int B, int mode, const int32_t *ids,
                          const int32_t *n_ids, bool x16, const Trace *tr, hipStream_t s);
-hipError_t launch_fc2_mm(const LayerView &L, int B, bool listed, const float *resid, float *y,
+hipError_t launch_fc2_mm(const LayerView &L, int B, bool all_rows, const float *resid, float *y,
                          const Trace *tr, hipStream_t s);
 // attention-head predictor: layer 1 (the FFN predictor's kernels), layer 2 +
 // threshold into per-token head words, masks / ascending lists / counts

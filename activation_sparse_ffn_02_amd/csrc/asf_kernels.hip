@@ -2780,7 +2780,7 @@ hipError_t launch_rank_table(const uint32_t *counts, int f, int32_t *table, hipS
 }
 
 hipError_t launch_fc2(const LayerView &L, int B, bool listed, const float *resid, float *y,
-                      const Trace *tr, hipStream_t s) {
+                      const Trace *tr, hipStream_t s, bool all_rows) {
     Fc2Params p;
     p.bundles = (const u32x4 *)L.bundles;
     p.bstride = (size_t)L.nmat * L.cd;
@@ -2798,7 +2798,7 @@ hipError_t launch_fc2(const LayerView &L, int B, bool listed, const float *resid
     p.y = y;
     p.partial = L.partial;
     p.arrive = L.arrive;
-    if (B > 1 && L.wtype == ASF_F16) return launch_fc2_mm(L, B, listed, resid, y, tr, s);
+    if (B > 1 && L.wtype == ASF_F16) return launch_fc2_mm(L, B, all_rows, resid, y, tr, s);
     const dim3 grid(kSlices * kGroups), blk(kThreads);
     if (L.wtype == ASF_F16) {
         ASF_LAUNCH(ASF_K_FC2, (k_fc2<1, 1>), grid, blk, p);   // one token (batches: above)

@@ -411,10 +411,12 @@ asf_status asf_layer_set_trace(asf_layer *layer, void *const *events, int32_t n)
  * owner workgroup resident at once; the layer checks this at creation)
  * followed by the owner-row sum (FC2), else 3 (PRED_L1, SCORE_FC1, FC2).
  * B >= 2 traces four phases, PRED_L1, SCORE, FC1 and FC2: with fp32 weights
- * one launch each (4); with fp16 weights FC1 and FC2 are two launches each
- * (the stream kernel and its sum of k-slice or group partials) and so is
- * predictor layer 1 from 5 tokens on (6 or 7), a phase's events spanning
- * its launches.  A caller tracing kernels learns from it which ids a step
+ * one launch each (4); with fp16 weights FC2 is two launches (the stream
+ * kernel and its sum of group partials), FC1 too (its sum of k-slice
+ * partials) except on plain layers with d_model <= 5120 at B <= 4, where the
+ * FC2 stream kernel forms the activations itself, and predictor layer 1 is
+ * two from 5 tokens on (5 to 7 in all), a phase's events spanning its
+ * launches.  A caller tracing kernels learns from it which ids a step
  * uses.  0 for a null layer or B outside 1 .. max_batch. */
 int32_t asf_step_launches(const asf_layer *layer, int32_t B);
 

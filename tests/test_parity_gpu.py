@@ -133,7 +133,7 @@ def test_empty_set_and_residual_alias(orc):
     assert rel_l2(rd.cpu().numpy(), y_orc) <= TOL["f32"]
 
 
-@pytest.mark.parametrize("B,gated", [(6, False), (32, False), (5, True)])
+@pytest.mark.parametrize("B,gated", [(3, False), (6, False), (32, False), (5, True)])
 def test_batched_caller_lists(orc, B, gated):
     """Batches over a caller's list on the matrix-core kernels (k-sliced FC1,
     hi + lo FC2), at a d whose last k slice is partly past the row: out-of-
