@@ -15,7 +15,8 @@
 //   FC1                 the union list spread over row groups x k slices
 //                       (1024 k, x slice in LDS), whole-row 1 KiB gathers;
 //                       a second kernel adds the slices' partials, then the
-//                       activation
+//                       activation (small batches on plain layers: the FC2
+//                       kernel does that itself)
 //   FC2                 tokens x outputs, k = the group's listed neurons;
 //                       down segments go through LDS to be read transposed;
 //                       a second kernel adds the groups' partials
