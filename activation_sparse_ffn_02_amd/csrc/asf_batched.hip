@@ -353,11 +353,18 @@ __device__ __forceinline__ void tile_to_lds_x(float *dst, const f32x16 &acc, int
     }
 }
 
+struct NoHook {
+    __device__ void operator()() const {}
+};
+
 // The weight stream of workgroup slice ks over its nr rows (slots in rslot,
-// x slice in xs), in passes of NRT row tiles.
-template <bool GATED, int NRT, bool HILO = false>
+// x slice in xs), in passes of NRT row tiles.  `hook` runs once the first
+// stages are requested and before their first barrier: a caller whose x
+// slice is still in flight stores it to xs there.
+template <bool GATED, int NRT, bool HILO = false, class Hook = NoHook>
 __device__ __forceinline__ void fc1_stream(const Fc1MmParams &p, const u32x4 *xs, u32x4 *stg,
-                                           const int *rslot, int ks, int r0, int nr) {
+                                           const int *rslot, int ks, int r0, int nr,
+                                           Hook hook = {}) {
     using G1 = Fc1Geo<GATED, NRT, HILO>;
     constexpr int NM = G1::NM, SPP = G1::SPP, SP = G1::SP, XC = G1::XC, PRE = G1::PRE;
     constexpr int TT = kTile * kTile;
@@ -394,6 +401,7 @@ __device__ __forceinline__ void fc1_stream(const Fc1MmParams &p, const u32x4 *xs
     u32x4 ring[PRE][4];
 #pragma unroll
     for (int u = 0; u < PRE; ++u) issue(0, u, ring[u]);
+    hook();
     f32x16 acc[NRT * NM];
     float *red = reinterpret_cast<float *>(stg);
     auto pass = [&](int ps) {
@@ -655,15 +663,18 @@ __global__ __launch_bounds__(kThreads) void k_pred_rows(Fc1MmParams p, const flo
     // x slice: token xt, chunks xc + 16j (8 k each); tokens past B read zeros,
     // k past d reads x of the next token (against zero weights) or zeros
     const int xt = tid >> 4, xc = tid & 15;
-    {
-        const rsrc_t xr = buf_rsrc(x, (uint32_t)p.B * d * 4);
-        u32x4 v[kPieceC / 16][2];
+    const rsrc_t xr = buf_rsrc(x, (uint32_t)p.B * d * 4);
+    u32x4 v[kPieceC / 16][2];
 #pragma unroll
-        for (int j = 0; j < kPieceC / 16; ++j) {
-            const uint32_t o = (uint32_t)(xt * d + kPieceK * ks + 8 * (xc + 16 * j)) * 4;
-            v[j][0] = ld_shared(xr, o);
-            v[j][1] = ld_shared(xr, o + 16);
-        }
+    for (int j = 0; j < kPieceC / 16; ++j) {
+        const uint32_t o = (uint32_t)(xt * d + kPieceK * ks + 8 * (xc + 16 * j)) * 4;
+        v[j][0] = ld_shared(xr, o);
+        v[j][1] = ld_shared(xr, o + 16);
+    }
+    // x as hi + lo into LDS, run by the stream once its first stages are
+    // requested (the x loads were issued first, so waiting for them does not
+    // wait for the weights)
+    auto store_x = [&]() {
 #pragma unroll
         for (int j = 0; j < kPieceC / 16; ++j) {
             const int c = xc + 16 * j;
@@ -679,7 +690,7 @@ __global__ __launch_bounds__(kThreads) void k_pred_rows(Fc1MmParams p, const flo
             xs[xt * kPieceC + (c ^ (xt & 15))] = __builtin_bit_cast(u32x4, hi);
             xs[(kTile + xt) * kPieceC + (c ^ (xt & 15))] = __builtin_bit_cast(u32x4, lo);
         }
-    }
+    };
     const int H = p.f;
     const int R = (H + GR - 1) / GR;
     const int r0 = R * g;
@@ -687,8 +698,8 @@ __global__ __launch_bounds__(kThreads) void k_pred_rows(Fc1MmParams p, const flo
     for (int i = tid; i < nr; i += kThreads) rslot[i] = r0 + i;
     __syncthreads();
     if (nr <= 0) return;
-    if (nr <= 2 * kTile) fc1_stream<false, 2, true>(p, xs, stg, rslot, ks, r0, nr);
-    else fc1_stream<false, 4, true>(p, xs, stg, rslot, ks, r0, nr);
+    if (nr <= 2 * kTile) fc1_stream<false, 2, true>(p, xs, stg, rslot, ks, r0, nr, store_x);
+    else fc1_stream<false, 4, true>(p, xs, stg, rslot, ks, r0, nr, store_x);
 }
 
 // Element (t, r): the KS partial sums of row r for token t in slice order,
