@@ -345,6 +345,27 @@ def test_batched_matrix_core_path(orc, B, gated):
     _batched_check(orc, L, x, lay, "mm %s" % ("gated" if gated else "plain"))
 
 
+@pytest.mark.parametrize("gated", [False, True])
+def test_largest_d_model(orc, gated):
+    """d_model 8192, the largest an fp16 layer takes (16 KiB rows): the
+    one-token kernels at 16 chunks per lane, and the batched path at its
+    limits (8 FC1 k slices, 16 predictor k slices at B = 5, the vector
+    predictor at B = 3), with a ragged f."""
+    need_gpu()
+    _, sh = wl.CONFIGS["llama7b_gated_relu" if gated else "opt6.7b_ffn"]
+    d, f, H = 8192, 1500 + (37 if gated else 0), 512
+    L = wl.make_layer(wl.scaled_shape(sh, d, f, H), 1700 + f)
+    lay = asf().layer_from_numpy(L, max_batch=8)
+    x = wl.make_tokens(d, 3, 1800 + f)
+    worst = _run_tokens(orc, L, x, lay, "d8192 B=1%s" % (" gated" if gated else ""),
+                        check_dense=False)
+    assert worst <= TOL["f16"]
+    for B in (3, 5):
+        xb = wl.make_tokens(d, B, 1900 + B + f)
+        _batched_check(orc, L, xb, lay, "d8192 B=%d%s" % (B, " gated" if gated else ""),
+                       check_dense=(B == 5))
+
+
 @pytest.mark.parametrize("B", [2, 4, 5, 32])
 def test_batched_fp32_weights(orc, B):
     """fp32 weights with B >= 2 run the vector kernels (predictor layer 1
