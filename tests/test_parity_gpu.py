@@ -366,6 +366,26 @@ def test_largest_d_model(orc, gated):
                        check_dense=(B == 5))
 
 
+@pytest.mark.parametrize("gated", [False, True])
+def test_largest_d_model_fp32(orc, gated):
+    """d_model 4096 with fp32 weights (16 KiB rows, the largest fp32 layer):
+    one token at 16 chunks per lane and batches of 4 on the vector kernels,
+    plain and gated, ragged f."""
+    need_gpu()
+    import dataclasses
+    _, sh = wl.CONFIGS["tiny_f32"]
+    shp = dataclasses.replace(wl.scaled_shape(sh, 4096, 1200 + (29 if gated else 0), 256),
+                              gated=gated)
+    L = wl.make_layer(shp, 2100 + shp.f)
+    lay = asf().layer_from_numpy(L, max_batch=8)
+    x = wl.make_tokens(4096, 2, 2200 + shp.f)
+    worst = _run_tokens(orc, L, x, lay, "fp32 d4096 B=1%s" % (" gated" if gated else ""),
+                        check_dense=False)
+    assert worst <= TOL["f32"]
+    xb = wl.make_tokens(4096, 4, 2300 + shp.f)
+    _batched_check(orc, L, xb, lay, "fp32 d4096 B=4%s" % (" gated" if gated else ""))
+
+
 @pytest.mark.parametrize("B", [2, 4, 5, 32])
 def test_batched_fp32_weights(orc, B):
     """fp32 weights with B >= 2 run the vector kernels (predictor layer 1
