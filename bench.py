@@ -841,7 +841,7 @@ def bench_ffn_only(args, ring, Xd, Y, L, dense_ms, dense_bytes, torch, wl, dev, 
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the per-GPU kernel is the neuron-sharded design's shard); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)

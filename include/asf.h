@@ -48,11 +48,11 @@
  *
  * Debug build
  *   libasf_debug.so (the same kernels, the host API compiled with ASF_DEBUG)
- *   checks the device content this build takes on trust, and synchronises
+ *   checks the device content the release library takes on trust, and synchronises
  *   the stream to do so: asf_sparse_ffn returns ASF_ERR_ARG for a caller
  *   list with an id out of range or listed twice, or a count outside
  *   0 .. d_ffn; asf_create_layer for a neuron table that is not a
- *   permutation of 0 .. d_ffn-1.  asf_version names the build.
+ *   permutation of 0 .. d_ffn-1.  asf_version names the library variant.
  */
 #ifndef ASF_H
 #define ASF_H
